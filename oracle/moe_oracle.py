@@ -1,0 +1,344 @@
+"""CPU oracle for the routed mixture-of-experts forward.
+
+TEST INFRASTRUCTURE.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import or run this module; the product path
+(the HIP library and its Python binding) never does, and this module imports
+nothing from it.
+
+Plain numpy, float64 throughout, written from the step list on the pages:
+
+* "vLLM-Ascend Kimi K3 MoE Forward Insight" (page 1): Stage 2 "Select
+  Experts" names the native routing chain in order -- scoring, grouped top-k,
+  correction bias, top-k, renormalisation, routed scaling; "Runner
+  Initialization" names the routing knobs; Stage 4 "Dispatch, MLP, Combine"
+  (its mode table, AllGather row) says dispatch sorts tokens by expert and
+  returns per-expert token counts and combine restores token order and applies
+  the probabilities; the MLP is grouped gate/up matmul -> activation ->
+  grouped down matmul; Stage 6 says the expert-token list may be per-expert
+  counts or cumulative.
+* "vllm.models.kimi_k3.nvidia.latent_moe_runner" (page 2): ``_fused_forward``
+  runs the routed experts on the transformed (latent) input while the shared
+  expert sees the original hidden states; the tail reduces the latent, applies
+  RMSNorm, up-projects with ``up_proj.weight`` transposed and adds the shared
+  output (``_overlap_allreduce_tail``; ``_shard_up_proj_tail`` folds the same
+  sum into the GEMM's beta-add); at tensor-parallel size 1,
+  ``allreduce_norm_latent_out`` is the plain norm.
+* "Kimi K3 三平台架构对比解读" (page 3): the PyTorch fallback of the attention
+  residual spells out the RMS convention used here -- fp32 values times
+  rsqrt(mean(x^2) + eps).
+
+Readings where the pages are silent (each is listed in the design notes):
+selection keys are the raw logits when the score map is monotone and no
+correction bias or group sum is involved, else the score evaluated in float64
+plus the bias; ties go to the lower expert index and -0.0 equals +0.0; the
+group score is the group's best key or the sum of its two best keys; groups
+are contiguous; renormalisation divides the unbiased scores of the selected
+experts by their sum and routed scaling multiplies afterwards; combine weights
+are applied to expert outputs, never to inputs; rows of w13 are gate then up;
+rows inside an expert's segment keep ascending pair order p = t*k + j.
+
+Parity pins: every function here is checked in the CPU test suite against
+something other than itself (closed forms, brute force over all subsets,
+textbook special cases, a dense every-expert reference written with torch).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+f64 = np.float64
+
+
+@dataclass(frozen=True)
+class RouteCfg:
+    """Routing settings copied from the model (page 1, "Runner Initialization")."""
+
+    num_experts: int
+    top_k: int
+    num_groups: int = 1
+    topk_group: int = 1
+    score: str = "softmax"        # softmax | sigmoid | sqrtsoftplus
+    group_score: str = "max"      # max | top2sum
+    renormalize: bool = True
+    routed_scaling: float = 1.0
+
+
+# ---------------------------------------------------------------- scoring ---
+
+def softplus(v: np.ndarray) -> np.ndarray:
+    """ln(1 + e^v) in float64, written so that it does not overflow."""
+    v = np.asarray(v, dtype=f64)
+    return np.maximum(v, 0.0) + np.log1p(np.exp(-np.abs(v)))
+
+
+def score(logits: np.ndarray, fn: str) -> np.ndarray:
+    """Scores s[T,E] from logits (page 1, Stage 2: softmax, sigmoid or
+    square-root-softplus scoring), evaluated in float64."""
+    l = np.asarray(logits, dtype=f64)
+    if fn == "softmax":
+        m = l.max(axis=-1, keepdims=True)
+        e = np.exp(l - m)
+        return e / e.sum(axis=-1, keepdims=True)
+    if fn == "sigmoid":
+        return 1.0 / (1.0 + np.exp(-l))
+    if fn == "sqrtsoftplus":
+        return np.sqrt(softplus(l))
+    raise ValueError(fn)
+
+
+def keys_are_raw_logits(cfg: RouteCfg, has_bias: bool) -> bool:
+    """True when ordering by score equals ordering by the raw logit.
+
+    All three score maps are strictly increasing in the logit, and a group's
+    best key is the image of its best logit, so without a correction bias and
+    without a two-key group sum the exact ordering is the ordering of the fp32
+    logits themselves (no rounding of exp/log can create false ties)."""
+    return (not has_bias) and (cfg.num_groups == 1 or cfg.group_score == "max")
+
+
+def selection_keys(logits: np.ndarray, cfg: RouteCfg,
+                   corr_bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """Per-expert selection keys kappa[T,E] (float64).
+
+    The correction bias enters selection only (page 1, Stage 2 lists it
+    between grouped top-k and the final top-k; renormalisation later uses the
+    unbiased scores)."""
+    l = np.asarray(logits, dtype=f64)
+    if keys_are_raw_logits(cfg, corr_bias is not None):
+        return l.copy()
+    s = score(l, cfg.score)
+    if corr_bias is not None:
+        s = s + np.asarray(corr_bias, dtype=f64)[None, :]
+    return s
+
+
+# -------------------------------------------------------------- selection ---
+
+def _order_desc(keys_row: np.ndarray) -> np.ndarray:
+    """Indices sorted by key descending, ties to the lower index.
+
+    numpy compares with '<', so -0.0 and +0.0 are equal keys."""
+    idx = np.arange(keys_row.shape[0])
+    return np.lexsort((idx, -keys_row))
+
+
+def group_scores(keys: np.ndarray, cfg: RouteCfg) -> np.ndarray:
+    """Group score g[T,G] over contiguous groups of E/G experts: the group's best
+    key ("max") or the sum of its two best keys ("top2sum")."""
+    T, E = keys.shape
+    G = cfg.num_groups
+    kg = keys.reshape(T, G, E // G)
+    if cfg.group_score == "max":
+        return kg.max(axis=-1)
+    if cfg.group_score == "top2sum":
+        srt = np.sort(kg, axis=-1)
+        return srt[..., -1] + srt[..., -2]
+    raise ValueError(cfg.group_score)
+
+
+def select_experts(keys: np.ndarray, cfg: RouteCfg) -> np.ndarray:
+    """Grouped top-k (page 1, Stage 2): keep the ``topk_group`` best groups,
+    then the k best keys among their experts, in descending key order."""
+    T, E = keys.shape
+    k = cfg.top_k
+    ids = np.empty((T, k), dtype=np.int64)
+    allowed = np.ones((T, E), dtype=bool)
+    if cfg.num_groups > 1:
+        gs = group_scores(keys, cfg)
+        per = E // cfg.num_groups
+        for t in range(T):
+            keep = _order_desc(gs[t])[: cfg.topk_group]
+            mask = np.zeros(cfg.num_groups, dtype=bool)
+            mask[keep] = True
+            allowed[t] = np.repeat(mask, per)
+    for t in range(T):
+        cand = np.nonzero(allowed[t])[0]
+        order = cand[_order_desc(keys[t, cand])]
+        ids[t] = order[:k]
+    return ids
+
+
+def route_weights(logits: np.ndarray, ids: np.ndarray, cfg: RouteCfg) -> np.ndarray:
+    """Combine weights w[T,k] (float64): unbiased scores of the chosen experts,
+    renormalised to sum 1 if asked, then times the routed scaling factor
+    (page 1, Stage 2 order: renormalisation, then routed scaling)."""
+    s = score(logits, cfg.score)
+    w = np.take_along_axis(s, ids, axis=1)
+    if cfg.renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return w * f64(cfg.routed_scaling)
+
+
+def route(logits: np.ndarray, cfg: RouteCfg, corr_bias: Optional[np.ndarray] = None):
+    """Scoring -> keys -> grouped top-k -> weights.  Returns (ids, weights, keys)."""
+    keys = selection_keys(logits, cfg, corr_bias)
+    ids = select_experts(keys, cfg)
+    w = route_weights(logits, ids, cfg)
+    return ids, w, keys
+
+
+# ---------------------------------------------------------------- permute ---
+
+def permute(ids: np.ndarray, num_experts: int):
+    """Sort (token, slot) pairs by expert (page 1, Stage 4, AllGather dispatch:
+    sort tokens by expert and return per-expert token counts).
+
+    Pairs are p = t*k + j.  Returns counts[E], offsets[E+1] (exclusive scan --
+    the cumulative form of the expert-token list, page 1 Stage 6),
+    row_to_pair[P] (stable: ascending p within an expert) and pair_to_row[P]
+    (its inverse)."""
+    flat = np.asarray(ids).reshape(-1)
+    counts = np.bincount(flat, minlength=num_experts).astype(np.int64)
+    offsets = np.zeros(num_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    row_to_pair = np.argsort(flat, kind="stable")
+    pair_to_row = np.empty_like(row_to_pair)
+    pair_to_row[row_to_pair] = np.arange(flat.shape[0])
+    return counts, offsets, row_to_pair, pair_to_row
+
+
+# ----------------------------------------------------------------- experts ---
+
+def silu(v: np.ndarray) -> np.ndarray:
+    return v / (1.0 + np.exp(-v))
+
+
+def expert_mlp(X: np.ndarray, w13_e: np.ndarray, w2_e: np.ndarray) -> np.ndarray:
+    """One expert (page 1, Stage 4: gate/up matmul -> SwiGLU -> down matmul).
+
+    w13_e is [2I, D] with gate rows first, then up rows; w2_e is [D, I]."""
+    w13_e = np.asarray(w13_e, dtype=f64)
+    w2_e = np.asarray(w2_e, dtype=f64)
+    I = w2_e.shape[1]
+    gu = np.asarray(X, dtype=f64) @ w13_e.T
+    h = silu(gu[:, :I]) * gu[:, I:]
+    return h @ w2_e.T
+
+
+def run_experts(xin: np.ndarray, k: int, offsets: np.ndarray, row_to_pair: np.ndarray,
+                w13, w2) -> np.ndarray:
+    """Grouped expert MLP over the expert-sorted rows.  Row r of expert e reads
+    token row_to_pair[r] // k.  ``w13[e]`` / ``w2[e]`` may be any indexable
+    that yields expert e's matrices.  Returns y_rows[P, D] (float64)."""
+    xin = np.asarray(xin)
+    P = row_to_pair.shape[0]
+    E = offsets.shape[0] - 1
+    D = xin.shape[1]
+    y = np.zeros((P, D), dtype=f64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        X = np.asarray(xin[row_to_pair[a:b] // k], dtype=f64)
+        y[a:b] = expert_mlp(X, w13[e], w2[e])
+    return y
+
+
+def combine(y_rows: np.ndarray, pair_to_row: np.ndarray, weights: np.ndarray) -> np.ndarray:
+    """Back to token order with the routing weights applied (page 1, Stage 4,
+    AllGather combine): out[t] = sum_j w[t,j] * y_rows[pair_to_row[t*k+j]]."""
+    T, k = weights.shape
+    rows = y_rows[pair_to_row.reshape(T, k)]          # [T, k, D]
+    return np.einsum("tk,tkd->td", np.asarray(weights, dtype=f64), rows)
+
+
+# ------------------------------------------------------ latent + shared tail ---
+
+def rmsnorm(v: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """v * rsqrt(mean(v^2) + eps) * gamma (page 3, fp32 RMS convention of the
+    attention-residual fallback; page 2 passes a zero weight bias, i.e. the
+    standard gamma, not 1 + gamma)."""
+    v = np.asarray(v, dtype=f64)
+    inv = 1.0 / np.sqrt((v * v).mean(axis=-1, keepdims=True) + eps)
+    return v * inv * np.asarray(gamma, dtype=f64)[None, :]
+
+
+def shared_expert(x: np.ndarray, w13_sh: np.ndarray, w2_sh: np.ndarray) -> np.ndarray:
+    """Shared SwiGLU expert on the original hidden states (page 2,
+    ``_fused_forward``: the shared expert receives the untransformed input)."""
+    return expert_mlp(x, w13_sh, w2_sh)
+
+
+# ---------------------------------------------------------------- forward ---
+
+def router_logits(x: np.ndarray, w_router: np.ndarray,
+                  router_bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """l = x . W_r^T (+ bias row), float64."""
+    l = np.asarray(x, dtype=f64) @ np.asarray(w_router, dtype=f64).T
+    if router_bias is not None:
+        l = l + np.asarray(router_bias, dtype=f64)[None, :]
+    return l
+
+
+def forward(x, cfg: RouteCfg, w13, w2, *, w_router=None, router_bias=None,
+            logits=None, corr_bias=None, latent=None, shared=None) -> dict:
+    """The whole routed-MoE forward as a chain of the steps above.
+
+    ``logits`` (if given) replaces the router product, as in the runner's
+    ``forward(hidden_states, router_logits, ...)`` signature (page 2).
+    ``latent`` = dict(w_down[L,H], gamma[L], w_up[H,L], eps) and
+    ``shared`` = dict(w13[2Is,H], w2[H,Is]) add the latent transform and tail
+    and the shared expert (page 2).  Returns every intermediate."""
+    x64 = np.asarray(x, dtype=f64)
+    if logits is None:
+        logits = router_logits(x64, w_router, router_bias)
+    logits = np.asarray(logits, dtype=f64)
+    k = cfg.top_k
+    ids, w, keys = route(logits, cfg, corr_bias)
+    counts, offsets, r2p, p2r = permute(ids, cfg.num_experts)
+    xin = x64
+    if latent is not None:
+        xin = x64 @ np.asarray(latent["w_down"], dtype=f64).T
+    y_rows = run_experts(xin, k, offsets, r2p, w13, w2)
+    routed = combine(y_rows, p2r, w)
+    res = dict(logits=logits, ids=ids, weights=w, keys=keys, counts=counts,
+               offsets=offsets, row_to_pair=r2p, pair_to_row=p2r, y_rows=y_rows,
+               routed=routed, xin=xin)
+    sh = shared_expert(x64, shared["w13"], shared["w2"]) if shared is not None else None
+    if latent is not None:
+        r = rmsnorm(routed, latent["gamma"], latent["eps"])
+        out = r @ np.asarray(latent["w_up"], dtype=f64).T
+        if sh is not None:
+            out = out + sh
+        res["normed"] = r
+    else:
+        out = routed if sh is None else routed + sh
+    res["shared"] = sh
+    res["out"] = out
+    return res
+
+
+def forward_tokens(tokens, x, cfg: RouteCfg, w13, w2, *, w_router=None, router_bias=None,
+                   logits=None, corr_bias=None, latent=None, shared=None) -> dict:
+    """The same layer evaluated token by token for a list of tokens, without
+    the permute (tokens are independent in a routed MoE).  Used to check
+    sampled outputs of very large layers, where ``w13[e]``/``w2[e]`` fetch one
+    expert at a time."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    xs = np.asarray(x[tokens], dtype=f64)
+    if logits is None:
+        lg = router_logits(xs, w_router, router_bias)
+    else:
+        lg = np.asarray(logits, dtype=f64)[tokens]
+    ids, w, keys = route(lg, cfg, corr_bias)
+    xin = xs if latent is None else xs @ np.asarray(latent["w_down"], dtype=f64).T
+    routed = np.zeros((tokens.shape[0], xin.shape[1]), dtype=f64)
+    cache = {}
+    for i in range(tokens.shape[0]):
+        for j in range(cfg.top_k):
+            e = int(ids[i, j])
+            if e not in cache:
+                cache[e] = (np.asarray(w13[e], dtype=f64), np.asarray(w2[e], dtype=f64))
+            y = expert_mlp(xin[i:i + 1], *cache[e])[0]
+            routed[i] += w[i, j] * y
+    sh = shared_expert(xs, shared["w13"], shared["w2"]) if shared is not None else None
+    if latent is not None:
+        out = rmsnorm(routed, latent["gamma"], latent["eps"]) @ \
+            np.asarray(latent["w_up"], dtype=f64).T
+        if sh is not None:
+            out = out + sh
+    else:
+        out = routed if sh is None else routed + sh
+    return dict(logits=lg, ids=ids, weights=w, keys=keys, routed=routed, out=out)

@@ -1,0 +1,192 @@
+"""Seeded synthetic inputs for the routed mixture-of-experts workloads.
+
+This module only draws random tensors of the right shapes, dtypes and value
+distributions.  It holds none of the layer's arithmetic (no router product, no
+scoring, no selection, no expert math), so that both the HIP path and the CPU
+oracle can take their inputs from it without sharing any computation.
+
+The workloads are the five shapes the routed-MoE forward is measured on:
+a tiny fp32 layer, a decode-sized and a prefill-sized bf16 layer with 384
+experts (top-8), a grouped top-k layer with square-root-softplus scoring and a
+selection-only correction bias, and a latent layer (down-projection, latent
+experts, RMSNorm, up-projection) with a shared expert.  The routing knobs are
+the ones the vLLM-Ascend page lists when the runner copies the model's routing
+configuration ("Runner Initialization": grouped top-k settings, renormalisation,
+scoring function, correction bias, routed scaling).
+
+Recipe (one seed per tensor, base seed 0):
+  x:0  router weight:1  w13:2  w2:3  router bias row:4  correction bias:5
+  down-proj:6  up-proj:7  shared w13:8  shared w2:9  calibration logits:10
+  expert-rank permutation:11  RMSNorm gamma:12
+Every weight is N(0, std^2) with std = 1/sqrt(fan_in) (fan_in = the input width
+of that matrix) unless the workload fixes it (the tiny layer's router: 0.02).
+Activations x ~ N(0, 1).  bf16 tensors are drawn in fp32 and rounded to nearest
+even.  The prefill layer's router bias row makes the expert load follow a
+Zipf(s) law over a seeded random ranking of the experts; it is calibrated on
+simulated i.i.d. N(0,1) logits (a stand-in for the router's output, whose
+per-expert logits are close to independent unit normals at this init).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import torch
+
+SEED_X, SEED_WR, SEED_W13, SEED_W2, SEED_BROW, SEED_CORR = 0, 1, 2, 3, 4, 5
+SEED_WDN, SEED_WUP, SEED_W13SH, SEED_W2SH, SEED_XCAL, SEED_PERM = 6, 7, 8, 9, 10, 11
+SEED_GAMMA = 12
+
+
+@dataclass(frozen=True)
+class Workload:
+    """Shapes and routing settings of one routed-MoE layer."""
+
+    name: str
+    T: int                      # tokens
+    H: int                      # hidden width
+    E: int                      # routed experts
+    k: int                      # experts per token
+    I: int                      # expert SwiGLU intermediate width
+    dtype: str = "bf16"         # "bf16" or "f32"
+    score: str = "softmax"      # "softmax" | "sigmoid" | "sqrtsoftplus"
+    num_groups: int = 1
+    topk_group: int = 1
+    group_score: str = "max"    # "max" | "top2sum"
+    renormalize: bool = True
+    routed_scaling: float = 1.0
+    router_std: Optional[float] = None   # None: 1/sqrt(H)
+    zipf_s: Optional[float] = None       # router bias row giving Zipf(s) load
+    corr_bias: Optional[float] = None    # correction bias ~ U(-a, a)
+    latent: Optional[int] = None         # latent width L (experts run on it)
+    shared_inter: Optional[int] = None   # shared expert intermediate width
+    rms_eps: float = 1e-6
+    gamma_std: float = 0.0               # RMSNorm gamma = 1 + N(0, gamma_std^2)
+
+    @property
+    def D(self) -> int:
+        """Width the routed experts read and write (latent if present)."""
+        return self.latent if self.latent else self.H
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", T=64, H=256, E=8, k=2, I=128, dtype="f32",
+                          router_std=0.02),
+    "decode": Workload("decode", T=128, H=7168, E=384, k=8, I=2048,
+                       routed_scaling=2.5),
+    "prefill_zipf": Workload("prefill_zipf", T=8192, H=7168, E=384, k=8, I=2048,
+                             zipf_s=1.1),
+    "grouped_sqrtsoftplus": Workload("grouped_sqrtsoftplus", T=4096, H=4096, E=256,
+                                     k=8, I=1536, score="sqrtsoftplus",
+                                     num_groups=8, topk_group=4,
+                                     group_score="top2sum", corr_bias=0.1),
+    "latent_shared": Workload("latent_shared", T=2048, H=7168, E=256, k=8, I=1024,
+                              latent=2048, shared_inter=2048),
+}
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def normal(shape, std: float, seed: int, dtype, device, chunk_rows: int = 0) -> torch.Tensor:
+    """N(0, std^2) drawn in fp32 and rounded to ``dtype``.
+
+    Large tensors are drawn in slabs along dim 0 (``chunk_rows`` rows at a time)
+    from one generator stream, so a 34 GB weight never needs an fp32 copy.
+    """
+    g = _gen(seed, device)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    n0 = shape[0]
+    step = chunk_rows if chunk_rows > 0 else n0
+    for s in range(0, n0, step):
+        e = min(n0, s + step)
+        slab = torch.randn((e - s,) + tuple(shape[1:]), generator=g, device=device,
+                           dtype=torch.float32)
+        if std != 1.0:
+            slab.mul_(std)
+        out[s:e].copy_(slab)
+        del slab
+    return out
+
+
+def uniform(shape, a: float, seed: int, device) -> torch.Tensor:
+    """U(-a, a) in fp32."""
+    g = _gen(seed, device)
+    return (torch.rand(shape, generator=g, device=device, dtype=torch.float32) * 2 - 1) * a
+
+
+def zipf_router_bias(E: int, k: int, T: int, s: float, iters: int = 60) -> torch.Tensor:
+    """Router bias row b[E] (fp32, CPU) that gives a Zipf(s) expert load.
+
+    Expert e gets rank r_e = 1 + perm[e] (seeded permutation, so hot experts are
+    scattered) and target load tau_e = min(T*k*r_e^-s / H_{E,s}, 0.999*T).
+    The bias is fitted on simulated i.i.d. N(0,1) logits with a damped
+    log-count update; it is input construction only.
+    """
+    perm = torch.randperm(E, generator=_gen(SEED_PERM, "cpu"))
+    r = (perm + 1).to(torch.float64)
+    harm = float((torch.arange(1, E + 1, dtype=torch.float64) ** (-s)).sum())
+    tau = torch.clamp(T * k * r ** (-s) / harm, max=0.999 * T)
+    b = -0.55 * torch.log(r)
+    sim = torch.randn((T, E), generator=_gen(SEED_XCAL, "cpu"), dtype=torch.float64)
+    for _ in range(iters):
+        top = torch.topk(sim + b, k, dim=1).indices
+        c = torch.bincount(top.reshape(-1), minlength=E).to(torch.float64)
+        b = b + 0.5 * (torch.log(tau) - torch.log(c + 0.5))
+        b = b - b.mean()
+    return b.to(torch.float32)
+
+
+def make_inputs(w: Workload, device="cpu", chunk_rows: int = 8) -> dict:
+    """All tensors of workload ``w`` on ``device``.
+
+    Keys: x[T,H], w_router[E,H], router_bias[E] (fp32) or None,
+    corr_bias[E] (fp32) or None, w13[E,2I,D], w2[E,D,I], and for the latent
+    layer w_down[L,H], gamma[L], w_up[H,L]; for a shared expert
+    w13_sh[2Is,H], w2_sh[H,Is].  Weights are row-major [out, in].
+    """
+    dt = w.torch_dtype
+    D = w.D
+    inp = {}
+    inp["x"] = normal((w.T, w.H), 1.0, SEED_X, dt, device)
+    rstd = w.router_std if w.router_std is not None else 1.0 / math.sqrt(w.H)
+    inp["w_router"] = normal((w.E, w.H), rstd, SEED_WR, dt, device)
+    inp["router_bias"] = (zipf_router_bias(w.E, w.k, w.T, w.zipf_s).to(device)
+                          if w.zipf_s else None)
+    inp["corr_bias"] = (uniform((w.E,), w.corr_bias, SEED_CORR, device)
+                        if w.corr_bias else None)
+    inp["w13"] = normal((w.E, 2 * w.I, D), 1.0 / math.sqrt(D), SEED_W13, dt, device,
+                        chunk_rows=chunk_rows)
+    inp["w2"] = normal((w.E, D, w.I), 1.0 / math.sqrt(w.I), SEED_W2, dt, device,
+                       chunk_rows=chunk_rows)
+    if w.latent:
+        L = w.latent
+        inp["w_down"] = normal((L, w.H), 1.0 / math.sqrt(w.H), SEED_WDN, dt, device)
+        inp["w_up"] = normal((w.H, L), 1.0 / math.sqrt(L), SEED_WUP, dt, device)
+        if w.gamma_std > 0:
+            g = normal((L,), w.gamma_std, SEED_GAMMA, torch.float32, device) + 1.0
+            inp["gamma"] = g.to(dt)
+        else:
+            inp["gamma"] = torch.ones((L,), dtype=dt, device=device)
+    if w.shared_inter:
+        Is = w.shared_inter
+        inp["w13_sh"] = normal((2 * Is, w.H), 1.0 / math.sqrt(w.H), SEED_W13SH, dt, device)
+        inp["w2_sh"] = normal((w.H, Is), 1.0 / math.sqrt(Is), SEED_W2SH, dt, device)
+    return inp
+
+
+def random_logits(T: int, E: int, seed: int = 0, std: float = 1.0, device="cpu") -> torch.Tensor:
+    """Plain fp32 N(0, std^2) logits for exercising the routing stage alone."""
+    return torch.randn((T, E), generator=_gen(seed, device), device=device,
+                       dtype=torch.float32) * std

@@ -1,0 +1,352 @@
+"""Pins the CPU oracle to things other than itself.
+
+Hand-derived cases (tests/golden), closed forms of the score maps, brute force
+over every subset for top-k and grouped top-k, the textbook dense SwiGLU MLP
+(written with torch, not numpy), a dense every-expert reference for the whole
+layer, and permutation invariants.  Each pin is chosen so that a plausible
+slip in the oracle (dropped bias, wrong tie order, swapped gate/up, transposed
+weight, weights applied before the experts, a non-stable permute) fails it.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "route_cases.json")))
+
+
+def _cfg(d):
+    return O.RouteCfg(num_experts=d["num_experts"], top_k=d["top_k"],
+                      num_groups=d.get("num_groups", 1), topk_group=d.get("topk_group", 1),
+                      score=d.get("score", "softmax"), group_score=d.get("group_score", "max"),
+                      renormalize=d.get("renormalize", True),
+                      routed_scaling=d.get("routed_scaling", 1.0))
+
+
+# ------------------------------------------------------------ golden cases ---
+
+@pytest.mark.parametrize("case", GOLD["cases"], ids=[c["name"] for c in GOLD["cases"]])
+def test_golden_route(case):
+    cfg = _cfg(case["cfg"])
+    logits = np.array(case["logits"], dtype=np.float32)
+    bias = None if case["bias"] is None else np.array(case["bias"], dtype=np.float32)
+    ids, w, _ = O.route(logits, cfg, bias)
+    assert ids.tolist() == case["ids"]
+    np.testing.assert_allclose(w, np.array(case["weights"]), rtol=0, atol=1e-6)
+
+
+def test_golden_permute():
+    g = GOLD["permute"]
+    c, off, r2p, p2r = O.permute(np.array(g["ids"]), g["num_experts"])
+    assert c.tolist() == g["counts"]
+    assert off.tolist() == g["offsets"]
+    assert r2p.tolist() == g["row_to_pair"]
+    assert p2r.tolist() == g["pair_to_row"]
+
+
+def test_golden_expert_mlp():
+    g = GOLD["expert_mlp"]
+    y = O.expert_mlp(np.array(g["x"]), np.array(g["w13"]), np.array(g["w2"]))
+    np.testing.assert_allclose(y, np.array(g["y"]), rtol=1e-14)
+
+
+def test_golden_rmsnorm():
+    g = GOLD["rmsnorm"]
+    out = O.rmsnorm(np.array(g["v"]), np.array(g["gamma"]), g["eps"])
+    np.testing.assert_allclose(out, np.array(g["out"]), rtol=1e-14)
+
+
+# ------------------------------------------------------------ closed forms ---
+
+def test_sqrtsoftplus_closed_forms():
+    assert O.score(np.array([[0.0]]), "sqrtsoftplus")[0, 0] == pytest.approx(
+        math.sqrt(math.log(2.0)), rel=1e-15)
+    v = np.linspace(-30, 30, 601)
+    # softplus(v) - softplus(-v) = v
+    np.testing.assert_allclose(O.softplus(v) - O.softplus(-v), v, atol=1e-12)
+    # large v: sqrt(softplus(v)) -> sqrt(v); very negative: -> exp(v/2)
+    big = np.array([[40.0, 100.0]])
+    np.testing.assert_allclose(O.score(big, "sqrtsoftplus"), np.sqrt(big), rtol=1e-15)
+    neg = np.array([[-40.0]])
+    np.testing.assert_allclose(O.score(neg, "sqrtsoftplus"), np.exp(neg / 2), rtol=1e-12)
+
+
+def test_sigmoid_softmax_closed_forms():
+    np.testing.assert_allclose(O.score(np.array([[math.log(3)]]), "sigmoid"), [[0.75]], rtol=1e-15)
+    np.testing.assert_allclose(O.score(np.array([[0.0, math.log(2)]]), "softmax"),
+                               [[1 / 3, 2 / 3]], rtol=1e-15)
+    # softmax is shift invariant and sums to 1
+    rng = np.random.default_rng(0)
+    l = rng.normal(size=(5, 9)) * 30
+    s = O.score(l, "softmax")
+    np.testing.assert_allclose(s.sum(1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(O.score(l + 123.0, "softmax"), s, rtol=1e-12)
+
+
+# ----------------------------------------------------- brute-force selection ---
+
+def _dominates(ka, a, kb, b):
+    """a ranks before b: larger key, or equal key and lower index."""
+    return ka > kb or (ka == kb and a < b)
+
+
+def _brute_topk(keys_row, allowed, k):
+    """The unique k-subset of allowed experts in which every member ranks
+    before every non-member, found by trying all subsets."""
+    cand = [e for e in range(len(keys_row)) if allowed[e]]
+    hits = []
+    for sub in itertools.combinations(cand, k):
+        rest = [e for e in cand if e not in sub]
+        if all(_dominates(keys_row[a], a, keys_row[b], b) for a in sub for b in rest):
+            hits.append(set(sub))
+    assert len(hits) == 1
+    return hits[0]
+
+
+def _brute_groups(keys_row, G, topk_group, rule):
+    per = len(keys_row) // G
+    gs = []
+    for g in range(G):
+        vals = sorted(float(v) for v in keys_row[g * per:(g + 1) * per])
+        gs.append(vals[-1] if rule == "max" else vals[-1] + vals[-2])
+    return _brute_topk(gs, [True] * G, topk_group), per
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("score", ["softmax", "sigmoid", "sqrtsoftplus"])
+def test_topk_brute_force_with_ties(seed, score):
+    rng = np.random.default_rng(seed)
+    E, k, T = 9, 3, 25
+    # few distinct values so ties are common; include both signed zeros
+    vals = np.array([-1.0, -0.0, 0.0, 0.5, 2.0], dtype=np.float32)
+    logits = vals[rng.integers(0, len(vals), size=(T, E))]
+    cfg = O.RouteCfg(num_experts=E, top_k=k, score=score)
+    ids, w, keys = O.route(logits, cfg)
+    for t in range(T):
+        assert set(ids[t].tolist()) == _brute_topk(keys[t], [True] * E, k)
+        for j in range(k - 1):
+            assert _dominates(keys[t, ids[t, j]], ids[t, j], keys[t, ids[t, j + 1]], ids[t, j + 1])
+
+
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("rule", ["max", "top2sum"])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_grouped_topk_brute_force(seed, rule, with_bias):
+    rng = np.random.default_rng(100 + seed)
+    E, G, tg, k, T = 12, 4, 2, 3, 20
+    logits = rng.normal(size=(T, E)).astype(np.float32)
+    logits[:, 5] = logits[:, 7]   # a cross-group tie
+    bias = rng.uniform(-0.1, 0.1, size=E).astype(np.float32) if with_bias else None
+    cfg = O.RouteCfg(num_experts=E, top_k=k, num_groups=G, topk_group=tg,
+                     score="sqrtsoftplus", group_score=rule)
+    ids, w, keys = O.route(logits, cfg, bias)
+    # keys themselves: raw logits only in the monotone case, else score + bias
+    if bias is None and rule == "max":
+        np.testing.assert_array_equal(keys, logits.astype(np.float64))
+    else:
+        sp = np.log1p(np.exp(logits.astype(np.float64)))
+        ref = np.sqrt(sp) + (0 if bias is None else bias.astype(np.float64))
+        np.testing.assert_allclose(keys, ref, rtol=1e-13)
+    for t in range(T):
+        groups, per = _brute_groups(keys[t], G, tg, rule)
+        allowed = [e // per in groups for e in range(E)]
+        assert set(ids[t].tolist()) == _brute_topk(keys[t], allowed, k)
+        assert all(allowed[e] for e in ids[t])
+
+
+def test_correction_bias_only_in_selection():
+    rng = np.random.default_rng(7)
+    E, k = 16, 4
+    logits = rng.normal(size=(50, E)).astype(np.float32)
+    bias = rng.uniform(-0.3, 0.3, size=E).astype(np.float32)
+    cfg = O.RouteCfg(num_experts=E, top_k=k, score="sigmoid", renormalize=True)
+    ids, w, _ = O.route(logits, cfg, bias)
+    s = 1 / (1 + np.exp(-logits.astype(np.float64)))
+    sel = np.take_along_axis(s, ids, 1)
+    np.testing.assert_allclose(w, sel / sel.sum(1, keepdims=True), rtol=1e-14)
+    # the bias must change at least one choice on this data
+    ids0, _, _ = O.route(logits, cfg, None)
+    assert (np.sort(ids0, 1) != np.sort(ids, 1)).any()
+
+
+def test_weights_closed_forms():
+    from scipy.special import softmax as sp_softmax
+    rng = np.random.default_rng(3)
+    E, k = 10, 4
+    logits = rng.normal(size=(30, E)).astype(np.float32)
+    cfg = O.RouteCfg(num_experts=E, top_k=k, routed_scaling=2.5)
+    ids, w, _ = O.route(logits, cfg)
+    sel = np.take_along_axis(logits.astype(np.float64), ids, 1)
+    np.testing.assert_allclose(w, 2.5 * sp_softmax(sel, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(w.sum(1), 2.5, rtol=1e-14)
+    # k = E with renormalisation is the full softmax, in descending order
+    cfgE = O.RouteCfg(num_experts=E, top_k=E)
+    idsE, wE, _ = O.route(logits, cfgE)
+    full = sp_softmax(logits.astype(np.float64), axis=1)
+    np.testing.assert_allclose(wE, np.take_along_axis(full, idsE, 1), rtol=1e-13)
+    # without renormalisation the softmax keeps the full-row partition
+    cfgN = O.RouteCfg(num_experts=E, top_k=k, renormalize=False)
+    idsN, wN, _ = O.route(logits, cfgN)
+    np.testing.assert_allclose(wN, np.take_along_axis(full, idsN, 1), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- permute ---
+
+@pytest.mark.parametrize("seed", range(4))
+def test_permute_invariants(seed):
+    rng = np.random.default_rng(seed)
+    T, k, E = 37, 3, 7
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+    c, off, r2p, p2r = O.permute(ids, E)
+    P = T * k
+    assert c.sum() == P and off[-1] == P and off[0] == 0
+    assert (np.diff(off) == c).all()
+    assert sorted(r2p.tolist()) == list(range(P))        # bijection
+    assert (p2r[r2p] == np.arange(P)).all()
+    flat = ids.reshape(-1)
+    # brute-force stable sort by (expert, pair index)
+    ref = sorted(range(P), key=lambda p: (flat[p], p))
+    assert r2p.tolist() == ref
+    for e in range(E):
+        seg = r2p[off[e]:off[e + 1]]
+        assert (flat[seg] == e).all() and (np.diff(seg) > 0).all()
+
+
+def test_permute_then_combine_is_identity():
+    rng = np.random.default_rng(11)
+    T, H, E, k = 23, 8, 6, 3
+    x = rng.normal(size=(T, H))
+    logits = rng.normal(size=(T, E)).astype(np.float32)
+    cfg = O.RouteCfg(num_experts=E, top_k=k)
+    ids, w, _ = O.route(logits, cfg)
+    c, off, r2p, p2r = O.permute(ids, E)
+    y_rows = x[r2p // k]                 # identity experts
+    np.testing.assert_allclose(O.combine(y_rows, p2r, w), x, rtol=1e-13)
+
+
+# ------------------------------------------------ expert MLP and whole layer ---
+
+def _torch_swiglu_mlp(x, w13, w2):
+    x, w13, w2 = (torch.as_tensor(np.asarray(a), dtype=torch.float64) for a in (x, w13, w2))
+    I = w2.shape[1]
+    g = torch.nn.functional.linear(x, w13[:I])
+    u = torch.nn.functional.linear(x, w13[I:])
+    return torch.nn.functional.linear(torch.nn.functional.silu(g) * u, w2).numpy()
+
+
+def test_single_expert_is_dense_swiglu():
+    rng = np.random.default_rng(5)
+    T, H, I = 17, 24, 40
+    x = rng.normal(size=(T, H))
+    w13 = rng.normal(size=(1, 2 * I, H)) / math.sqrt(H)
+    w2 = rng.normal(size=(1, H, I)) / math.sqrt(I)
+    cfg = O.RouteCfg(num_experts=1, top_k=1)
+    res = O.forward(x, cfg, w13, w2, logits=np.zeros((T, 1), dtype=np.float32))
+    np.testing.assert_allclose(res["out"], _torch_swiglu_mlp(x, w13[0], w2[0]), rtol=1e-12)
+    assert (res["weights"] == 1.0).all()
+
+
+def _dense_reference(x, logits, bias, cfg, w13, w2):
+    """Every expert on every token (torch float64), then mask with the
+    selection and weight.  Selection/weights use a brute-force subset search
+    on torch-computed keys, independent of the oracle's code."""
+    T, E = logits.shape
+    xt = torch.as_tensor(x, dtype=torch.float64)
+    lt = torch.as_tensor(logits, dtype=torch.float64)
+    if cfg.score == "softmax":
+        s = torch.softmax(lt, dim=1)
+    elif cfg.score == "sigmoid":
+        s = torch.sigmoid(lt)
+    else:
+        s = torch.sqrt(torch.nn.functional.softplus(lt))
+    raw = bias is None and (cfg.num_groups == 1 or cfg.group_score == "max")
+    keys = lt if raw else s + (0 if bias is None else torch.as_tensor(bias, dtype=torch.float64))
+    keys = keys.numpy()
+    y_all = torch.stack([torch.as_tensor(_torch_swiglu_mlp(x, w13[e], w2[e])) for e in range(E)], 1)
+    out = torch.zeros(T, y_all.shape[2], dtype=torch.float64)
+    for t in range(T):
+        if cfg.num_groups > 1:
+            groups, per = _brute_groups(keys[t], cfg.num_groups, cfg.topk_group, cfg.group_score)
+            allowed = [e // per in groups for e in range(E)]
+        else:
+            allowed = [True] * E
+        sel = sorted(_brute_topk(keys[t], allowed, cfg.top_k))
+        mask = torch.zeros(E, dtype=torch.float64)
+        mask[sel] = 1.0
+        ws = s[t] * mask
+        if cfg.renormalize:
+            ws = ws / ws.sum()
+        ws = ws * cfg.routed_scaling
+        out[t] = (ws[:, None] * y_all[t]).sum(0)
+    return out.numpy()
+
+
+@pytest.mark.parametrize("variant", ["softmax", "grouped_bias", "sigmoid_norenorm"])
+def test_layer_matches_dense_every_expert_reference(variant):
+    rng = np.random.default_rng(21)
+    T, H, E, I = 19, 16, 8, 12
+    if variant == "softmax":
+        cfg, bias = O.RouteCfg(num_experts=E, top_k=2, routed_scaling=2.5), None
+    elif variant == "grouped_bias":
+        cfg = O.RouteCfg(num_experts=E, top_k=3, num_groups=4, topk_group=2,
+                         score="sqrtsoftplus", group_score="top2sum")
+        bias = rng.uniform(-0.1, 0.1, size=E).astype(np.float32)
+    else:
+        cfg, bias = O.RouteCfg(num_experts=E, top_k=2, score="sigmoid", renormalize=False), None
+    x = rng.normal(size=(T, H))
+    w_r = rng.normal(size=(E, H)) / math.sqrt(H)
+    w13 = rng.normal(size=(E, 2 * I, H)) / math.sqrt(H)
+    w2 = rng.normal(size=(E, H, I)) / math.sqrt(I)
+    res = O.forward(x, cfg, w13, w2, w_router=w_r, corr_bias=bias)
+    np.testing.assert_allclose(res["logits"], x @ w_r.T, rtol=1e-12)
+    ref = _dense_reference(x, res["logits"], bias, cfg, w13, w2)
+    np.testing.assert_allclose(res["out"], ref, rtol=1e-11, atol=1e-13)
+    # token-by-token evaluation agrees with the batched chain
+    tok = np.array([0, 5, 18, 7])
+    ft = O.forward_tokens(tok, x, cfg, w13, w2, w_router=w_r, corr_bias=bias)
+    np.testing.assert_allclose(ft["out"], res["out"][tok], rtol=1e-12, atol=1e-14)
+    assert (ft["ids"] == res["ids"][tok]).all()
+
+
+def test_latent_shared_layer_against_torch_composition():
+    rng = np.random.default_rng(31)
+    T, H, L, E, I, Is, k = 11, 24, 16, 6, 8, 10, 2
+    x = rng.normal(size=(T, H))
+    w_r = rng.normal(size=(E, H)) / math.sqrt(H)
+    w13 = rng.normal(size=(E, 2 * I, L)) / math.sqrt(L)
+    w2 = rng.normal(size=(E, L, I)) / math.sqrt(I)
+    lat = dict(w_down=rng.normal(size=(L, H)) / math.sqrt(H),
+               gamma=1 + 0.1 * rng.normal(size=L),
+               w_up=rng.normal(size=(H, L)) / math.sqrt(L), eps=1e-6)
+    sh = dict(w13=rng.normal(size=(2 * Is, H)) / math.sqrt(H),
+              w2=rng.normal(size=(H, Is)) / math.sqrt(Is))
+    cfg = O.RouteCfg(num_experts=E, top_k=k)
+    res = O.forward(x, cfg, w13, w2, w_router=w_r, latent=lat, shared=sh)
+    # independent composition in torch: routing on x, experts on z, RMSNorm,
+    # up-projection, plus the shared expert on x
+    z = x @ lat["w_down"].T
+    routed = _dense_reference(z, x @ w_r.T, None, cfg, w13, w2)
+    rt = torch.as_tensor(routed)
+    normed = (rt * torch.rsqrt(rt.pow(2).mean(-1, keepdim=True) + 1e-6)
+              * torch.as_tensor(lat["gamma"])).numpy()
+    ref = normed @ lat["w_up"].T + _torch_swiglu_mlp(x, sh["w13"], sh["w2"])
+    np.testing.assert_allclose(res["out"], ref, rtol=1e-11, atol=1e-12)
+    ft = O.forward_tokens(np.arange(T), x, cfg, w13, w2, w_router=w_r, latent=lat, shared=sh)
+    np.testing.assert_allclose(ft["out"], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_rmsnorm_constant_row_and_scale_invariance():
+    g = np.array([0.5, 1.0, 2.0, -1.0])
+    c = 3.0
+    out = O.rmsnorm(np.full((1, 4), c), g, 1e-6)
+    np.testing.assert_allclose(out[0], g * c / math.sqrt(c * c + 1e-6), rtol=1e-15)
+    rng = np.random.default_rng(2)
+    v = rng.normal(size=(3, 64))
+    np.testing.assert_allclose(O.rmsnorm(7.0 * v, np.ones(64), 0.0),
+                               O.rmsnorm(v, np.ones(64), 0.0), rtol=1e-13)
