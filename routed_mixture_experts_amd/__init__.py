@@ -1,0 +1,9 @@
+"""Routed mixture-of-experts forward for AMD MI355X (gfx950).
+
+The compute path is libmoe.so (hand-written HIP kernels behind a C ABI,
+include/moe.h); this package is its thin ctypes binding plus the seeded
+synthetic input generator.
+"""
+from ._lib import (EXPORTS, LIB_PATH, MOE_NUM_STAGES, STAGES, MoeError,  # noqa: F401
+                   RouteConfig, load, moe_combine, moe_experts, moe_forward,
+                   moe_forward_workspace, moe_permute, moe_route)

@@ -1,0 +1,127 @@
+// Combine: back to token order with the routing weights applied
+// ("vLLM-Ascend Kimi K3 MoE Forward Insight", Stage 4 mode table, AllGather
+// row: combine restores token order and applies the probabilities).
+//
+//   out[t, d] = sum_{j = 0..k-1} w[t, j] * y_rows[pair_to_row[t*k + j], d]
+//
+// A gather, not a scatter: every output element is owned by one thread, the
+// k rows are read through the inverse permutation, the sum runs in fp32 in
+// ascending j and is rounded once.  No atomics.  Optional fused extras:
+//  * an fp32 addend (the shared expert's output) added before the rounding;
+//  * RMSNorm of the whole row (the latent tail's norm, page
+//    "vllm.models.kimi_k3.nvidia.latent_moe_runner", allreduce_norm_latent_out
+//    at tensor-parallel size 1), y * rsqrt(mean(y^2) + eps) * gamma in fp32,
+//    in which case one workgroup keeps the whole row in registers.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ void store4(void* out, int out_dtype, int64_t idx, f32x4_t v) {
+    if (out_dtype == 0) {
+        *(f32x4_t*)((float*)out + idx) = v;
+    } else {
+        uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+        *(uint2*)((bf16_t*)out + idx) = make_uint2(lo, hi);
+    }
+}
+
+__device__ __forceinline__ float gamma_at(const void* gamma, int out_dtype, int d) {
+    return out_dtype == 0 ? ((const float*)gamma)[d] : bf16_to_f32(((const bf16_t*)gamma)[d]);
+}
+
+// grid (T, ceil(D / 1024)); each thread one float4 of one token row.
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+    __shared__ int rows[kMaxTopK];
+    __shared__ float ws[kMaxTopK];
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (tid < a.k) {
+        rows[tid] = a.pair_to_row[t * a.k + tid];
+        ws[tid] = a.weights[t * a.k + tid];
+    }
+    __syncthreads();
+    const int d = (blockIdx.y * 256 + tid) * 4;
+    if (d >= a.D) return;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < a.k; ++j) {
+        const f32x4_t v = *(const f32x4_t*)(a.y_rows + (int64_t)rows[j] * a.D + d);
+        const float w = ws[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+    }
+    if (a.addend) {
+        const f32x4_t s = *(const f32x4_t*)(a.addend + t * a.D + d);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += s[i];
+    }
+    store4(a.out, a.out_dtype, t * a.D + d, acc);
+}
+
+// One workgroup per token; the row (D <= 1024 * NV) stays in registers.
+template <int NV>
+__global__ __launch_bounds__(256) void combine_norm_kernel(CombineArgs a) {
+    __shared__ int rows[kMaxTopK];
+    __shared__ float ws[kMaxTopK];
+    __shared__ float part[4];
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (tid < a.k) {
+        rows[tid] = a.pair_to_row[t * a.k + tid];
+        ws[tid] = a.weights[t * a.k + tid];
+    }
+    __syncthreads();
+    f32x4_t acc[NV];
+    float ss = 0.f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int d = (v * 256 + tid) * 4;
+        if (d < a.D) {
+            for (int j = 0; j < a.k; ++j) {
+                const f32x4_t y = *(const f32x4_t*)(a.y_rows + (int64_t)rows[j] * a.D + d);
+                const float w = ws[j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[v][i] = fmaf(w, y[i], acc[v][i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ss = fmaf(acc[v][i], acc[v][i], ss);
+        }
+    }
+    // block sum of squares: wave tree, then 4 partials in a fixed order
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if ((tid & 63) == 0) part[tid >> 6] = ss;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float inv = 1.0f / sqrtf(tot / (float)a.D + a.eps);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int d = (v * 256 + tid) * 4;
+        if (d >= a.D) continue;
+        f32x4_t o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = acc[v][i] * inv * gamma_at(a.gamma, a.out_dtype, d + i);
+        store4(a.out, a.out_dtype, t * a.D + d, o);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+    if (a.T <= 0) return hipSuccess;
+    if (a.gamma) {
+        const int nv = (a.D + 1023) / 1024;
+        dim3 grid((unsigned)a.T), block(256);
+        if (nv <= 1) combine_norm_kernel<1><<<grid, block, 0, s>>>(a);
+        else if (nv <= 2) combine_norm_kernel<2><<<grid, block, 0, s>>>(a);
+        else if (nv <= 4) combine_norm_kernel<4><<<grid, block, 0, s>>>(a);
+        else combine_norm_kernel<8><<<grid, block, 0, s>>>(a);
+    } else {
+        dim3 grid((unsigned)a.T, (unsigned)((a.D + 1023) / 1024)), block(256);
+        combine_kernel<<<grid, block, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,124 @@
+// Internal declarations shared by the HIP translation units of the routed-MoE
+// library (gfx950 only).  Nothing here is part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;   // IEEE bfloat16 bit pattern
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxGroups = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+    return __uint_as_float(((uint32_t)v) << 16);
+}
+
+// Round to nearest even (inputs are finite in this library).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7fffu + lsb;
+    return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float silu_f32(float g) {
+    return g / (1.0f + __expf(-g));
+}
+
+// Tile-list entry of a grouped GEMM: rows [row0, row1) of group g.
+struct Tile {
+    int32_t group, row0, row1, pad;
+};
+
+// Epilogues of the GEMM kernels.
+enum Epilogue : int {
+    EPI_F32 = 0,        // C f32 [M, N]
+    EPI_F32_BIAS = 1,   // C f32 [M, N] = acc + bias[n]
+    EPI_OUT = 2,        // C in the layer dtype [M, N]
+    EPI_SWIGLU = 3      // C in the layer dtype [M, N]: silu(acc_gate) * acc_up
+};
+
+// One GEMM launch: C[r, n] = sum_k A[arow(r), k] * B_g[n, k]
+//   (+ sum_k A2[r, k] * B2[n, k] when a second K segment is given).
+// A rows: a_map ? a_map[r] / a_div : r.  B_g = B + g * b_gstride elements,
+// row-major [Nb, K].  For EPI_SWIGLU, B_g holds 2N rows (gate rows, then up
+// rows) and C has N columns.
+struct GemmArgs {
+    const void* A;
+    int64_t lda;
+    const int32_t* a_map;
+    int32_t a_div;
+    const void* B;
+    int64_t b_gstride;
+    int32_t K;
+    const void* A2;   // optional second K segment (dense rows only)
+    int64_t lda2;
+    const void* B2;
+    int32_t K2;
+    int32_t N;
+    int32_t M;                 // dense row count (ignored when tiles != null)
+    const Tile* tiles;         // grouped tile list (null: dense)
+    const int32_t* num_tiles;  // device count of valid tiles
+    int32_t max_tiles;         // upper bound used for the grid
+    int32_t tile_m;            // rows per tile the list was built with
+    int32_t epi;
+    void* C;
+    int64_t ldc;
+    const float* bias;
+};
+
+// ----- launchers (return hipSuccess or the launch error) -----
+struct RouteArgs {
+    int64_t T;
+    int32_t E, k, G, topk_group, score, group_score, renormalize;
+    float scaling;
+    int32_t raw_keys;
+    const float* logits;
+    const float* bias;
+    int32_t* ids;
+    float* weights;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+int permute_chunks(int64_t P);
+hipError_t launch_permute(int64_t P, int32_t E, const int32_t* ids, int32_t* counts,
+                          int32_t* offsets, int32_t* row_to_pair, int32_t* pair_to_row,
+                          int32_t* chunk_scratch, hipStream_t s);
+hipError_t launch_build_tiles(const int32_t* offsets, int32_t E, int32_t tile_m, Tile* tiles,
+                              int32_t* num_tiles, hipStream_t s);
+
+// dtype: 0 = f32, 1 = bf16.  path: see gemm.hip (chosen by the caller).
+enum GemmPath : int { GEMM_TILED = 0, GEMM_STREAM = 1 };
+hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s);
+// Rows per tile of a kernel (a grouped tile list must be built with it).
+int gemm_row_tile(int dtype, int path);
+
+struct CombineArgs {
+    int64_t T;
+    int32_t k, D;
+    const float* y_rows;
+    const int32_t* pair_to_row;
+    const float* weights;
+    const float* addend;     // optional [T, D] f32 added before rounding
+    const void* gamma;       // optional: fused RMSNorm (layer dtype)
+    float eps;
+    int32_t out_dtype;       // 0 f32, 1 bf16
+    void* out;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,499 @@
+// Grouped and dense GEMMs of the routed-MoE forward on gfx950.
+//
+// The expert MLP is grouped matmul gate/up -> activation -> grouped matmul
+// down ("vLLM-Ascend Kimi K3 MoE Forward Insight", Stage 4); the router
+// product, the latent down-projection, the shared expert and the tail
+// up-projection ("vllm.models.kimi_k3.nvidia.latent_moe_runner",
+// _fused_forward, _overlap_allreduce_tail / _shard_up_proj_tail) are the same
+// "NT" product with one group.  Every product here is
+//     C[r, n] = sum_k A[arow(r), k] * B_g[n, k]  (+ a second K segment),
+// both operands K-contiguous, with the epilogue fused (fp32 store, fp32 + bias
+// row, layer-dtype store, or SwiGLU silu(gate) * up).
+//
+// Three kernels:
+//  * gemm_bf16_tiled  -- 128x128x64 LDS double-buffered tiles, 4 waves in a
+//    2x2 layout, each wave a 64x64 block of v_mfma_f32_32x32x16_bf16.  For
+//    groups with many rows (prefill) and the dense products.
+//  * gemm_bf16_stream -- for groups with at most 16 rows (decode): the
+//    weights are the streamed operand.  A workgroup owns 64 weight rows of one
+//    group and splits K over its 4 waves; each wave keeps two batches of
+//    16-byte weight loads in flight and feeds v_mfma_f32_16x16x32_bf16 with
+//    the weights as the 16-row operand and the (<= 16) token rows as the
+//    other; partial sums meet in LDS once at the end.
+//  * gemm_f32_tiled   -- fp32 VALU 64x64 tiles for the fp32 layer.
+// Work is a flat list of (row tile, column tile); workgroup i runs on XCD
+// i % 8, so logical tile ids are remapped to give each XCD a contiguous range
+// (consecutive ids share the activation tile, which then stays in that XCD's
+// L2).
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ int xcd_remap(int i, int total) {
+    const int xcd = i & 7, local = i >> 3;
+    const int per = total >> 3, rem = total & 7;
+    return xcd * per + min(xcd, rem) + local;
+}
+
+struct TileCoord {
+    int group, row0, row1, nt;
+};
+
+// Returns false when this workgroup has no tile (grids are sized from an
+// upper bound of the tile count).
+__device__ __forceinline__ bool fetch_tile(const GemmArgs& g, int tile_m, int ntn, TileCoord& c) {
+    const int nm = g.tiles ? *g.num_tiles : (g.M + tile_m - 1) / tile_m;
+    const int total = nm * ntn;
+    const int i = blockIdx.x;
+    if (i >= total) return false;
+    const int lid = xcd_remap(i, total);
+    const int mt = lid / ntn;
+    c.nt = lid - mt * ntn;
+    if (g.tiles) {
+        const Tile t = g.tiles[mt];
+        c.group = t.group;
+        c.row0 = t.row0;
+        c.row1 = t.row1;
+    } else {
+        c.group = 0;
+        c.row0 = mt * tile_m;
+        c.row1 = min(c.row0 + tile_m, g.M);
+    }
+    return true;
+}
+
+__device__ __forceinline__ int64_t a_row_of(const GemmArgs& g, int r) {
+    return g.a_map ? (int64_t)(g.a_map[r] / g.a_div) : (int64_t)r;
+}
+
+// ------------------------------------------------------------------------
+// bf16 LDS-tiled MFMA kernel
+// ------------------------------------------------------------------------
+constexpr int TBM = 128, TBN = 128, TBK = 64, TLD = TBK + 8;  // LDS row stride (elements)
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
+    constexpr bool SW = EPI == EPI_SWIGLU;
+    const int ntn = SW ? (g.N + 63) / 64 : (g.N + TBN - 1) / TBN;
+    TileCoord tc;
+    if (!fetch_tile(g, TBM, ntn, tc)) return;
+
+    __shared__ __attribute__((aligned(16))) bf16_t smem[2][2][TBM * TLD];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lrow = tid >> 3, lcol = (tid & 7) * 8;
+
+    const bf16_t* A = (const bf16_t*)g.A;
+    const bf16_t* Bg = (const bf16_t*)g.B + (int64_t)tc.group * g.b_gstride;
+    const bf16_t* A2 = (const bf16_t*)g.A2;
+    const bf16_t* B2 = (const bf16_t*)g.B2;
+
+    const bf16_t* ap[4];
+    const bf16_t* bp[4];
+    const bf16_t* ap2[4];
+    const bf16_t* bp2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = min(tc.row0 + lrow + 32 * i, tc.row1 - 1);
+        ap[i] = A + a_row_of(g, rr) * g.lda + lcol;
+        ap2[i] = A2 ? A2 + (int64_t)rr * g.lda2 + lcol : nullptr;
+        const int rho = lrow + 32 * i;
+        int wrow;
+        if (SW) {
+            const int c = min(tc.nt * 64 + (rho & 63), g.N - 1);
+            wrow = rho < 64 ? c : g.N + c;
+        } else {
+            wrow = min(tc.nt * TBN + rho, g.N - 1);
+        }
+        bp[i] = Bg + (int64_t)wrow * g.K + lcol;
+        bp2[i] = B2 ? B2 + (int64_t)wrow * g.K2 + lcol : nullptr;
+    }
+
+    const int nk1 = g.K / TBK;
+    const int nk = nk1 + (A2 ? g.K2 / TBK : 0);
+
+    u32x4_t ra[4], rb[4];
+    auto gload = [&](int kt) {
+        if (kt < nk1) {
+            const int ko = kt * TBK;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ra[i] = *(const u32x4_t*)(ap[i] + ko);
+                rb[i] = *(const u32x4_t*)(bp[i] + ko);
+            }
+        } else {
+            const int ko = (kt - nk1) * TBK;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ra[i] = *(const u32x4_t*)(ap2[i] + ko);
+                rb[i] = *(const u32x4_t*)(bp2[i] + ko);
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *(u32x4_t*)(&smem[buf][0][(lrow + 32 * i) * TLD + lcol]) = ra[i];
+            *(u32x4_t*)(&smem[buf][1][(lrow + 32 * i) * TLD + lcol]) = rb[i];
+        }
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 2; ++nj)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[mi][nj][j] = 0.0f;
+
+    const int fr = lane & 31, fk = (lane >> 5) * 8;
+    int brow[2];
+#pragma unroll
+    for (int nj = 0; nj < 2; ++nj) brow[nj] = SW ? (nj * 64 + wn * 32) : (wn * 64 + nj * 32);
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload(kt + 1);
+        const bf16_t* sa = smem[buf][0];
+        const bf16_t* sb = smem[buf][1];
+#pragma unroll
+        for (int kk = 0; kk < TBK / 16; ++kk) {
+            bf16x8_t fa[2], fb[2];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+                fa[mi] = *(const bf16x8_t*)(&sa[(wm * 64 + mi * 32 + fr) * TLD + kk * 16 + fk]);
+#pragma unroll
+            for (int nj = 0; nj < 2; ++nj)
+                fb[nj] = *(const bf16x8_t*)(&sb[(brow[nj] + fr) * TLD + kk * 16 + fk]);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int nj = 0; nj < 2; ++nj)
+                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[nj],
+                                                                           acc[mi][nj], 0, 0, 0);
+        }
+        if (kt + 1 < nk) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: lane holds column fr of each 32x32 block, rows 8*(j/4)+4*(lane/32)+j%4
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int r = tc.row0 + wm * 64 + mi * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+            if (r >= tc.row1) continue;
+            if (SW) {
+                const int hc = tc.nt * 64 + wn * 32 + fr;
+                if (hc < g.N) {
+                    const float h = silu_f32(acc[mi][0][j]) * acc[mi][1][j];
+                    ((bf16_t*)g.C)[(int64_t)r * g.ldc + hc] = f32_to_bf16(h);
+                }
+            } else {
+#pragma unroll
+                for (int nj = 0; nj < 2; ++nj) {
+                    const int c = tc.nt * TBN + wn * 64 + nj * 32 + fr;
+                    if (c >= g.N) continue;
+                    float v = acc[mi][nj][j];
+                    if (EPI == EPI_F32_BIAS && g.bias) v += g.bias[c];
+                    if (EPI == EPI_OUT)
+                        ((bf16_t*)g.C)[(int64_t)r * g.ldc + c] = f32_to_bf16(v);
+                    else
+                        ((float*)g.C)[(int64_t)r * g.ldc + c] = v;
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// bf16 weight-streaming MFMA kernel (<= 16 rows per tile)
+// ------------------------------------------------------------------------
+constexpr int SROWS = 16;   // token rows per tile
+constexpr int SNW = 64;     // weight rows per workgroup
+constexpr int SU = 4;       // k-steps (of 32) per load batch
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_stream(GemmArgs g) {
+    constexpr bool SW = EPI == EPI_SWIGLU;
+    const int ntn = SW ? (g.N + 31) / 32 : (g.N + SNW - 1) / SNW;
+    TileCoord tc;
+    if (!fetch_tile(g, SROWS, ntn, tc)) return;
+
+    __shared__ float red[4][4][4][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, kofs = (lane >> 4) * 8;
+
+    const bf16_t* Bg = (const bf16_t*)g.B + (int64_t)tc.group * g.b_gstride;
+    const bf16_t* B2 = (const bf16_t*)g.B2;
+    const bf16_t* wp[4];
+    const bf16_t* wp2[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        int wrow;
+        if (SW) {
+            const int c = min(tc.nt * 32 + (q & 1) * 16 + l16, g.N - 1);
+            wrow = q < 2 ? c : g.N + c;
+        } else {
+            wrow = min(tc.nt * SNW + q * 16 + l16, g.N - 1);
+        }
+        wp[q] = Bg + (int64_t)wrow * g.K + kofs;
+        wp2[q] = B2 ? B2 + (int64_t)wrow * g.K2 + kofs : nullptr;
+    }
+    const int r = tc.row0 + l16;
+    const bool xvalid = r < tc.row1;
+    const bf16_t* xp = (const bf16_t*)g.A + (xvalid ? a_row_of(g, r) : 0) * g.lda + kofs;
+    const bf16_t* xp2 =
+        g.A2 ? (const bf16_t*)g.A2 + (int64_t)(xvalid ? r : 0) * g.lda2 + kofs : nullptr;
+
+    const int ns1 = g.K / 32;
+    const int ns = ns1 + (g.A2 ? g.K2 / 32 : 0);
+    const int s0 = (int)((int64_t)wave * ns / 4), s1 = (int)((int64_t)(wave + 1) * ns / 4);
+
+    f32x4_t acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    u32x4_t wa[SU][4], xa[SU], wb[SU][4], xb[SU];
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+
+    auto load = [&](int sbase, u32x4_t (&w)[SU][4], u32x4_t (&x)[SU]) {
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            const int st = sbase + u;
+            if (st < s1) {
+                if (st < ns1) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) w[u][q] = *(const u32x4_t*)(wp[q] + st * 32);
+                    x[u] = xvalid ? *(const u32x4_t*)(xp + st * 32) : zero;
+                } else {
+                    const int so = (st - ns1) * 32;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) w[u][q] = *(const u32x4_t*)(wp2[q] + so);
+                    x[u] = xvalid ? *(const u32x4_t*)(xp2 + so) : zero;
+                }
+            }
+        }
+    };
+    auto compute = [&](int sbase, u32x4_t (&w)[SU][4], u32x4_t (&x)[SU]) {
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            if (sbase + u < s1) {
+                const bf16x8_t xb8 = __builtin_bit_cast(bf16x8_t, x[u]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, w[u][q]), xb8, acc[q], 0, 0, 0);
+            }
+        }
+    };
+
+    load(s0, wa, xa);
+    for (int s = s0; s < s1; s += 2 * SU) {
+        load(s + SU, wb, xb);
+        compute(s, wa, xa);
+        load(s + 2 * SU, wa, xa);
+        compute(s + SU, wb, xb);
+    }
+
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[wave][q][j][lane] = acc[q][j];
+    __syncthreads();
+
+    // acc[q][j] holds C[weight row 4*(lane/16)+j of group q][token lane%16]
+    const int tok = l16, wr = (lane >> 4) * 4;
+    const int rr = tc.row0 + tok;
+    if (SW) {
+        if (wave >= 2) return;
+        const int q = wave;
+        float gsum[4], usum[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            gsum[j] = red[0][q][j][lane] + red[1][q][j][lane] + red[2][q][j][lane] +
+                      red[3][q][j][lane];
+            usum[j] = red[0][q + 2][j][lane] + red[1][q + 2][j][lane] +
+                      red[2][q + 2][j][lane] + red[3][q + 2][j][lane];
+        }
+        if (rr >= tc.row1) return;
+        bf16_t* crow = (bf16_t*)g.C + (int64_t)rr * g.ldc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int hc = tc.nt * 32 + q * 16 + wr + j;
+            if (hc < g.N) crow[hc] = f32_to_bf16(silu_f32(gsum[j]) * usum[j]);
+        }
+    } else {
+        const int q = wave;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = red[0][q][j][lane] + red[1][q][j][lane] + red[2][q][j][lane] +
+                   red[3][q][j][lane];
+        if (rr >= tc.row1) return;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = tc.nt * SNW + q * 16 + wr + j;
+            if (c >= g.N) continue;
+            float o = v[j];
+            if (EPI == EPI_F32_BIAS && g.bias) o += g.bias[c];
+            if (EPI == EPI_OUT)
+                ((bf16_t*)g.C)[(int64_t)rr * g.ldc + c] = f32_to_bf16(o);
+            else
+                ((float*)g.C)[(int64_t)rr * g.ldc + c] = o;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// fp32 VALU tiled kernel (64x64 tiles, 4x4 outputs per thread)
+// ------------------------------------------------------------------------
+constexpr int FBM = 64, FBN = 64, FBK = 16;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_tiled(GemmArgs g) {
+    constexpr bool SW = EPI == EPI_SWIGLU;
+    const int ntn = SW ? (g.N + 31) / 32 : (g.N + FBN - 1) / FBN;
+    TileCoord tc;
+    if (!fetch_tile(g, FBM, ntn, tc)) return;
+
+    __shared__ float As[FBK][FBM + 4];
+    __shared__ float Bs[FBK][FBN + 4];
+
+    const int tid = threadIdx.x;
+    const int ty = tid >> 4, tx = tid & 15;
+    const int lr = tid >> 2, lk = (tid & 3) * 4;
+
+    const float* A = (const float*)g.A;
+    const float* Bg = (const float*)g.B + (int64_t)tc.group * g.b_gstride;
+    const int rr = min(tc.row0 + lr, tc.row1 - 1);
+    const float* ap = A + a_row_of(g, rr) * g.lda + lk;
+    const float* ap2 = g.A2 ? (const float*)g.A2 + (int64_t)rr * g.lda2 + lk : nullptr;
+    int wrow;
+    if (SW) {
+        const int c = min(tc.nt * 32 + (lr & 31), g.N - 1);
+        wrow = lr < 32 ? c : g.N + c;
+    } else {
+        wrow = min(tc.nt * FBN + lr, g.N - 1);
+    }
+    const float* bp = Bg + (int64_t)wrow * g.K + lk;
+    const float* bp2 = g.B2 ? (const float*)g.B2 + (int64_t)wrow * g.K2 + lk : nullptr;
+
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+
+    int bcol[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bcol[j] = SW ? (j < 2 ? tx * 2 + j : 32 + tx * 2 + j - 2) : tx * 4 + j;
+
+    const int nk1 = g.K / FBK;
+    const int nk = nk1 + (g.A2 ? g.K2 / FBK : 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        f32x4_t av, bv;
+        if (kt < nk1) {
+            av = *(const f32x4_t*)(ap + kt * FBK);
+            bv = *(const f32x4_t*)(bp + kt * FBK);
+        } else {
+            av = *(const f32x4_t*)(ap2 + (kt - nk1) * FBK);
+            bv = *(const f32x4_t*)(bp2 + (kt - nk1) * FBK);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            As[lk + i][lr] = av[i];
+            Bs[lk + i][lr] = bv[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < FBK; ++k) {
+            float a4[4], b4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a4[i] = As[k][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b4[j] = Bs[k][bcol[j]];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a4[i], b4[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = tc.row0 + ty * 4 + i;
+        if (r >= tc.row1) continue;
+        if (SW) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int hc = tc.nt * 32 + tx * 2 + j;
+                if (hc < g.N) {
+                    const float gt = acc[i][j], up = acc[i][j + 2];
+                    ((float*)g.C)[(int64_t)r * g.ldc + hc] = gt / (1.0f + expf(-gt)) * up;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = tc.nt * FBN + tx * 4 + j;
+                if (c >= g.N) continue;
+                float v = acc[i][j];
+                if (EPI == EPI_F32_BIAS && g.bias) v += g.bias[c];
+                ((float*)g.C)[(int64_t)r * g.ldc + c] = v;
+            }
+        }
+    }
+}
+
+int col_tiles(int path, int dtype, int epi, int N) {
+    const bool sw = epi == EPI_SWIGLU;
+    if (dtype == 0) return sw ? (N + 31) / 32 : (N + FBN - 1) / FBN;
+    if (path == GEMM_STREAM) return sw ? (N + 31) / 32 : (N + SNW - 1) / SNW;
+    return sw ? (N + 63) / 64 : (N + TBN - 1) / TBN;
+}
+
+int row_tile(int path, int dtype) {
+    if (dtype == 0) return FBM;
+    return path == GEMM_STREAM ? SROWS : TBM;
+}
+
+}  // namespace
+
+int gemm_row_tile(int dtype, int path) { return row_tile(path, dtype); }
+
+hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
+    const int tm = row_tile(path, dtype);
+    const int nm = g.tiles ? g.max_tiles : (g.M + tm - 1) / tm;
+    const int64_t grid = (int64_t)nm * col_tiles(path, dtype, g.epi, g.N);
+    if (grid <= 0) return hipSuccess;
+    dim3 gd((unsigned)grid), bd(256);
+#define MOE_GEMM_SWITCH(KERNEL)                                                   \
+    switch (g.epi) {                                                              \
+        case EPI_F32: KERNEL<EPI_F32><<<gd, bd, 0, s>>>(g); break;                \
+        case EPI_F32_BIAS: KERNEL<EPI_F32_BIAS><<<gd, bd, 0, s>>>(g); break;      \
+        case EPI_OUT: KERNEL<EPI_OUT><<<gd, bd, 0, s>>>(g); break;                \
+        default: KERNEL<EPI_SWIGLU><<<gd, bd, 0, s>>>(g); break;                  \
+    }
+    if (dtype == 0) {
+        MOE_GEMM_SWITCH(gemm_f32_tiled)
+    } else if (path == GEMM_STREAM) {
+        MOE_GEMM_SWITCH(gemm_bf16_stream)
+    } else {
+        MOE_GEMM_SWITCH(gemm_bf16_tiled)
+    }
+#undef MOE_GEMM_SWITCH
+    return hipGetLastError();
+}
+
+}  // namespace moe

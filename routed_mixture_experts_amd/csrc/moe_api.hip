@@ -1,0 +1,490 @@
+// C ABI of the routed-MoE forward: host-side validation, workspace layout and
+// the launch sequence.  See include/moe.h for the contract of every call.
+//
+// The stage order is the one of the pages' forward skeleton
+// ("vLLM-Ascend Kimi K3 MoE Forward Insight": select_experts, then
+// MoECommMethod.fused_experts = dispatch -> unified_apply_mlp -> combine, with
+// shared experts beside it) and of the latent runner
+// ("vllm.models.kimi_k3.nvidia.latent_moe_runner", _fused_forward: routed input
+// transform, experts, tail = RMSNorm -> up-projection -> + shared output).
+// Everything is enqueued on the caller's stream; nothing waits on the host.
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+// Bump allocator over the caller's workspace.  With base == nullptr it only
+// measures, so sizing and carving share one code path.
+struct Carve {
+    char* base;
+    size_t off = 0;
+    explicit Carve(void* b) : base((char*)b) {}
+    template <class T>
+    T* take(size_t n) {
+        off = (off + kAlign - 1) / kAlign * kAlign;
+        T* p = base ? (T*)(base + off) : nullptr;
+        off += n * sizeof(T);
+        return p;
+    }
+};
+
+size_t elem_size(moe_dtype_t dt) { return dt == MOE_DTYPE_F32 ? 4 : 2; }
+
+bool bad_dtype(moe_dtype_t dt) { return dt != MOE_DTYPE_F32 && dt != MOE_DTYPE_BF16; }
+
+moe_status_t check_cfg(const moe_route_cfg_t* c) {
+    if (!c) return MOE_EINVAL;
+    const int E = c->num_experts, k = c->top_k, G = c->num_groups;
+    if (E < 1 || k < 1 || G < 1 || c->topk_group < 1) return MOE_EINVAL;
+    if (E > kMaxExperts || k > kMaxTopK || G > kMaxGroups) return MOE_ENOTSUP;
+    if (k > E || E % G != 0 || c->topk_group > G) return MOE_EINVAL;
+    if ((int64_t)c->topk_group * (E / G) < k) return MOE_EINVAL;
+    if (c->score < 0 || c->score > 2) return MOE_EINVAL;
+    if (c->group_score < 0 || c->group_score > 1) return MOE_EINVAL;
+    if (G > 1 && c->group_score == MOE_GROUP_TOP2SUM && E / G < 2) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+#define MOE_TRY(expr)                              \
+    do {                                           \
+        moe_status_t st__ = (expr);                \
+        if (st__ != MOE_OK) return st__;           \
+    } while (0)
+#define MOE_HIP(expr) MOE_TRY(hip_status(expr))
+
+bool width_ok(int64_t w) { return w > 0 && w % 64 == 0; }
+
+// Decode-shaped groups (few rows per expert on average) stream the weights;
+// the rest use LDS tiles.
+int expert_path(moe_dtype_t dt, int64_t T, int k, int E) {
+    if (dt == MOE_DTYPE_F32) return GEMM_TILED;
+    return (T * k) <= (int64_t)24 * E ? GEMM_STREAM : GEMM_TILED;
+}
+
+int dense_path(moe_dtype_t dt, int64_t T) {
+    if (dt == MOE_DTYPE_F32) return GEMM_TILED;
+    return T <= 256 ? GEMM_STREAM : GEMM_TILED;
+}
+
+int64_t max_tiles_for(int64_t P, int E, int tile_m) { return (P + tile_m - 1) / tile_m + E; }
+
+// Smallest row tile any path uses: sizes the tile list for every path.
+int64_t tile_capacity(moe_dtype_t dt, int64_t P, int E) {
+    const int tm = gemm_row_tile(dt == MOE_DTYPE_F32 ? 0 : 1,
+                                 dt == MOE_DTYPE_F32 ? GEMM_TILED : GEMM_STREAM);
+    return max_tiles_for(P, E, tm);
+}
+
+struct ExpertsWs {
+    Tile* tiles;
+    int32_t* ntiles;
+    void* h;
+};
+
+ExpertsWs carve_experts(Carve& c, moe_dtype_t dt, int64_t max_T, int k, int E, int I) {
+    ExpertsWs w;
+    const int64_t P = max_T * k;
+    w.tiles = c.take<Tile>((size_t)tile_capacity(dt, P, E));
+    w.ntiles = c.take<int32_t>(1);
+    w.h = c.take<char>((size_t)P * I * elem_size(dt));
+    return w;
+}
+
+GemmArgs gemm_defaults() {
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.a_div = 1;
+    return g;
+}
+
+// Grouped gate/up + SwiGLU, then grouped down, over expert-sorted rows.
+moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, const void* x,
+                         const int32_t* offsets, const int32_t* row_to_pair, const void* w13,
+                         const void* w2, float* y_rows, const ExpertsWs& w, hipStream_t s,
+                         hipEvent_t* ev) {
+    const int64_t P = T * k;
+    const int path = expert_path(dt, T, k, E);
+    const int idt = dt == MOE_DTYPE_F32 ? 0 : 1;
+    const int tm = gemm_row_tile(idt, path);
+    if (ev) MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM1], s));
+    MOE_HIP(launch_build_tiles(offsets, E, tm, w.tiles, w.ntiles, s));
+
+    GemmArgs g1 = gemm_defaults();
+    g1.A = x;
+    g1.lda = D;
+    g1.a_map = row_to_pair;
+    g1.a_div = k;
+    g1.B = w13;
+    g1.b_gstride = (int64_t)2 * I * D;
+    g1.K = D;
+    g1.N = I;
+    g1.tiles = w.tiles;
+    g1.num_tiles = w.ntiles;
+    g1.max_tiles = (int32_t)max_tiles_for(P, E, tm);
+    g1.tile_m = tm;
+    g1.epi = EPI_SWIGLU;
+    g1.C = w.h;
+    g1.ldc = I;
+    MOE_HIP(launch_gemm(idt, path, g1, s));
+    if (ev) {
+        MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM1 + 1], s));
+        MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM2], s));
+    }
+
+    GemmArgs g2 = gemm_defaults();
+    g2.A = w.h;
+    g2.lda = I;
+    g2.B = w2;
+    g2.b_gstride = (int64_t)D * I;
+    g2.K = I;
+    g2.N = D;
+    g2.tiles = w.tiles;
+    g2.num_tiles = w.ntiles;
+    g2.max_tiles = g1.max_tiles;
+    g2.tile_m = tm;
+    g2.epi = EPI_F32;
+    g2.C = y_rows;
+    g2.ldc = D;
+    MOE_HIP(launch_gemm(idt, path, g2, s));
+    if (ev) MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM2 + 1], s));
+    return MOE_OK;
+}
+
+// Dense C = A . B^T (+ A2 . B2^T) over T rows.
+moe_status_t dense_gemm(moe_dtype_t dt, int64_t T, const void* A, int64_t lda, const void* B,
+                        int K, const void* A2, int64_t lda2, const void* B2, int K2, int N,
+                        int epi, void* C, int64_t ldc, const float* bias, hipStream_t s) {
+    GemmArgs g = gemm_defaults();
+    g.A = A;
+    g.lda = lda;
+    g.B = B;
+    g.K = K;
+    g.A2 = A2;
+    g.lda2 = lda2;
+    g.B2 = B2;
+    g.K2 = A2 ? K2 : 0;
+    g.N = N;
+    g.M = (int32_t)T;
+    g.epi = epi;
+    g.C = C;
+    g.ldc = ldc;
+    g.bias = bias;
+    return hip_status(launch_gemm(dt == MOE_DTYPE_F32 ? 0 : 1, dense_path(dt, T), g, s));
+}
+
+struct ForwardWs {
+    float* logits;
+    int32_t* ids;
+    float* weights;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* r2p;
+    int32_t* p2r;
+    int32_t* chunks;
+    ExpertsWs ex;
+    float* y_rows;
+    void* z;        // latent input [T, L]
+    void* normed;   // latent RMSNorm output [T, L]
+    void* h_sh;     // shared intermediate [T, Is]
+    float* sh;      // shared output [T, H] (no latent)
+};
+
+ForwardWs carve_forward(Carve& c, const moe_route_cfg_t* cfg, moe_dtype_t dt, int64_t max_T,
+                        int H, int I, const moe_latent_t* lat, const moe_shared_t* sh) {
+    ForwardWs w;
+    const int E = cfg->num_experts, k = cfg->top_k;
+    const int64_t P = max_T * k;
+    const int D = lat ? lat->latent : H;
+    const size_t es = elem_size(dt);
+    w.logits = c.take<float>((size_t)max_T * E);
+    w.ids = c.take<int32_t>((size_t)P);
+    w.weights = c.take<float>((size_t)P);
+    w.counts = c.take<int32_t>((size_t)E);
+    w.offsets = c.take<int32_t>((size_t)E + 1);
+    w.r2p = c.take<int32_t>((size_t)P);
+    w.p2r = c.take<int32_t>((size_t)P);
+    w.chunks = c.take<int32_t>((size_t)permute_chunks(P) * E);
+    w.ex = carve_experts(c, dt, max_T, k, E, I);
+    w.y_rows = c.take<float>((size_t)P * D);
+    w.z = lat ? c.take<char>((size_t)max_T * D * es) : nullptr;
+    w.normed = lat ? c.take<char>((size_t)max_T * D * es) : nullptr;
+    w.h_sh = sh ? c.take<char>((size_t)max_T * sh->inter * es) : nullptr;
+    w.sh = (sh && !lat) ? c.take<float>((size_t)max_T * H) : nullptr;
+    return w;
+}
+
+moe_status_t check_forward_shapes(const moe_route_cfg_t* cfg, moe_dtype_t dt, int64_t T, int H,
+                                  int I, const moe_latent_t* lat, const moe_shared_t* sh) {
+    MOE_TRY(check_cfg(cfg));
+    if (bad_dtype(dt) || T < 0) return MOE_EINVAL;
+    if (T * (int64_t)cfg->top_k > INT32_MAX / 2) return MOE_ENOTSUP;
+    if (!width_ok(H) || !width_ok(I)) return MOE_ENOTSUP;
+    if (lat) {
+        if (!lat->w_down || !lat->gamma || !lat->w_up) return MOE_EINVAL;
+        if (!width_ok(lat->latent) || lat->latent > 8192) return MOE_ENOTSUP;
+        if (!(lat->rms_eps >= 0.0f)) return MOE_EINVAL;
+    }
+    if (sh) {
+        if (!sh->w13 || !sh->w2) return MOE_EINVAL;
+        if (!width_ok(sh->inter)) return MOE_ENOTSUP;
+    }
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t st) {
+    switch (st) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+        case MOE_ENOTSUP: return "MOE_ENOTSUP: shape not supported by this build";
+        case MOE_ENOSPACE: return "MOE_ENOSPACE: workspace too small";
+        case MOE_EHIP: return "MOE_EHIP: HIP launch failed";
+        default: return "unknown moe_status_t";
+    }
+}
+
+moe_status_t moe_route(const moe_route_cfg_t* cfg, int64_t T, const float* logits,
+                       const float* correction_bias, int32_t* topk_ids, float* topk_weights,
+                       void* stream) {
+    MOE_TRY(check_cfg(cfg));
+    if (T < 0) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_weights) return MOE_EINVAL;
+    RouteArgs a;
+    a.T = T;
+    a.E = cfg->num_experts;
+    a.k = cfg->top_k;
+    a.G = cfg->num_groups;
+    a.topk_group = cfg->topk_group;
+    a.score = cfg->score;
+    a.group_score = cfg->group_score;
+    a.renormalize = cfg->renormalize != 0;
+    a.scaling = cfg->routed_scaling;
+    a.raw_keys = !correction_bias && (cfg->num_groups == 1 || cfg->group_score == MOE_GROUP_MAX);
+    a.logits = logits;
+    a.bias = correction_bias;
+    a.ids = topk_ids;
+    a.weights = topk_weights;
+    return hip_status(launch_route(a, (hipStream_t)stream));
+}
+
+size_t moe_permute_workspace(int64_t max_T, int32_t k, int32_t E) {
+    if (max_T < 0 || k < 1 || E < 1) return 0;
+    Carve c(nullptr);
+    c.take<int32_t>((size_t)permute_chunks(max_T * k) * E);
+    return c.off;
+}
+
+moe_status_t moe_permute(int64_t T, int32_t k, int32_t E, const int32_t* topk_ids,
+                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_to_pair,
+                         int32_t* pair_to_row, void* ws, size_t ws_bytes, void* stream) {
+    if (T < 0 || k < 1 || E < 1 || k > E) return MOE_EINVAL;
+    if (E > kMaxExperts || k > kMaxTopK) return MOE_ENOTSUP;
+    if (T * (int64_t)k > INT32_MAX / 2) return MOE_ENOTSUP;
+    if (!expert_counts || !expert_offsets) return MOE_EINVAL;
+    if (T > 0 && (!topk_ids || !row_to_pair || !pair_to_row)) return MOE_EINVAL;
+    if (ws_bytes < moe_permute_workspace(T, k, E) || (T > 0 && !ws)) return MOE_ENOSPACE;
+    // T == 0 still writes zero counts and offsets.
+    Carve c(ws);
+    int32_t* chunks = c.take<int32_t>((size_t)permute_chunks(T * k) * E);
+    return hip_status(launch_permute(T * k, E, topk_ids, expert_counts, expert_offsets,
+                                     row_to_pair, pair_to_row, chunks, (hipStream_t)stream));
+}
+
+size_t moe_experts_workspace(moe_dtype_t dtype, int64_t max_T, int32_t k, int32_t E, int32_t D,
+                             int32_t I) {
+    if (bad_dtype(dtype) || max_T < 0 || k < 1 || E < 1 || D < 1 || I < 1) return 0;
+    Carve c(nullptr);
+    carve_experts(c, dtype, max_T, k, E, I);
+    return c.off;
+}
+
+moe_status_t moe_experts(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, int32_t D,
+                         int32_t I, const void* x, const int32_t* expert_offsets,
+                         const int32_t* row_to_pair, const void* w13, const void* w2,
+                         float* y_rows, void* ws, size_t ws_bytes, void* stream) {
+    if (bad_dtype(dtype) || T < 0 || k < 1 || E < 1 || k > E) return MOE_EINVAL;
+    if (E > kMaxExperts || k > kMaxTopK) return MOE_ENOTSUP;
+    if (!width_ok(D) || !width_ok(I)) return MOE_ENOTSUP;
+    if (T * (int64_t)k > INT32_MAX / 2) return MOE_ENOTSUP;
+    if (T == 0) return MOE_OK;
+    if (!x || !expert_offsets || !row_to_pair || !w13 || !w2 || !y_rows) return MOE_EINVAL;
+    if (!ws || ws_bytes < moe_experts_workspace(dtype, T, k, E, D, I)) return MOE_ENOSPACE;
+    Carve c(ws);
+    ExpertsWs w = carve_experts(c, dtype, T, k, E, I);
+    return run_experts(dtype, T, k, E, D, I, x, expert_offsets, row_to_pair, w13, w2, y_rows, w,
+                       (hipStream_t)stream, nullptr);
+}
+
+moe_status_t moe_combine(moe_dtype_t out_dtype, int64_t T, int32_t k, int32_t D,
+                         const float* y_rows, const int32_t* pair_to_row,
+                         const float* topk_weights, void* out, void* stream) {
+    if (bad_dtype(out_dtype) || T < 0 || k < 1 || D < 1) return MOE_EINVAL;
+    if (k > kMaxTopK) return MOE_ENOTSUP;
+    if (D % 4 != 0) return MOE_ENOTSUP;
+    if (T == 0) return MOE_OK;
+    if (!y_rows || !pair_to_row || !topk_weights || !out) return MOE_EINVAL;
+    CombineArgs a;
+    memset(&a, 0, sizeof(a));
+    a.T = T;
+    a.k = k;
+    a.D = D;
+    a.y_rows = y_rows;
+    a.pair_to_row = pair_to_row;
+    a.weights = topk_weights;
+    a.out_dtype = out_dtype == MOE_DTYPE_F32 ? 0 : 1;
+    a.out = out;
+    return hip_status(launch_combine(a, (hipStream_t)stream));
+}
+
+size_t moe_forward_workspace(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t max_T,
+                             int32_t H, int32_t I, const moe_latent_t* latent,
+                             const moe_shared_t* shared) {
+    if (check_forward_shapes(cfg, dtype, max_T, H, I, latent, shared) != MOE_OK) return 0;
+    Carve c(nullptr);
+    carve_forward(c, cfg, dtype, max_T, H, I, latent, shared);
+    return c.off;
+}
+
+moe_status_t moe_forward(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t T, int32_t H,
+                         int32_t I, const void* x, const void* w_router, const float* router_bias,
+                         const float* router_logits, const float* correction_bias,
+                         const void* w13, const void* w2, const moe_latent_t* latent,
+                         const moe_shared_t* shared, void* out, float* logits_out,
+                         int32_t* topk_ids_out, float* topk_weights_out,
+                         int32_t* expert_counts_out, void* const* stage_events, void* ws,
+                         size_t ws_bytes, void* stream) {
+    MOE_TRY(check_forward_shapes(cfg, dtype, T, H, I, latent, shared));
+    if (T == 0) return MOE_OK;
+    if (!x || !w13 || !w2 || !out) return MOE_EINVAL;
+    if (!router_logits && !w_router) return MOE_EINVAL;
+    if (!ws || ws_bytes < moe_forward_workspace(cfg, dtype, T, H, I, latent, shared))
+        return MOE_ENOSPACE;
+
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t* ev = (hipEvent_t*)stage_events;
+    const int E = cfg->num_experts, k = cfg->top_k;
+    const int D = latent ? latent->latent : H;
+    Carve c(ws);
+    ForwardWs w = carve_forward(c, cfg, dtype, T, H, I, latent, shared);
+    auto mark = [&](int stage, int end) -> moe_status_t {
+        if (!ev) return MOE_OK;
+        return hip_status(hipEventRecord(ev[2 * stage + end], s));
+    };
+    auto skip = [&](int stage) -> moe_status_t {
+        MOE_TRY(mark(stage, 0));
+        return mark(stage, 1);
+    };
+
+    // router logits (fp32 accumulate, fp32 out, + optional bias row)
+    const float* logits = router_logits;
+    if (!logits) {
+        float* lo = logits_out ? logits_out : w.logits;
+        MOE_TRY(mark(MOE_STAGE_ROUTER, 0));
+        MOE_TRY(dense_gemm(dtype, T, x, H, w_router, H, nullptr, 0, nullptr, 0, E, EPI_F32_BIAS,
+                           lo, E, router_bias, s));
+        MOE_TRY(mark(MOE_STAGE_ROUTER, 1));
+        logits = lo;
+    } else {
+        MOE_TRY(skip(MOE_STAGE_ROUTER));
+        if (logits_out && logits_out != router_logits)
+            MOE_HIP(hipMemcpyAsync(logits_out, router_logits, (size_t)T * E * sizeof(float),
+                                   hipMemcpyDeviceToDevice, s));
+    }
+
+    // latent down-projection of the routed input
+    const void* xin = x;
+    if (latent) {
+        MOE_TRY(mark(MOE_STAGE_DOWNPROJ, 0));
+        MOE_TRY(dense_gemm(dtype, T, x, H, latent->w_down, H, nullptr, 0, nullptr, 0, D, EPI_OUT,
+                           w.z, D, nullptr, s));
+        MOE_TRY(mark(MOE_STAGE_DOWNPROJ, 1));
+        xin = w.z;
+    } else {
+        MOE_TRY(skip(MOE_STAGE_DOWNPROJ));
+    }
+
+    // routing
+    int32_t* ids = topk_ids_out ? topk_ids_out : w.ids;
+    float* wts = topk_weights_out ? topk_weights_out : w.weights;
+    MOE_TRY(mark(MOE_STAGE_ROUTE, 0));
+    MOE_TRY(moe_route(cfg, T, logits, correction_bias, ids, wts, stream));
+    MOE_TRY(mark(MOE_STAGE_ROUTE, 1));
+
+    // dispatch bookkeeping
+    int32_t* counts = expert_counts_out ? expert_counts_out : w.counts;
+    MOE_TRY(mark(MOE_STAGE_PERMUTE, 0));
+    MOE_HIP(launch_permute(T * k, E, ids, counts, w.offsets, w.r2p, w.p2r, w.chunks, s));
+    MOE_TRY(mark(MOE_STAGE_PERMUTE, 1));
+
+    // routed experts
+    MOE_TRY(run_experts(dtype, T, k, E, D, I, xin, w.offsets, w.r2p, w13, w2, w.y_rows, w.ex, s,
+                        ev));
+
+    // shared expert without a latent tail: its output is the combine addend
+    if (shared && !latent) {
+        MOE_TRY(mark(MOE_STAGE_SHARED, 0));
+        MOE_TRY(dense_gemm(dtype, T, x, H, shared->w13, H, nullptr, 0, nullptr, 0, shared->inter,
+                           EPI_SWIGLU, w.h_sh, shared->inter, nullptr, s));
+        MOE_TRY(dense_gemm(dtype, T, w.h_sh, shared->inter, shared->w2, shared->inter, nullptr,
+                           0, nullptr, 0, H, EPI_F32, w.sh, H, nullptr, s));
+        MOE_TRY(mark(MOE_STAGE_SHARED, 1));
+    }
+
+    // combine (+ fused RMSNorm when latent, + shared addend otherwise)
+    CombineArgs ca;
+    memset(&ca, 0, sizeof(ca));
+    ca.T = T;
+    ca.k = k;
+    ca.D = D;
+    ca.y_rows = w.y_rows;
+    ca.pair_to_row = w.p2r;
+    ca.weights = wts;
+    ca.out_dtype = dtype == MOE_DTYPE_F32 ? 0 : 1;
+    if (latent) {
+        ca.gamma = latent->gamma;
+        ca.eps = latent->rms_eps;
+        ca.out = w.normed;
+    } else {
+        ca.addend = w.sh;
+        ca.out = out;
+    }
+    MOE_TRY(mark(MOE_STAGE_COMBINE, 0));
+    MOE_HIP(launch_combine(ca, s));
+    MOE_TRY(mark(MOE_STAGE_COMBINE, 1));
+
+    if (latent) {
+        if (shared) {
+            MOE_TRY(mark(MOE_STAGE_SHARED, 0));
+            MOE_TRY(dense_gemm(dtype, T, x, H, shared->w13, H, nullptr, 0, nullptr, 0,
+                               shared->inter, EPI_SWIGLU, w.h_sh, shared->inter, nullptr, s));
+            MOE_TRY(mark(MOE_STAGE_SHARED, 1));
+        } else {
+            MOE_TRY(skip(MOE_STAGE_SHARED));
+        }
+        // out = normed . w_up^T (+ h_sh . w2_sh^T): one K-concatenated product,
+        // one fp32 sum, one rounding
+        MOE_TRY(mark(MOE_STAGE_TAIL, 0));
+        MOE_TRY(dense_gemm(dtype, T, w.normed, D, latent->w_up, D, shared ? w.h_sh : nullptr,
+                           shared ? shared->inter : 0, shared ? shared->w2 : nullptr,
+                           shared ? shared->inter : 0, H, EPI_OUT, out, H, nullptr, s));
+        MOE_TRY(mark(MOE_STAGE_TAIL, 1));
+    } else {
+        if (!shared) MOE_TRY(skip(MOE_STAGE_SHARED));
+        MOE_TRY(skip(MOE_STAGE_TAIL));
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// Dispatch bookkeeping: per-expert counts, their exclusive prefix sum, and a
+// stable expert-sorted order of the (token, slot) pairs.
+//
+// "vLLM-Ascend Kimi K3 MoE Forward Insight", Stage 4 (mode table, AllGather
+// row): dispatch sorts tokens by expert and returns the expert token counts;
+// Stage 6: that list is per-expert counts or cumulative -- both are produced.
+//
+// Three small kernels, deterministic by construction (LDS atomics only count;
+// no atomic decides a position):
+//   count   -- one block per chunk of 1024 pairs builds the chunk's histogram;
+//   scan    -- one block turns the chunk histograms into per-(chunk, expert)
+//              base rows, and writes counts and offsets;
+//   scatter -- one wavefront per chunk walks its pairs in order, 64 at a
+//              time; lanes holding the same expert find each other with one
+//              ballot per id bit (a wave-wide multi-split), take their rank
+//              among lower lanes, and the lowest of them advances the
+//              expert's running row in LDS.
+// A fourth kernel turns the offsets into the tile list of a grouped GEMM.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kChunk = 1024;
+
+__global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ ids, int64_t P,
+                                                   int E, int32_t* __restrict__ chunk_counts) {
+    __shared__ int hist[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kChunk;
+    for (int i = threadIdx.x; i < kChunk; i += blockDim.x) {
+        int64_t p = base + i;
+        if (p < P) atomicAdd(&hist[ids[p]], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// Exclusive scan of one int per thread across a 1024-thread block.
+__device__ int block_exclusive_scan(int v, int* sh, int& total) {
+    const int tid = threadIdx.x;
+    sh[tid] = v;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        int add = tid >= d ? sh[tid - d] : 0;
+        __syncthreads();
+        sh[tid] += add;
+        __syncthreads();
+    }
+    total = sh[1023];
+    int incl = sh[tid];
+    __syncthreads();
+    return incl - v;
+}
+
+__global__ __launch_bounds__(1024) void perm_scan(int nchunk, int E, int32_t* __restrict__ cc,
+                                                  int32_t* __restrict__ counts,
+                                                  int32_t* __restrict__ offsets) {
+    __shared__ int sh[1024];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        for (int c = 0; c < nchunk; ++c) {
+            int v = cc[(int64_t)c * E + e];
+            cc[(int64_t)c * E + e] = run;
+            run += v;
+        }
+    }
+    int total;
+    int off = block_exclusive_scan(e < E ? run : 0, sh, total);
+    if (e < E) {
+        counts[e] = run;
+        offsets[e] = off;
+        for (int c = 0; c < nchunk; ++c) cc[(int64_t)c * E + e] += off;
+    }
+    if (e == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(64) void perm_scatter(const int32_t* __restrict__ ids, int64_t P,
+                                                   int E, int nbits,
+                                                   const int32_t* __restrict__ chunk_base,
+                                                   int32_t* __restrict__ row_to_pair,
+                                                   int32_t* __restrict__ pair_to_row) {
+    __shared__ int cur[kMaxExperts];
+    const int lane = threadIdx.x;
+    for (int e = lane; e < E; e += 64) cur[e] = chunk_base[(int64_t)blockIdx.x * E + e];
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kChunk;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int s = 0; s < kChunk && base + s < P; s += 64) {
+        const int64_t p = base + s + lane;
+        const bool valid = p < P;
+        const int id = valid ? ids[p] : 0;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (id >> b) & 1;
+            const uint64_t bb = __ballot(valid && bit);
+            peers &= bit ? bb : ~bb;
+        }
+        const int rank = __popcll(peers & below);
+        const int cnt = __popcll(peers);
+        const int b0 = valid ? cur[id] : 0;
+        __syncthreads();
+        if (valid) {
+            const int row = b0 + rank;
+            row_to_pair[row] = (int32_t)p;
+            pair_to_row[p] = row;
+            if (rank == 0) cur[id] = b0 + cnt;
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                           int E, int tile_m, Tile* __restrict__ tiles,
+                                                           int32_t* __restrict__ num_tiles) {
+    __shared__ int sh[1024];
+    const int e = threadIdx.x;
+    const int a = e < E ? offsets[e] : 0;
+    const int b = e < E ? offsets[e + 1] : 0;
+    const int nt = (b - a + tile_m - 1) / tile_m;
+    int total;
+    const int start = block_exclusive_scan(nt, sh, total);
+    for (int i = 0; i < nt; ++i) {
+        Tile t;
+        t.group = e;
+        t.row0 = a + i * tile_m;
+        t.row1 = min(a + (i + 1) * tile_m, b);
+        t.pad = 0;
+        tiles[start + i] = t;
+    }
+    if (e == 0) *num_tiles = total;
+}
+
+}  // namespace
+
+int permute_chunks(int64_t P) { return (int)((P + kChunk - 1) / kChunk); }
+
+hipError_t launch_permute(int64_t P, int32_t E, const int32_t* ids, int32_t* counts,
+                          int32_t* offsets, int32_t* row_to_pair, int32_t* pair_to_row,
+                          int32_t* chunk_scratch, hipStream_t s) {
+    const int nchunk = permute_chunks(P);
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    if (nchunk > 0) perm_count<<<nchunk, 256, 0, s>>>(ids, P, E, chunk_scratch);
+    perm_scan<<<1, 1024, 0, s>>>(nchunk, E, chunk_scratch, counts, offsets);
+    if (nchunk > 0)
+        perm_scatter<<<nchunk, 64, 0, s>>>(ids, P, E, nbits, chunk_scratch, row_to_pair,
+                                           pair_to_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_build_tiles(const int32_t* offsets, int32_t E, int32_t tile_m, Tile* tiles,
+                              int32_t* num_tiles, hipStream_t s) {
+    build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_m, tiles, num_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,108 @@
+"""Shared helpers of the parity tests: conversions between torch tensors and
+the oracle's numpy arrays, routing settings in both vocabularies, and the
+tolerance checks written out once."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+from routed_mixture_experts_amd import RouteConfig
+from routed_mixture_experts_amd.synth import Workload
+
+# Float output bars: bf16 layers -- relative L2 <= 1e-2 and max |err| <= 3e-2 * rms(ref);
+# fp32 layers -- relative L2 <= 1e-5.
+BF16_REL_L2 = 1e-2
+BF16_MAX_ABS_OVER_RMS = 3e-2
+F32_REL_L2 = 1e-5
+WEIGHT_ATOL = 1e-6
+
+
+def np64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 copy of a torch tensor (bf16 and fp32 upcast exactly)."""
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def npi(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().astype(np.int64)
+
+
+def oracle_cfg(w: Workload) -> O.RouteCfg:
+    return O.RouteCfg(num_experts=w.E, top_k=w.k, num_groups=w.num_groups,
+                      topk_group=w.topk_group, score=w.score, group_score=w.group_score,
+                      renormalize=w.renormalize, routed_scaling=w.routed_scaling)
+
+
+def lib_cfg(w: Workload) -> RouteConfig:
+    return RouteConfig(num_experts=w.E, top_k=w.k, num_groups=w.num_groups,
+                       topk_group=w.topk_group, score=w.score, group_score=w.group_score,
+                       renormalize=w.renormalize, routed_scaling=w.routed_scaling)
+
+
+class ExpertFetch:
+    """w[e] -> expert e's matrix as float64 numpy, copied from the device one
+    expert at a time (the full weight tensor can be tens of GB)."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t = t
+
+    def __getitem__(self, e):
+        return self.t[int(e)].to(torch.float64).cpu().numpy()
+
+
+def latent_np(inp: dict, w: Workload):
+    if not w.latent:
+        return None
+    return dict(w_down=np64(inp["w_down"]), gamma=np64(inp["gamma"]),
+                w_up=np64(inp["w_up"]), eps=w.rms_eps)
+
+
+def shared_np(inp: dict, w: Workload):
+    if not w.shared_inter:
+        return None
+    return dict(w13=np64(inp["w13_sh"]), w2=np64(inp["w2_sh"]))
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_float(gpu: np.ndarray, ref: np.ndarray, is_bf16: bool, what: str = "out"):
+    """The float bar, printed next to the unavoidable bf16 rounding floor."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    err = gpu - ref
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    rel = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-300))
+    mx = float(np.abs(err).max() / max(rms, 1e-300)) if err.size else 0.0
+    if is_bf16:
+        floor = torch.from_numpy(ref).to(torch.bfloat16).to(torch.float64).numpy() - ref
+        fl = float(np.abs(floor).max() / max(rms, 1e-300)) if err.size else 0.0
+        log(f"[{what}] rel_l2={rel:.3e} (bar {BF16_REL_L2}) max_abs/rms={mx:.3e} "
+            f"(bar {BF16_MAX_ABS_OVER_RMS}, bf16 rounding floor {fl:.3e}) n={ref.size}")
+        assert rel <= BF16_REL_L2, (what, rel)
+        assert mx <= BF16_MAX_ABS_OVER_RMS, (what, mx)
+    else:
+        log(f"[{what}] rel_l2={rel:.3e} (bar {F32_REL_L2}) n={ref.size}")
+        assert rel <= F32_REL_L2, (what, rel)
+
+
+def check_ids_allowing_near_ties(gpu_ids: np.ndarray, ref_ids: np.ndarray, keys: np.ndarray,
+                                 eps: float):
+    """Ids must match exactly, except where the oracle's keys of the two
+    experts in a differing slot lie within ``eps`` of each other (routing
+    there depends on the last bits of a float product, so both answers are
+    valid).  Returns the mask of tokens that matched exactly."""
+    T, k = ref_ids.shape
+    same = (gpu_ids == ref_ids).all(axis=1)
+    for t in np.nonzero(~same)[0]:
+        assert len(set(gpu_ids[t].tolist())) == k, f"token {t}: repeated expert {gpu_ids[t]}"
+        for j in np.nonzero(gpu_ids[t] != ref_ids[t])[0]:
+            gap = abs(keys[t, gpu_ids[t, j]] - keys[t, ref_ids[t, j]])
+            assert gap <= eps, (f"token {t} slot {j}: ids {gpu_ids[t]} vs {ref_ids[t]}, "
+                                f"key gap {gap:.3e} > {eps:.1e}")
+    return same

@@ -1,0 +1,136 @@
+"""Host-side checks of the C-ABI library that need no GPU.
+
+The library loads, exports every function include/moe.h declares, sizes its
+workspaces consistently, and rejects bad arguments on the host before it
+would launch anything (so none of these calls reaches the GPU).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routed_mixture_experts_amd as moe
+from routed_mixture_experts_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\*?\s+\*?(moe_[a-z_]+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libmoe.so is not built (python -m routed_mixture_experts_amd.build)")
+    return L.load()
+
+
+def test_header_declares_the_five_calls():
+    names = _declared_functions()
+    for n in ["moe_route", "moe_permute", "moe_experts", "moe_combine", "moe_forward"]:
+        assert n in names
+    assert sorted(L.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert lib.moe_status_string(st)
+    assert b"unknown" in lib.moe_status_string(99)
+
+
+def _cfg(**kw):
+    base = dict(num_experts=16, top_k=4)
+    base.update(kw)
+    return moe.RouteConfig(**base).c()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_experts=0), L.MOE_EINVAL),
+    (dict(top_k=0), L.MOE_EINVAL),
+    (dict(top_k=17), L.MOE_EINVAL),               # k > E
+    (dict(num_experts=2048, top_k=4), L.MOE_ENOTSUP),
+    (dict(top_k=33, num_experts=64), L.MOE_ENOTSUP),
+    (dict(num_groups=3), L.MOE_EINVAL),           # E % G != 0
+    (dict(num_groups=4, topk_group=5), L.MOE_EINVAL),
+    (dict(num_groups=8, topk_group=1), L.MOE_EINVAL),   # 1 group of 2 < k
+    (dict(num_groups=16, topk_group=16, group_score="top2sum"), L.MOE_EINVAL),
+])
+def test_route_rejects_bad_config(lib, kw, code):
+    c = _cfg(**kw)
+    st = lib.moe_route(ctypes.byref(c), 8, ctypes.c_void_p(16), None, ctypes.c_void_p(16),
+                       ctypes.c_void_p(16), None)
+    assert st == code
+
+
+def test_route_null_pointers_and_empty(lib):
+    c = _cfg()
+    assert lib.moe_route(ctypes.byref(c), 8, None, None, None, None, None) == L.MOE_EINVAL
+    assert lib.moe_route(ctypes.byref(c), -1, None, None, None, None, None) == L.MOE_EINVAL
+    assert lib.moe_route(None, 8, None, None, None, None, None) == L.MOE_EINVAL
+    # T == 0 launches nothing and succeeds
+    assert lib.moe_route(ctypes.byref(c), 0, None, None, None, None, None) == L.MOE_OK
+
+
+def test_workspace_sizes_grow_with_capacity(lib):
+    a = lib.moe_permute_workspace(128, 8, 384)
+    b = lib.moe_permute_workspace(8192, 8, 384)
+    assert 0 < a < b
+    e1 = lib.moe_experts_workspace(L.MOE_DTYPE_BF16, 128, 8, 384, 7168, 2048)
+    e2 = lib.moe_experts_workspace(L.MOE_DTYPE_BF16, 8192, 8, 384, 7168, 2048)
+    # the intermediate h alone is P * I bf16 values
+    assert e1 >= 128 * 8 * 2048 * 2 and e2 >= 8192 * 8 * 2048 * 2 and e2 > e1
+    c = _cfg(num_experts=384, top_k=8)
+    f = lib.moe_forward_workspace(ctypes.byref(c), L.MOE_DTYPE_BF16, 8192, 7168, 2048, None,
+                                  None)
+    # y_rows in fp32 dominates: P * D * 4 bytes
+    assert f >= 8192 * 8 * 7168 * 4
+    assert lib.moe_forward_workspace(ctypes.byref(c), 7, 128, 7168, 2048, None, None) == 0
+
+
+def test_forward_rejects_unaligned_and_missing(lib):
+    c = _cfg(num_experts=8, top_k=2)
+    # H not a multiple of 64
+    st = lib.moe_forward(ctypes.byref(c), L.MOE_DTYPE_BF16, 4, 100, 64, *([None] * 15), None, 0,
+                         None)
+    assert st == L.MOE_ENOTSUP
+    # missing weights
+    st = lib.moe_forward(ctypes.byref(c), L.MOE_DTYPE_BF16, 4, 128, 64, *([None] * 15), None, 0,
+                         None)
+    assert st == L.MOE_EINVAL
+    # workspace too small (pointers only need to be non-null for the check)
+    p = ctypes.c_void_p(256)
+    st = lib.moe_forward(ctypes.byref(c), L.MOE_DTYPE_BF16, 4, 128, 64, p, p, None, None, None,
+                         p, p, None, None, p, None, None, None, None, None, p, 16, None)
+    assert st == L.MOE_ENOSPACE
+    lat = L.moe_latent_t(p, p, p, 100, 1e-6)
+    st = lib.moe_forward(ctypes.byref(c), L.MOE_DTYPE_BF16, 4, 128, 64, p, p, None, None, None,
+                         p, p, ctypes.byref(lat), None, p, None, None, None, None, None, p,
+                         1 << 30, None)
+    assert st == L.MOE_ENOTSUP
+
+
+def test_experts_and_combine_validation(lib):
+    p = ctypes.c_void_p(256)
+    assert lib.moe_experts(L.MOE_DTYPE_BF16, 4, 2, 8, 100, 64, p, p, p, p, p, p, p, 1 << 20,
+                           None) == L.MOE_ENOTSUP
+    assert lib.moe_experts(L.MOE_DTYPE_BF16, 4, 2, 8, 128, 64, p, p, p, p, p, p, p, 16,
+                           None) == L.MOE_ENOSPACE
+    assert lib.moe_experts(L.MOE_DTYPE_BF16, 0, 2, 8, 128, 64, None, None, None, None, None,
+                           None, None, 0, None) == L.MOE_OK
+    assert lib.moe_combine(L.MOE_DTYPE_BF16, 4, 2, 6, p, p, p, p, None) == L.MOE_ENOTSUP
+    assert lib.moe_combine(L.MOE_DTYPE_BF16, 4, 40, 8, p, p, p, p, None) == L.MOE_ENOTSUP
+    assert lib.moe_combine(L.MOE_DTYPE_BF16, 0, 2, 8, None, None, None, None, None) == L.MOE_OK
+    assert lib.moe_permute(4, 9, 8, p, p, p, p, p, p, 1 << 20, None) == L.MOE_EINVAL
+    assert lib.moe_permute(4, 2, 8, p, p, p, p, p, p, 0, None) == L.MOE_ENOSPACE
