@@ -1,0 +1,267 @@
+"""Routed-MoE layer throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+A step is one moe_forward (router logits -> scoring/top-k -> permute ->
+gate/up+SwiGLU -> down -> combine) over one batch of synthetic tokens already
+resident in HBM.  The headline workload is the decode-shaped bf16 layer
+(T=128, H=7168, 384 experts, top-8, I=2048, routed scaling 2.5); the
+prefill-shaped layer (T=8192, Zipf(1.1) expert load) runs on the same weights
+and is reported beside it.  Prints ONE JSON line.
+
+Per-stage times come from HIP events recorded by the library between its
+kernels on the timed stream, over the timed steps themselves.  The roofline
+entry is the dominant kernel (gate/up + SwiGLU): algorithmic bytes = the
+touched experts' gate/up weights + the token activations read + h written.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
+METRIC = "MoE layer tokens/s (T=128 decode, T=8192 prefill); % of HBM/MFMA roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill_zipf", "grouped_sqrtsoftplus", "latent_shared"])
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill line")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=48)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run three plain 1 GiB device-to-device copies (a known-size "
+                         "reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def describe(w) -> str:
+    s = (f"{w.name} {w.dtype} T={w.T} H={w.H} E={w.E} top-{w.k} I={w.I} score={w.score}"
+         f" renormalize={w.renormalize} routed_scaling={w.routed_scaling}")
+    if w.num_groups > 1:
+        s += f" groups={w.num_groups} topk_group={w.topk_group} group_score={w.group_score}"
+    if w.corr_bias:
+        s += f" correction_bias=U(-{w.corr_bias},{w.corr_bias})"
+    if w.zipf_s:
+        s += f" router_bias=Zipf({w.zipf_s})"
+    if w.latent:
+        s += f" latent={w.latent}"
+    if w.shared_inter:
+        s += f" shared_I={w.shared_inter}"
+    return s
+
+
+def layer_work(w, counts):
+    """Algorithmic bytes and FLOPs of one forward: touched expert weights,
+    router (and dense) weights, x in, out out; intermediates excluded."""
+    es = 2 if w.dtype == "bf16" else 4
+    D = w.D
+    touched = int((counts > 0).sum())
+    P = w.T * w.k
+    wbytes = touched * 3 * w.I * D * es + w.E * w.H * es
+    flops = 2.0 * P * 3 * D * w.I + 2.0 * w.T * w.H * w.E
+    if w.latent:
+        wbytes += 2 * w.latent * w.H * es
+        flops += 2.0 * w.T * w.H * w.latent * 2
+    if w.shared_inter:
+        wbytes += 3 * w.shared_inter * w.H * es
+        flops += 2.0 * w.T * 3 * w.H * w.shared_inter
+    abytes = 2 * w.T * w.H * es
+    return wbytes + abytes, flops, touched
+
+
+def gemm1_bytes(w, counts):
+    """Algorithmic bytes of one gate/up + SwiGLU launch: gate/up weights of the
+    touched experts (unit: one expert, 2*I*D elements), the token activations
+    read once, and h written."""
+    es = 2 if w.dtype == "bf16" else 4
+    touched = int((counts > 0).sum())
+    return touched * 2 * w.I * w.D * es + w.T * w.D * es + w.T * w.k * w.I * es, touched
+
+
+class Runner:
+    """Holds inputs, outputs, workspace and events of one workload."""
+
+    def __init__(self, w, inp, torch, moe, stream):
+        self.w, self.inp, self.torch, self.moe, self.stream = w, inp, torch, moe, stream
+        dev = inp["x"].device
+        self.cfg = moe.RouteConfig(w.E, w.k, w.num_groups, w.topk_group, w.score,
+                                   w.group_score, w.renormalize, w.routed_scaling)
+        self.lat = (dict(w_down=inp["w_down"], gamma=inp["gamma"], w_up=inp["w_up"],
+                         eps=w.rms_eps) if w.latent else None)
+        self.sh = dict(w13=inp["w13_sh"], w2=inp["w2_sh"]) if w.shared_inter else None
+        nbytes = moe.moe_forward_workspace(self.cfg, inp["x"].dtype, w.T, w.H, w.I,
+                                           self.lat, self.sh)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.out = torch.empty((w.T, w.H), dtype=inp["x"].dtype, device=dev)
+        self.counts = torch.empty((w.E,), dtype=torch.int32, device=dev)
+
+    def step(self, events=None):
+        i = self.inp
+        self.moe.moe_forward(self.cfg, i["x"], i["w13"], i["w2"], w_router=i["w_router"],
+                             router_bias=i["router_bias"], correction_bias=i["corr_bias"],
+                             latent=self.lat, shared=self.sh, out=self.out,
+                             expert_counts_out=self.counts, stage_events=events,
+                             workspace=self.ws, stream=self.stream)
+
+    def timed(self, steps, warmup):
+        torch, moe = self.torch, self.moe
+        for _ in range(warmup):
+            self.step()
+        nev = 2 * moe.MOE_NUM_STAGES
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+        for row in evs:             # materialise the HIP events on this stream
+            for e in row:
+                e.record(self.stream)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(self.stream)
+        for s in range(steps):
+            self.step(evs[s])
+        end.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = start.elapsed_time(end) / steps
+        stage = {}
+        for i, name in enumerate(moe.STAGES):
+            d = [evs[s][2 * i].elapsed_time(evs[s][2 * i + 1]) for s in range(steps)]
+            stage[name] = sum(d) / steps
+        return ms, wall * 1e3 / steps, stage
+
+
+def cpu_baseline(w, inp, torch, ntok):
+    """The oracle as it stands, timed on the host cores on the first ``ntok``
+    tokens of the batch (routing from its own float64 router product, stable
+    permute, per-expert float64 MLPs of the experts those tokens touch,
+    combine).  Weight copies to the host are made before the clock starts."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle as O
+    x = inp["x"][:ntok].to(torch.float64).cpu().numpy()
+    wr = inp["w_router"].to(torch.float64).cpu().numpy()
+    rb = None if inp["router_bias"] is None else inp["router_bias"].double().cpu().numpy()
+    cb = None if inp["corr_bias"] is None else inp["corr_bias"].double().cpu().numpy()
+    cfg = O.RouteCfg(num_experts=w.E, top_k=w.k, num_groups=w.num_groups,
+                     topk_group=w.topk_group, score=w.score, group_score=w.group_score,
+                     renormalize=w.renormalize, routed_scaling=w.routed_scaling)
+    ids, _, _ = O.route(O.router_logits(x, wr, rb), cfg, cb)
+    used = sorted(set(ids.reshape(-1).tolist()))
+    # host copies (fp32, exact for bf16) of just the experts the sample touches
+    w13 = {e: inp["w13"][e].float().cpu().numpy() for e in used}
+    w2 = {e: inp["w2"][e].float().cpu().numpy() for e in used}
+    info = threadpoolctl.threadpool_info()
+    cores = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    O.forward(x, cfg, w13, w2, w_router=wr, router_bias=rb, corr_bias=cb)
+    dt = time.perf_counter() - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"first {ntok} of {w.T} tokens of the {w.name} batch ({len(used)} "
+                       f"experts touched), numpy float64 oracle forward incl. its own router "
+                       f"product; {dt:.2f} s")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import routed_mixture_experts_amd as moe
+    from routed_mixture_experts_amd.synth import WORKLOADS, make_inputs
+
+    moe.load()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    w = WORKLOADS[args.workload]
+    print(f"[bench] generating inputs for {w.name}", file=sys.stderr, flush=True)
+    inp = make_inputs(w, dev, chunk_rows=16)
+    run = Runner(w, inp, torch, moe, stream)
+    print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr,
+          flush=True)
+    ms, wall_ms, stage = run.timed(args.steps, args.warmup)
+    counts = run.counts.cpu().numpy()
+    abytes, aflops, touched = layer_work(w, counts)
+    g1b, _ = gemm1_bytes(w, counts)
+    g1_ms = stage["gemm1"]
+    g1_gbs = g1b / (g1_ms * 1e-3) / 1e9
+    t_s = ms * 1e-3
+    res = {
+        "metric": METRIC,
+        "value": w.T / t_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": {"workload": describe(w), "tokens": w.T, "touched_experts": touched,
+                   "parallelism": "none (1 GPU holds all experts)"},
+        "roofline": {"bound": "hbm", "achieved": g1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": g1_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gemm_bf16_stream<SWIGLU> (gate/up + SwiGLU)"
+                     if w.T * w.k <= 24 * w.E else "gemm_bf16_tiled<SWIGLU> (gate/up + SwiGLU)",
+                     "kernel_ms": g1_ms, "algorithmic_bytes": g1b},
+        "layer": {"hbm_GBps": abytes / t_s / 1e9, "hbm_frac": abytes / t_s / 1e9 / HBM_PEAK_GBS,
+                  "mfma_frac": aflops / t_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                  "algorithmic_bytes": abytes, "algorithmic_flops": aflops,
+                  "host_wall_ms_per_step": wall_ms},
+        "stages_ms": stage,
+    }
+    if args.workload == "decode" and not args.no_prefill:
+        wp = WORKLOADS["prefill_zipf"]
+        print("[bench] prefill on the same weights", file=sys.stderr, flush=True)
+        from routed_mixture_experts_amd.synth import SEED_X, normal, zipf_router_bias
+        pin = dict(inp)
+        pin["x"] = normal((wp.T, wp.H), 1.0, SEED_X, torch.bfloat16, dev)
+        pin["router_bias"] = zipf_router_bias(wp.E, wp.k, wp.T, wp.zipf_s).to(dev)
+        prun = Runner(wp, pin, torch, moe, stream)
+        psteps = max(3, args.steps // 2)
+        pms, _, pstage = prun.timed(psteps, max(1, args.warmup // 2))
+        pc = prun.counts.cpu().numpy()
+        pbytes, pflops, ptouched = layer_work(wp, pc)
+        res["prefill"] = {
+            "workload": describe(wp), "value": wp.T / (pms * 1e-3), "unit": "tokens/s",
+            "ms_per_step": pms, "steps": psteps,
+            "hbm_frac": pbytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_frac": pflops / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "load": {"max": int(pc.max()), "min": int(pc.min()), "empty": int((pc == 0).sum())},
+            "stages_ms": pstage}
+        del prun, pin
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, inp, torch, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -114,8 +114,8 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
     const int path = expert_path(dt, T, k, E);
     const int idt = dt == MOE_DTYPE_F32 ? 0 : 1;
     const int tm = gemm_row_tile(idt, path);
-    if (ev) MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM1], s));
     MOE_HIP(launch_build_tiles(offsets, E, tm, w.tiles, w.ntiles, s));
+    if (ev) MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM1], s));
 
     GemmArgs g1 = gemm_defaults();
     g1.A = x;
