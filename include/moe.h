@@ -27,7 +27,9 @@
  *   - Errors: arguments are validated on the host before anything is
  *     launched; a failed check launches nothing and returns MOE_EINVAL
  *     (inconsistent or null arguments), MOE_ENOTSUP (a shape this build does
- *     not handle: widths not multiples of 64, E > 1024, k > 32) or
+ *     not handle: widths not multiples of 64, E > 1024, k > 32, an
+ *     activation, intermediate or single-expert weight tensor of 4 GiB or
+ *     more) or
  *     MOE_ENOSPACE (workspace too small).  A failed launch returns MOE_EHIP.
  *     T == 0 is valid and launches nothing.  No C++ exception crosses the ABI.
  *   - Preconditions the kernels do not check: logits finite; topk_ids in [0,E).

@@ -36,7 +36,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ float silu_f32(float g) {
-    return g / (1.0f + __expf(-g));
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
 // Tile-list entry of a grouped GEMM: rows [row0, row1) of group g.
@@ -98,14 +98,19 @@ int permute_chunks(int64_t P);
 hipError_t launch_permute(int64_t P, int32_t E, const int32_t* ids, int32_t* counts,
                           int32_t* offsets, int32_t* row_to_pair, int32_t* pair_to_row,
                           int32_t* chunk_scratch, hipStream_t s);
-hipError_t launch_build_tiles(const int32_t* offsets, int32_t E, int32_t tile_m, Tile* tiles,
-                              int32_t* num_tiles, hipStream_t s);
+// Splits the groups into a small-tile list (one tile per group of 1..small_max
+// rows) and a big-tile list (big_m-row tiles of the larger groups).
+hipError_t launch_build_tiles(const int32_t* offsets, int32_t E, int32_t small_max,
+                              int32_t big_m, Tile* small_tiles, int32_t* num_small,
+                              Tile* big_tiles, int32_t* num_big, hipStream_t s);
 
 // dtype: 0 = f32, 1 = bf16.  path: see gemm.hip (chosen by the caller).
-enum GemmPath : int { GEMM_TILED = 0, GEMM_STREAM = 1 };
+enum GemmPath : int { GEMM_TILED = 0, GEMM_STREAM = 1, GEMM_BIG = 2 };
 hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s);
 // Rows per tile of a kernel (a grouped tile list must be built with it).
 int gemm_row_tile(int dtype, int path);
+// Largest group the streaming kernel takes as a single tile.
+constexpr int kStreamMaxRows = 64;
 
 struct CombineArgs {
     int64_t T;

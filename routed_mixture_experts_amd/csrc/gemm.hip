@@ -53,9 +53,11 @@ __device__ __forceinline__ bool fetch_tile(const GemmArgs& g, int tile_m, int nt
     c.nt = lid - mt * ntn;
     if (g.tiles) {
         const Tile t = g.tiles[mt];
-        c.group = t.group;
-        c.row0 = t.row0;
-        c.row1 = t.row1;
+        // the tile is the same for the whole workgroup: keep it in SGPRs so
+        // that every branch on it is a scalar branch
+        c.group = __builtin_amdgcn_readfirstlane(t.group);
+        c.row0 = __builtin_amdgcn_readfirstlane(t.row0);
+        c.row1 = __builtin_amdgcn_readfirstlane(t.row1);
     } else {
         c.group = 0;
         c.row0 = mt * tile_m;
@@ -214,29 +216,224 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------------
-// bf16 weight-streaming MFMA kernel (<= 16 rows per tile)
+// bf16 256x256 MFMA kernel for grouped products with many rows per group
 // ------------------------------------------------------------------------
-constexpr int SROWS = 16;   // token rows per tile
-constexpr int SNW = 64;     // weight rows per workgroup
-constexpr int SU = 4;       // k-steps (of 32) per load batch
+// 4 waves in a 2x2 layout, each a 128x128 block of 4x4 v_mfma_f32_32x32x16_bf16
+// tiles (256 fp32 accumulators per lane).  K advances 32 at a time; global
+// loads run two stages ahead through registers into a 2-slot LDS ring.  LDS
+// rows are 64 bytes (32 bf16) and the four 16-byte chunks of row r sit at
+// chunk ^ (((r >> 1) ^ (r >> 2)) & 3): any 8 consecutive rows (one 128-byte
+// bank sweep) and any 16 consecutive rows (one 256-byte sweep) then touch
+// distinct banks, for the writes and for the MFMA operand reads.  A wave
+// skips the MFMAs (and operand reads) of its 32-row blocks that lie past the
+// tile's last row, and threads skip loading those activation rows, so a group
+// with few rows costs little more than streaming its weights once.
+constexpr int GBM = 256, GBN = 256, GBK = 32;
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+    return chunk ^ (((row >> 1) ^ (row >> 2)) & 3);
+}
 
 template <int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_stream(GemmArgs g) {
+__global__ __launch_bounds__(256, 1) void gemm_bf16_big(GemmArgs g) {
     constexpr bool SW = EPI == EPI_SWIGLU;
-    const int ntn = SW ? (g.N + 31) / 32 : (g.N + SNW - 1) / SNW;
+    const int ntn = SW ? (g.N + 127) / 128 : (g.N + GBN - 1) / GBN;
     TileCoord tc;
-    if (!fetch_tile(g, SROWS, ntn, tc)) return;
+    if (!fetch_tile(g, GBM, ntn, tc)) return;
 
-    __shared__ float red[4][4][4][64];
+    __shared__ __attribute__((aligned(16))) bf16_t sA[2][GBM * GBK];
+    __shared__ __attribute__((aligned(16))) bf16_t sB[2][GBN * GBK];
 
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = tid >> 2, lc = tid & 3;
+
+    const bf16_t* Bg = (const bf16_t*)g.B + (int64_t)tc.group * g.b_gstride;
+
+    // 32-bit byte offsets from the (wave-uniform) operand bases: one VGPR per
+    // row and scalar-base addressing; each group's operands fit in 4 GiB
+    // (checked on the host).
+    const char* Ab = (const char*)g.A;
+    const char* Bb = (const char*)Bg;
+    const char* A2b = (const char*)g.A2;
+    const char* B2b = (const char*)g.B2;
+    // Rows past the tile's end load the tile's first row instead: the loop
+    // then has no divergent branches, and the repeated address costs one
+    // request per load instruction.
+    uint32_t ao[4], bo[4], ao2[4], bo2[4];
+    int soff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = lr + 64 * i;
+        const int r = tc.row0 + row;
+        const int rr = r < tc.row1 ? r : tc.row0;
+        ao[i] = (uint32_t)(a_row_of(g, rr) * g.lda * 2) + lc * 16;
+        ao2[i] = (uint32_t)((int64_t)rr * g.lda2 * 2) + lc * 16;
+        int wrow;
+        if (SW) {
+            const int c = min(tc.nt * 128 + (row & 127), g.N - 1);
+            wrow = row < 128 ? c : g.N + c;
+        } else {
+            wrow = min(tc.nt * GBN + row, g.N - 1);
+        }
+        bo[i] = (uint32_t)((int64_t)wrow * g.K * 2) + lc * 16;
+        bo2[i] = (uint32_t)((int64_t)wrow * g.K2 * 2) + lc * 16;
+        soff[i] = row * GBK + swz(row, lc) * 8;
+    }
+
+    const int nk1 = g.K / GBK;
+    const int nk = nk1 + (g.A2 ? g.K2 / GBK : 0);
+
+    // rows of this wave's 32-row blocks that hold data (wave-uniform)
+    const int wrows = tc.row1 - tc.row0 - wm * 128;
+    const int nvalid = wrows <= 0 ? 0 : min(4, (wrows + 31) / 32);
+
+    u32x4_t ra0[4], rb0[4], ra1[4], rb1[4];
+    auto gload = [&](int kt, u32x4_t (&a)[4], u32x4_t (&b)[4]) __attribute__((always_inline)) {
+        if (kt < nk1) {
+            const uint32_t ko = kt * GBK * 2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[i] = *(const u32x4_t*)(Ab + (ao[i] + ko));
+                b[i] = *(const u32x4_t*)(Bb + (bo[i] + ko));
+            }
+        } else {
+            const uint32_t ko = (kt - nk1) * GBK * 2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[i] = *(const u32x4_t*)(A2b + (ao2[i] + ko));
+                b[i] = *(const u32x4_t*)(B2b + (bo2[i] + ko));
+            }
+        }
+    };
+    auto sstore = [&](int slot, u32x4_t (&a)[4], u32x4_t (&b)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *(u32x4_t*)(&sA[slot][soff[i]]) = a[i];
+            *(u32x4_t*)(&sB[slot][soff[i]]) = b[i];
+        }
+    };
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[mi][nj][j] = 0.0f;
+
+    const int fr = lane & 31, fh = lane >> 5;
+    int arow[4], brow[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) arow[mi] = wm * 128 + mi * 32 + fr;
+#pragma unroll
+    for (int nj = 0; nj < 4; ++nj)
+        brow[nj] = (SW ? (nj < 2 ? wn * 64 + nj * 32 : 128 + wn * 64 + (nj - 2) * 32)
+                       : wn * 128 + nj * 32) + fr;
+
+    auto compute = [&](int slot) __attribute__((always_inline)) {
+        if (nvalid == 0) return;
+        const bf16_t* a = sA[slot];
+        const bf16_t* b = sB[slot];
+#pragma unroll
+        for (int ks = 0; ks < GBK / 16; ++ks) {
+            const int ch = ks * 2 + fh;
+            bf16x8_t fb[4];
+#pragma unroll
+            for (int nj = 0; nj < 4; ++nj)
+                fb[nj] = *(const bf16x8_t*)(&b[brow[nj] * GBK + swz(brow[nj], ch) * 8]);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                if (mi < nvalid) {
+                    const bf16x8_t fa =
+                        *(const bf16x8_t*)(&a[arow[mi] * GBK + swz(arow[mi], ch) * 8]);
+#pragma unroll
+                    for (int nj = 0; nj < 4; ++nj)
+                        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[nj],
+                                                                               acc[mi][nj], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // Prefetches are issued unconditionally (past the end they re-read the last
+    // stage): a load behind a branch makes the wait-count merge at the join
+    // wait for every outstanding load, which would serialise the stages.
+    gload(0, ra0, rb0);
+    gload(min(1, nk - 1), ra1, rb1);
+    sstore(0, ra0, rb0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        gload(min(kt + 2, nk - 1), ra0, rb0);
+        compute(0);
+        if (kt + 1 < nk) sstore(1, ra1, rb1);
+        __syncthreads();
+        if (kt + 1 >= nk) break;
+        gload(min(kt + 3, nk - 1), ra1, rb1);
+        compute(1);
+        if (kt + 2 < nk) sstore(0, ra0, rb0);
+        __syncthreads();
+    }
+
+    // epilogue: block (mi, nj) lane holds column fr, rows 8*(j/4)+4*fh+j%4
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        if (mi >= nvalid) continue;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int r = tc.row0 + wm * 128 + mi * 32 + 8 * (j >> 2) + 4 * fh + (j & 3);
+            if (r >= tc.row1) continue;
+            if (SW) {
+#pragma unroll
+                for (int nj = 0; nj < 2; ++nj) {
+                    const int hc = tc.nt * 128 + wn * 64 + nj * 32 + fr;
+                    if (hc < g.N) {
+                        const float h = silu_f32(acc[mi][nj][j]) * acc[mi][nj + 2][j];
+                        ((bf16_t*)g.C)[(int64_t)r * g.ldc + hc] = f32_to_bf16(h);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int nj = 0; nj < 4; ++nj) {
+                    const int c = tc.nt * GBN + wn * 128 + nj * 32 + fr;
+                    if (c >= g.N) continue;
+                    float v = acc[mi][nj][j];
+                    if (EPI == EPI_F32_BIAS && g.bias) v += g.bias[c];
+                    if (EPI == EPI_OUT)
+                        ((bf16_t*)g.C)[(int64_t)r * g.ldc + c] = f32_to_bf16(v);
+                    else
+                        ((float*)g.C)[(int64_t)r * g.ldc + c] = v;
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// bf16 weight-streaming MFMA kernel (<= 64 rows per tile)
+// ------------------------------------------------------------------------
+constexpr int SROWS = 16;   // token rows per MFMA block (and per dense tile)
+constexpr int SNW = 64;     // weight rows per workgroup
+
+// One tile of up to 16*NB token rows: each wave streams its quarter of K for
+// 64 weight rows and applies every weight fragment to all NB token blocks.
+// SU k-steps (of 32) form one load batch; two batches are in flight.
+template <int EPI, int NB, int SU>
+__device__ __forceinline__ void stream_tile(const GemmArgs& g, const TileCoord& tc,
+                                            float (*red)[4][4][64]) {
+    constexpr bool SW = EPI == EPI_SWIGLU;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kofs = (lane >> 4) * 8;
 
-    const bf16_t* Bg = (const bf16_t*)g.B + (int64_t)tc.group * g.b_gstride;
-    const bf16_t* B2 = (const bf16_t*)g.B2;
-    const bf16_t* wp[4];
-    const bf16_t* wp2[4];
+    // 32-bit byte offsets from wave-uniform bases (one VGPR per row); every
+    // operand of one group fits in 4 GiB (checked on the host)
+    const char* Bb = (const char*)((const bf16_t*)g.B + (int64_t)tc.group * g.b_gstride);
+    const char* B2b = (const char*)g.B2;
+    const char* Ab = (const char*)g.A;
+    const char* A2b = (const char*)g.A2;
+    uint32_t wo[4], wo2[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         int wrow;
@@ -246,53 +443,70 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream(GemmArgs g) {
         } else {
             wrow = min(tc.nt * SNW + q * 16 + l16, g.N - 1);
         }
-        wp[q] = Bg + (int64_t)wrow * g.K + kofs;
-        wp2[q] = B2 ? B2 + (int64_t)wrow * g.K2 + kofs : nullptr;
+        wo[q] = (uint32_t)((int64_t)wrow * g.K * 2) + kofs * 2;
+        wo2[q] = (uint32_t)((int64_t)wrow * g.K2 * 2) + kofs * 2;
     }
-    const int r = tc.row0 + l16;
-    const bool xvalid = r < tc.row1;
-    const bf16_t* xp = (const bf16_t*)g.A + (xvalid ? a_row_of(g, r) : 0) * g.lda + kofs;
-    const bf16_t* xp2 =
-        g.A2 ? (const bf16_t*)g.A2 + (int64_t)(xvalid ? r : 0) * g.lda2 + kofs : nullptr;
+    uint32_t xo[NB], xo2[NB];
+    bool xvalid[NB];
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) {
+        const int r = tc.row0 + tb * 16 + l16;
+        xvalid[tb] = r < tc.row1;
+        xo[tb] = (uint32_t)((xvalid[tb] ? a_row_of(g, r) : 0) * g.lda * 2) + kofs * 2;
+        xo2[tb] = (uint32_t)((int64_t)(xvalid[tb] ? r : 0) * g.lda2 * 2) + kofs * 2;
+    }
 
     const int ns1 = g.K / 32;
     const int ns = ns1 + (g.A2 ? g.K2 / 32 : 0);
     const int s0 = (int)((int64_t)wave * ns / 4), s1 = (int)((int64_t)(wave + 1) * ns / 4);
 
-    f32x4_t acc[4];
+    f32x4_t acc[4][NB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) acc[q][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    u32x4_t wa[SU][4], xa[SU], wb[SU][4], xb[SU];
+    u32x4_t wa[SU][4], xa[SU][NB], wb[SU][4], xb[SU][NB];
     const u32x4_t zero = {0u, 0u, 0u, 0u};
 
-    auto load = [&](int sbase, u32x4_t (&w)[SU][4], u32x4_t (&x)[SU]) {
+    auto load = [&](int sbase, u32x4_t (&w)[SU][4], u32x4_t (&x)[SU][NB])
+                    __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < SU; ++u) {
             const int st = sbase + u;
             if (st < s1) {
                 if (st < ns1) {
+                    const uint32_t ko = st * 64;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) w[u][q] = *(const u32x4_t*)(wp[q] + st * 32);
-                    x[u] = xvalid ? *(const u32x4_t*)(xp + st * 32) : zero;
+                    for (int q = 0; q < 4; ++q) w[u][q] = *(const u32x4_t*)(Bb + (wo[q] + ko));
+#pragma unroll
+                    for (int tb = 0; tb < NB; ++tb)
+                        x[u][tb] = xvalid[tb] ? *(const u32x4_t*)(Ab + (xo[tb] + ko)) : zero;
                 } else {
-                    const int so = (st - ns1) * 32;
+                    const uint32_t ko = (st - ns1) * 64;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) w[u][q] = *(const u32x4_t*)(wp2[q] + so);
-                    x[u] = xvalid ? *(const u32x4_t*)(xp2 + so) : zero;
+                    for (int q = 0; q < 4; ++q)
+                        w[u][q] = *(const u32x4_t*)(B2b + (wo2[q] + ko));
+#pragma unroll
+                    for (int tb = 0; tb < NB; ++tb)
+                        x[u][tb] = xvalid[tb] ? *(const u32x4_t*)(A2b + (xo2[tb] + ko)) : zero;
                 }
             }
         }
     };
-    auto compute = [&](int sbase, u32x4_t (&w)[SU][4], u32x4_t (&x)[SU]) {
+    auto compute = [&](int sbase, u32x4_t (&w)[SU][4], u32x4_t (&x)[SU][NB])
+                       __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < SU; ++u) {
             if (sbase + u < s1) {
-                const bf16x8_t xb8 = __builtin_bit_cast(bf16x8_t, x[u]);
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, w[u][q]), xb8, acc[q], 0, 0, 0);
+                for (int tb = 0; tb < NB; ++tb) {
+                    const bf16x8_t xb8 = __builtin_bit_cast(bf16x8_t, x[u][tb]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[q][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, w[u][q]), xb8, acc[q][tb], 0, 0, 0);
+                }
             }
         }
     };
@@ -305,53 +519,74 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream(GemmArgs g) {
         compute(s + SU, wb, xb);
     }
 
+    // acc[q][tb][j] holds C[weight row 4*(lane/16)+j of group q][token 16*tb + lane%16]
+    const int wr = (lane >> 4) * 4;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int tb = 0; tb < NB; ++tb) {
+        if (tb > 0) __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) red[wave][q][j][lane] = acc[q][j];
-    __syncthreads();
-
-    // acc[q][j] holds C[weight row 4*(lane/16)+j of group q][token lane%16]
-    const int tok = l16, wr = (lane >> 4) * 4;
-    const int rr = tc.row0 + tok;
-    if (SW) {
-        if (wave >= 2) return;
-        const int q = wave;
-        float gsum[4], usum[4];
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            gsum[j] = red[0][q][j][lane] + red[1][q][j][lane] + red[2][q][j][lane] +
-                      red[3][q][j][lane];
-            usum[j] = red[0][q + 2][j][lane] + red[1][q + 2][j][lane] +
-                      red[2][q + 2][j][lane] + red[3][q + 2][j][lane];
-        }
-        if (rr >= tc.row1) return;
-        bf16_t* crow = (bf16_t*)g.C + (int64_t)rr * g.ldc;
+            for (int j = 0; j < 4; ++j) red[wave][q][j][lane] = acc[q][tb][j];
+        __syncthreads();
+        const int rr = tc.row0 + tb * 16 + l16;
+        if (SW) {
+            if (wave < 2) {
+                const int q = wave;
+                float gsum[4], usum[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int hc = tc.nt * 32 + q * 16 + wr + j;
-            if (hc < g.N) crow[hc] = f32_to_bf16(silu_f32(gsum[j]) * usum[j]);
-        }
-    } else {
-        const int q = wave;
-        float v[4];
+                for (int j = 0; j < 4; ++j) {
+                    gsum[j] = red[0][q][j][lane] + red[1][q][j][lane] + red[2][q][j][lane] +
+                              red[3][q][j][lane];
+                    usum[j] = red[0][q + 2][j][lane] + red[1][q + 2][j][lane] +
+                              red[2][q + 2][j][lane] + red[3][q + 2][j][lane];
+                }
+                if (rr < tc.row1) {
+                    bf16_t* crow = (bf16_t*)g.C + (int64_t)rr * g.ldc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            v[j] = red[0][q][j][lane] + red[1][q][j][lane] + red[2][q][j][lane] +
-                   red[3][q][j][lane];
-        if (rr >= tc.row1) return;
+                    for (int j = 0; j < 4; ++j) {
+                        const int hc = tc.nt * 32 + q * 16 + wr + j;
+                        if (hc < g.N) crow[hc] = f32_to_bf16(silu_f32(gsum[j]) * usum[j]);
+                    }
+                }
+            }
+        } else {
+            const int q = wave;
+            float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = tc.nt * SNW + q * 16 + wr + j;
-            if (c >= g.N) continue;
-            float o = v[j];
-            if (EPI == EPI_F32_BIAS && g.bias) o += g.bias[c];
-            if (EPI == EPI_OUT)
-                ((bf16_t*)g.C)[(int64_t)rr * g.ldc + c] = f32_to_bf16(o);
-            else
-                ((float*)g.C)[(int64_t)rr * g.ldc + c] = o;
+            for (int j = 0; j < 4; ++j)
+                v[j] = red[0][q][j][lane] + red[1][q][j][lane] + red[2][q][j][lane] +
+                       red[3][q][j][lane];
+            if (rr < tc.row1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = tc.nt * SNW + q * 16 + wr + j;
+                    if (c >= g.N) continue;
+                    float o = v[j];
+                    if (EPI == EPI_F32_BIAS && g.bias) o += g.bias[c];
+                    if (EPI == EPI_OUT)
+                        ((bf16_t*)g.C)[(int64_t)rr * g.ldc + c] = f32_to_bf16(o);
+                    else
+                        ((float*)g.C)[(int64_t)rr * g.ldc + c] = o;
+                }
+            }
         }
     }
+}
+
+// Grouped tiles here hold one whole group of at most 64 rows; dense products
+// are cut into 16-row tiles.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_stream(GemmArgs g) {
+    constexpr bool SW = EPI == EPI_SWIGLU;
+    const int ntn = SW ? (g.N + 31) / 32 : (g.N + SNW - 1) / SNW;
+    TileCoord tc;
+    if (!fetch_tile(g, SROWS, ntn, tc)) return;
+    __shared__ float red[4][4][4][64];
+    const int rows = tc.row1 - tc.row0;
+    if (rows <= 16) stream_tile<EPI, 1, 4>(g, tc, red);
+    else if (rows <= 32) stream_tile<EPI, 2, 2>(g, tc, red);
+    else stream_tile<EPI, 4, 2>(g, tc, red);
 }
 
 // ------------------------------------------------------------------------
@@ -460,12 +695,14 @@ int col_tiles(int path, int dtype, int epi, int N) {
     const bool sw = epi == EPI_SWIGLU;
     if (dtype == 0) return sw ? (N + 31) / 32 : (N + FBN - 1) / FBN;
     if (path == GEMM_STREAM) return sw ? (N + 31) / 32 : (N + SNW - 1) / SNW;
+    if (path == GEMM_BIG) return sw ? (N + 127) / 128 : (N + GBN - 1) / GBN;
     return sw ? (N + 63) / 64 : (N + TBN - 1) / TBN;
 }
 
 int row_tile(int path, int dtype) {
     if (dtype == 0) return FBM;
-    return path == GEMM_STREAM ? SROWS : TBM;
+    if (path == GEMM_STREAM) return SROWS;
+    return path == GEMM_BIG ? GBM : TBM;
 }
 
 }  // namespace
@@ -489,6 +726,8 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
         MOE_GEMM_SWITCH(gemm_f32_tiled)
     } else if (path == GEMM_STREAM) {
         MOE_GEMM_SWITCH(gemm_bf16_stream)
+    } else if (path == GEMM_BIG) {
+        MOE_GEMM_SWITCH(gemm_bf16_big)
     } else {
         MOE_GEMM_SWITCH(gemm_bf16_tiled)
     }

@@ -10,6 +10,8 @@
 // Everything is enqueued on the caller's stream; nothing waits on the host.
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/moe.h"
 #include "common.h"
 
@@ -62,38 +64,47 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EH
 
 bool width_ok(int64_t w) { return w > 0 && w % 64 == 0; }
 
-// Decode-shaped groups (few rows per expert on average) stream the weights;
-// the rest use LDS tiles.
-int expert_path(moe_dtype_t dt, int64_t T, int k, int E) {
-    if (dt == MOE_DTYPE_F32) return GEMM_TILED;
-    return (T * k) <= (int64_t)24 * E ? GEMM_STREAM : GEMM_TILED;
+// The GEMM kernels address one operand (activations, one expert's weights,
+// the intermediate h) with 32-bit byte offsets.
+bool fits_u32(int64_t rows, int64_t cols, moe_dtype_t dt) {
+    return rows * cols * (int64_t)elem_size(dt) < ((int64_t)1 << 32);
 }
 
-int dense_path(moe_dtype_t dt, int64_t T) {
+// Experts with at most kStreamMaxRows rows stream their weights once through
+// registers (gemm_bf16_stream, one tile per expert); larger experts use
+// 256-row LDS tiles (gemm_bf16_big).  fp32 layers use 64-row VALU tiles.
+constexpr int kBigRows = 256;
+constexpr int kF32Rows = 64;
+
+// Dense products: stream the weights for small batches; otherwise the larger
+// tile when it still gives every CU a couple of workgroups, else 128x128.
+int dense_path(moe_dtype_t dt, int64_t T, int N, int epi) {
     if (dt == MOE_DTYPE_F32) return GEMM_TILED;
-    return T <= 256 ? GEMM_STREAM : GEMM_TILED;
+    if (T <= 256) return GEMM_STREAM;
+    const int64_t cols = epi == EPI_SWIGLU ? (N + 127) / 128 : (N + 255) / 256;
+    return ((T + 255) / 256) * cols >= 512 ? GEMM_BIG : GEMM_TILED;
 }
 
-int64_t max_tiles_for(int64_t P, int E, int tile_m) { return (P + tile_m - 1) / tile_m + E; }
-
-// Smallest row tile any path uses: sizes the tile list for every path.
-int64_t tile_capacity(moe_dtype_t dt, int64_t P, int E) {
-    const int tm = gemm_row_tile(dt == MOE_DTYPE_F32 ? 0 : 1,
-                                 dt == MOE_DTYPE_F32 ? GEMM_TILED : GEMM_STREAM);
-    return max_tiles_for(P, E, tm);
+// Upper bounds of the two tile lists.
+int64_t small_capacity(moe_dtype_t dt, int E) { return dt == MOE_DTYPE_F32 ? 1 : E; }
+int64_t big_capacity(moe_dtype_t dt, int64_t P, int E) {
+    if (dt == MOE_DTYPE_F32) return (P + kF32Rows - 1) / kF32Rows + E;
+    return (P + kBigRows - 1) / kBigRows + std::min<int64_t>(E, P / (kStreamMaxRows + 1)) + 1;
 }
 
 struct ExpertsWs {
-    Tile* tiles;
-    int32_t* ntiles;
+    Tile* small_tiles;
+    Tile* big_tiles;
+    int32_t* counts;   // [0] small tiles, [1] big tiles
     void* h;
 };
 
 ExpertsWs carve_experts(Carve& c, moe_dtype_t dt, int64_t max_T, int k, int E, int I) {
     ExpertsWs w;
     const int64_t P = max_T * k;
-    w.tiles = c.take<Tile>((size_t)tile_capacity(dt, P, E));
-    w.ntiles = c.take<int32_t>(1);
+    w.small_tiles = c.take<Tile>((size_t)small_capacity(dt, E));
+    w.big_tiles = c.take<Tile>((size_t)big_capacity(dt, P, E));
+    w.counts = c.take<int32_t>(2);
     w.h = c.take<char>((size_t)P * I * elem_size(dt));
     return w;
 }
@@ -105,16 +116,37 @@ GemmArgs gemm_defaults() {
     return g;
 }
 
+// One grouped product over both tile lists.
+moe_status_t grouped_gemm(moe_dtype_t dt, GemmArgs g, const ExpertsWs& w, int64_t P, int E,
+                          hipStream_t s) {
+    if (dt == MOE_DTYPE_F32) {
+        g.tiles = w.big_tiles;
+        g.num_tiles = w.counts + 1;
+        g.max_tiles = (int32_t)big_capacity(dt, P, E);
+        g.tile_m = kF32Rows;
+        return hip_status(launch_gemm(0, GEMM_TILED, g, s));
+    }
+    g.tiles = w.small_tiles;
+    g.num_tiles = w.counts;
+    g.max_tiles = (int32_t)small_capacity(dt, E);
+    g.tile_m = kStreamMaxRows;
+    MOE_HIP(launch_gemm(1, GEMM_STREAM, g, s));
+    g.tiles = w.big_tiles;
+    g.num_tiles = w.counts + 1;
+    g.max_tiles = (int32_t)big_capacity(dt, P, E);
+    g.tile_m = kBigRows;
+    return hip_status(launch_gemm(1, GEMM_BIG, g, s));
+}
+
 // Grouped gate/up + SwiGLU, then grouped down, over expert-sorted rows.
 moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, const void* x,
                          const int32_t* offsets, const int32_t* row_to_pair, const void* w13,
                          const void* w2, float* y_rows, const ExpertsWs& w, hipStream_t s,
                          hipEvent_t* ev) {
     const int64_t P = T * k;
-    const int path = expert_path(dt, T, k, E);
-    const int idt = dt == MOE_DTYPE_F32 ? 0 : 1;
-    const int tm = gemm_row_tile(idt, path);
-    MOE_HIP(launch_build_tiles(offsets, E, tm, w.tiles, w.ntiles, s));
+    const bool f32 = dt == MOE_DTYPE_F32;
+    MOE_HIP(launch_build_tiles(offsets, E, f32 ? 0 : kStreamMaxRows, f32 ? kF32Rows : kBigRows,
+                               w.small_tiles, w.counts, w.big_tiles, w.counts + 1, s));
     if (ev) MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM1], s));
 
     GemmArgs g1 = gemm_defaults();
@@ -126,14 +158,10 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
     g1.b_gstride = (int64_t)2 * I * D;
     g1.K = D;
     g1.N = I;
-    g1.tiles = w.tiles;
-    g1.num_tiles = w.ntiles;
-    g1.max_tiles = (int32_t)max_tiles_for(P, E, tm);
-    g1.tile_m = tm;
     g1.epi = EPI_SWIGLU;
     g1.C = w.h;
     g1.ldc = I;
-    MOE_HIP(launch_gemm(idt, path, g1, s));
+    MOE_TRY(grouped_gemm(dt, g1, w, P, E, s));
     if (ev) {
         MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM1 + 1], s));
         MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM2], s));
@@ -146,14 +174,10 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
     g2.b_gstride = (int64_t)D * I;
     g2.K = I;
     g2.N = D;
-    g2.tiles = w.tiles;
-    g2.num_tiles = w.ntiles;
-    g2.max_tiles = g1.max_tiles;
-    g2.tile_m = tm;
     g2.epi = EPI_F32;
     g2.C = y_rows;
     g2.ldc = D;
-    MOE_HIP(launch_gemm(idt, path, g2, s));
+    MOE_TRY(grouped_gemm(dt, g2, w, P, E, s));
     if (ev) MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM2 + 1], s));
     return MOE_OK;
 }
@@ -177,7 +201,7 @@ moe_status_t dense_gemm(moe_dtype_t dt, int64_t T, const void* A, int64_t lda, c
     g.C = C;
     g.ldc = ldc;
     g.bias = bias;
-    return hip_status(launch_gemm(dt == MOE_DTYPE_F32 ? 0 : 1, dense_path(dt, T), g, s));
+    return hip_status(launch_gemm(dt == MOE_DTYPE_F32 ? 0 : 1, dense_path(dt, T, N, epi), g, s));
 }
 
 struct ForwardWs {
@@ -227,6 +251,15 @@ moe_status_t check_forward_shapes(const moe_route_cfg_t* cfg, moe_dtype_t dt, in
     if (bad_dtype(dt) || T < 0) return MOE_EINVAL;
     if (T * (int64_t)cfg->top_k > INT32_MAX / 2) return MOE_ENOTSUP;
     if (!width_ok(H) || !width_ok(I)) return MOE_ENOTSUP;
+    {
+        const int64_t D = lat ? lat->latent : H;
+        const int64_t P = T * cfg->top_k;
+        if (!fits_u32(T, std::max<int64_t>(H, D), dt) || !fits_u32(P, I, dt) ||
+            !fits_u32(2 * (int64_t)I, D, dt))
+            return MOE_ENOTSUP;
+        if (sh && (!fits_u32(T, sh->inter, dt) || !fits_u32(2 * (int64_t)sh->inter, H, dt)))
+            return MOE_ENOTSUP;
+    }
     if (lat) {
         if (!lat->w_down || !lat->gamma || !lat->w_up) return MOE_EINVAL;
         if (!width_ok(lat->latent) || lat->latent > 8192) return MOE_ENOTSUP;
@@ -318,6 +351,8 @@ moe_status_t moe_experts(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, int
     if (E > kMaxExperts || k > kMaxTopK) return MOE_ENOTSUP;
     if (!width_ok(D) || !width_ok(I)) return MOE_ENOTSUP;
     if (T * (int64_t)k > INT32_MAX / 2) return MOE_ENOTSUP;
+    if (!fits_u32(T, D, dtype) || !fits_u32(T * k, I, dtype) || !fits_u32(2 * (int64_t)I, D, dtype))
+        return MOE_ENOTSUP;
     if (T == 0) return MOE_OK;
     if (!x || !expert_offsets || !row_to_pair || !w13 || !w2 || !y_rows) return MOE_EINVAL;
     if (!ws || ws_bytes < moe_experts_workspace(dtype, T, k, E, D, I)) return MOE_ENOSPACE;

@@ -114,25 +114,44 @@ __global__ __launch_bounds__(64) void perm_scatter(const int32_t* __restrict__ i
     }
 }
 
+// Groups with 1..small_max rows get one tile each in the small list; larger
+// groups are cut into big_m-row tiles in the big list.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
-                                                           int E, int tile_m, Tile* __restrict__ tiles,
-                                                           int32_t* __restrict__ num_tiles) {
+                                                           int E, int small_max, int big_m,
+                                                           Tile* __restrict__ small_tiles,
+                                                           int32_t* __restrict__ num_small,
+                                                           Tile* __restrict__ big_tiles,
+                                                           int32_t* __restrict__ num_big) {
     __shared__ int sh[1024];
     const int e = threadIdx.x;
     const int a = e < E ? offsets[e] : 0;
     const int b = e < E ? offsets[e + 1] : 0;
-    const int nt = (b - a + tile_m - 1) / tile_m;
-    int total;
-    const int start = block_exclusive_scan(nt, sh, total);
-    for (int i = 0; i < nt; ++i) {
+    const int c = b - a;
+    const bool small = c > 0 && c <= small_max;
+    const int nb = small ? 0 : (c + big_m - 1) / big_m;
+    int total_s, total_b;
+    const int start_s = block_exclusive_scan(small ? 1 : 0, sh, total_s);
+    const int start_b = block_exclusive_scan(nb, sh, total_b);
+    if (small) {
         Tile t;
         t.group = e;
-        t.row0 = a + i * tile_m;
-        t.row1 = min(a + (i + 1) * tile_m, b);
+        t.row0 = a;
+        t.row1 = b;
         t.pad = 0;
-        tiles[start + i] = t;
+        small_tiles[start_s] = t;
     }
-    if (e == 0) *num_tiles = total;
+    for (int i = 0; i < nb; ++i) {
+        Tile t;
+        t.group = e;
+        t.row0 = a + i * big_m;
+        t.row1 = min(a + (i + 1) * big_m, b);
+        t.pad = 0;
+        big_tiles[start_b + i] = t;
+    }
+    if (e == 0) {
+        *num_small = total_s;
+        *num_big = total_b;
+    }
 }
 
 }  // namespace
@@ -153,9 +172,11 @@ hipError_t launch_permute(int64_t P, int32_t E, const int32_t* ids, int32_t* cou
     return hipGetLastError();
 }
 
-hipError_t launch_build_tiles(const int32_t* offsets, int32_t E, int32_t tile_m, Tile* tiles,
-                              int32_t* num_tiles, hipStream_t s) {
-    build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_m, tiles, num_tiles);
+hipError_t launch_build_tiles(const int32_t* offsets, int32_t E, int32_t small_max,
+                              int32_t big_m, Tile* small_tiles, int32_t* num_small,
+                              Tile* big_tiles, int32_t* num_big, hipStream_t s) {
+    build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, E, small_max, big_m, small_tiles, num_small,
+                                          big_tiles, num_big);
     return hipGetLastError();
 }
 
