@@ -325,13 +325,10 @@ def forward_tokens(tokens, x, cfg: RouteCfg, w13, w2, *, w_router=None, router_b
     ids, w, keys = route(lg, cfg, corr_bias)
     xin = xs if latent is None else xs @ np.asarray(latent["w_down"], dtype=f64).T
     routed = np.zeros((tokens.shape[0], xin.shape[1]), dtype=f64)
-    cache = {}
     for i in range(tokens.shape[0]):
         for j in range(cfg.top_k):
             e = int(ids[i, j])
-            if e not in cache:
-                cache[e] = (np.asarray(w13[e], dtype=f64), np.asarray(w2[e], dtype=f64))
-            y = expert_mlp(xin[i:i + 1], *cache[e])[0]
+            y = expert_mlp(xin[i:i + 1], w13[e], w2[e])[0]
             routed[i] += w[i, j] * y
     sh = shared_expert(xs, shared["w13"], shared["w2"]) if shared is not None else None
     if latent is not None:
