@@ -39,9 +39,10 @@ __device__ __forceinline__ float silu_f32(float g) {
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
-// Tile-list entry of a grouped GEMM: rows [row0, row1) of group g.
+// Tile-list entry of a grouped GEMM: rows [row0, row1) of group g; the
+// group's tiles are the contiguous entries [first, first + count).
 struct Tile {
-    int32_t group, row0, row1, pad;
+    int32_t group, row0, row1, first, count, pad0, pad1, pad2;
 };
 
 // Epilogues of the GEMM kernels.

@@ -49,9 +49,20 @@ __device__ __forceinline__ bool fetch_tile(const GemmArgs& g, int tile_m, int nt
     const int i = blockIdx.x;
     if (i >= total) return false;
     const int lid = xcd_remap(i, total);
-    const int mt = lid / ntn;
+    int mt = lid / ntn;
     c.nt = lid - mt * ntn;
     if (g.tiles) {
+        // Inside one group's block of count*ntn workgroups the row tiles vary
+        // fastest, so the row tiles that share a weight tile run side by side
+        // on one XCD and read it once from HBM.
+        const Tile t0 = g.tiles[mt];
+        const int first = __builtin_amdgcn_readfirstlane(t0.first);
+        const int cnt = __builtin_amdgcn_readfirstlane(t0.count);
+        if (cnt > 1) {
+            const int o = lid - first * ntn;
+            c.nt = o / cnt;
+            mt = first + (o - c.nt * cnt);
+        }
         const Tile t = g.tiles[mt];
         // the tile is the same for the whole workgroup: keep it in SGPRs so
         // that every branch on it is a scalar branch
@@ -218,58 +229,71 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
 // ------------------------------------------------------------------------
 // bf16 256x256 MFMA kernel for grouped products with many rows per group
 // ------------------------------------------------------------------------
-// 4 waves in a 2x2 layout, each a 128x128 block of 4x4 v_mfma_f32_32x32x16_bf16
-// tiles (256 fp32 accumulators per lane).  K advances 32 at a time; global
-// loads run two stages ahead through registers into a 2-slot LDS ring.  LDS
-// rows are 64 bytes (32 bf16) and the four 16-byte chunks of row r sit at
-// chunk ^ (((r >> 1) ^ (r >> 2)) & 3): any 8 consecutive rows (one 128-byte
-// bank sweep) and any 16 consecutive rows (one 256-byte sweep) then touch
-// distinct banks, for the writes and for the MFMA operand reads.  A wave
-// skips the MFMAs (and operand reads) of its 32-row blocks that lie past the
-// tile's last row, and threads skip loading those activation rows, so a group
-// with few rows costs little more than streaming its weights once.
-constexpr int GBM = 256, GBN = 256, GBK = 32;
+// 8 waves (two per SIMD) in a 2x4 layout; each wave owns a 128x64 block of
+// 4x2 v_mfma_f32_32x32x16_bf16 tiles (128 fp32 accumulators per lane).  K
+// advances 32 at a time through a 4-slot LDS ring filled directly from global
+// memory (global_load_lds_dwordx4: no register staging, no LDS write
+// instructions) three stages ahead of the MFMAs.  Each wave's DMA
+// instruction fills one contiguous 1 KB block of 16 rows x 64 bytes; LDS row r
+// keeps its four 16-byte chunks at chunk ^ (((r >> 1) ^ (r >> 2)) & 3), so any
+// 8 consecutive rows (a 128-byte bank sweep) and any 16 (a 256-byte sweep)
+// touch distinct banks on the MFMA operand reads; a lane therefore fetches
+// the global chunk whose swizzled slot is its own.  The ring is ordered by
+// explicit waits: before stage kt is read, each wave waits until only the two
+// newer stages' DMAs remain outstanding, then one barrier makes every wave's
+// stage visible and frees the slot the next DMA overwrites.  A wave whose 128
+// rows all lie past the tile's end skips its MFMAs.
+constexpr int GBM = 256, GBN = 256, GBK = 32, GSLOTS = 4;
 
 __device__ __forceinline__ int swz(int row, int chunk) {
     return chunk ^ (((row >> 1) ^ (row >> 2)) & 3);
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_big(GemmArgs g) {
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt with only a vector-memory count (gfx9 encoding: vmcnt[3:0] in
+// bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int EPI, bool KCAT>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     constexpr bool SW = EPI == EPI_SWIGLU;
     const int ntn = SW ? (g.N + 127) / 128 : (g.N + GBN - 1) / GBN;
     TileCoord tc;
     if (!fetch_tile(g, GBM, ntn, tc)) return;
 
-    __shared__ __attribute__((aligned(16))) bf16_t sA[2][GBM * GBK];
-    __shared__ __attribute__((aligned(16))) bf16_t sB[2][GBN * GBK];
+    // one LDS buffer: ring slot s holds the A tile at [s][0] and the B tile at
+    // [s][1]; after the K loop the epilogue reuses it as a flat fp32 buffer
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[GSLOTS][2][GBM * GBK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-    const int lr = tid >> 2, lc = tid & 3;
+    const int wm = wave >> 2, wn = wave & 3;
 
     const bf16_t* Bg = (const bf16_t*)g.B + (int64_t)tc.group * g.b_gstride;
-
-    // 32-bit byte offsets from the (wave-uniform) operand bases: one VGPR per
-    // row and scalar-base addressing; each group's operands fit in 4 GiB
-    // (checked on the host).
     const char* Ab = (const char*)g.A;
     const char* Bb = (const char*)Bg;
     const char* A2b = (const char*)g.A2;
     const char* B2b = (const char*)g.B2;
-    // Rows past the tile's end load the tile's first row instead: the loop
-    // then has no divergent branches, and the repeated address costs one
-    // request per load instruction.
-    uint32_t ao[4], bo[4], ao2[4], bo2[4];
-    int soff[4];
+
+    // DMA block i of this wave covers tile rows 32*wave + 16*i .. +15; lane l
+    // fills row +l/4, slot l%4, i.e. global chunk (l%4) ^ swizzle(row).  The
+    // swizzle reads only bits 1..2 of the row, which 32*wave + 16*i keeps.
+    // 32-bit byte offsets from wave-uniform bases; rows past the tile's end
+    // load the tile's first row (never stored).
+    const int lrow = lane >> 2;
+    const int chunk_bytes = swz(lrow, lane & 3) * 16;
+    uint32_t ao[2], bo[2], ao2[KCAT ? 2 : 1], bo2[KCAT ? 2 : 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = lr + 64 * i;
+    for (int i = 0; i < 2; ++i) {
+        const int row = 32 * wave + 16 * i + lrow;
         const int r = tc.row0 + row;
         const int rr = r < tc.row1 ? r : tc.row0;
-        ao[i] = (uint32_t)(a_row_of(g, rr) * g.lda * 2) + lc * 16;
-        ao2[i] = (uint32_t)((int64_t)rr * g.lda2 * 2) + lc * 16;
+        ao[i] = (uint32_t)(a_row_of(g, rr) * g.lda * 2) + chunk_bytes;
         int wrow;
         if (SW) {
             const int c = min(tc.nt * 128 + (row & 127), g.N - 1);
@@ -277,136 +301,169 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big(GemmArgs g) {
         } else {
             wrow = min(tc.nt * GBN + row, g.N - 1);
         }
-        bo[i] = (uint32_t)((int64_t)wrow * g.K * 2) + lc * 16;
-        bo2[i] = (uint32_t)((int64_t)wrow * g.K2 * 2) + lc * 16;
-        soff[i] = row * GBK + swz(row, lc) * 8;
+        bo[i] = (uint32_t)((int64_t)wrow * g.K * 2) + chunk_bytes;
+        if (KCAT) {
+            ao2[i] = (uint32_t)((int64_t)rr * g.lda2 * 2) + chunk_bytes;
+            bo2[i] = (uint32_t)((int64_t)wrow * g.K2 * 2) + chunk_bytes;
+        }
     }
 
     const int nk1 = g.K / GBK;
-    const int nk = nk1 + (g.A2 ? g.K2 / GBK : 0);
+    const int nk = nk1 + (KCAT ? g.K2 / GBK : 0);
 
-    // rows of this wave's 32-row blocks that hold data (wave-uniform)
-    const int wrows = tc.row1 - tc.row0 - wm * 128;
-    const int nvalid = wrows <= 0 ? 0 : min(4, (wrows + 31) / 32);
-
-    u32x4_t ra0[4], rb0[4], ra1[4], rb1[4];
-    auto gload = [&](int kt, u32x4_t (&a)[4], u32x4_t (&b)[4]) __attribute__((always_inline)) {
-        if (kt < nk1) {
-            const uint32_t ko = kt * GBK * 2;
+    // Issue stage kt (clamped to the last stage) into its ring slot.  The K
+    // segment of a K-concatenated product is picked with selects.
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+        const int slot = kt & (GSLOTS - 1);
+        kt = min(kt, nk - 1);
+        const bool seg1 = !KCAT || kt < nk1;
+        const char* abase = seg1 ? Ab : A2b;
+        const char* bbase = seg1 ? Bb : B2b;
+        const uint32_t ko = (uint32_t)(seg1 ? kt : kt - nk1) * GBK * 2;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = *(const u32x4_t*)(Ab + (ao[i] + ko));
-                b[i] = *(const u32x4_t*)(Bb + (bo[i] + ko));
-            }
-        } else {
-            const uint32_t ko = (kt - nk1) * GBK * 2;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = *(const u32x4_t*)(A2b + (ao2[i] + ko));
-                b[i] = *(const u32x4_t*)(B2b + (bo2[i] + ko));
-            }
-        }
-    };
-    auto sstore = [&](int slot, u32x4_t (&a)[4], u32x4_t (&b)[4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *(u32x4_t*)(&sA[slot][soff[i]]) = a[i];
-            *(u32x4_t*)(&sB[slot][soff[i]]) = b[i];
+        for (int i = 0; i < 2; ++i) {
+            const int blk = (32 * wave + 16 * i) * GBK;
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(abase + ((seg1 ? ao[i] : ao2[KCAT ? i : 0]) + ko)),
+                (lds_ptr_t)&smem[slot][0][blk], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(bbase + ((seg1 ? bo[i] : bo2[KCAT ? i : 0]) + ko)),
+                (lds_ptr_t)&smem[slot][1][blk], 16, 0, 0);
         }
     };
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj)
+        for (int nj = 0; nj < 2; ++nj)
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[mi][nj][j] = 0.0f;
 
     const int fr = lane & 31, fh = lane >> 5;
-    int arow[4], brow[4];
+    int aoffs[2][4], boffs[2][2];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) arow[mi] = wm * 128 + mi * 32 + fr;
+    for (int ks = 0; ks < 2; ++ks) {
+        const int ch = ks * 2 + fh;
 #pragma unroll
-    for (int nj = 0; nj < 4; ++nj)
-        brow[nj] = (SW ? (nj < 2 ? wn * 64 + nj * 32 : 128 + wn * 64 + (nj - 2) * 32)
-                       : wn * 128 + nj * 32) + fr;
-
-    auto compute = [&](int slot) __attribute__((always_inline)) {
-        if (nvalid == 0) return;
-        const bf16_t* a = sA[slot];
-        const bf16_t* b = sB[slot];
-#pragma unroll
-        for (int ks = 0; ks < GBK / 16; ++ks) {
-            const int ch = ks * 2 + fh;
-            bf16x8_t fb[4];
-#pragma unroll
-            for (int nj = 0; nj < 4; ++nj)
-                fb[nj] = *(const bf16x8_t*)(&b[brow[nj] * GBK + swz(brow[nj], ch) * 8]);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                if (mi < nvalid) {
-                    const bf16x8_t fa =
-                        *(const bf16x8_t*)(&a[arow[mi] * GBK + swz(arow[mi], ch) * 8]);
-#pragma unroll
-                    for (int nj = 0; nj < 4; ++nj)
-                        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[nj],
-                                                                               acc[mi][nj], 0, 0, 0);
-                }
-            }
+        for (int mi = 0; mi < 4; ++mi) {
+            const int row = wm * 128 + mi * 32 + fr;
+            aoffs[ks][mi] = row * GBK + swz(row, ch) * 8;
         }
-    };
-
-    // Prefetches are issued unconditionally (past the end they re-read the last
-    // stage): a load behind a branch makes the wait-count merge at the join
-    // wait for every outstanding load, which would serialise the stages.
-    gload(0, ra0, rb0);
-    gload(min(1, nk - 1), ra1, rb1);
-    sstore(0, ra0, rb0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-        gload(min(kt + 2, nk - 1), ra0, rb0);
-        compute(0);
-        if (kt + 1 < nk) sstore(1, ra1, rb1);
-        __syncthreads();
-        if (kt + 1 >= nk) break;
-        gload(min(kt + 3, nk - 1), ra1, rb1);
-        compute(1);
-        if (kt + 2 < nk) sstore(0, ra0, rb0);
-        __syncthreads();
+#pragma unroll
+        for (int nj = 0; nj < 2; ++nj) {
+            const int row = (SW ? nj * 128 + wn * 32 : wn * 64 + nj * 32) + fr;
+            boffs[ks][nj] = row * GBK + swz(row, ch) * 8;
+        }
     }
 
-    // epilogue: block (mi, nj) lane holds column fr, rows 8*(j/4)+4*fh+j%4
+    // does this wave's 128-row half hold any row of the tile (wave-uniform)
+    const bool active = tc.row1 - tc.row0 > wm * 128;
+
+    issue(0);
+    issue(1);
+    issue(2);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vmcnt<8>();             // this wave's DMAs of stage kt have landed
+        __builtin_amdgcn_s_barrier();  // ... and every other wave's; slot (kt-1)&3 is free
+        asm volatile("" ::: "memory");
+        issue(kt + 3);
+        if (active) {
+            const bf16_t* a = smem[kt & (GSLOTS - 1)][0];
+            const bf16_t* b = smem[kt & (GSLOTS - 1)][1];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8_t fa[4], fb[2];
+#pragma unroll
+                for (int nj = 0; nj < 2; ++nj) fb[nj] = *(const bf16x8_t*)(&b[boffs[ks][nj]]);
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) fa[mi] = *(const bf16x8_t*)(&a[aoffs[ks][mi]]);
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int nj = 0; nj < 2; ++nj)
+                        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            fa[mi], fb[nj], acc[mi][nj], 0, 0, 0);
+            }
+        }
+        asm volatile("" ::: "memory");
+    }
+    // The ring's trailing DMAs must land before the LDS is reused below.
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    // Epilogue through LDS, one 32-row block of each wave at a time: the
+    // accumulators are written in MFMA layout (lane = column, 16 rows), then
+    // each lane reads back half a row and stores it with 16-byte writes.  Only
+    // one block's accumulators are live in VGPRs at a time.  Row stride 72
+    // floats keeps the writes free of bank
+    // write conflicts (reads see at most two-way ones).  Each wave uses its
+    // own region, so LDS order within the wave suffices between the writes and
+    // the reads.
+    if (!active) return;
+    constexpr int ELD = 72;
+    float* ep = (float*)&smem[0][0][0] + wave * 32 * ELD;
+    const int er = lane >> 1, eh = lane & 1;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-        if (mi >= nvalid) continue;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int r = tc.row0 + wm * 128 + mi * 32 + 8 * (j >> 2) + 4 * fh + (j & 3);
-            if (r >= tc.row1) continue;
+        for (int nj = 0; nj < 2; ++nj)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                ep[(8 * (j >> 2) + 4 * fh + (j & 3)) * ELD + nj * 32 + fr] = acc[mi][nj][j];
+        asm volatile("" ::: "memory");
+        const int r = tc.row0 + wm * 128 + mi * 32 + er;
+        const float* src = ep + er * ELD;
+        if (r < tc.row1) {
             if (SW) {
+                // columns 0..31 of the wave block are gate, 32..63 up, for the
+                // wave's 32 h columns; this lane takes 16 of them
+                const int hc0 = tc.nt * 128 + wn * 32 + eh * 16;
+                bf16_t* dst = (bf16_t*)g.C + (int64_t)r * g.ldc + hc0;
 #pragma unroll
-                for (int nj = 0; nj < 2; ++nj) {
-                    const int hc = tc.nt * 128 + wn * 64 + nj * 32 + fr;
-                    if (hc < g.N) {
-                        const float h = silu_f32(acc[mi][nj][j]) * acc[mi][nj + 2][j];
-                        ((bf16_t*)g.C)[(int64_t)r * g.ldc + hc] = f32_to_bf16(h);
-                    }
+                for (int q = 0; q < 2; ++q) {
+                    const f32x4_t g0 = *(const f32x4_t*)(src + eh * 16 + q * 8);
+                    const f32x4_t g1 = *(const f32x4_t*)(src + eh * 16 + q * 8 + 4);
+                    const f32x4_t u0 = *(const f32x4_t*)(src + 32 + eh * 16 + q * 8);
+                    const f32x4_t u1 = *(const f32x4_t*)(src + 32 + eh * 16 + q * 8 + 4);
+                    u32x4_t o;
+                    o[0] = pack_bf16x2(silu_f32(g0[0]) * u0[0], silu_f32(g0[1]) * u0[1]);
+                    o[1] = pack_bf16x2(silu_f32(g0[2]) * u0[2], silu_f32(g0[3]) * u0[3]);
+                    o[2] = pack_bf16x2(silu_f32(g1[0]) * u1[0], silu_f32(g1[1]) * u1[1]);
+                    o[3] = pack_bf16x2(silu_f32(g1[2]) * u1[2], silu_f32(g1[3]) * u1[3]);
+                    if (hc0 + q * 8 < g.N) *(u32x4_t*)(dst + q * 8) = o;
                 }
             } else {
+                const int c0 = tc.nt * GBN + wn * 64 + eh * 32;
 #pragma unroll
-                for (int nj = 0; nj < 4; ++nj) {
-                    const int c = tc.nt * GBN + wn * 128 + nj * 32 + fr;
+                for (int q = 0; q < 4; ++q) {
+                    const int c = c0 + q * 8;
                     if (c >= g.N) continue;
-                    float v = acc[mi][nj][j];
-                    if (EPI == EPI_F32_BIAS && g.bias) v += g.bias[c];
-                    if (EPI == EPI_OUT)
-                        ((bf16_t*)g.C)[(int64_t)r * g.ldc + c] = f32_to_bf16(v);
-                    else
-                        ((float*)g.C)[(int64_t)r * g.ldc + c] = v;
+                    f32x4_t v0 = *(const f32x4_t*)(src + eh * 32 + q * 8);
+                    f32x4_t v1 = *(const f32x4_t*)(src + eh * 32 + q * 8 + 4);
+                    if (EPI == EPI_F32_BIAS && g.bias) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            v0[t] += g.bias[c + t];
+                            v1[t] += g.bias[c + 4 + t];
+                        }
+                    }
+                    if (EPI == EPI_OUT) {
+                        u32x4_t o;
+                        o[0] = pack_bf16x2(v0[0], v0[1]);
+                        o[1] = pack_bf16x2(v0[2], v0[3]);
+                        o[2] = pack_bf16x2(v1[0], v1[1]);
+                        o[3] = pack_bf16x2(v1[2], v1[3]);
+                        *(u32x4_t*)((bf16_t*)g.C + (int64_t)r * g.ldc + c) = o;
+                    } else {
+                        float* dst = (float*)g.C + (int64_t)r * g.ldc + c;
+                        *(f32x4_t*)dst = v0;
+                        *(f32x4_t*)(dst + 4) = v1;
+                    }
                 }
             }
         }
+        asm volatile("" ::: "memory");
     }
 }
 
@@ -691,6 +748,17 @@ __global__ __launch_bounds__(256) void gemm_f32_tiled(GemmArgs g) {
     }
 }
 
+template <bool KC>
+void launch_big(const GemmArgs& g, dim3 gd, hipStream_t s) {
+    const dim3 bd(512);
+    switch (g.epi) {
+        case EPI_F32: gemm_bf16_big<EPI_F32, KC><<<gd, bd, 0, s>>>(g); break;
+        case EPI_F32_BIAS: gemm_bf16_big<EPI_F32_BIAS, KC><<<gd, bd, 0, s>>>(g); break;
+        case EPI_OUT: gemm_bf16_big<EPI_OUT, KC><<<gd, bd, 0, s>>>(g); break;
+        default: gemm_bf16_big<EPI_SWIGLU, KC><<<gd, bd, 0, s>>>(g); break;
+    }
+}
+
 int col_tiles(int path, int dtype, int epi, int N) {
     const bool sw = epi == EPI_SWIGLU;
     if (dtype == 0) return sw ? (N + 31) / 32 : (N + FBN - 1) / FBN;
@@ -727,7 +795,8 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
     } else if (path == GEMM_STREAM) {
         MOE_GEMM_SWITCH(gemm_bf16_stream)
     } else if (path == GEMM_BIG) {
-        MOE_GEMM_SWITCH(gemm_bf16_big)
+        if (g.A2) launch_big<true>(g, gd, s);
+        else launch_big<false>(g, gd, s);
     } else {
         MOE_GEMM_SWITCH(gemm_bf16_tiled)
     }

@@ -82,7 +82,8 @@ int dense_path(moe_dtype_t dt, int64_t T, int N, int epi) {
     if (dt == MOE_DTYPE_F32) return GEMM_TILED;
     if (T <= 256) return GEMM_STREAM;
     const int64_t cols = epi == EPI_SWIGLU ? (N + 127) / 128 : (N + 255) / 256;
-    return ((T + 255) / 256) * cols >= 512 ? GEMM_BIG : GEMM_TILED;
+    // the 256-row kernel stores 8-column groups and needs N % 64 == 0
+    return (N % 64 == 0 && ((T + 255) / 256) * cols >= 512) ? GEMM_BIG : GEMM_TILED;
 }
 
 // Upper bounds of the two tile lists.

@@ -133,19 +133,21 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     const int start_s = block_exclusive_scan(small ? 1 : 0, sh, total_s);
     const int start_b = block_exclusive_scan(nb, sh, total_b);
     if (small) {
-        Tile t;
+        Tile t = {};
         t.group = e;
         t.row0 = a;
         t.row1 = b;
-        t.pad = 0;
+        t.first = start_s;
+        t.count = 1;
         small_tiles[start_s] = t;
     }
     for (int i = 0; i < nb; ++i) {
-        Tile t;
+        Tile t = {};
         t.group = e;
         t.row0 = a + i * big_m;
         t.row1 = min(a + (i + 1) * big_m, b);
-        t.pad = 0;
+        t.first = start_b;
+        t.count = nb;
         big_tiles[start_b + i] = t;
     }
     if (e == 0) {
