@@ -83,6 +83,24 @@ def layer_work(w, counts):
     return wbytes + abytes, flops, touched
 
 
+def profiled_traffic(workload: str):
+    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, or None when the kernel source no longer
+    matches the one the counters were taken on."""
+    import glob
+    import hashlib
+    src = os.path.join(ROOT, "routed_mixture_experts_amd", "csrc", "gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*hbm_counters*.md")):
+        for line in open(path):
+            if not line.startswith("traffic:"):
+                continue
+            kv = dict(f.split("=", 1) for f in line.split()[1:])
+            if kv.get("workload") == workload and kv.get("gemm_hip_sha256_16") == sha:
+                return int(kv["bytes_per_launch"])
+    return None
+
+
 def gemm1_bytes(w, counts):
     """Algorithmic bytes of one gate/up + SwiGLU launch: gate/up weights of the
     touched experts (unit: one expert, 2*I*D elements), the token activations
@@ -203,6 +221,7 @@ def main():
     g1b, _ = gemm1_bytes(w, counts)
     g1_ms = stage["gemm1"]
     g1_gbs = g1b / (g1_ms * 1e-3) / 1e9
+    traffic = profiled_traffic(w.name)
     t_s = ms * 1e-3
     res = {
         "metric": METRIC,
@@ -220,9 +239,9 @@ def main():
         "config": {"workload": describe(w), "tokens": w.T, "touched_experts": touched,
                    "parallelism": "none (1 GPU holds all experts)"},
         "roofline": {"bound": "hbm", "achieved": g1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": g1_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gemm_bf16_stream<SWIGLU> (gate/up + SwiGLU)"
-                     if w.T * w.k <= 24 * w.E else "gemm_bf16_tiled<SWIGLU> (gate/up + SwiGLU)",
+                     "frac": g1_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "gate/up + SwiGLU stage: gemm_bf16_stream<3> (experts <= 64 rows)"
+                               " + gemm_bf16_big<3> (larger experts)",
                      "kernel_ms": g1_ms, "algorithmic_bytes": g1b},
         "layer": {"hbm_GBps": abytes / t_s / 1e9, "hbm_frac": abytes / t_s / 1e9 / HBM_PEAK_GBS,
                   "mfma_frac": aflops / t_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
