@@ -41,7 +41,7 @@ def parse():
                     choices=["decode", "prefill_zipf", "grouped_sqrtsoftplus", "latent_shared"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=48)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=64)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run three plain 1 GiB device-to-device copies (a known-size "
                          "reference for HBM byte counters)")
