@@ -43,6 +43,21 @@ struct TileCoord {
     int group, row0, row1, nt;
 };
 
+// Row tiles per band in the launch order of one group's tiles.
+constexpr int kBandRows = 4;
+
+// Position o of a block of cnt row tiles x ntn column tiles, taken in bands of
+// kBandRows row tiles; inside a band the row tile varies fastest, so the
+// workgroups resident on one XCD at a time form a kBandRows x (32 /
+// kBandRows) block and reuse both operands' K slices from its L2.
+__device__ __forceinline__ void band_order(int o, int cnt, int ntn, int& mt, int& nt) {
+    const int band = o / (kBandRows * ntn);
+    const int in_band = o - band * kBandRows * ntn;
+    const int rows = min(kBandRows, cnt - band * kBandRows);
+    nt = in_band / rows;
+    mt = band * kBandRows + (in_band - nt * rows);
+}
+
 // Returns false when this workgroup has no tile (grids are sized from an
 // upper bound of the tile count).
 __device__ __forceinline__ bool fetch_tile(const GemmArgs& g, int tile_m, int ntn, TileCoord& c) {
@@ -51,27 +66,22 @@ __device__ __forceinline__ bool fetch_tile(const GemmArgs& g, int tile_m, int nt
     const int i = blockIdx.x;
     if (i >= total) return false;
     const int lid = xcd_remap(i, total);
-    int mt = lid / ntn;
-    c.nt = lid - mt * ntn;
+    int mt;
     if (g.tiles) {
-        // Inside one group's block of count*ntn workgroups the row tiles vary
-        // fastest, so the row tiles that share a weight tile run side by side
-        // on one XCD and read it once from HBM.
-        const Tile t0 = g.tiles[mt];
+        // the tiles of one group are contiguous: tile lid / ntn belongs to the
+        // group whose block of count * ntn workgroups holds lid
+        const Tile t0 = g.tiles[lid / ntn];
         const int first = __builtin_amdgcn_readfirstlane(t0.first);
         const int cnt = __builtin_amdgcn_readfirstlane(t0.count);
-        if (cnt > 1) {
-            const int o = lid - first * ntn;
-            c.nt = o / cnt;
-            mt = first + (o - c.nt * cnt);
-        }
-        const Tile t = g.tiles[mt];
+        band_order(lid - first * ntn, cnt, ntn, mt, c.nt);
+        const Tile t = g.tiles[first + mt];
         // the tile is the same for the whole workgroup: keep it in SGPRs so
         // that every branch on it is a scalar branch
         c.group = __builtin_amdgcn_readfirstlane(t.group);
         c.row0 = __builtin_amdgcn_readfirstlane(t.row0);
         c.row1 = __builtin_amdgcn_readfirstlane(t.row1);
     } else {
+        band_order(lid, nm, ntn, mt, c.nt);
         c.group = 0;
         c.row0 = mt * tile_m;
         c.row1 = min(c.row0 + tile_m, g.M);
@@ -259,6 +269,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// The same with lgkmcnt(0) as well.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
 template <int EPI, bool KCAT>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     constexpr bool SW = EPI == EPI_SWIGLU;
@@ -314,7 +331,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     // Issue stage kt (clamped to the last stage) into its ring slot.  The K
     // segment of a K-concatenated product is picked with selects.
     auto issue = [&](int kt) __attribute__((always_inline)) {
-        const int slot = kt & (GSLOTS - 1);
+        const int slot = kt % GSLOTS;
         kt = min(kt, nk - 1);
         const bool seg1 = !KCAT || kt < nk1;
         const char* abase = seg1 ? Ab : A2b;
@@ -360,33 +377,59 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     // does this wave's 128-row half hold any row of the tile (wave-uniform)
     const bool active = tc.row1 - tc.row0 > wm * 128;
 
-    issue(0);
-    issue(1);
-    issue(2);
-    for (int kt = 0; kt < nk; ++kt) {
-        wait_vmcnt<8>();             // this wave's DMAs of stage kt have landed
-        __builtin_amdgcn_s_barrier();  // ... and every other wave's; slot (kt-1)&3 is free
+    // One stage's operand fragments (both 16-deep k-steps).
+    struct Frags {
+        bf16x8_t a[2][4], b[2][2];
+    };
+    auto read_frags = [&](int kt, Frags& f) __attribute__((always_inline)) {
+        const bf16_t* a = smem[kt % GSLOTS][0];
+        const bf16_t* b = smem[kt % GSLOTS][1];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int nj = 0; nj < 2; ++nj) f.b[ks][nj] = *(const bf16x8_t*)(&b[boffs[ks][nj]]);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) f.a[ks][mi] = *(const bf16x8_t*)(&a[aoffs[ks][mi]]);
+        }
+    };
+    auto mma = [&](const Frags& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int nj = 0; nj < 2; ++nj)
+                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        f.a[ks][mi], f.b[ks][nj], acc[mi][nj], 0, 0, 0);
+    };
+    // Iteration kt: once stage kt + 1 is visible to all waves, its fragments
+    // are read into the idle register set while the MFMAs consume stage kt's
+    // (read one iteration earlier).  Each wave's reads of stage kt are retired
+    // (lgkmcnt 0) before the barrier, so after it the slot of stage kt takes
+    // the DMA of stage kt + GSLOTS.  Stages kt + 2 and kt + 3 stay in flight.
+    auto step = [&](int kt, const Frags& cur, Frags& next) __attribute__((always_inline)) {
+        wait_vmcnt_lgkm0<4 * (GSLOTS - 2)>();
+        __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue(kt + 3);
+        issue(kt + GSLOTS);
         if (active) {
-            const bf16_t* a = smem[kt & (GSLOTS - 1)][0];
-            const bf16_t* b = smem[kt & (GSLOTS - 1)][1];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8_t fa[4], fb[2];
-#pragma unroll
-                for (int nj = 0; nj < 2; ++nj) fb[nj] = *(const bf16x8_t*)(&b[boffs[ks][nj]]);
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi) fa[mi] = *(const bf16x8_t*)(&a[aoffs[ks][mi]]);
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int nj = 0; nj < 2; ++nj)
-                        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            fa[mi], fb[nj], acc[mi][nj], 0, 0, 0);
-            }
+            read_frags(kt + 1, next);
+            mma(cur);
         }
         asm volatile("" ::: "memory");
+    };
+
+#pragma unroll
+    for (int s = 0; s < GSLOTS; ++s) issue(s);
+    wait_vmcnt_lgkm0<4 * (GSLOTS - 1)>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    Frags f0, f1;
+    if (active) read_frags(0, f0);
+    // nk is even (K and K2 are multiples of 64)
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, f0, f1);
+        step(kt + 1, f1, f0);
     }
     // The ring's trailing DMAs must land before the LDS is reused below.
     wait_vmcnt<0>();

@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "common.h"
@@ -117,29 +118,62 @@ GemmArgs gemm_defaults() {
     return g;
 }
 
-// One grouped product over both tile lists.
-moe_status_t grouped_gemm(moe_dtype_t dt, GemmArgs g, const ExpertsWs& w, int64_t P, int E,
-                          hipStream_t s) {
-    if (dt == MOE_DTYPE_F32) {
-        g.tiles = w.big_tiles;
-        g.num_tiles = w.counts + 1;
-        g.max_tiles = (int32_t)big_capacity(dt, P, E);
-        g.tile_m = kF32Rows;
-        return hip_status(launch_gemm(0, GEMM_TILED, g, s));
-    }
+// The two halves of one grouped product: groups of at most kStreamMaxRows
+// rows (weight streaming) and the rest (256-row MFMA tiles).
+moe_status_t small_groups_gemm(GemmArgs g, const ExpertsWs& w, int E, hipStream_t s) {
     g.tiles = w.small_tiles;
     g.num_tiles = w.counts;
-    g.max_tiles = (int32_t)small_capacity(dt, E);
+    g.max_tiles = (int32_t)small_capacity(MOE_DTYPE_BF16, E);
     g.tile_m = kStreamMaxRows;
-    MOE_HIP(launch_gemm(1, GEMM_STREAM, g, s));
+    return hip_status(launch_gemm(1, GEMM_STREAM, g, s));
+}
+
+moe_status_t large_groups_gemm(moe_dtype_t dt, GemmArgs g, const ExpertsWs& w, int64_t P, int E,
+                               hipStream_t s) {
+    const bool f32 = dt == MOE_DTYPE_F32;
     g.tiles = w.big_tiles;
     g.num_tiles = w.counts + 1;
     g.max_tiles = (int32_t)big_capacity(dt, P, E);
-    g.tile_m = kBigRows;
-    return hip_status(launch_gemm(1, GEMM_BIG, g, s));
+    g.tile_m = f32 ? kF32Rows : kBigRows;
+    return hip_status(launch_gemm(f32 ? 0 : 1, f32 ? GEMM_TILED : GEMM_BIG, g, s));
+}
+
+// A second stream per device, owned by the library (default priority), on
+// which the small-group chain runs beside the large-group chain.  The mutex
+// also keeps the fork/join events of concurrent host threads apart.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// Called with g_side_mu held.
+moe_status_t side_stream(SideStream** out) {
+    int dev = 0;
+    MOE_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ENOTSUP;
+    SideStream& ss = g_side[dev];
+    if (!ss.s) {
+        MOE_HIP(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
+        MOE_HIP(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming));
+        MOE_HIP(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking));
+    }
+    *out = &ss;
+    return MOE_OK;
 }
 
 // Grouped gate/up + SwiGLU, then grouped down, over expert-sorted rows.
+//
+// When groups average at least kOverlapMinRows rows (prefill-like batches)
+// the small groups' chain (gate/up, then down: HBM-bound weight streaming)
+// runs on the side stream while the large groups' chain (MFMA-bound) runs on
+// the caller's stream; the two touch disjoint rows of h and y_rows.  The
+// GEMM1 stage then ends when the large groups' gate/up product ends, and
+// GEMM2 covers the rest of both chains.
+constexpr int64_t kOverlapMinRows = 16;
+
 moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, const void* x,
                          const int32_t* offsets, const int32_t* row_to_pair, const void* w13,
                          const void* w2, float* y_rows, const ExpertsWs& w, hipStream_t s,
@@ -162,11 +196,6 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
     g1.epi = EPI_SWIGLU;
     g1.C = w.h;
     g1.ldc = I;
-    MOE_TRY(grouped_gemm(dt, g1, w, P, E, s));
-    if (ev) {
-        MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM1 + 1], s));
-        MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM2], s));
-    }
 
     GemmArgs g2 = gemm_defaults();
     g2.A = w.h;
@@ -178,9 +207,37 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
     g2.epi = EPI_F32;
     g2.C = y_rows;
     g2.ldc = D;
-    MOE_TRY(grouped_gemm(dt, g2, w, P, E, s));
-    if (ev) MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM2 + 1], s));
-    return MOE_OK;
+
+    const auto stage_mark = [&](int stage, int end) -> moe_status_t {
+        if (ev) MOE_HIP(hipEventRecord(ev[2 * stage + end], s));
+        return MOE_OK;
+    };
+    if (!f32 && P >= kOverlapMinRows * E) {
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        SideStream* ss = nullptr;
+        MOE_TRY(side_stream(&ss));
+        MOE_HIP(hipEventRecord(ss->fork, s));
+        MOE_HIP(hipStreamWaitEvent(ss->s, ss->fork, 0));
+        moe_status_t st = small_groups_gemm(g1, w, E, ss->s);
+        if (st == MOE_OK) st = small_groups_gemm(g2, w, E, ss->s);
+        // the caller's stream joins the side stream even after an error
+        const moe_status_t sj = hip_status(hipEventRecord(ss->join, ss->s));
+        if (st == MOE_OK) st = large_groups_gemm(dt, g1, w, P, E, s);
+        if (st == MOE_OK) st = stage_mark(MOE_STAGE_GEMM1, 1);
+        if (st == MOE_OK) st = stage_mark(MOE_STAGE_GEMM2, 0);
+        if (st == MOE_OK) st = large_groups_gemm(dt, g2, w, P, E, s);
+        if (sj == MOE_OK) MOE_HIP(hipStreamWaitEvent(s, ss->join, 0));
+        MOE_TRY(sj);
+        MOE_TRY(st);
+        return stage_mark(MOE_STAGE_GEMM2, 1);
+    }
+    if (!f32) MOE_TRY(small_groups_gemm(g1, w, E, s));
+    MOE_TRY(large_groups_gemm(dt, g1, w, P, E, s));
+    MOE_TRY(stage_mark(MOE_STAGE_GEMM1, 1));
+    MOE_TRY(stage_mark(MOE_STAGE_GEMM2, 0));
+    if (!f32) MOE_TRY(small_groups_gemm(g2, w, E, s));
+    MOE_TRY(large_groups_gemm(dt, g2, w, P, E, s));
+    return stage_mark(MOE_STAGE_GEMM2, 1);
 }
 
 // Dense C = A . B^T (+ A2 . B2^T) over T rows.
