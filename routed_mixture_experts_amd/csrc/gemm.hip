@@ -10,21 +10,24 @@
 // both operands K-contiguous, with the epilogue fused (fp32 store, fp32 + bias
 // row, layer-dtype store, or SwiGLU silu(gate) * up).
 //
-// Three kernels:
+// Kernels:
+//  * gemm_bf16_big    -- 256x256 tiles, 8 waves, a 4-slot LDS ring filled by
+//    global_load_lds and operand fragments pipelined one K stage ahead: groups
+//    with more than 64 rows (prefill) and large dense products.
 //  * gemm_bf16_tiled  -- 128x128x64 LDS double-buffered tiles, 4 waves in a
-//    2x2 layout, each wave a 64x64 block of v_mfma_f32_32x32x16_bf16.  For
-//    groups with many rows (prefill) and the dense products.
-//  * gemm_bf16_stream -- for groups with at most 16 rows (decode): the
-//    weights are the streamed operand.  A workgroup owns 64 weight rows of one
-//    group and splits K over its 4 waves; each wave keeps two batches of
-//    16-byte weight loads in flight and feeds v_mfma_f32_16x16x32_bf16 with
-//    the weights as the 16-row operand and the (<= 16) token rows as the
-//    other; partial sums meet in LDS once at the end.
+//    2x2 layout, each wave a 64x64 block of v_mfma_f32_32x32x16_bf16: mid-size
+//    dense products.
+//  * gemm_bf16_stream -- groups of at most 64 rows (all of decode): the weights
+//    are the streamed operand.  Each wave of an 8-wave workgroup streams 16
+//    whole weight rows straight into MFMA registers; the token rows come from
+//    an LDS double buffer.
+//  * gemm_bf16_stream_ksplit -- the same product with K split over 4 waves, for
+//    dense products too small to fill the chip with whole-row streams.
 //  * gemm_f32_tiled   -- fp32 VALU 64x64 tiles for the fp32 layer.
 // Work is a flat list of (row tile, column tile); workgroup i runs on XCD
-// i % 8, so logical tile ids are remapped to give each XCD a contiguous range
-// (consecutive ids share the activation tile, which then stays in that XCD's
-// L2).
+// i % 8, so logical tile ids are remapped to give each XCD a contiguous range,
+// taken in bands of row tiles so that the workgroups resident on one XCD share
+// both operands' K slices in its L2.
 #include "common.h"
 
 namespace moe {
