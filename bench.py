@@ -83,20 +83,28 @@ def layer_work(w, counts):
     return wbytes + abytes, flops, touched
 
 
+# The files the decode gate/up kernel (gemm_bf16_stream) is built from; the
+# committed counter summary applies while their hash matches.
+STREAM_KERNEL_SOURCES = ("gemm_stream.hip", "gemm_tiles.h", "common.h")
+
+
 def profiled_traffic(workload: str):
     """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
     FETCH_SIZE/WRITE_SIZE summary, or None when the kernel source no longer
     matches the one the counters were taken on."""
     import glob
     import hashlib
-    src = os.path.join(ROOT, "routed_mixture_experts_amd", "csrc", "gemm.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    csrc = os.path.join(ROOT, "routed_mixture_experts_amd", "csrc")
+    h = hashlib.sha256()
+    for name in STREAM_KERNEL_SOURCES:
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    sha = h.hexdigest()[:16]
     for path in glob.glob(os.path.join(ROOT, "profiles", "*hbm_counters*.md")):
         for line in open(path):
             if not line.startswith("traffic:"):
                 continue
             kv = dict(f.split("=", 1) for f in line.split()[1:])
-            if kv.get("workload") == workload and kv.get("gemm_hip_sha256_16") == sha:
+            if kv.get("workload") == workload and kv.get("stream_src_sha256_16") == sha:
                 return int(kv["bytes_per_launch"])
     return None
 

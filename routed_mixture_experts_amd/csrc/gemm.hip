@@ -11,90 +11,27 @@
 // row, layer-dtype store, or SwiGLU silu(gate) * up).
 //
 // Kernels:
-//  * gemm_bf16_big    -- 256x256 tiles, 8 waves, a 4-slot LDS ring filled by
-//    global_load_lds and operand fragments pipelined one K stage ahead: groups
-//    with more than 64 rows (prefill) and large dense products.
+//  * gemm_bf16_big    -- 256x256 tiles, 8 waves, a 2-slot LDS ring of 64-deep
+//    K stages filled by global_load_lds in whole 128-byte lines, operand
+//    fragments read half a stage ahead: groups with more than 64 rows
+//    (prefill) and large dense products.
 //  * gemm_bf16_tiled  -- 128x128x64 LDS double-buffered tiles, 4 waves in a
 //    2x2 layout, each wave a 64x64 block of v_mfma_f32_32x32x16_bf16: mid-size
 //    dense products.
-//  * gemm_bf16_stream -- groups of at most 64 rows (all of decode): the weights
-//    are the streamed operand.  Each wave of an 8-wave workgroup streams 16
-//    whole weight rows straight into MFMA registers; the token rows come from
-//    an LDS double buffer.
-//  * gemm_bf16_stream_ksplit -- the same product with K split over 4 waves, for
-//    dense products too small to fill the chip with whole-row streams.
+//  * the weight-streaming kernels for groups of at most 64 rows (all of
+//    decode) and small dense products live in gemm_stream.hip.
 //  * gemm_f32_tiled   -- fp32 VALU 64x64 tiles for the fp32 layer.
 // Work is a flat list of (row tile, column tile); workgroup i runs on XCD
 // i % 8, so logical tile ids are remapped to give each XCD a contiguous range,
 // taken in bands of row tiles so that the workgroups resident on one XCD share
 // both operands' K slices in its L2.
-#include "common.h"
+#include "gemm_tiles.h"
 
 namespace moe {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ int xcd_remap(int i, int total) {
-    const int xcd = i & 7, local = i >> 3;
-    const int per = total >> 3, rem = total & 7;
-    return xcd * per + min(xcd, rem) + local;
-}
-
-struct TileCoord {
-    int group, row0, row1, nt;
-};
-
-// Row tiles per band in the launch order of one group's tiles.
-constexpr int kBandRows = 4;
-
-// Position o of a block of cnt row tiles x ntn column tiles, taken in bands of
-// kBandRows row tiles; inside a band the row tile varies fastest, so the
-// workgroups resident on one XCD at a time form a kBandRows x (32 /
-// kBandRows) block and reuse both operands' K slices from its L2.
-__device__ __forceinline__ void band_order(int o, int cnt, int ntn, int& mt, int& nt) {
-    const int band = o / (kBandRows * ntn);
-    const int in_band = o - band * kBandRows * ntn;
-    const int rows = min(kBandRows, cnt - band * kBandRows);
-    nt = in_band / rows;
-    mt = band * kBandRows + (in_band - nt * rows);
-}
-
-// Returns false when this workgroup has no tile (grids are sized from an
-// upper bound of the tile count).
-__device__ __forceinline__ bool fetch_tile(const GemmArgs& g, int tile_m, int ntn, TileCoord& c) {
-    const int nm = g.tiles ? *g.num_tiles : (g.M + tile_m - 1) / tile_m;
-    const int total = nm * ntn;
-    const int i = blockIdx.x;
-    if (i >= total) return false;
-    const int lid = xcd_remap(i, total);
-    int mt;
-    if (g.tiles) {
-        // the tiles of one group are contiguous: tile lid / ntn belongs to the
-        // group whose block of count * ntn workgroups holds lid
-        const Tile t0 = g.tiles[lid / ntn];
-        const int first = __builtin_amdgcn_readfirstlane(t0.first);
-        const int cnt = __builtin_amdgcn_readfirstlane(t0.count);
-        band_order(lid - first * ntn, cnt, ntn, mt, c.nt);
-        const Tile t = g.tiles[first + mt];
-        // the tile is the same for the whole workgroup: keep it in SGPRs so
-        // that every branch on it is a scalar branch
-        c.group = __builtin_amdgcn_readfirstlane(t.group);
-        c.row0 = __builtin_amdgcn_readfirstlane(t.row0);
-        c.row1 = __builtin_amdgcn_readfirstlane(t.row1);
-    } else {
-        band_order(lid, nm, ntn, mt, c.nt);
-        c.group = 0;
-        c.row0 = mt * tile_m;
-        c.row1 = min(c.row0 + tile_m, g.M);
-    }
-    return true;
-}
-
-__device__ __forceinline__ int64_t a_row_of(const GemmArgs& g, int r) {
-    return g.a_map ? (int64_t)(g.a_map[r] / g.a_div) : (int64_t)r;
-}
+using namespace tiles;
 
 // ------------------------------------------------------------------------
 // bf16 LDS-tiled MFMA kernel
@@ -265,21 +202,6 @@ constexpr int GBM = 256, GBN = 256, GBK = 64, GSLOTS = 2;
 
 __device__ __forceinline__ int swz(int row, int chunk) {
     return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
-}
-
-// s_waitcnt with only a vector-memory count (gfx9 encoding: vmcnt[3:0] in
-// bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at "no wait").
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// The same with lgkmcnt(0) as well.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
 template <int EPI, bool KCAT>
@@ -518,380 +440,6 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------------
-// bf16 weight-streaming MFMA kernel (<= 64 rows per tile)
-// ------------------------------------------------------------------------
-constexpr int SROWS = 16;   // token rows per MFMA block (and per dense tile)
-constexpr int SNW = 64;     // weight rows per workgroup
-
-// One tile of up to 16*NB token rows: each wave streams its quarter of K for
-// 64 weight rows and applies every weight fragment to all NB token blocks.
-// SU k-steps (of 32) form one load batch; two batches are in flight.
-template <int EPI, int NB, int SU>
-__device__ __forceinline__ void stream_tile(const GemmArgs& g, const TileCoord& tc,
-                                            float (*red)[4][4][64]) {
-    constexpr bool SW = EPI == EPI_SWIGLU;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, kofs = (lane >> 4) * 8;
-
-    // 32-bit byte offsets from wave-uniform bases (one VGPR per row); every
-    // operand of one group fits in 4 GiB (checked on the host)
-    const char* Bb = (const char*)((const bf16_t*)g.B + (int64_t)tc.group * g.b_gstride);
-    const char* B2b = (const char*)g.B2;
-    const char* Ab = (const char*)g.A;
-    const char* A2b = (const char*)g.A2;
-    uint32_t wo[4], wo2[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        int wrow;
-        if (SW) {
-            const int c = min(tc.nt * 32 + (q & 1) * 16 + l16, g.N - 1);
-            wrow = q < 2 ? c : g.N + c;
-        } else {
-            wrow = min(tc.nt * SNW + q * 16 + l16, g.N - 1);
-        }
-        wo[q] = (uint32_t)((int64_t)wrow * g.K * 2) + kofs * 2;
-        wo2[q] = (uint32_t)((int64_t)wrow * g.K2 * 2) + kofs * 2;
-    }
-    uint32_t xo[NB], xo2[NB];
-    bool xvalid[NB];
-#pragma unroll
-    for (int tb = 0; tb < NB; ++tb) {
-        const int r = tc.row0 + tb * 16 + l16;
-        xvalid[tb] = r < tc.row1;
-        xo[tb] = (uint32_t)((xvalid[tb] ? a_row_of(g, r) : 0) * g.lda * 2) + kofs * 2;
-        xo2[tb] = (uint32_t)((int64_t)(xvalid[tb] ? r : 0) * g.lda2 * 2) + kofs * 2;
-    }
-
-    const int ns1 = g.K / 32;
-    const int ns = ns1 + (g.A2 ? g.K2 / 32 : 0);
-    const int s0 = (int)((int64_t)wave * ns / 4), s1 = (int)((int64_t)(wave + 1) * ns / 4);
-
-    f32x4_t acc[4][NB];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int tb = 0; tb < NB; ++tb) acc[q][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    u32x4_t wa[SU][4], xa[SU][NB], wb[SU][4], xb[SU][NB];
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-
-    auto load = [&](int sbase, u32x4_t (&w)[SU][4], u32x4_t (&x)[SU][NB])
-                    __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < SU; ++u) {
-            const int st = sbase + u;
-            if (st < s1) {
-                if (st < ns1) {
-                    const uint32_t ko = st * 64;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) w[u][q] = *(const u32x4_t*)(Bb + (wo[q] + ko));
-#pragma unroll
-                    for (int tb = 0; tb < NB; ++tb)
-                        x[u][tb] = xvalid[tb] ? *(const u32x4_t*)(Ab + (xo[tb] + ko)) : zero;
-                } else {
-                    const uint32_t ko = (st - ns1) * 64;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        w[u][q] = *(const u32x4_t*)(B2b + (wo2[q] + ko));
-#pragma unroll
-                    for (int tb = 0; tb < NB; ++tb)
-                        x[u][tb] = xvalid[tb] ? *(const u32x4_t*)(A2b + (xo2[tb] + ko)) : zero;
-                }
-            }
-        }
-    };
-    auto compute = [&](int sbase, u32x4_t (&w)[SU][4], u32x4_t (&x)[SU][NB])
-                       __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < SU; ++u) {
-            if (sbase + u < s1) {
-#pragma unroll
-                for (int tb = 0; tb < NB; ++tb) {
-                    const bf16x8_t xb8 = __builtin_bit_cast(bf16x8_t, x[u][tb]);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        acc[q][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, w[u][q]), xb8, acc[q][tb], 0, 0, 0);
-                }
-            }
-        }
-    };
-
-    load(s0, wa, xa);
-    for (int s = s0; s < s1; s += 2 * SU) {
-        load(s + SU, wb, xb);
-        compute(s, wa, xa);
-        load(s + 2 * SU, wa, xa);
-        compute(s + SU, wb, xb);
-    }
-
-    // acc[q][tb][j] holds C[weight row 4*(lane/16)+j of group q][token 16*tb + lane%16]
-    const int wr = (lane >> 4) * 4;
-#pragma unroll
-    for (int tb = 0; tb < NB; ++tb) {
-        if (tb > 0) __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) red[wave][q][j][lane] = acc[q][tb][j];
-        __syncthreads();
-        const int rr = tc.row0 + tb * 16 + l16;
-        if (SW) {
-            if (wave < 2) {
-                const int q = wave;
-                float gsum[4], usum[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    gsum[j] = red[0][q][j][lane] + red[1][q][j][lane] + red[2][q][j][lane] +
-                              red[3][q][j][lane];
-                    usum[j] = red[0][q + 2][j][lane] + red[1][q + 2][j][lane] +
-                              red[2][q + 2][j][lane] + red[3][q + 2][j][lane];
-                }
-                if (rr < tc.row1) {
-                    bf16_t* crow = (bf16_t*)g.C + (int64_t)rr * g.ldc;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int hc = tc.nt * 32 + q * 16 + wr + j;
-                        if (hc < g.N) crow[hc] = f32_to_bf16(silu_f32(gsum[j]) * usum[j]);
-                    }
-                }
-            }
-        } else {
-            const int q = wave;
-            float v[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                v[j] = red[0][q][j][lane] + red[1][q][j][lane] + red[2][q][j][lane] +
-                       red[3][q][j][lane];
-            if (rr < tc.row1) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int c = tc.nt * SNW + q * 16 + wr + j;
-                    if (c >= g.N) continue;
-                    float o = v[j];
-                    if (EPI == EPI_F32_BIAS && g.bias) o += g.bias[c];
-                    if (EPI == EPI_OUT)
-                        ((bf16_t*)g.C)[(int64_t)rr * g.ldc + c] = f32_to_bf16(o);
-                    else
-                        ((float*)g.C)[(int64_t)rr * g.ldc + c] = o;
-                }
-            }
-        }
-    }
-}
-
-// Dense products with few tiles: splitting K over the waves keeps more of
-// the chip busy than whole-row streams would.
-template <int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_stream_ksplit(GemmArgs g) {
-    constexpr bool SW = EPI == EPI_SWIGLU;
-    const int ntn = SW ? (g.N + 31) / 32 : (g.N + SNW - 1) / SNW;
-    TileCoord tc;
-    if (!fetch_tile(g, SROWS, ntn, tc)) return;
-    __shared__ float red[4][4][4][64];
-    const int rows = tc.row1 - tc.row0;
-    if (rows <= 16) stream_tile<EPI, 1, 4>(g, tc, red);
-    else if (rows <= 32) stream_tile<EPI, 2, 2>(g, tc, red);
-    else stream_tile<EPI, 4, 2>(g, tc, red);
-}
-
-// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt left at "no wait").
-__device__ __forceinline__ void wait_lgkm0() {
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
-}
-
-// Whole-row weight streams.  Each wave owns 16 weight rows (SwiGLU: 8 gate
-// rows and the 8 up rows of the same hidden columns) over the full K, so
-// every wave reads 16 long contiguous rows -- the pattern that keeps HBM
-// near its streaming rate; splitting K over waves (four read positions per
-// row) runs about 12% slower.  The token rows, shared by the 4 waves, come
-// from LDS: chunks of CS k-steps are loaded a chunk ahead into registers
-// (each wave a quarter of the chunk), written to a double buffer, and
-// published with one barrier per chunk.  Weight fragments run PD k-steps
-// ahead in registers.  Reading the token operand straight from global
-// memory beside the weights costs up to a third of the bandwidth, which is
-// why it is staged.  Every vector-memory operation here is a register load,
-// so the compiler's in-order vmcnt bookkeeping stays exact (LDS-DMA loads
-// mixed with register loads make it fall back to draining the counter).
-constexpr int SX_BYTES = 64 * 1024;  // token-chunk double buffer
-constexpr int SRW = 8;               // waves per workgroup
-constexpr int SRN = 16 * SRW;        // weight rows per workgroup (SwiGLU: SRN / 2 columns)
-
-template <int EPI, int NB, bool KCAT>
-__device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCoord& tc,
-                                                 char* xs) {
-    constexpr bool SW = EPI == EPI_SWIGLU;
-    constexpr int CS = NB == 4 ? 8 : 16;   // k-steps (of 32) per token chunk
-    constexpr int PD = 8;                  // weight prefetch distance in k-steps
-    constexpr int XI = CS * NB / SRW;      // 1 KB token blocks per wave per chunk
-    constexpr int CHUNK = CS * NB * 1024;  // bytes of one token chunk
-    static_assert(2 * CHUNK <= SX_BYTES && CS % PD == 0 && XI % NB == 0, "stream tiling");
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int l16 = lane & 15, g4 = lane >> 4;
-
-    // 32-bit byte offsets from wave-uniform bases; every operand of one group
-    // fits in 4 GiB (checked on the host)
-    const char* Bb = (const char*)((const bf16_t*)g.B + (int64_t)tc.group * g.b_gstride);
-    const char* B2b = (const char*)g.B2;
-    const char* Ab = (const char*)g.A;
-    const char* A2b = (const char*)g.A2;
-    int wrow;
-    if (SW) {
-        const int c = min(tc.nt * (SRN / 2) + wave * 8 + (l16 & 7), g.N - 1);
-        wrow = l16 < 8 ? c : g.N + c;
-    } else {
-        wrow = min(tc.nt * SRN + wave * 16 + l16, g.N - 1);
-    }
-    const uint32_t wo = (uint32_t)((int64_t)wrow * g.K * 2) + g4 * 16;
-    const uint32_t wo2 = KCAT ? (uint32_t)((int64_t)wrow * g.K2 * 2) + g4 * 16 : 0u;
-    // token rows past the tile's end load its last row (never stored)
-    uint32_t xo[NB], xo2[NB];
-#pragma unroll
-    for (int tb = 0; tb < NB; ++tb) {
-        const int r = min(tc.row0 + tb * 16 + l16, tc.row1 - 1);
-        xo[tb] = (uint32_t)(a_row_of(g, r) * g.lda * 2) + g4 * 16;
-        xo2[tb] = KCAT ? (uint32_t)((int64_t)r * g.lda2 * 2) + g4 * 16 : 0u;
-    }
-
-    const int ns1 = g.K / 32;
-    const int ns = ns1 + (KCAT ? g.K2 / 32 : 0);
-    const int nch = (ns + CS - 1) / CS;
-
-    // Token chunk c lives in LDS buffer c & 1 as 1 KB blocks b = (k-step
-    // b / NB, 16-row block b % NB), each in MFMA operand order (lane l holds
-    // row l % 16, k 8 * (l / 16) .. +7 of the step).  This wave moves blocks
-    // wave * XI .. +XI-1; steps past K re-read the last step (never used).
-    u32x4_t xr[XI];
-    auto load_x = [&](int c) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < XI; ++i) {
-            const int b = wave * XI + i;
-            const int tb = i % NB;
-            const int st = min(c * CS + b / NB, ns - 1);
-            const bool seg1 = !KCAT || st < ns1;
-            const char* src = seg1 ? Ab + (xo[tb] + (uint32_t)st * 64)
-                                   : A2b + (xo2[tb] + (uint32_t)(st - ns1) * 64);
-            xr[i] = *(const u32x4_t*)src;
-        }
-    };
-    auto store_x = [&](int c) __attribute__((always_inline)) {
-        char* dst = xs + (c & 1) * CHUNK + lane * 16;
-#pragma unroll
-        for (int i = 0; i < XI; ++i) *(u32x4_t*)(dst + (wave * XI + i) * 1024) = xr[i];
-    };
-    auto load_w = [&](int st) __attribute__((always_inline)) {
-        st = min(st, ns - 1);
-        const bool seg1 = !KCAT || st < ns1;
-        const char* src = seg1 ? Bb + (wo + (uint32_t)st * 64) : B2b + (wo2 + (uint32_t)(st - ns1) * 64);
-        return *(const u32x4_t*)src;
-    };
-
-    f32x4_t acc[NB];
-#pragma unroll
-    for (int tb = 0; tb < NB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    u32x4_t w[PD];
-
-    // The first weight fragments go out before the wait for chunk 0.  Order
-    // is pinned (empty asm with a memory clobber) so that on both paths into
-    // the store of chunk c + 1 the token loads are followed by exactly the CS
-    // weight loads of chunk c: the compiler's wait for the token registers
-    // then leaves the newest weight loads in flight.
-    load_x(0);
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int v = 0; v < PD; ++v) w[v] = load_w(v);
-    asm volatile("" ::: "memory");
-    store_x(0);
-    asm volatile("" ::: "memory");
-    load_x(1);
-    asm volatile("" ::: "memory");
-
-    for (int c = 0; c < nch; ++c) {
-        // this wave's LDS writes of chunk c are done, and its LDS reads of
-        // chunk c - 1; after the barrier every wave's part of chunk c is
-        // visible and no wave reads buffer (c + 1) & 1 any more.  (A
-        // __syncthreads fence would also drain the weight loads in flight.)
-        wait_lgkm0();
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        const char* xc = xs + (c & 1) * CHUNK + lane * 16;
-#pragma unroll
-        for (int u = 0; u < CS; u += PD) {
-#pragma unroll
-            for (int v = 0; v < PD; ++v) {
-                // steps past K (the ragged last chunk) multiply zero weights
-                const int st = c * CS + u + v;
-                const u32x4_t wz = st < ns ? w[v] : u32x4_t{0u, 0u, 0u, 0u};
-                const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, wz);
-#pragma unroll
-                for (int tb = 0; tb < NB; ++tb) {
-                    const u32x4_t xv = *(const u32x4_t*)(xc + ((u + v) * NB + tb) * 1024);
-                    acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        wf, __builtin_bit_cast(bf16x8_t, xv), acc[tb], 0, 0, 0);
-                }
-                w[v] = load_w(st + PD);
-            }
-        }
-        asm volatile("" ::: "memory");
-        // chunk c + 1 has had a whole chunk to arrive; chunks past the end
-        // only touch the idle buffer, which keeps this branch-free
-        store_x(c + 1);
-        asm volatile("" ::: "memory");
-        load_x(c + 2);
-        asm volatile("" ::: "memory");
-    }
-
-    // acc[tb][j] = C[weight row 4*g4 + j of this wave][token 16*tb + l16]
-#pragma unroll
-    for (int tb = 0; tb < NB; ++tb) {
-        const int r = tc.row0 + tb * 16 + l16;
-        if (SW) {
-            // lanes 32..63 hold the up rows of lane - 32's gate rows
-            float up[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) up[j] = __shfl_xor(acc[tb][j], 32);
-            if (g4 < 2 && r < tc.row1) {
-                bf16_t* crow = (bf16_t*)g.C + (int64_t)r * g.ldc;
-                const int hc0 = tc.nt * (SRN / 2) + wave * 8 + g4 * 4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (hc0 + j < g.N) crow[hc0 + j] = f32_to_bf16(silu_f32(acc[tb][j]) * up[j]);
-            }
-        } else if (r < tc.row1) {
-            const int c0 = tc.nt * SRN + wave * 16 + g4 * 4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = c0 + j;
-                if (c >= g.N) continue;
-                float o = acc[tb][j];
-                if (EPI == EPI_F32_BIAS && g.bias) o += g.bias[c];
-                if (EPI == EPI_OUT)
-                    ((bf16_t*)g.C)[(int64_t)r * g.ldc + c] = f32_to_bf16(o);
-                else
-                    ((float*)g.C)[(int64_t)r * g.ldc + c] = o;
-            }
-        }
-    }
-}
-
-// Grouped tiles here hold one whole group of at most 64 rows; dense products
-// are cut into 16-row tiles.
-template <int EPI, bool KCAT>
-__global__ __launch_bounds__(64 * SRW, 4) void gemm_bf16_stream(GemmArgs g) {
-    constexpr bool SW = EPI == EPI_SWIGLU;
-    const int ntn = SW ? (g.N + SRN / 2 - 1) / (SRN / 2) : (g.N + SRN - 1) / SRN;
-    TileCoord tc;
-    if (!fetch_tile(g, SROWS, ntn, tc)) return;
-    __shared__ __attribute__((aligned(1024))) char xs[SX_BYTES];
-    const int rows = tc.row1 - tc.row0;
-    if (rows <= 16) stream_rows_tile<EPI, 1, KCAT>(g, tc, xs);
-    else if (rows <= 32) stream_rows_tile<EPI, 2, KCAT>(g, tc, xs);
-    else stream_rows_tile<EPI, 4, KCAT>(g, tc, xs);
-}
-
-// ------------------------------------------------------------------------
 // fp32 VALU tiled kernel (64x64 tiles, 4x4 outputs per thread)
 // ------------------------------------------------------------------------
 constexpr int FBM = 64, FBN = 64, FBK = 16;
@@ -1004,31 +552,17 @@ void launch_big(const GemmArgs& g, dim3 gd, hipStream_t s) {
     }
 }
 
-// Dense products with fewer workgroups than this split K over the waves.
-constexpr int64_t kStreamRowsMinGrid = 1024;
-
-template <bool KC>
-void launch_stream_rows(const GemmArgs& g, dim3 gd, hipStream_t s) {
-    const dim3 bd(64 * SRW);
-    switch (g.epi) {
-        case EPI_F32: gemm_bf16_stream<EPI_F32, KC><<<gd, bd, 0, s>>>(g); break;
-        case EPI_F32_BIAS: gemm_bf16_stream<EPI_F32_BIAS, KC><<<gd, bd, 0, s>>>(g); break;
-        case EPI_OUT: gemm_bf16_stream<EPI_OUT, KC><<<gd, bd, 0, s>>>(g); break;
-        default: gemm_bf16_stream<EPI_SWIGLU, KC><<<gd, bd, 0, s>>>(g); break;
-    }
-}
-
 int col_tiles(int path, int dtype, int epi, int N) {
     const bool sw = epi == EPI_SWIGLU;
     if (dtype == 0) return sw ? (N + 31) / 32 : (N + FBN - 1) / FBN;
-    if (path == GEMM_STREAM) return sw ? (N + SRN / 2 - 1) / (SRN / 2) : (N + SRN - 1) / SRN;
+    if (path == GEMM_STREAM) return stream_col_tiles(epi, N);
     if (path == GEMM_BIG) return sw ? (N + 127) / 128 : (N + GBN - 1) / GBN;
     return sw ? (N + 63) / 64 : (N + TBN - 1) / TBN;
 }
 
 int row_tile(int path, int dtype) {
     if (dtype == 0) return FBM;
-    if (path == GEMM_STREAM) return SROWS;
+    if (path == GEMM_STREAM) return stream_row_tile();
     return path == GEMM_BIG ? GBM : TBM;
 }
 
@@ -1052,16 +586,7 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
     if (dtype == 0) {
         MOE_GEMM_SWITCH(gemm_f32_tiled)
     } else if (path == GEMM_STREAM) {
-        const bool sw = g.epi == EPI_SWIGLU;
-        const int64_t grid_ks = (int64_t)nm * (sw ? (g.N + 31) / 32 : (g.N + SNW - 1) / SNW);
-        if (!g.tiles && grid_ks < kStreamRowsMinGrid) {
-            gd = dim3((unsigned)grid_ks);
-            MOE_GEMM_SWITCH(gemm_bf16_stream_ksplit)
-        } else if (g.A2) {
-            launch_stream_rows<true>(g, gd, s);
-        } else {
-            launch_stream_rows<false>(g, gd, s);
-        }
+        return launch_stream_gemm(g, nm, s);
     } else if (path == GEMM_BIG) {
         if (g.A2) launch_big<true>(g, gd, s);
         else launch_big<false>(g, gd, s);
