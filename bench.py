@@ -38,8 +38,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill_zipf", "grouped_sqrtsoftplus", "latent_shared"])
+                    choices=["decode", "prefill_zipf", "grouped_sqrtsoftplus", "latent_shared",
+                             "decode_fp8"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill line")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the decode line with FP8 E4M3 expert weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=64)
     ap.add_argument("--copy-probe", action="store_true",
@@ -71,7 +74,10 @@ def layer_work(w, counts):
     D = w.D
     touched = int((counts > 0).sum())
     P = w.T * w.k
-    wbytes = touched * 3 * w.I * D * es + w.E * w.H * es
+    if w.weights == "fp8_e4m3":   # one byte per weight plus an fp32 scale per row
+        wbytes = touched * (3 * w.I * D + 4 * (2 * w.I + D)) + w.E * w.H * es
+    else:
+        wbytes = touched * 3 * w.I * D * es + w.E * w.H * es
     flops = 2.0 * P * 3 * D * w.I + 2.0 * w.T * w.H * w.E
     if w.latent:
         wbytes += 2 * w.latent * w.H * es
@@ -115,7 +121,11 @@ def gemm1_bytes(w, counts):
     read once, and h written."""
     es = 2 if w.dtype == "bf16" else 4
     touched = int((counts > 0).sum())
-    return touched * 2 * w.I * w.D * es + w.T * w.D * es + w.T * w.k * w.I * es, touched
+    if w.weights == "fp8_e4m3":
+        wb = touched * (2 * w.I * w.D + 4 * 2 * w.I)
+    else:
+        wb = touched * 2 * w.I * w.D * es
+    return wb + w.T * w.D * es + w.T * w.k * w.I * es, touched
 
 
 class Runner:
@@ -134,14 +144,20 @@ class Runner:
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.out = torch.empty((w.T, w.H), dtype=inp["x"].dtype, device=dev)
         self.counts = torch.empty((w.E,), dtype=torch.int32, device=dev)
+        self.experts = (moe.ExpertWeights.fp8(inp["w13"], inp["w2"], inp["w13_scale"],
+                                              inp["w2_scale"])
+                        if w.weights == "fp8_e4m3" else None)
 
     def step(self, events=None):
         i = self.inp
-        self.moe.moe_forward(self.cfg, i["x"], i["w13"], i["w2"], w_router=i["w_router"],
-                             router_bias=i["router_bias"], correction_bias=i["corr_bias"],
-                             latent=self.lat, shared=self.sh, out=self.out,
-                             expert_counts_out=self.counts, stage_events=events,
-                             workspace=self.ws, stream=self.stream)
+        kw = dict(w_router=i["w_router"], router_bias=i["router_bias"],
+                  correction_bias=i["corr_bias"], latent=self.lat, shared=self.sh,
+                  out=self.out, expert_counts_out=self.counts, stage_events=events,
+                  workspace=self.ws, stream=self.stream)
+        if self.experts is not None:
+            self.moe.moe_forward_ex(self.cfg, i["x"], self.experts, **kw)
+        else:
+            self.moe.moe_forward(self.cfg, i["x"], i["w13"], i["w2"], **kw)
 
     def timed(self, steps, warmup):
         torch, moe = self.torch, self.moe
@@ -188,9 +204,16 @@ def cpu_baseline(w, inp, torch, ntok):
                      renormalize=w.renormalize, routed_scaling=w.routed_scaling)
     ids, _, _ = O.route(O.router_logits(x, wr, rb), cfg, cb)
     used = sorted(set(ids.reshape(-1).tolist()))
-    # host copies (fp32, exact for bf16) of just the experts the sample touches
-    w13 = {e: inp["w13"][e].float().cpu().numpy() for e in used}
-    w2 = {e: inp["w2"][e].float().cpu().numpy() for e in used}
+    # host copies (fp32, exact for bf16) of just the experts the sample touches;
+    # FP8 codes are decoded by the oracle (outside the timed region)
+    if w.weights == "fp8_e4m3":
+        w13 = {e: O.dequantize_rows(inp["w13"][e].cpu().numpy(), inp["w13_scale"][e].cpu().numpy())
+               for e in used}
+        w2 = {e: O.dequantize_rows(inp["w2"][e].cpu().numpy(), inp["w2_scale"][e].cpu().numpy())
+              for e in used}
+    else:
+        w13 = {e: inp["w13"][e].float().cpu().numpy() for e in used}
+        w2 = {e: inp["w2"][e].float().cpu().numpy() for e in used}
     info = threadpoolctl.threadpool_info()
     cores = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
     t0 = time.perf_counter()
@@ -277,6 +300,29 @@ def main():
             "load": {"max": int(pc.max()), "min": int(pc.min()), "empty": int((pc == 0).sum())},
             "stages_ms": pstage}
         del prun, pin
+    if args.workload == "decode" and not args.no_fp8:
+        # the same layer with the same weight draws quantised to FP8 E4M3 (one
+        # fp32 scale per weight row): a separate line, not the headline value
+        wf = WORKLOADS["decode_fp8"]
+        print("[bench] decode with FP8 expert weights", file=sys.stderr, flush=True)
+        from routed_mixture_experts_amd.synth import fp8_rows
+        fin = dict(inp)
+        fin["w13"], fin["w13_scale"] = fp8_rows(inp["w13"])
+        fin["w2"], fin["w2_scale"] = fp8_rows(inp["w2"])
+        frun = Runner(wf, fin, torch, moe, stream)
+        fms, _, fstage = frun.timed(args.steps, args.warmup)
+        fc = frun.counts.cpu().numpy()
+        fbytes, _, _ = layer_work(wf, fc)
+        f1b, _ = gemm1_bytes(wf, fc)
+        f1 = f1b / (fstage["gemm1"] * 1e-3) / 1e9
+        res["fp8_decode"] = {
+            "workload": describe(wf) + " weights=fp8_e4m3 (per-row fp32 scales)",
+            "value": wf.T / (fms * 1e-3), "unit": "tokens/s", "ms_per_step": fms,
+            "steps": args.steps, "hbm_frac": fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "gemm1": {"kernel": "gemm_bf16_stream<3, false, true>", "kernel_ms": fstage["gemm1"],
+                      "algorithmic_bytes": f1b, "achieved_GBps": f1, "frac": f1 / HBM_PEAK_GBS},
+            "stages_ms": fstage}
+        del frun, fin
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -237,6 +237,52 @@ moe_status_t moe_forward(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t 
                          void* const* stage_events, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* ------------------------------------------------------------------------
+ * Expert weights in a storage format other than the layer dtype (page 1,
+ * Stage 4: the grouped-matmul paths include W8A8FP and MXFP variants with
+ * the dequantisation fused into the grouped matmul).
+ *   MOE_WEIGHT_DTYPE     w13 / w2 in the layer dtype, as for moe_experts;
+ *                        the scale pointers are ignored.
+ *   MOE_WEIGHT_FP8_E4M3  w13 [E, 2I, D] and w2 [E, D, I] hold one OCP e4m3
+ *                        code per element (1 sign, 4 exponent bits with
+ *                        bias 7, 3 mantissa bits; 0x7F / 0xFF are NaN, there
+ *                        is no infinity; largest finite value 448), with one
+ *                        fp32 scale per weight row: the expert uses
+ *                        W[e, n, :] = decode(codes[e, n, :]) * scale[e, n].
+ *                        w13_scale [E, 2I] f32, w2_scale [E, D] f32.  Needs
+ *                        layer dtype bf16.  Activations (x, h) stay bf16 and
+ *                        every sum is fp32, as in the bf16 layer.
+ * ---------------------------------------------------------------------- */
+typedef enum { MOE_WEIGHT_DTYPE = 0, MOE_WEIGHT_FP8_E4M3 = 1 } moe_weight_format_t;
+
+typedef struct {
+    int32_t format;           /* moe_weight_format_t */
+    const void* w13;          /* [E, 2I, D] */
+    const void* w2;           /* [E, D, I] */
+    const float* w13_scale;   /* [E, 2I] f32 (FP8 only) */
+    const float* w2_scale;    /* [E, D] f32 (FP8 only) */
+} moe_expert_weights_t;
+
+/* moe_experts with the expert weights described by `w` (same workspace as
+ * moe_experts).  MOE_EINVAL for an unknown format or missing pointers;
+ * MOE_ENOTSUP for FP8 weights with an fp32 layer. */
+moe_status_t moe_experts_ex(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, int32_t D,
+                            int32_t I, const void* x, const int32_t* expert_offsets,
+                            const int32_t* row_to_pair, const moe_expert_weights_t* w,
+                            float* y_rows, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_forward with the routed experts described by `experts` instead of
+ * w13 / w2 (same workspace as moe_forward); errors as moe_experts_ex. */
+moe_status_t moe_forward_ex(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t T,
+                            int32_t H, int32_t I, const void* x, const void* w_router,
+                            const float* router_bias, const float* router_logits,
+                            const float* correction_bias, const moe_expert_weights_t* experts,
+                            const moe_latent_t* latent, const moe_shared_t* shared,
+                            void* out, float* logits_out, int32_t* topk_ids_out,
+                            float* topk_weights_out, int32_t* expert_counts_out,
+                            void* const* stage_events, void* ws, size_t ws_bytes,
+                            void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_string(moe_status_t status);
 

@@ -1,5 +1,5 @@
 """CPU oracle for the routed-MoE forward (test infrastructure only)."""
-from .moe_oracle import (RouteCfg, combine, expert_mlp, forward, forward_tokens,  # noqa: F401
-                         group_scores, keys_are_raw_logits, permute, rmsnorm, route,
+from .moe_oracle import (RouteCfg, combine, dequantize_rows, expert_mlp,  # noqa: F401
+                         forward, forward_tokens, fp8_e4m3_decode, group_scores, keys_are_raw_logits, permute, rmsnorm, route,
                          route_weights, router_logits, run_experts, score,
                          select_experts, selection_keys, shared_expert, silu, softplus)

@@ -37,6 +37,13 @@ experts by their sum and routed scaling multiplies afterwards; combine weights
 are applied to expert outputs, never to inputs; rows of w13 are gate then up;
 rows inside an expert's segment keep ascending pair order p = t*k + j.
 
+Expert weights may also come as 8-bit floating-point codes (page 1, Stage 4:
+the grouped-matmul paths include W8A8FP, W4A8 and MXFP variants with the
+dequantisation fused into the matmul; the pages give no format).  Reading:
+OCP FP8 E4M3 codes with one fp32 scale per weight row, the expert using
+decode(code) * scale; activations and every sum stay as in the unquantised
+layer.
+
 Parity pins: every function here is checked in the CPU test suite against
 something other than itself (closed forms, brute force over all subsets,
 textbook special cases, a dense every-expert reference written with torch).
@@ -200,6 +207,26 @@ def permute(ids: np.ndarray, num_experts: int):
 
 
 # ----------------------------------------------------------------- experts ---
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (the 8-bit floating-point format behind
+    page 1's W8A8FP path, per the reading in the header): bit 7 is the sign,
+    bits 6..3 the exponent field e with bias 7, bits 2..0 the mantissa m.
+    e > 0 gives (1 + m/8) * 2^(e-7); e = 0 gives the subnormal (m/8) * 2^-6;
+    e = 15 with m = 7 is NaN (the format has no infinities, so e = 15 with
+    m < 7 is an ordinary value, up to 448)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign, e, m = (c >> 7) & 1, (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where(sign == 1, -mag, mag)
+    return np.where((e == 15) & (m == 7), np.nan, val).astype(f64)
+
+
+def dequantize_rows(codes, scale) -> np.ndarray:
+    """Weights from FP8 codes with one scale per row (the last axis is the
+    input width): W[..., n, :] = decode(codes[..., n, :]) * scale[..., n]."""
+    return fp8_e4m3_decode(codes) * np.asarray(scale, dtype=f64)[..., None]
+
 
 def silu(v: np.ndarray) -> np.ndarray:
     return v / (1.0 + np.exp(-v))

@@ -23,9 +23,11 @@ GROUP_SCORES = {"max": 0, "top2sum": 1}
 STAGES = ["router", "downproj", "route", "permute", "gemm1", "gemm2", "combine", "shared", "tail"]
 MOE_NUM_STAGES = len(STAGES)
 
+MOE_WEIGHT_DTYPE, MOE_WEIGHT_FP8_E4M3 = 0, 1
+
 EXPORTS = ["moe_route", "moe_permute_workspace", "moe_permute", "moe_experts_workspace",
            "moe_experts", "moe_combine", "moe_forward_workspace", "moe_forward",
-           "moe_status_string"]
+           "moe_experts_ex", "moe_forward_ex", "moe_status_string"]
 
 
 class moe_route_cfg_t(ctypes.Structure):
@@ -43,6 +45,11 @@ class moe_latent_t(ctypes.Structure):
 
 class moe_shared_t(ctypes.Structure):
     _fields_ = [("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p), ("inter", ctypes.c_int32)]
+
+
+class moe_expert_weights_t(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -106,6 +113,14 @@ def load() -> ctypes.CDLL:
     lib.moe_forward_workspace.argtypes = [ctypes.POINTER(moe_route_cfg_t), _I32, _I64, _I32,
                                           _I32, ctypes.POINTER(moe_latent_t),
                                           ctypes.POINTER(moe_shared_t)]
+    lib.moe_experts_ex.restype = _I32
+    lib.moe_experts_ex.argtypes = [_I32, _I64, _I32, _I32, _I32, _I32, _P, _P, _P,
+                                   ctypes.POINTER(moe_expert_weights_t), _P, _P, _SZ, _P]
+    lib.moe_forward_ex.restype = _I32
+    lib.moe_forward_ex.argtypes = [ctypes.POINTER(moe_route_cfg_t), _I32, _I64, _I32, _I32, _P,
+                                   _P, _P, _P, _P, ctypes.POINTER(moe_expert_weights_t),
+                                   ctypes.POINTER(moe_latent_t), ctypes.POINTER(moe_shared_t),
+                                   _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.moe_forward.restype = _I32
     lib.moe_forward.argtypes = [ctypes.POINTER(moe_route_cfg_t), _I32, _I64, _I32, _I32, _P, _P,
                                 _P, _P, _P, _P, _P, ctypes.POINTER(moe_latent_t),
@@ -210,6 +225,72 @@ def moe_experts(x: torch.Tensor, expert_offsets: torch.Tensor, row_to_pair: torc
     return y_rows
 
 
+class ExpertWeights:
+    """Routed expert weights for moe_experts_ex / moe_forward_ex.
+
+    ``ExpertWeights(w13, w2)``: weights in the layer dtype.
+    ``ExpertWeights.fp8(w13, w2, w13_scale, w2_scale)``: OCP e4m3 codes
+    (torch.uint8 or torch.float8_e4m3fn) [E, 2I, D] / [E, D, I] with one fp32
+    scale per weight row, [E, 2I] / [E, D]."""
+
+    def __init__(self, w13: torch.Tensor, w2: torch.Tensor, w13_scale=None, w2_scale=None,
+                 fmt: int = MOE_WEIGHT_DTYPE):
+        self.w13, self.w2 = w13, w2
+        self.w13_scale, self.w2_scale = w13_scale, w2_scale
+        self.format = fmt
+        E, twoI, D = w13.shape
+        self.E, self.I, self.D = E, twoI // 2, D
+        if tuple(w2.shape) != (E, D, self.I):
+            raise ValueError("w13 must be [E, 2I, D] and w2 [E, D, I]")
+        if fmt == MOE_WEIGHT_FP8_E4M3:
+            for name, t in (("w13", w13), ("w2", w2)):
+                if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or not t.is_contiguous():
+                    raise ValueError(f"{name} must be contiguous uint8 / float8_e4m3fn codes")
+            _need(w13_scale, torch.float32, "w13_scale")
+            _need(w2_scale, torch.float32, "w2_scale")
+            if w13_scale is None or w2_scale is None:
+                raise ValueError("FP8 weights need w13_scale and w2_scale")
+            if tuple(w13_scale.shape) != (E, 2 * self.I) or tuple(w2_scale.shape) != (E, D):
+                raise ValueError("w13_scale must be [E, 2I] and w2_scale [E, D]")
+
+    @classmethod
+    def fp8(cls, w13, w2, w13_scale, w2_scale) -> "ExpertWeights":
+        return cls(w13, w2, w13_scale, w2_scale, MOE_WEIGHT_FP8_E4M3)
+
+    def c(self) -> moe_expert_weights_t:
+        return moe_expert_weights_t(self.format, _ptr(self.w13), _ptr(self.w2),
+                                    _ptr(self.w13_scale), _ptr(self.w2_scale))
+
+    def check_dtype(self, dtype: torch.dtype):
+        if self.format == MOE_WEIGHT_DTYPE:
+            _need(self.w13, dtype, "w13")
+            _need(self.w2, dtype, "w2")
+
+
+def moe_experts_ex(x: torch.Tensor, expert_offsets: torch.Tensor, row_to_pair: torch.Tensor,
+                   weights: ExpertWeights, top_k: int, y_rows=None, workspace=None):
+    """moe_experts with the weights described by an ExpertWeights."""
+    lib = load()
+    T, D = x.shape
+    if weights.D != D:
+        raise ValueError("weights do not match x's width")
+    weights.check_dtype(x.dtype)
+    _need(expert_offsets, torch.int32, "expert_offsets")
+    _need(row_to_pair, torch.int32, "row_to_pair")
+    dt = _dtype_code(x.dtype)
+    E, I = weights.E, weights.I
+    if y_rows is None:
+        y_rows = torch.empty((T * top_k, D), dtype=torch.float32, device=x.device)
+    nbytes = lib.moe_experts_workspace(dt, T, top_k, E, D, I)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    wc = weights.c()
+    _check(lib.moe_experts_ex(dt, T, top_k, E, D, I, _ptr(x), _ptr(expert_offsets),
+                              _ptr(row_to_pair), ctypes.byref(wc), _ptr(y_rows),
+                              _ptr(workspace), workspace.numel(), _stream()))
+    return y_rows
+
+
 def moe_combine(y_rows: torch.Tensor, pair_to_row: torch.Tensor, topk_weights: torch.Tensor,
                 out_dtype: torch.dtype = torch.bfloat16, out=None):
     """out[t] = sum_j w[t,j] * y_rows[pair_to_row[t*k+j]] (fp32 sum, one rounding)."""
@@ -250,20 +331,13 @@ def moe_forward_workspace(cfg: RouteConfig, dtype: torch.dtype, max_T: int, H: i
                                      ctypes.byref(sh) if sh else None)
 
 
-def moe_forward(cfg: RouteConfig, x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *,
-                w_router=None, router_bias=None, router_logits=None, correction_bias=None,
-                latent: Optional[dict] = None, shared: Optional[dict] = None, out=None,
-                logits_out=None, topk_ids_out=None, topk_weights_out=None,
-                expert_counts_out=None, stage_events=None, workspace=None, stream=None):
-    """The whole layer on one stream.  ``latent`` = dict(w_down, gamma, w_up, eps);
-    ``shared`` = dict(w13, w2).  ``stage_events``: list of 2*MOE_NUM_STAGES
-    recorded torch.cuda.Event objects (start/end per stage) or None."""
+def _forward(cfg, x, I, experts, w_router, router_bias, router_logits, correction_bias,
+             latent, shared, out, logits_out, topk_ids_out, topk_weights_out,
+             expert_counts_out, stage_events, workspace, stream):
     lib = load()
     T, H = x.shape
-    I = w2.shape[2]
     dt = _dtype_code(x.dtype)
-    for name, t in (("w_router", w_router), ("w13", w13), ("w2", w2)):
-        _need(t, x.dtype, name)
+    _need(w_router, x.dtype, "w_router")
     for name, t in (("router_bias", router_bias), ("router_logits", router_logits),
                     ("correction_bias", correction_bias)):
         _need(t, torch.float32, name)
@@ -284,10 +358,42 @@ def moe_forward(cfg: RouteConfig, x: torch.Tensor, w13: torch.Tensor, w2: torch.
         if len(stage_events) != 2 * MOE_NUM_STAGES:
             raise ValueError("stage_events needs 2*MOE_NUM_STAGES events")
         ev = (ctypes.c_void_p * len(stage_events))(*[e.cuda_event for e in stage_events])
-    _check(lib.moe_forward(ctypes.byref(c), dt, T, H, I, _ptr(x), _ptr(w_router),
-                           _ptr(router_bias), _ptr(router_logits), _ptr(correction_bias),
-                           _ptr(w13), _ptr(w2), ctypes.byref(lat) if lat else None,
-                           ctypes.byref(sh) if sh else None, _ptr(out), _ptr(logits_out),
-                           _ptr(topk_ids_out), _ptr(topk_weights_out), _ptr(expert_counts_out),
-                           ev, _ptr(workspace), workspace.numel(), _stream(stream)))
+    common = (ctypes.byref(lat) if lat else None, ctypes.byref(sh) if sh else None, _ptr(out),
+              _ptr(logits_out), _ptr(topk_ids_out), _ptr(topk_weights_out),
+              _ptr(expert_counts_out), ev, _ptr(workspace), workspace.numel(), _stream(stream))
+    head = (ctypes.byref(c), dt, T, H, I, _ptr(x), _ptr(w_router), _ptr(router_bias),
+            _ptr(router_logits), _ptr(correction_bias))
+    if isinstance(experts, ExpertWeights):
+        wc = experts.c()
+        _check(lib.moe_forward_ex(*head, ctypes.byref(wc), *common))
+    else:
+        w13, w2 = experts
+        _check(lib.moe_forward(*head, _ptr(w13), _ptr(w2), *common))
     return out
+
+
+def moe_forward(cfg: RouteConfig, x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *,
+                w_router=None, router_bias=None, router_logits=None, correction_bias=None,
+                latent: Optional[dict] = None, shared: Optional[dict] = None, out=None,
+                logits_out=None, topk_ids_out=None, topk_weights_out=None,
+                expert_counts_out=None, stage_events=None, workspace=None, stream=None):
+    """The whole layer on one stream.  ``latent`` = dict(w_down, gamma, w_up, eps);
+    ``shared`` = dict(w13, w2).  ``stage_events``: list of 2*MOE_NUM_STAGES
+    recorded torch.cuda.Event objects (start/end per stage) or None."""
+    _need(w13, x.dtype, "w13")
+    _need(w2, x.dtype, "w2")
+    return _forward(cfg, x, w2.shape[2], (w13, w2), w_router, router_bias, router_logits,
+                    correction_bias, latent, shared, out, logits_out, topk_ids_out,
+                    topk_weights_out, expert_counts_out, stage_events, workspace, stream)
+
+
+def moe_forward_ex(cfg: RouteConfig, x: torch.Tensor, experts: ExpertWeights, *,
+                   w_router=None, router_bias=None, router_logits=None, correction_bias=None,
+                   latent: Optional[dict] = None, shared: Optional[dict] = None, out=None,
+                   logits_out=None, topk_ids_out=None, topk_weights_out=None,
+                   expert_counts_out=None, stage_events=None, workspace=None, stream=None):
+    """moe_forward with the routed experts given as an ExpertWeights."""
+    experts.check_dtype(x.dtype)
+    return _forward(cfg, x, experts.I, experts, w_router, router_bias, router_logits,
+                    correction_bias, latent, shared, out, logits_out, topk_ids_out,
+                    topk_weights_out, expert_counts_out, stage_events, workspace, stream)

@@ -80,6 +80,11 @@ struct GemmArgs {
     void* C;
     int64_t ldc;
     const float* bias;
+    // B as OCP e4m3 codes (one byte per element) with one fp32 scale per B
+    // row: row n of group g is scaled by b_scale[g * b_scale_gstride + n]
+    int32_t b_fp8;
+    const float* b_scale;
+    int64_t b_scale_gstride;
 };
 
 // ----- launchers (return hipSuccess or the launch error) -----

@@ -38,7 +38,11 @@ using namespace tiles;
 // ------------------------------------------------------------------------
 constexpr int TBM = 128, TBN = 128, TBK = 64, TLD = TBK + 8;  // LDS row stride (elements)
 
-template <int EPI>
+// With FP8 weights (OCP e4m3 codes, one fp32 scale per weight row; grouped
+// products only) each lane loads 8 codes per row segment and turns them into
+// bf16 (exactly) on the way to LDS; the row scale multiplies the fp32 sums in
+// the epilogue.
+template <int EPI, bool FP8>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
     constexpr bool SW = EPI == EPI_SWIGLU;
     const int ntn = SW ? (g.N + 63) / 64 : (g.N + TBN - 1) / TBN;
@@ -59,6 +63,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
 
     const bf16_t* ap[4];
     const bf16_t* bp[4];
+    const uint8_t* bp8[4];
     const bf16_t* ap2[4];
     const bf16_t* bp2[4];
 #pragma unroll
@@ -75,6 +80,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
             wrow = min(tc.nt * TBN + rho, g.N - 1);
         }
         bp[i] = Bg + (int64_t)wrow * g.K + lcol;
+        bp8[i] = (const uint8_t*)g.B + (int64_t)tc.group * g.b_gstride + (int64_t)wrow * g.K + lcol;
         bp2[i] = B2 ? B2 + (int64_t)wrow * g.K2 + lcol : nullptr;
     }
 
@@ -82,13 +88,20 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
     const int nk = nk1 + (A2 ? g.K2 / TBK : 0);
 
     u32x4_t ra[4], rb[4];
+    uint32_t rb8[4][2];  // FP8: raw codes, converted when stored to LDS
     auto gload = [&](int kt) {
         if (kt < nk1) {
             const int ko = kt * TBK;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 ra[i] = *(const u32x4_t*)(ap[i] + ko);
-                rb[i] = *(const u32x4_t*)(bp[i] + ko);
+                if (FP8) {
+                    const uint64_t q = *(const uint64_t*)(bp8[i] + ko);
+                    rb8[i][0] = (uint32_t)q;
+                    rb8[i][1] = (uint32_t)(q >> 32);
+                } else {
+                    rb[i] = *(const u32x4_t*)(bp[i] + ko);
+                }
             }
         } else {
             const int ko = (kt - nk1) * TBK;
@@ -102,6 +115,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
     auto sstore = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            if (FP8) rb[i] = fp8x8_to_bf16x8(rb8[i][0], rb8[i][1]);
             *(u32x4_t*)(&smem[buf][0][(lrow + 32 * i) * TLD + lcol]) = ra[i];
             *(u32x4_t*)(&smem[buf][1][(lrow + 32 * i) * TLD + lcol]) = rb[i];
         }
@@ -148,6 +162,20 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
         __syncthreads();
     }
 
+    // FP8 row scales of the two weight rows (output columns) of this lane
+    float cs[2] = {1.f, 1.f};
+    if (FP8) {
+        const float* sc = g.b_scale + (int64_t)tc.group * g.b_scale_gstride;
+        if (SW) {
+            const int hc = min(tc.nt * 64 + wn * 32 + fr, g.N - 1);
+            cs[0] = sc[hc];
+            cs[1] = sc[g.N + hc];
+        } else {
+#pragma unroll
+            for (int nj = 0; nj < 2; ++nj) cs[nj] = sc[min(tc.nt * TBN + wn * 64 + nj * 32 + fr, g.N - 1)];
+        }
+    }
+
     // epilogue: lane holds column fr of each 32x32 block, rows 8*(j/4)+4*(lane/32)+j%4
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
@@ -158,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
             if (SW) {
                 const int hc = tc.nt * 64 + wn * 32 + fr;
                 if (hc < g.N) {
-                    const float h = silu_f32(acc[mi][0][j]) * acc[mi][1][j];
+                    const float h = silu_f32(acc[mi][0][j] * cs[0]) * (acc[mi][1][j] * cs[1]);
                     ((bf16_t*)g.C)[(int64_t)r * g.ldc + hc] = f32_to_bf16(h);
                 }
             } else {
@@ -166,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
                 for (int nj = 0; nj < 2; ++nj) {
                     const int c = tc.nt * TBN + wn * 64 + nj * 32 + fr;
                     if (c >= g.N) continue;
-                    float v = acc[mi][nj][j];
+                    float v = acc[mi][nj][j] * cs[nj];
                     if (EPI == EPI_F32_BIAS && g.bias) v += g.bias[c];
                     if (EPI == EPI_OUT)
                         ((bf16_t*)g.C)[(int64_t)r * g.ldc + c] = f32_to_bf16(v);
@@ -583,6 +611,14 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
         case EPI_OUT: KERNEL<EPI_OUT><<<gd, bd, 0, s>>>(g); break;                \
         default: KERNEL<EPI_SWIGLU><<<gd, bd, 0, s>>>(g); break;                  \
     }
+#define MOE_TILED_SWITCH(FP8)                                                         \
+    switch (g.epi) {                                                                  \
+        case EPI_F32: gemm_bf16_tiled<EPI_F32, FP8><<<gd, bd, 0, s>>>(g); break;           \
+        case EPI_F32_BIAS: gemm_bf16_tiled<EPI_F32_BIAS, FP8><<<gd, bd, 0, s>>>(g); break; \
+        case EPI_OUT: gemm_bf16_tiled<EPI_OUT, FP8><<<gd, bd, 0, s>>>(g); break;           \
+        default: gemm_bf16_tiled<EPI_SWIGLU, FP8><<<gd, bd, 0, s>>>(g); break;             \
+    }
+    if (g.b_fp8 && (dtype == 0 || path == GEMM_BIG || g.A2)) return hipErrorInvalidValue;
     if (dtype == 0) {
         MOE_GEMM_SWITCH(gemm_f32_tiled)
     } else if (path == GEMM_STREAM) {
@@ -590,10 +626,13 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
     } else if (path == GEMM_BIG) {
         if (g.A2) launch_big<true>(g, gd, s);
         else launch_big<false>(g, gd, s);
+    } else if (g.b_fp8) {
+        MOE_TILED_SWITCH(true)
     } else {
-        MOE_GEMM_SWITCH(gemm_bf16_tiled)
+        MOE_TILED_SWITCH(false)
     }
 #undef MOE_GEMM_SWITCH
+#undef MOE_TILED_SWITCH
     return hipGetLastError();
 }
 

@@ -213,22 +213,32 @@ constexpr int SX_BYTES = 64 * 1024;  // token-chunk double buffer
 constexpr int SRW = 8;               // waves per workgroup
 constexpr int SRN = 16 * SRW;        // weight rows per workgroup (SwiGLU: SRN / 2 columns)
 
-template <int EPI, int NB, bool KCAT>
+// With FP8 weights (OCP e4m3 codes, one fp32 scale per weight row) each
+// 16-byte weight load holds 16 codes, i.e. two 32-deep k-steps: lane g4 of a
+// 64-deep block takes k 16*g4 .. +15, its first 8 for the even step and the
+// rest for the odd one.  The token operand is staged with the same k order,
+// the codes become bf16 exactly in registers, and the row scale multiplies
+// the fp32 sums in the epilogue.
+template <int EPI, int NB, bool KCAT, bool FP8>
 __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCoord& tc,
                                                  char* xs) {
     constexpr bool SW = EPI == EPI_SWIGLU;
     constexpr int CS = NB == 4 ? 8 : 16;   // k-steps (of 32) per token chunk
-    constexpr int PD = 8;                  // weight prefetch distance in k-steps
+    constexpr int UNIT = FP8 ? 2 : 1;      // k-steps per weight load
+    constexpr int PD = FP8 && NB == 4 ? 4 : 8;  // weight loads in flight
     constexpr int XI = CS * NB / SRW;      // 1 KB token blocks per wave per chunk
     constexpr int CHUNK = CS * NB * 1024;  // bytes of one token chunk
-    static_assert(2 * CHUNK <= SX_BYTES && CS % PD == 0 && XI % NB == 0, "stream tiling");
+    constexpr int WB = FP8 ? 1 : 2;        // bytes per weight element
+    static_assert(!(FP8 && KCAT), "FP8 weights are grouped products only");
+    static_assert(2 * CHUNK <= SX_BYTES && CS % (PD * UNIT) == 0 && XI % NB == 0,
+                  "stream tiling");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
 
     // 32-bit byte offsets from wave-uniform bases; every operand of one group
     // fits in 4 GiB (checked on the host)
-    const char* Bb = (const char*)((const bf16_t*)g.B + (int64_t)tc.group * g.b_gstride);
+    const char* Bb = (const char*)g.B + (int64_t)tc.group * g.b_gstride * WB;
     const char* B2b = (const char*)g.B2;
     const char* Ab = (const char*)g.A;
     const char* A2b = (const char*)g.A2;
@@ -239,14 +249,14 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     } else {
         wrow = min(tc.nt * SRN + wave * 16 + l16, g.N - 1);
     }
-    const uint32_t wo = (uint32_t)((int64_t)wrow * g.K * 2) + g4 * 16;
+    const uint32_t wo = (uint32_t)((int64_t)wrow * g.K * WB) + g4 * 16;
     const uint32_t wo2 = KCAT ? (uint32_t)((int64_t)wrow * g.K2 * 2) + g4 * 16 : 0u;
     // token rows past the tile's end load its last row (never stored)
     uint32_t xo[NB], xo2[NB];
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
         const int r = min(tc.row0 + tb * 16 + l16, tc.row1 - 1);
-        xo[tb] = (uint32_t)(a_row_of(g, r) * g.lda * 2) + g4 * 16;
+        xo[tb] = (uint32_t)(a_row_of(g, r) * g.lda * 2) + g4 * (FP8 ? 32 : 16);
         xo2[tb] = KCAT ? (uint32_t)((int64_t)r * g.lda2 * 2) + g4 * 16 : 0u;
     }
 
@@ -266,7 +276,11 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
             const int tb = i % NB;
             const int st = min(c * CS + b / NB, ns - 1);
             const bool seg1 = !KCAT || st < ns1;
-            const char* src = seg1 ? Ab + (xo[tb] + (uint32_t)st * 64)
+            // byte offset of step st's 8 elements for this lane (FP8: the
+            // k order of the weight loads)
+            const uint32_t ko = FP8 ? (uint32_t)(st >> 1) * 128 + (uint32_t)(st & 1) * 16
+                                    : (uint32_t)st * 64;
+            const char* src = seg1 ? Ab + (xo[tb] + ko)
                                    : A2b + (xo2[tb] + (uint32_t)(st - ns1) * 64);
             xr[i] = *(const u32x4_t*)src;
         }
@@ -276,10 +290,12 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
 #pragma unroll
         for (int i = 0; i < XI; ++i) *(u32x4_t*)(dst + (wave * XI + i) * 1024) = xr[i];
     };
-    auto load_w = [&](int st) __attribute__((always_inline)) {
-        st = min(st, ns - 1);
-        const bool seg1 = !KCAT || st < ns1;
-        const char* src = seg1 ? Bb + (wo + (uint32_t)st * 64) : B2b + (wo2 + (uint32_t)(st - ns1) * 64);
+    // weight load unit u covers k-steps UNIT*u .. +UNIT-1, 64 bytes of the row
+    const int nu = ns / UNIT;
+    auto load_w = [&](int u) __attribute__((always_inline)) {
+        u = min(u, nu - 1);
+        const bool seg1 = !KCAT || u < ns1;
+        const char* src = seg1 ? Bb + (wo + (uint32_t)u * 64) : B2b + (wo2 + (uint32_t)(u - ns1) * 64);
         return *(const u32x4_t*)src;
     };
 
@@ -313,20 +329,30 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
         asm volatile("" ::: "memory");
         const char* xc = xs + (c & 1) * CHUNK + lane * 16;
 #pragma unroll
-        for (int u = 0; u < CS; u += PD) {
+        for (int u = 0; u < CS; u += PD * UNIT) {
 #pragma unroll
             for (int v = 0; v < PD; ++v) {
-                // steps past K (the ragged last chunk) multiply zero weights
-                const int st = c * CS + u + v;
-                const u32x4_t wz = st < ns ? w[v] : u32x4_t{0u, 0u, 0u, 0u};
-                const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, wz);
+                const int ul = (c * CS + u) / UNIT + v;  // weight load unit
 #pragma unroll
-                for (int tb = 0; tb < NB; ++tb) {
-                    const u32x4_t xv = *(const u32x4_t*)(xc + ((u + v) * NB + tb) * 1024);
-                    acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        wf, __builtin_bit_cast(bf16x8_t, xv), acc[tb], 0, 0, 0);
+                for (int hh = 0; hh < UNIT; ++hh) {
+                    const int sl = u + v * UNIT + hh;  // step within the chunk
+                    const int st = c * CS + sl;
+                    u32x4_t wv = w[v];
+                    if (FP8) wv = fp8x8_to_bf16x8(w[v][2 * hh], w[v][2 * hh + 1]);
+                    // steps past K (the ragged last chunk) multiply zero weights
+                    const u32x4_t wz = st < ns ? wv : u32x4_t{0u, 0u, 0u, 0u};
+                    const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, wz);
+#pragma unroll
+                    for (int tb = 0; tb < NB; ++tb) {
+                        const u32x4_t xv = *(const u32x4_t*)(xc + (sl * NB + tb) * 1024);
+                        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            wf, __builtin_bit_cast(bf16x8_t, xv), acc[tb], 0, 0, 0);
+                    }
                 }
-                w[v] = load_w(st + PD);
+                w[v] = load_w(ul + PD);
+                // keep each refill where its slot frees up (the scheduler
+                // otherwise sinks them all to the end of the chunk)
+                if (FP8) asm volatile("" ::: "memory");
             }
         }
         asm volatile("" ::: "memory");
@@ -338,6 +364,23 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
         asm volatile("" ::: "memory");
     }
 
+    // row scales of FP8 weights, for the 4 weight rows this lane's sums belong to
+    float rs[4] = {1.f, 1.f, 1.f, 1.f};
+    if (FP8) {
+        const float* sc = g.b_scale + (int64_t)tc.group * g.b_scale_gstride;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int n;
+            if (SW) {
+                const int hc = min(tc.nt * (SRN / 2) + wave * 8 + (g4 & 1) * 4 + j, g.N - 1);
+                n = g4 < 2 ? hc : g.N + hc;
+            } else {
+                n = min(tc.nt * SRN + wave * 16 + g4 * 4 + j, g.N - 1);
+            }
+            rs[j] = sc[n];
+        }
+    }
+
     // acc[tb][j] = C[weight row 4*g4 + j of this wave][token 16*tb + l16]
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
@@ -346,13 +389,14 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
             // lanes 32..63 hold the up rows of lane - 32's gate rows
             float up[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) up[j] = __shfl_xor(acc[tb][j], 32);
+            for (int j = 0; j < 4; ++j) up[j] = __shfl_xor(acc[tb][j] * rs[j], 32);
             if (g4 < 2 && r < tc.row1) {
                 bf16_t* crow = (bf16_t*)g.C + (int64_t)r * g.ldc;
                 const int hc0 = tc.nt * (SRN / 2) + wave * 8 + g4 * 4;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (hc0 + j < g.N) crow[hc0 + j] = f32_to_bf16(silu_f32(acc[tb][j]) * up[j]);
+                    if (hc0 + j < g.N)
+                        crow[hc0 + j] = f32_to_bf16(silu_f32(acc[tb][j] * rs[j]) * up[j]);
             }
         } else if (r < tc.row1) {
             const int c0 = tc.nt * SRN + wave * 16 + g4 * 4;
@@ -360,7 +404,7 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
             for (int j = 0; j < 4; ++j) {
                 const int c = c0 + j;
                 if (c >= g.N) continue;
-                float o = acc[tb][j];
+                float o = acc[tb][j] * rs[j];
                 if (EPI == EPI_F32_BIAS && g.bias) o += g.bias[c];
                 if (EPI == EPI_OUT)
                     ((bf16_t*)g.C)[(int64_t)r * g.ldc + c] = f32_to_bf16(o);
@@ -373,7 +417,7 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
 
 // Grouped tiles here hold one whole group of at most 64 rows; dense products
 // are cut into 16-row tiles.
-template <int EPI, bool KCAT>
+template <int EPI, bool KCAT, bool FP8>
 __global__ __launch_bounds__(64 * SRW, 4) void gemm_bf16_stream(GemmArgs g) {
     constexpr bool SW = EPI == EPI_SWIGLU;
     const int ntn = SW ? (g.N + SRN / 2 - 1) / (SRN / 2) : (g.N + SRN - 1) / SRN;
@@ -381,22 +425,22 @@ __global__ __launch_bounds__(64 * SRW, 4) void gemm_bf16_stream(GemmArgs g) {
     if (!fetch_tile(g, SROWS, ntn, tc)) return;
     __shared__ __attribute__((aligned(1024))) char xs[SX_BYTES];
     const int rows = tc.row1 - tc.row0;
-    if (rows <= 16) stream_rows_tile<EPI, 1, KCAT>(g, tc, xs);
-    else if (rows <= 32) stream_rows_tile<EPI, 2, KCAT>(g, tc, xs);
-    else stream_rows_tile<EPI, 4, KCAT>(g, tc, xs);
+    if (rows <= 16) stream_rows_tile<EPI, 1, KCAT, FP8>(g, tc, xs);
+    else if (rows <= 32) stream_rows_tile<EPI, 2, KCAT, FP8>(g, tc, xs);
+    else stream_rows_tile<EPI, 4, KCAT, FP8>(g, tc, xs);
 }
 
 // Dense products with fewer workgroups than this split K over the waves.
 constexpr int64_t kStreamRowsMinGrid = 1024;
 
-template <bool KC>
+template <bool KC, bool FP8>
 void launch_stream_rows(const GemmArgs& g, dim3 gd, hipStream_t s) {
     const dim3 bd(64 * SRW);
     switch (g.epi) {
-        case EPI_F32: gemm_bf16_stream<EPI_F32, KC><<<gd, bd, 0, s>>>(g); break;
-        case EPI_F32_BIAS: gemm_bf16_stream<EPI_F32_BIAS, KC><<<gd, bd, 0, s>>>(g); break;
-        case EPI_OUT: gemm_bf16_stream<EPI_OUT, KC><<<gd, bd, 0, s>>>(g); break;
-        default: gemm_bf16_stream<EPI_SWIGLU, KC><<<gd, bd, 0, s>>>(g); break;
+        case EPI_F32: gemm_bf16_stream<EPI_F32, KC, FP8><<<gd, bd, 0, s>>>(g); break;
+        case EPI_F32_BIAS: gemm_bf16_stream<EPI_F32_BIAS, KC, FP8><<<gd, bd, 0, s>>>(g); break;
+        case EPI_OUT: gemm_bf16_stream<EPI_OUT, KC, FP8><<<gd, bd, 0, s>>>(g); break;
+        default: gemm_bf16_stream<EPI_SWIGLU, KC, FP8><<<gd, bd, 0, s>>>(g); break;
     }
 }
 
@@ -412,7 +456,7 @@ hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
     const bool sw = g.epi == EPI_SWIGLU;
     const int64_t grid_ks = (int64_t)nm * (sw ? (g.N + 31) / 32 : (g.N + SNW - 1) / SNW);
     if (grid_ks <= 0) return hipSuccess;
-    if (!g.tiles && grid_ks < kStreamRowsMinGrid) {
+    if (!g.tiles && grid_ks < kStreamRowsMinGrid && !g.b_fp8) {
         const dim3 gd((unsigned)grid_ks), bd(256);
         switch (g.epi) {
             case EPI_F32: gemm_bf16_stream_ksplit<EPI_F32><<<gd, bd, 0, s>>>(g); break;
@@ -422,8 +466,14 @@ hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
         }
     } else {
         const dim3 gd((unsigned)((int64_t)nm * stream_col_tiles(g.epi, g.N)));
-        if (g.A2) launch_stream_rows<true>(g, gd, s);
-        else launch_stream_rows<false>(g, gd, s);
+        if (g.b_fp8) {
+            if (g.A2) return hipErrorInvalidValue;
+            launch_stream_rows<false, true>(g, gd, s);
+        } else if (g.A2) {
+            launch_stream_rows<true, false>(g, gd, s);
+        } else {
+            launch_stream_rows<false, false>(g, gd, s);
+        }
     }
     return hipGetLastError();
 }

@@ -76,6 +76,9 @@ bool fits_u32(int64_t rows, int64_t cols, moe_dtype_t dt) {
 // 256-row LDS tiles (gemm_bf16_big).  fp32 layers use 64-row VALU tiles.
 constexpr int kBigRows = 256;
 constexpr int kF32Rows = 64;
+// Experts with FP8 weights and more than kStreamMaxRows rows use the 128-row
+// register-staged tiles (the codes become bf16 on their way to LDS).
+constexpr int kTiledRows = 128;
 
 // Dense products: stream the weights for small batches; otherwise the larger
 // tile when it still gives every CU a couple of workgroups, else 128x128.
@@ -87,12 +90,25 @@ int dense_path(moe_dtype_t dt, int64_t T, int N, int epi) {
     return (N % 64 == 0 && ((T + 255) / 256) * cols >= 512) ? GEMM_BIG : GEMM_TILED;
 }
 
-// Upper bounds of the two tile lists.
+// Upper bounds of the two tile lists: the large-group list holds tiles of
+// `rows` rows; the workspace is sized for the smallest tile of the dtype.
 int64_t small_capacity(moe_dtype_t dt, int E) { return dt == MOE_DTYPE_F32 ? 1 : E; }
-int64_t big_capacity(moe_dtype_t dt, int64_t P, int E) {
+int64_t big_capacity(moe_dtype_t dt, int64_t P, int E, int rows) {
     if (dt == MOE_DTYPE_F32) return (P + kF32Rows - 1) / kF32Rows + E;
-    return (P + kBigRows - 1) / kBigRows + std::min<int64_t>(E, P / (kStreamMaxRows + 1)) + 1;
+    return (P + rows - 1) / rows + std::min<int64_t>(E, P / (kStreamMaxRows + 1)) + 1;
 }
+int64_t big_capacity_ws(moe_dtype_t dt, int64_t P, int E) {
+    return big_capacity(dt, P, E, dt == MOE_DTYPE_F32 ? kF32Rows : kTiledRows);
+}
+
+// Routed expert weights as the kernels take them.
+struct ExpertWeights {
+    bool fp8;
+    const void* w13;
+    const void* w2;
+    const float* s13;  // [E, 2I] row scales (fp8)
+    const float* s2;   // [E, D]
+};
 
 struct ExpertsWs {
     Tile* small_tiles;
@@ -105,7 +121,7 @@ ExpertsWs carve_experts(Carve& c, moe_dtype_t dt, int64_t max_T, int k, int E, i
     ExpertsWs w;
     const int64_t P = max_T * k;
     w.small_tiles = c.take<Tile>((size_t)small_capacity(dt, E));
-    w.big_tiles = c.take<Tile>((size_t)big_capacity(dt, P, E));
+    w.big_tiles = c.take<Tile>((size_t)big_capacity_ws(dt, P, E));
     w.counts = c.take<int32_t>(2);
     w.h = c.take<char>((size_t)P * I * elem_size(dt));
     return w;
@@ -128,14 +144,21 @@ moe_status_t small_groups_gemm(GemmArgs g, const ExpertsWs& w, int E, hipStream_
     return hip_status(launch_gemm(1, GEMM_STREAM, g, s));
 }
 
+// Rows per tile of the large-group list.
+int large_rows(moe_dtype_t dt, bool fp8) {
+    return dt == MOE_DTYPE_F32 ? kF32Rows : fp8 ? kTiledRows : kBigRows;
+}
+
 moe_status_t large_groups_gemm(moe_dtype_t dt, GemmArgs g, const ExpertsWs& w, int64_t P, int E,
                                hipStream_t s) {
     const bool f32 = dt == MOE_DTYPE_F32;
+    const int rows = large_rows(dt, g.b_fp8 != 0);
     g.tiles = w.big_tiles;
     g.num_tiles = w.counts + 1;
-    g.max_tiles = (int32_t)big_capacity(dt, P, E);
-    g.tile_m = f32 ? kF32Rows : kBigRows;
-    return hip_status(launch_gemm(f32 ? 0 : 1, f32 ? GEMM_TILED : GEMM_BIG, g, s));
+    g.max_tiles = (int32_t)big_capacity(dt, P, E, rows);
+    g.tile_m = rows;
+    const int path = f32 || g.b_fp8 ? GEMM_TILED : GEMM_BIG;
+    return hip_status(launch_gemm(f32 ? 0 : 1, path, g, s));
 }
 
 // A second stream per device, owned by the library (default priority), on
@@ -175,12 +198,12 @@ moe_status_t side_stream(SideStream** out) {
 constexpr int64_t kOverlapMinRows = 16;
 
 moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, const void* x,
-                         const int32_t* offsets, const int32_t* row_to_pair, const void* w13,
-                         const void* w2, float* y_rows, const ExpertsWs& w, hipStream_t s,
-                         hipEvent_t* ev) {
+                         const int32_t* offsets, const int32_t* row_to_pair,
+                         const ExpertWeights& ew, float* y_rows, const ExpertsWs& w,
+                         hipStream_t s, hipEvent_t* ev) {
     const int64_t P = T * k;
     const bool f32 = dt == MOE_DTYPE_F32;
-    MOE_HIP(launch_build_tiles(offsets, E, f32 ? 0 : kStreamMaxRows, f32 ? kF32Rows : kBigRows,
+    MOE_HIP(launch_build_tiles(offsets, E, f32 ? 0 : kStreamMaxRows, large_rows(dt, ew.fp8),
                                w.small_tiles, w.counts, w.big_tiles, w.counts + 1, s));
     if (ev) MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM1], s));
 
@@ -189,8 +212,11 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
     g1.lda = D;
     g1.a_map = row_to_pair;
     g1.a_div = k;
-    g1.B = w13;
+    g1.B = ew.w13;
     g1.b_gstride = (int64_t)2 * I * D;
+    g1.b_fp8 = ew.fp8;
+    g1.b_scale = ew.s13;
+    g1.b_scale_gstride = (int64_t)2 * I;
     g1.K = D;
     g1.N = I;
     g1.epi = EPI_SWIGLU;
@@ -200,8 +226,11 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
     GemmArgs g2 = gemm_defaults();
     g2.A = w.h;
     g2.lda = I;
-    g2.B = w2;
+    g2.B = ew.w2;
     g2.b_gstride = (int64_t)D * I;
+    g2.b_fp8 = ew.fp8;
+    g2.b_scale = ew.s2;
+    g2.b_scale_gstride = D;
     g2.K = I;
     g2.N = D;
     g2.epi = EPI_F32;
@@ -401,10 +430,32 @@ size_t moe_experts_workspace(moe_dtype_t dtype, int64_t max_T, int32_t k, int32_
     return c.off;
 }
 
-moe_status_t moe_experts(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, int32_t D,
-                         int32_t I, const void* x, const int32_t* expert_offsets,
-                         const int32_t* row_to_pair, const void* w13, const void* w2,
-                         float* y_rows, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Expert weights from the C description; MOE_OK or the error of the entry
+// point.
+moe_status_t expert_weights(moe_dtype_t dtype, const moe_expert_weights_t* d, ExpertWeights* ew) {
+    if (!d) return MOE_EINVAL;
+    if (d->format != MOE_WEIGHT_DTYPE && d->format != MOE_WEIGHT_FP8_E4M3) return MOE_EINVAL;
+    ew->fp8 = d->format == MOE_WEIGHT_FP8_E4M3;
+    ew->w13 = d->w13;
+    ew->w2 = d->w2;
+    ew->s13 = ew->fp8 ? d->w13_scale : nullptr;
+    ew->s2 = ew->fp8 ? d->w2_scale : nullptr;
+    if (ew->fp8 && dtype != MOE_DTYPE_BF16) return MOE_ENOTSUP;
+    return MOE_OK;
+}
+
+bool weights_present(const ExpertWeights& ew) {
+    return ew.w13 && ew.w2 && (!ew.fp8 || (ew.s13 && ew.s2));
+}
+
+moe_status_t experts_impl(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, int32_t D,
+                          int32_t I, const void* x, const int32_t* expert_offsets,
+                          const int32_t* row_to_pair, const ExpertWeights& ew, float* y_rows,
+                          void* ws, size_t ws_bytes, void* stream) {
     if (bad_dtype(dtype) || T < 0 || k < 1 || E < 1 || k > E) return MOE_EINVAL;
     if (E > kMaxExperts || k > kMaxTopK) return MOE_ENOTSUP;
     if (!width_ok(D) || !width_ok(I)) return MOE_ENOTSUP;
@@ -412,12 +463,36 @@ moe_status_t moe_experts(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, int
     if (!fits_u32(T, D, dtype) || !fits_u32(T * k, I, dtype) || !fits_u32(2 * (int64_t)I, D, dtype))
         return MOE_ENOTSUP;
     if (T == 0) return MOE_OK;
-    if (!x || !expert_offsets || !row_to_pair || !w13 || !w2 || !y_rows) return MOE_EINVAL;
+    if (!x || !expert_offsets || !row_to_pair || !weights_present(ew) || !y_rows)
+        return MOE_EINVAL;
     if (!ws || ws_bytes < moe_experts_workspace(dtype, T, k, E, D, I)) return MOE_ENOSPACE;
     Carve c(ws);
     ExpertsWs w = carve_experts(c, dtype, T, k, E, I);
-    return run_experts(dtype, T, k, E, D, I, x, expert_offsets, row_to_pair, w13, w2, y_rows, w,
+    return run_experts(dtype, T, k, E, D, I, x, expert_offsets, row_to_pair, ew, y_rows, w,
                        (hipStream_t)stream, nullptr);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_experts(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, int32_t D,
+                         int32_t I, const void* x, const int32_t* expert_offsets,
+                         const int32_t* row_to_pair, const void* w13, const void* w2,
+                         float* y_rows, void* ws, size_t ws_bytes, void* stream) {
+    const ExpertWeights ew = {false, w13, w2, nullptr, nullptr};
+    return experts_impl(dtype, T, k, E, D, I, x, expert_offsets, row_to_pair, ew, y_rows, ws,
+                        ws_bytes, stream);
+}
+
+moe_status_t moe_experts_ex(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, int32_t D,
+                            int32_t I, const void* x, const int32_t* expert_offsets,
+                            const int32_t* row_to_pair, const moe_expert_weights_t* wd,
+                            float* y_rows, void* ws, size_t ws_bytes, void* stream) {
+    ExpertWeights ew;
+    MOE_TRY(expert_weights(dtype, wd, &ew));
+    return experts_impl(dtype, T, k, E, D, I, x, expert_offsets, row_to_pair, ew, y_rows, ws,
+                        ws_bytes, stream);
 }
 
 moe_status_t moe_combine(moe_dtype_t out_dtype, int64_t T, int32_t k, int32_t D,
@@ -450,17 +525,21 @@ size_t moe_forward_workspace(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int6
     return c.off;
 }
 
-moe_status_t moe_forward(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t T, int32_t H,
-                         int32_t I, const void* x, const void* w_router, const float* router_bias,
-                         const float* router_logits, const float* correction_bias,
-                         const void* w13, const void* w2, const moe_latent_t* latent,
-                         const moe_shared_t* shared, void* out, float* logits_out,
-                         int32_t* topk_ids_out, float* topk_weights_out,
-                         int32_t* expert_counts_out, void* const* stage_events, void* ws,
-                         size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t T, int32_t H,
+                          int32_t I, const void* x, const void* w_router, const float* router_bias,
+                          const float* router_logits, const float* correction_bias,
+                          const ExpertWeights& ew, const moe_latent_t* latent,
+                          const moe_shared_t* shared, void* out, float* logits_out,
+                          int32_t* topk_ids_out, float* topk_weights_out,
+                          int32_t* expert_counts_out, void* const* stage_events, void* ws,
+                          size_t ws_bytes, void* stream) {
     MOE_TRY(check_forward_shapes(cfg, dtype, T, H, I, latent, shared));
     if (T == 0) return MOE_OK;
-    if (!x || !w13 || !w2 || !out) return MOE_EINVAL;
+    if (!x || !weights_present(ew) || !out) return MOE_EINVAL;
     if (!router_logits && !w_router) return MOE_EINVAL;
     if (!ws || ws_bytes < moe_forward_workspace(cfg, dtype, T, H, I, latent, shared))
         return MOE_ENOSPACE;
@@ -522,8 +601,7 @@ moe_status_t moe_forward(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t 
     MOE_TRY(mark(MOE_STAGE_PERMUTE, 1));
 
     // routed experts
-    MOE_TRY(run_experts(dtype, T, k, E, D, I, xin, w.offsets, w.r2p, w13, w2, w.y_rows, w.ex, s,
-                        ev));
+    MOE_TRY(run_experts(dtype, T, k, E, D, I, xin, w.offsets, w.r2p, ew, w.y_rows, w.ex, s, ev));
 
     // shared expert without a latent tail: its output is the combine addend
     if (shared && !latent) {
@@ -578,6 +656,40 @@ moe_status_t moe_forward(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t 
         MOE_TRY(skip(MOE_STAGE_TAIL));
     }
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_forward(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t T, int32_t H,
+                         int32_t I, const void* x, const void* w_router, const float* router_bias,
+                         const float* router_logits, const float* correction_bias,
+                         const void* w13, const void* w2, const moe_latent_t* latent,
+                         const moe_shared_t* shared, void* out, float* logits_out,
+                         int32_t* topk_ids_out, float* topk_weights_out,
+                         int32_t* expert_counts_out, void* const* stage_events, void* ws,
+                         size_t ws_bytes, void* stream) {
+    const ExpertWeights ew = {false, w13, w2, nullptr, nullptr};
+    return forward_impl(cfg, dtype, T, H, I, x, w_router, router_bias, router_logits,
+                        correction_bias, ew, latent, shared, out, logits_out, topk_ids_out,
+                        topk_weights_out, expert_counts_out, stage_events, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_forward_ex(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t T, int32_t H,
+                            int32_t I, const void* x, const void* w_router,
+                            const float* router_bias, const float* router_logits,
+                            const float* correction_bias, const moe_expert_weights_t* experts,
+                            const moe_latent_t* latent, const moe_shared_t* shared, void* out,
+                            float* logits_out, int32_t* topk_ids_out, float* topk_weights_out,
+                            int32_t* expert_counts_out, void* const* stage_events, void* ws,
+                            size_t ws_bytes, void* stream) {
+    MOE_TRY(check_forward_shapes(cfg, dtype, T, H, I, latent, shared));
+    ExpertWeights ew;
+    MOE_TRY(expert_weights(dtype, experts, &ew));
+    return forward_impl(cfg, dtype, T, H, I, x, w_router, router_bias, router_logits,
+                        correction_bias, ew, latent, shared, out, logits_out, topk_ids_out,
+                        topk_weights_out, expert_counts_out, stage_events, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -63,6 +63,7 @@ class Workload:
     shared_inter: Optional[int] = None   # shared expert intermediate width
     rms_eps: float = 1e-6
     gamma_std: float = 0.0               # RMSNorm gamma = 1 + N(0, gamma_std^2)
+    weights: str = "dtype"               # routed expert weights: "dtype" | "fp8_e4m3"
 
     @property
     def D(self) -> int:
@@ -90,7 +91,33 @@ WORKLOADS = {
                                      group_score="top2sum", corr_bias=0.1),
     "latent_shared": Workload("latent_shared", T=2048, H=7168, E=256, k=8, I=1024,
                               latent=2048, shared_inter=2048),
+    # the decode layer with FP8 E4M3 expert weights (one fp32 scale per row)
+    "decode_fp8": Workload("decode_fp8", T=128, H=7168, E=384, k=8, I=2048,
+                           routed_scaling=2.5, weights="fp8_e4m3"),
 }
+
+FP8_E4M3_MAX = 448.0  # largest finite E4M3 value
+
+
+def fp8_rows(w: torch.Tensor, chunk: int = 16):
+    """FP8 E4M3 codes and per-row scales of a weight tensor [E, n, in].
+
+    scale[e, n] = max|w[e, n, :]| / 448 (1 where the row is all zero) and
+    codes = round-to-nearest-even E4M3 encoding of w / scale (torch's
+    float8_e4m3fn cast), returned as uint8.  Input construction only: the
+    layer and the oracle decode the codes themselves.  Works through ``chunk``
+    experts at a time to bound temporary memory."""
+    E = w.shape[0]
+    codes = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    for e0 in range(0, E, chunk):
+        blk = w[e0:e0 + chunk].float()
+        amax = blk.abs().amax(dim=-1)
+        sc = torch.where(amax > 0, amax / FP8_E4M3_MAX, torch.ones_like(amax))
+        codes[e0:e0 + chunk] = (blk / sc[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        scales[e0:e0 + chunk] = sc
+        del blk
+    return codes, scales
 
 
 def _gen(seed: int, device) -> torch.Generator:
@@ -152,7 +179,8 @@ def make_inputs(w: Workload, device="cpu", chunk_rows: int = 8) -> dict:
     """All tensors of workload ``w`` on ``device``.
 
     Keys: x[T,H], w_router[E,H], router_bias[E] (fp32) or None,
-    corr_bias[E] (fp32) or None, w13[E,2I,D], w2[E,D,I], and for the latent
+    corr_bias[E] (fp32) or None, w13[E,2I,D], w2[E,D,I] (for FP8 weights:
+    uint8 E4M3 codes plus w13_scale[E,2I], w2_scale[E,D] fp32), and for the latent
     layer w_down[L,H], gamma[L], w_up[H,L]; for a shared expert
     w13_sh[2Is,H], w2_sh[H,Is].  Weights are row-major [out, in].
     """
@@ -170,6 +198,12 @@ def make_inputs(w: Workload, device="cpu", chunk_rows: int = 8) -> dict:
                         chunk_rows=chunk_rows)
     inp["w2"] = normal((w.E, D, w.I), 1.0 / math.sqrt(w.I), SEED_W2, dt, device,
                        chunk_rows=chunk_rows)
+    if w.weights == "fp8_e4m3":
+        # the same draws, quantised per row (the bf16 tensors are dropped)
+        for name in ("w13", "w2"):
+            codes, scales = fp8_rows(inp[name])
+            inp[name] = codes
+            inp[name + "_scale"] = scales
     if w.latent:
         L = w.latent
         inp["w_down"] = normal((L, w.H), 1.0 / math.sqrt(w.H), SEED_WDN, dt, device)

@@ -52,6 +52,18 @@ class ExpertFetch:
         return self.t[int(e)].to(torch.float64).cpu().numpy()
 
 
+class ExpertFetchFP8:
+    """w[e] -> expert e's weights decoded by the oracle from its FP8 E4M3
+    codes and row scales (copied from the device one expert at a time)."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor):
+        self.codes, self.scales = codes, scales
+
+    def __getitem__(self, e):
+        e = int(e)
+        return O.dequantize_rows(self.codes[e].cpu().numpy(), self.scales[e].cpu().numpy())
+
+
 def latent_np(inp: dict, w: Workload):
     if not w.latent:
         return None

@@ -350,3 +350,60 @@ def test_rmsnorm_constant_row_and_scale_invariance():
     v = rng.normal(size=(3, 64))
     np.testing.assert_allclose(O.rmsnorm(7.0 * v, np.ones(64), 0.0),
                                O.rmsnorm(v, np.ones(64), 0.0), rtol=1e-13)
+
+
+# ------------------------------------------------------- FP8 E4M3 weights ---
+# The decode is pinned by values fixed by the format's definition, by its
+# symmetry and order, and by torch's float8_e4m3fn (a library decoding of the
+# same format).
+
+@pytest.mark.parametrize("code,value", [
+    (0x00, 0.0), (0x38, 1.0), (0x3C, 1.5), (0x40, 2.0), (0x77, 240.0), (0x7E, 448.0),
+    (0x08, 2.0 ** -6), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0xB8, -1.0), (0xFE, -448.0),
+])
+def test_fp8_decode_closed_forms(code, value):
+    assert O.fp8_e4m3_decode(np.array([code]))[0] == value
+
+
+def test_fp8_decode_nan_and_signed_zero():
+    v = O.fp8_e4m3_decode(np.array([0x7F, 0xFF, 0x80]))
+    assert np.isnan(v[0]) and np.isnan(v[1])
+    assert v[2] == 0.0 and np.signbit(v[2])
+
+
+def test_fp8_decode_order_and_symmetry():
+    pos = O.fp8_e4m3_decode(np.arange(0, 127))
+    assert np.all(np.diff(pos) > 0)
+    neg = O.fp8_e4m3_decode(np.arange(128, 255))
+    assert np.array_equal(neg, -pos)
+
+
+def test_fp8_decode_matches_torch_float8_e4m3fn():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(O.fp8_e4m3_decode(codes), ref, equal_nan=True)
+
+
+def test_dequantize_rows_scales_each_row():
+    codes = np.array([[[0x38, 0x40], [0x3C, 0xB8]]], dtype=np.uint8)   # [1, 2, 2]
+    scale = np.array([[0.5, 3.0]])
+    got = O.dequantize_rows(codes, scale)
+    assert np.array_equal(got, np.array([[[0.5, 1.0], [4.5, -3.0]]]))
+
+
+def test_fp8_expert_mlp_is_the_mlp_of_the_decoded_weights():
+    # an expert with FP8 weights is the textbook SwiGLU MLP of decode * scale
+    rng = np.random.default_rng(3)
+    D, I, n = 16, 8, 5
+    c13 = rng.integers(0, 0x7E, size=(2 * I, D)).astype(np.uint8)
+    c2 = rng.integers(0x80, 0xFE, size=(D, I)).astype(np.uint8)
+    s13, s2 = rng.uniform(0.01, 0.1, size=2 * I), rng.uniform(0.01, 0.1, size=D)
+    X = rng.standard_normal((n, D))
+    W13 = np.stack([[O.fp8_e4m3_decode(np.array([c]))[0] * s13[r] for c in c13[r]]
+                    for r in range(2 * I)])
+    W2 = np.stack([[O.fp8_e4m3_decode(np.array([c]))[0] * s2[r] for c in c2[r]]
+                   for r in range(D)])
+    g, u = X @ W13[:I].T, X @ W13[I:].T
+    ref = (g / (1 + np.exp(-g)) * u) @ W2.T
+    got = O.expert_mlp(X, O.dequantize_rows(c13, s13), O.dequantize_rows(c2, s2))
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
