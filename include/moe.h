@@ -271,12 +271,55 @@ moe_status_t moe_experts_ex(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, 
                             const int32_t* row_to_pair, const moe_expert_weights_t* w,
                             float* y_rows, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Logical -> physical expert placement and EPLB load (page 1: routing selects
+ * logical experts and dispatch may map them through log2phy to physical
+ * slots, keeping the router's logical output -- Stage 4, "Runner
+ * Initialization"; Stage 6: dispatch's per-expert token counts are added into
+ * the layer's moe_load).
+ *   num_physical   physical expert slots; the routed expert weights are laid
+ *                  out by slot ([num_physical, ...]); a slot holds one
+ *                  logical expert's weights (redundant slots hold copies)
+ *   log2phy        [num_experts] int32: the slot each logical expert's tokens
+ *                  go to; entries in [0, num_physical) (precondition: an
+ *                  out-of-range entry is clamped into range, never faults)
+ *   load           [num_physical] int64 or NULL: load[s] += tokens sent to
+ *                  slot s, once per call
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int32_t num_physical;
+    const int32_t* log2phy;
+    int64_t* load;
+} moe_placement_t;
+
+/* phys_ids[t, j] = log2phy[topk_ids[t, j]] for the T*k pairs. */
+moe_status_t moe_log2phy(int64_t T, int32_t k, int32_t num_logical, int32_t num_physical,
+                         const int32_t* log2phy, const int32_t* topk_ids, int32_t* phys_ids,
+                         void* stream);
+
+/* load[s] += counts[s] for s < n (counts from moe_permute over the slots). */
+moe_status_t moe_load_accumulate(int32_t n, const int32_t* counts, int64_t* load,
+                                 void* stream);
+
+/* Workspace of moe_forward_ex: as moe_forward_workspace, with the permute and
+ * expert stages sized for max(num_experts, placement->num_physical) when a
+ * placement is given (NULL: the same as moe_forward_workspace). */
+size_t moe_forward_workspace_ex(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t max_T,
+                                int32_t H, int32_t I, const moe_latent_t* latent,
+                                const moe_shared_t* shared, const moe_placement_t* placement);
+
 /* moe_forward with the routed experts described by `experts` instead of
- * w13 / w2 (same workspace as moe_forward); errors as moe_experts_ex. */
+ * w13 / w2, and an optional placement (NULL: slot = logical id).  With a
+ * placement, topk_ids_out keeps the logical ids, the experts run on the slots
+ * log2phy gives, expert_counts_out (if given) holds num_physical per-slot
+ * counts, and load (if given) accumulates them.  Workspace: at least
+ * moe_forward_workspace_ex(...).  Errors as moe_experts_ex; a placement with
+ * num_physical outside [1, 1024] or no log2phy is MOE_EINVAL / MOE_ENOTSUP. */
 moe_status_t moe_forward_ex(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t T,
                             int32_t H, int32_t I, const void* x, const void* w_router,
                             const float* router_bias, const float* router_logits,
                             const float* correction_bias, const moe_expert_weights_t* experts,
+                            const moe_placement_t* placement,
                             const moe_latent_t* latent, const moe_shared_t* shared,
                             void* out, float* logits_out, int32_t* topk_ids_out,
                             float* topk_weights_out, int32_t* expert_counts_out,

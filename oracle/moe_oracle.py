@@ -228,6 +228,19 @@ def dequantize_rows(codes, scale) -> np.ndarray:
     return fp8_e4m3_decode(codes) * np.asarray(scale, dtype=f64)[..., None]
 
 
+def map_to_physical(ids, log2phy) -> np.ndarray:
+    """Physical slot of every selected expert (page 1, Stage 4: with dynamic
+    placement, dispatch maps the logical topk_ids through log2phy; the
+    router's logical output is kept): phys[t, j] = log2phy[ids[t, j]]."""
+    return np.asarray(log2phy, dtype=np.int64)[np.asarray(ids, dtype=np.int64)]
+
+
+def accumulate_load(load, counts) -> np.ndarray:
+    """EPLB heat (page 1, Stage 6): the dispatch's per-expert token counts
+    are added into the layer's load."""
+    return np.asarray(load, dtype=np.int64) + np.asarray(counts, dtype=np.int64)
+
+
 def silu(v: np.ndarray) -> np.ndarray:
     return v / (1.0 + np.exp(-v))
 

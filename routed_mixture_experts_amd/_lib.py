@@ -27,7 +27,8 @@ MOE_WEIGHT_DTYPE, MOE_WEIGHT_FP8_E4M3 = 0, 1
 
 EXPORTS = ["moe_route", "moe_permute_workspace", "moe_permute", "moe_experts_workspace",
            "moe_experts", "moe_combine", "moe_forward_workspace", "moe_forward",
-           "moe_experts_ex", "moe_forward_ex", "moe_status_string"]
+           "moe_experts_ex", "moe_forward_ex", "moe_forward_workspace_ex", "moe_log2phy",
+           "moe_load_accumulate", "moe_status_string"]
 
 
 class moe_route_cfg_t(ctypes.Structure):
@@ -50,6 +51,11 @@ class moe_shared_t(ctypes.Structure):
 class moe_expert_weights_t(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
+
+
+class moe_placement_t(ctypes.Structure):
+    _fields_ = [("num_physical", ctypes.c_int32), ("log2phy", ctypes.c_void_p),
+                ("load", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -119,8 +125,18 @@ def load() -> ctypes.CDLL:
     lib.moe_forward_ex.restype = _I32
     lib.moe_forward_ex.argtypes = [ctypes.POINTER(moe_route_cfg_t), _I32, _I64, _I32, _I32, _P,
                                    _P, _P, _P, _P, ctypes.POINTER(moe_expert_weights_t),
+                                   ctypes.POINTER(moe_placement_t),
                                    ctypes.POINTER(moe_latent_t), ctypes.POINTER(moe_shared_t),
                                    _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.moe_forward_workspace_ex.restype = _SZ
+    lib.moe_forward_workspace_ex.argtypes = [ctypes.POINTER(moe_route_cfg_t), _I32, _I64, _I32,
+                                             _I32, ctypes.POINTER(moe_latent_t),
+                                             ctypes.POINTER(moe_shared_t),
+                                             ctypes.POINTER(moe_placement_t)]
+    lib.moe_log2phy.restype = _I32
+    lib.moe_log2phy.argtypes = [_I64, _I32, _I32, _I32, _P, _P, _P, _P]
+    lib.moe_load_accumulate.restype = _I32
+    lib.moe_load_accumulate.argtypes = [_I32, _P, _P, _P]
     lib.moe_forward.restype = _I32
     lib.moe_forward.argtypes = [ctypes.POINTER(moe_route_cfg_t), _I32, _I64, _I32, _I32, _P, _P,
                                 _P, _P, _P, _P, _P, ctypes.POINTER(moe_latent_t),
@@ -128,6 +144,9 @@ def load() -> ctypes.CDLL:
                                 _P]
     _lib = lib
     return lib
+
+
+_library = load  # the loader, for functions whose arguments shadow its name
 
 
 def _check(st: int):
@@ -291,6 +310,49 @@ def moe_experts_ex(x: torch.Tensor, expert_offsets: torch.Tensor, row_to_pair: t
     return y_rows
 
 
+class Placement:
+    """Logical -> physical expert placement for moe_forward_ex.
+
+    ``log2phy``: int32 [num_experts], the physical slot of each logical
+    expert; ``num_physical``: slots (the expert weights are laid out by slot);
+    ``load``: optional int64 [num_physical] that accumulates the tokens sent
+    to each slot, once per call."""
+
+    def __init__(self, log2phy: torch.Tensor, num_physical: int, load=None):
+        _need(log2phy, torch.int32, "log2phy")
+        _need(load, torch.int64, "load")
+        if load is not None and load.numel() != num_physical:
+            raise ValueError("load must have num_physical entries")
+        self.log2phy, self.num_physical, self.load = log2phy, int(num_physical), load
+
+    def c(self) -> moe_placement_t:
+        return moe_placement_t(self.num_physical, _ptr(self.log2phy), _ptr(self.load))
+
+
+def moe_log2phy(topk_ids: torch.Tensor, log2phy: torch.Tensor, num_physical: int, out=None):
+    """phys_ids[t, j] = log2phy[topk_ids[t, j]] (int32, same shape)."""
+    lib = load()
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(log2phy, torch.int32, "log2phy")
+    T, k = topk_ids.shape
+    if out is None:
+        out = torch.empty_like(topk_ids)
+    _check(lib.moe_log2phy(T, k, log2phy.numel(), num_physical, _ptr(log2phy), _ptr(topk_ids),
+                           _ptr(out), _stream()))
+    return out
+
+
+def moe_load_accumulate(counts: torch.Tensor, load: torch.Tensor):
+    """load += counts (int32 counts into an int64 accumulator, on the stream)."""
+    lib = _library()
+    _need(counts, torch.int32, "counts")
+    _need(load, torch.int64, "load")
+    if counts.numel() != load.numel():
+        raise ValueError("counts and load differ in length")
+    _check(lib.moe_load_accumulate(counts.numel(), _ptr(counts), _ptr(load), _stream()))
+    return load
+
+
 def moe_combine(y_rows: torch.Tensor, pair_to_row: torch.Tensor, topk_weights: torch.Tensor,
                 out_dtype: torch.dtype = torch.bfloat16, out=None):
     """out[t] = sum_j w[t,j] * y_rows[pair_to_row[t*k+j]] (fp32 sum, one rounding)."""
@@ -333,7 +395,7 @@ def moe_forward_workspace(cfg: RouteConfig, dtype: torch.dtype, max_T: int, H: i
 
 def _forward(cfg, x, I, experts, w_router, router_bias, router_logits, correction_bias,
              latent, shared, out, logits_out, topk_ids_out, topk_weights_out,
-             expert_counts_out, stage_events, workspace, stream):
+             expert_counts_out, stage_events, workspace, stream, placement=None):
     lib = load()
     T, H = x.shape
     dt = _dtype_code(x.dtype)
@@ -346,9 +408,11 @@ def _forward(cfg, x, I, experts, w_router, router_bias, router_logits, correctio
     c = cfg.c()
     lat = _latent_struct(latent)
     sh = _shared_struct(shared)
-    nbytes = lib.moe_forward_workspace(ctypes.byref(c), dt, T, H, I,
-                                       ctypes.byref(lat) if lat else None,
-                                       ctypes.byref(sh) if sh else None)
+    pl = placement.c() if placement is not None else None
+    nbytes = lib.moe_forward_workspace_ex(ctypes.byref(c), dt, T, H, I,
+                                          ctypes.byref(lat) if lat else None,
+                                          ctypes.byref(sh) if sh else None,
+                                          ctypes.byref(pl) if pl else None)
     if nbytes == 0:
         raise MoeError(MOE_EINVAL, "moe_forward_workspace rejected the shapes")
     if workspace is None:
@@ -365,7 +429,8 @@ def _forward(cfg, x, I, experts, w_router, router_bias, router_logits, correctio
             _ptr(router_logits), _ptr(correction_bias))
     if isinstance(experts, ExpertWeights):
         wc = experts.c()
-        _check(lib.moe_forward_ex(*head, ctypes.byref(wc), *common))
+        _check(lib.moe_forward_ex(*head, ctypes.byref(wc), ctypes.byref(pl) if pl else None,
+                                  *common))
     else:
         w13, w2 = experts
         _check(lib.moe_forward(*head, _ptr(w13), _ptr(w2), *common))
@@ -391,9 +456,13 @@ def moe_forward_ex(cfg: RouteConfig, x: torch.Tensor, experts: ExpertWeights, *,
                    w_router=None, router_bias=None, router_logits=None, correction_bias=None,
                    latent: Optional[dict] = None, shared: Optional[dict] = None, out=None,
                    logits_out=None, topk_ids_out=None, topk_weights_out=None,
-                   expert_counts_out=None, stage_events=None, workspace=None, stream=None):
-    """moe_forward with the routed experts given as an ExpertWeights."""
+                   expert_counts_out=None, stage_events=None, workspace=None, stream=None,
+                   placement: Optional[Placement] = None):
+    """moe_forward with the routed experts given as an ExpertWeights, and an
+    optional logical -> physical Placement (the weights are then laid out by
+    physical slot; topk_ids_out stays logical, expert_counts_out is per slot)."""
     experts.check_dtype(x.dtype)
     return _forward(cfg, x, experts.I, experts, w_router, router_bias, router_logits,
                     correction_bias, latent, shared, out, logits_out, topk_ids_out,
-                    topk_weights_out, expert_counts_out, stage_events, workspace, stream)
+                    topk_weights_out, expert_counts_out, stage_events, workspace, stream,
+                    placement)

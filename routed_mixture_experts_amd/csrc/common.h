@@ -106,6 +106,12 @@ hipError_t launch_permute(int64_t P, int32_t E, const int32_t* ids, int32_t* cou
                           int32_t* chunk_scratch, hipStream_t s);
 // Splits the groups into a small-tile list (one tile per group of 1..small_max
 // rows) and a big-tile list (big_m-row tiles of the larger groups).
+// phys[p] = log2phy[ids[p]] (both clamped into range).
+hipError_t launch_log2phy(int64_t P, const int32_t* ids, const int32_t* log2phy,
+                          int32_t num_logical, int32_t num_physical, int32_t* phys,
+                          hipStream_t s);
+// load[e] += counts[e] for e < n.
+hipError_t launch_load_accumulate(int32_t n, const int32_t* counts, int64_t* load, hipStream_t s);
 hipError_t launch_build_tiles(const int32_t* offsets, int32_t E, int32_t small_max,
                               int32_t big_m, Tile* small_tiles, int32_t* num_small,
                               Tile* big_tiles, int32_t* num_big, hipStream_t s);

@@ -172,7 +172,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
             cs[1] = sc[g.N + hc];
         } else {
 #pragma unroll
-            for (int nj = 0; nj < 2; ++nj) cs[nj] = sc[min(tc.nt * TBN + wn * 64 + nj * 32 + fr, g.N - 1)];
+            for (int nj = 0; nj < 2; ++nj)
+                cs[nj] = sc[min(tc.nt * TBN + wn * 64 + nj * 32 + fr, g.N - 1)];
         }
     }
 
@@ -509,7 +510,8 @@ __global__ __launch_bounds__(256) void gemm_f32_tiled(GemmArgs g) {
 
     int bcol[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bcol[j] = SW ? (j < 2 ? tx * 2 + j : 32 + tx * 2 + j - 2) : tx * 4 + j;
+    for (int j = 0; j < 4; ++j)
+        bcol[j] = SW ? (j < 2 ? tx * 2 + j : 32 + tx * 2 + j - 2) : tx * 4 + j;
 
     const int nk1 = g.K / FBK;
     const int nk = nk1 + (g.A2 ? g.K2 / FBK : 0);

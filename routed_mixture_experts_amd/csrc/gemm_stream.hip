@@ -295,7 +295,8 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     auto load_w = [&](int u) __attribute__((always_inline)) {
         u = min(u, nu - 1);
         const bool seg1 = !KCAT || u < ns1;
-        const char* src = seg1 ? Bb + (wo + (uint32_t)u * 64) : B2b + (wo2 + (uint32_t)(u - ns1) * 64);
+        const char* src = seg1 ? Bb + (wo + (uint32_t)u * 64)
+                               : B2b + (wo2 + (uint32_t)(u - ns1) * 64);
         return *(const u32x4_t*)src;
     };
 

@@ -306,16 +306,21 @@ struct ForwardWs {
     void* normed;   // latent RMSNorm output [T, L]
     void* h_sh;     // shared intermediate [T, Is]
     float* sh;      // shared output [T, H] (no latent)
+    int32_t* phys;  // physical slots of the pairs (with a placement)
 };
 
+// E: experts the permute and expert stages run over (the physical slots
+// when a placement is given).
 ForwardWs carve_forward(Carve& c, const moe_route_cfg_t* cfg, moe_dtype_t dt, int64_t max_T,
-                        int H, int I, const moe_latent_t* lat, const moe_shared_t* sh) {
+                        int H, int I, const moe_latent_t* lat, const moe_shared_t* sh,
+                        int E, bool placed) {
     ForwardWs w;
-    const int E = cfg->num_experts, k = cfg->top_k;
+    const int k = cfg->top_k;
+    const int El = cfg->num_experts;
     const int64_t P = max_T * k;
     const int D = lat ? lat->latent : H;
     const size_t es = elem_size(dt);
-    w.logits = c.take<float>((size_t)max_T * E);
+    w.logits = c.take<float>((size_t)max_T * El);
     w.ids = c.take<int32_t>((size_t)P);
     w.weights = c.take<float>((size_t)P);
     w.counts = c.take<int32_t>((size_t)E);
@@ -329,7 +334,18 @@ ForwardWs carve_forward(Carve& c, const moe_route_cfg_t* cfg, moe_dtype_t dt, in
     w.normed = lat ? c.take<char>((size_t)max_T * D * es) : nullptr;
     w.h_sh = sh ? c.take<char>((size_t)max_T * sh->inter * es) : nullptr;
     w.sh = (sh && !lat) ? c.take<float>((size_t)max_T * H) : nullptr;
+    w.phys = placed ? c.take<int32_t>((size_t)P) : nullptr;
     return w;
+}
+
+// Slots the permute and expert stages run over; MOE_OK or the error.
+moe_status_t placement_slots(const moe_route_cfg_t* cfg, const moe_placement_t* pl, int* E) {
+    *E = cfg->num_experts;
+    if (!pl) return MOE_OK;
+    if (!pl->log2phy || pl->num_physical < 1) return MOE_EINVAL;
+    if (pl->num_physical > kMaxExperts) return MOE_ENOTSUP;
+    *E = pl->num_physical;
+    return MOE_OK;
 }
 
 moe_status_t check_forward_shapes(const moe_route_cfg_t* cfg, moe_dtype_t dt, int64_t T, int H,
@@ -519,10 +535,38 @@ moe_status_t moe_combine(moe_dtype_t out_dtype, int64_t T, int32_t k, int32_t D,
 size_t moe_forward_workspace(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t max_T,
                              int32_t H, int32_t I, const moe_latent_t* latent,
                              const moe_shared_t* shared) {
+    return moe_forward_workspace_ex(cfg, dtype, max_T, H, I, latent, shared, nullptr);
+}
+
+size_t moe_forward_workspace_ex(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t max_T,
+                                int32_t H, int32_t I, const moe_latent_t* latent,
+                                const moe_shared_t* shared, const moe_placement_t* placement) {
     if (check_forward_shapes(cfg, dtype, max_T, H, I, latent, shared) != MOE_OK) return 0;
+    int E = 0;
+    if (placement_slots(cfg, placement, &E) != MOE_OK) return 0;
     Carve c(nullptr);
-    carve_forward(c, cfg, dtype, max_T, H, I, latent, shared);
+    carve_forward(c, cfg, dtype, max_T, H, I, latent, shared, std::max(E, cfg->num_experts),
+                  placement != nullptr);
     return c.off;
+}
+
+moe_status_t moe_log2phy(int64_t T, int32_t k, int32_t num_logical, int32_t num_physical,
+                         const int32_t* log2phy, const int32_t* topk_ids, int32_t* phys_ids,
+                         void* stream) {
+    if (T < 0 || k < 1 || num_logical < 1 || num_physical < 1) return MOE_EINVAL;
+    if (num_logical > kMaxExperts || num_physical > kMaxExperts) return MOE_ENOTSUP;
+    if (T * (int64_t)k > INT32_MAX / 2) return MOE_ENOTSUP;
+    if (T == 0) return MOE_OK;
+    if (!log2phy || !topk_ids || !phys_ids) return MOE_EINVAL;
+    return hip_status(launch_log2phy(T * k, topk_ids, log2phy, num_logical, num_physical,
+                                     phys_ids, (hipStream_t)stream));
+}
+
+moe_status_t moe_load_accumulate(int32_t n, const int32_t* counts, int64_t* load, void* stream) {
+    if (n < 0) return MOE_EINVAL;
+    if (n == 0) return MOE_OK;
+    if (!counts || !load) return MOE_EINVAL;
+    return hip_status(launch_load_accumulate(n, counts, load, (hipStream_t)stream));
 }
 
 }  // extern "C"
@@ -532,8 +576,9 @@ namespace {
 moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t T, int32_t H,
                           int32_t I, const void* x, const void* w_router, const float* router_bias,
                           const float* router_logits, const float* correction_bias,
-                          const ExpertWeights& ew, const moe_latent_t* latent,
-                          const moe_shared_t* shared, void* out, float* logits_out,
+                          const ExpertWeights& ew, const moe_placement_t* placement,
+                          const moe_latent_t* latent, const moe_shared_t* shared, void* out,
+                          float* logits_out,
                           int32_t* topk_ids_out, float* topk_weights_out,
                           int32_t* expert_counts_out, void* const* stage_events, void* ws,
                           size_t ws_bytes, void* stream) {
@@ -541,7 +586,9 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
     if (T == 0) return MOE_OK;
     if (!x || !weights_present(ew) || !out) return MOE_EINVAL;
     if (!router_logits && !w_router) return MOE_EINVAL;
-    if (!ws || ws_bytes < moe_forward_workspace(cfg, dtype, T, H, I, latent, shared))
+    int Es = 0;  // experts the permute and expert stages run over
+    MOE_TRY(placement_slots(cfg, placement, &Es));
+    if (!ws || ws_bytes < moe_forward_workspace_ex(cfg, dtype, T, H, I, latent, shared, placement))
         return MOE_ENOSPACE;
 
     hipStream_t s = (hipStream_t)stream;
@@ -549,7 +596,8 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
     const int E = cfg->num_experts, k = cfg->top_k;
     const int D = latent ? latent->latent : H;
     Carve c(ws);
-    ForwardWs w = carve_forward(c, cfg, dtype, T, H, I, latent, shared);
+    ForwardWs w = carve_forward(c, cfg, dtype, T, H, I, latent, shared,
+                                std::max(Es, cfg->num_experts), placement != nullptr);
     auto mark = [&](int stage, int end) -> moe_status_t {
         if (!ev) return MOE_OK;
         return hip_status(hipEventRecord(ev[2 * stage + end], s));
@@ -596,12 +644,21 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
 
     // dispatch bookkeeping
     int32_t* counts = expert_counts_out ? expert_counts_out : w.counts;
+    // (with a placement: logical ids -> physical slots first; the logical ids
+    // stay the routing output, the slots decide which weights run)
     MOE_TRY(mark(MOE_STAGE_PERMUTE, 0));
-    MOE_HIP(launch_permute(T * k, E, ids, counts, w.offsets, w.r2p, w.p2r, w.chunks, s));
+    const int32_t* disp = ids;
+    if (placement) {
+        MOE_HIP(launch_log2phy(T * k, ids, placement->log2phy, E, Es, w.phys, s));
+        disp = w.phys;
+    }
+    MOE_HIP(launch_permute(T * k, Es, disp, counts, w.offsets, w.r2p, w.p2r, w.chunks, s));
+    if (placement && placement->load)
+        MOE_HIP(launch_load_accumulate(Es, counts, placement->load, s));
     MOE_TRY(mark(MOE_STAGE_PERMUTE, 1));
 
     // routed experts
-    MOE_TRY(run_experts(dtype, T, k, E, D, I, xin, w.offsets, w.r2p, ew, w.y_rows, w.ex, s, ev));
+    MOE_TRY(run_experts(dtype, T, k, Es, D, I, xin, w.offsets, w.r2p, ew, w.y_rows, w.ex, s, ev));
 
     // shared expert without a latent tail: its output is the combine addend
     if (shared && !latent) {
@@ -672,15 +729,17 @@ moe_status_t moe_forward(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t 
                          size_t ws_bytes, void* stream) {
     const ExpertWeights ew = {false, w13, w2, nullptr, nullptr};
     return forward_impl(cfg, dtype, T, H, I, x, w_router, router_bias, router_logits,
-                        correction_bias, ew, latent, shared, out, logits_out, topk_ids_out,
-                        topk_weights_out, expert_counts_out, stage_events, ws, ws_bytes, stream);
+                        correction_bias, ew, nullptr, latent, shared, out, logits_out,
+                        topk_ids_out, topk_weights_out, expert_counts_out, stage_events, ws,
+                        ws_bytes, stream);
 }
 
 moe_status_t moe_forward_ex(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t T, int32_t H,
                             int32_t I, const void* x, const void* w_router,
                             const float* router_bias, const float* router_logits,
                             const float* correction_bias, const moe_expert_weights_t* experts,
-                            const moe_latent_t* latent, const moe_shared_t* shared, void* out,
+                            const moe_placement_t* placement, const moe_latent_t* latent,
+                            const moe_shared_t* shared, void* out,
                             float* logits_out, int32_t* topk_ids_out, float* topk_weights_out,
                             int32_t* expert_counts_out, void* const* stage_events, void* ws,
                             size_t ws_bytes, void* stream) {
@@ -688,8 +747,9 @@ moe_status_t moe_forward_ex(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64
     ExpertWeights ew;
     MOE_TRY(expert_weights(dtype, experts, &ew));
     return forward_impl(cfg, dtype, T, H, I, x, w_router, router_bias, router_logits,
-                        correction_bias, ew, latent, shared, out, logits_out, topk_ids_out,
-                        topk_weights_out, expert_counts_out, stage_events, ws, ws_bytes, stream);
+                        correction_bias, ew, placement, latent, shared, out, logits_out,
+                        topk_ids_out, topk_weights_out, expert_counts_out, stage_events, ws,
+                        ws_bytes, stream);
 }
 
 }  // extern "C"

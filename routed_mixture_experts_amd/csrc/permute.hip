@@ -156,7 +156,45 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     }
 }
 
+// Logical -> physical expert slot of every (token, slot) pair ("vLLM-Ascend
+// Kimi K3 MoE Forward Insight", Stage 4: dispatch maps the logical topk_ids
+// through log2phy when dynamic placement is active).  Out-of-range ids or
+// table entries are clamped, so a stale table cannot index outside the
+// weights.
+__global__ __launch_bounds__(256) void log2phy_kernel(int64_t P, const int32_t* __restrict__ ids,
+                                                      const int32_t* __restrict__ log2phy,
+                                                      int32_t num_logical, int32_t num_physical,
+                                                      int32_t* __restrict__ phys) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= P) return;
+    const int l = min(max(ids[p], 0), num_logical - 1);
+    phys[p] = min(max(log2phy[l], 0), num_physical - 1);
+}
+
+// load[e] += counts[e] (Stage 6: the dispatch's per-expert token counts are
+// added into the layer's EPLB load).
+__global__ __launch_bounds__(256) void load_accumulate_kernel(int32_t n,
+                                                              const int32_t* __restrict__ counts,
+                                                              int64_t* __restrict__ load) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e < n) load[e] += counts[e];
+}
+
 }  // namespace
+
+hipError_t launch_log2phy(int64_t P, const int32_t* ids, const int32_t* log2phy,
+                          int32_t num_logical, int32_t num_physical, int32_t* phys,
+                          hipStream_t s) {
+    if (P > 0)
+        log2phy_kernel<<<(unsigned)((P + 255) / 256), 256, 0, s>>>(P, ids, log2phy, num_logical,
+                                                                    num_physical, phys);
+    return hipGetLastError();
+}
+
+hipError_t launch_load_accumulate(int32_t n, const int32_t* counts, int64_t* load, hipStream_t s) {
+    if (n > 0) load_accumulate_kernel<<<(n + 255) / 256, 256, 0, s>>>(n, counts, load);
+    return hipGetLastError();
+}
 
 int permute_chunks(int64_t P) { return (int)((P + kChunk - 1) / kChunk); }
 

@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\*?\s+\*?(moe_[a-z_]+)\s*\(",
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\*?\s+\*?(moe_[a-z0-9_]+)\s*\(",
                        src, flags=re.M)
     return sorted(set(names))
 

@@ -407,3 +407,29 @@ def test_fp8_expert_mlp_is_the_mlp_of_the_decoded_weights():
     ref = (g / (1 + np.exp(-g)) * u) @ W2.T
     got = O.expert_mlp(X, O.dequantize_rows(c13, s13), O.dequantize_rows(c2, s2))
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------- logical -> physical placement ---
+
+def test_map_to_physical_identity_and_gather():
+    ids = np.array([[3, 0, 7], [1, 1, 2]])
+    assert np.array_equal(O.map_to_physical(ids, np.arange(8)), ids)
+    table = np.array([10, 4, 5, 9, 0, 1, 2, 3])
+    assert np.array_equal(O.map_to_physical(ids, table), np.array([[9, 10, 3], [4, 4, 5]]))
+
+
+def test_map_to_physical_moves_counts_with_the_table():
+    # an injective table moves each logical expert's count to its slot
+    rng = np.random.default_rng(0)
+    E, S = 12, 20
+    ids = np.stack([rng.choice(E, 3, replace=False) for _ in range(50)])
+    table = rng.choice(S, E, replace=False)
+    slot_counts = np.bincount(O.map_to_physical(ids, table).ravel(), minlength=S)
+    logical_counts = np.bincount(ids.ravel(), minlength=E)
+    assert np.array_equal(slot_counts[table], logical_counts)
+    assert slot_counts.sum() == ids.size
+
+
+def test_accumulate_load_adds_counts():
+    assert np.array_equal(O.accumulate_load(np.array([5, 0, 2]), np.array([1, 2, 3])),
+                          np.array([6, 2, 5]))
