@@ -255,17 +255,39 @@ moe_status_t moe_forward(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t 
  * ---------------------------------------------------------------------- */
 typedef enum { MOE_WEIGHT_DTYPE = 0, MOE_WEIGHT_FP8_E4M3 = 1 } moe_weight_format_t;
 
+/* Gate/up activation of the routed experts, h = act(gate, up) (page 1,
+ * Stage 4: the activation branches of the grouped MLP; the pages name them
+ * without formulas -- these are the readings):
+ *   MOE_ACT_SILU        silu(g) * u                       (SwiGLU, default)
+ *   MOE_ACT_GELU        0.5 g (1 + erf(g / sqrt 2)) * u
+ *   MOE_ACT_GELU_TANH   0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))) * u
+ *   MOE_ACT_SWIGLU_CLIP gc * sigmoid(alpha gc) * (uc + 1), gc = min(g, limit),
+ *                       uc = clamp(u, -limit, limit): the clipped SwiGLU on
+ *                       the gate|up (un-interleaved) row layout; needs
+ *                       alpha > 0 and limit > 0 (1.702 and 7 are the usual
+ *                       values). */
+typedef enum {
+    MOE_ACT_SILU = 0,
+    MOE_ACT_GELU = 1,
+    MOE_ACT_GELU_TANH = 2,
+    MOE_ACT_SWIGLU_CLIP = 3
+} moe_activation_t;
+
 typedef struct {
     int32_t format;           /* moe_weight_format_t */
     const void* w13;          /* [E, 2I, D] */
     const void* w2;           /* [E, D, I] */
     const float* w13_scale;   /* [E, 2I] f32 (FP8 only) */
     const float* w2_scale;    /* [E, D] f32 (FP8 only) */
+    int32_t activation;       /* moe_activation_t (0 = SwiGLU) */
+    float act_alpha;          /* MOE_ACT_SWIGLU_CLIP only */
+    float act_limit;          /* MOE_ACT_SWIGLU_CLIP only */
 } moe_expert_weights_t;
 
-/* moe_experts with the expert weights described by `w` (same workspace as
- * moe_experts).  MOE_EINVAL for an unknown format or missing pointers;
- * MOE_ENOTSUP for FP8 weights with an fp32 layer. */
+/* moe_experts with the expert weights and activation described by `w` (same
+ * workspace as moe_experts).  MOE_EINVAL for an unknown format or activation,
+ * missing pointers, or clip parameters that are not positive; MOE_ENOTSUP
+ * for FP8 weights with an fp32 layer.  A shared expert always uses SwiGLU. */
 moe_status_t moe_experts_ex(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, int32_t D,
                             int32_t I, const void* x, const int32_t* expert_offsets,
                             const int32_t* row_to_pair, const moe_expert_weights_t* w,

@@ -37,6 +37,14 @@ experts by their sum and routed scaling multiplies afterwards; combine weights
 are applied to expert outputs, never to inputs; rows of w13 are gate then up;
 rows inside an expert's segment keep ascending pair order p = t*k + j.
 
+The expert activation is SwiGLU unless set otherwise (page 1, Stage 4 also
+lists a clipped SwiGLU on the un-interleaved gate|up layout, GELU and
+GELU-tanh, without formulas).  Readings: GELU = x * Phi(x) (erf form) and its
+tanh approximation, applied as gelu(gate) * up; the clipped SwiGLU is
+min(g, L) * sigmoid(alpha * min(g, L)) * (clamp(u, -L, L) + 1), the form of
+the published open-weight MLP that names it, with alpha and L as
+parameters.
+
 Expert weights may also come as 8-bit floating-point codes (page 1, Stage 4:
 the grouped-matmul paths include W8A8FP, W4A8 and MXFP variants with the
 dequantisation fused into the matmul; the pages give no format).  Reading:
@@ -245,20 +253,56 @@ def silu(v: np.ndarray) -> np.ndarray:
     return v / (1.0 + np.exp(-v))
 
 
-def expert_mlp(X: np.ndarray, w13_e: np.ndarray, w2_e: np.ndarray) -> np.ndarray:
-    """One expert (page 1, Stage 4: gate/up matmul -> SwiGLU -> down matmul).
+def gelu(v: np.ndarray) -> np.ndarray:
+    """GELU, x * Phi(x) with the normal CDF written through erf."""
+    from scipy.special import erf
+    v = np.asarray(v, dtype=f64)
+    return 0.5 * v * (1.0 + erf(v / np.sqrt(2.0)))
+
+
+def gelu_tanh(v: np.ndarray) -> np.ndarray:
+    """The tanh approximation of GELU."""
+    v = np.asarray(v, dtype=f64)
+    return 0.5 * v * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (v + 0.044715 * v ** 3)))
+
+
+def glu(g: np.ndarray, u: np.ndarray, act: Optional[dict] = None) -> np.ndarray:
+    """Gate/up activation h = act(gate, up) (page 1, Stage 4 lists SwiGLU, a
+    clipped SwiGLU on the un-interleaved gate|up layout, GELU and GELU-tanh
+    as the MLP's activation branches; the formulas are the readings in the
+    header).  ``act`` = None or dict(kind="silu" | "gelu" | "gelu_tanh" |
+    "swiglu_clip", alpha=..., limit=...)."""
+    kind = (act or {}).get("kind", "silu")
+    if kind == "silu":
+        return silu(g) * u
+    if kind == "gelu":
+        return gelu(g) * u
+    if kind == "gelu_tanh":
+        return gelu_tanh(g) * u
+    if kind == "swiglu_clip":
+        alpha, limit = float(act["alpha"]), float(act["limit"])
+        gc = np.minimum(g, limit)
+        uc = np.clip(u, -limit, limit)
+        return gc / (1.0 + np.exp(-alpha * gc)) * (uc + 1.0)
+    raise ValueError(kind)
+
+
+def expert_mlp(X: np.ndarray, w13_e: np.ndarray, w2_e: np.ndarray,
+               act: Optional[dict] = None) -> np.ndarray:
+    """One expert (page 1, Stage 4: gate/up matmul -> activation -> down
+    matmul; SwiGLU unless ``act`` says otherwise, see glu).
 
     w13_e is [2I, D] with gate rows first, then up rows; w2_e is [D, I]."""
     w13_e = np.asarray(w13_e, dtype=f64)
     w2_e = np.asarray(w2_e, dtype=f64)
     I = w2_e.shape[1]
     gu = np.asarray(X, dtype=f64) @ w13_e.T
-    h = silu(gu[:, :I]) * gu[:, I:]
+    h = glu(gu[:, :I], gu[:, I:], act)
     return h @ w2_e.T
 
 
 def run_experts(xin: np.ndarray, k: int, offsets: np.ndarray, row_to_pair: np.ndarray,
-                w13, w2) -> np.ndarray:
+                w13, w2, act: Optional[dict] = None) -> np.ndarray:
     """Grouped expert MLP over the expert-sorted rows.  Row r of expert e reads
     token row_to_pair[r] // k.  ``w13[e]`` / ``w2[e]`` may be any indexable
     that yields expert e's matrices.  Returns y_rows[P, D] (float64)."""
@@ -272,7 +316,7 @@ def run_experts(xin: np.ndarray, k: int, offsets: np.ndarray, row_to_pair: np.nd
         if a == b:
             continue
         X = np.asarray(xin[row_to_pair[a:b] // k], dtype=f64)
-        y[a:b] = expert_mlp(X, w13[e], w2[e])
+        y[a:b] = expert_mlp(X, w13[e], w2[e], act)
     return y
 
 
@@ -313,14 +357,15 @@ def router_logits(x: np.ndarray, w_router: np.ndarray,
 
 
 def forward(x, cfg: RouteCfg, w13, w2, *, w_router=None, router_bias=None,
-            logits=None, corr_bias=None, latent=None, shared=None) -> dict:
+            logits=None, corr_bias=None, latent=None, shared=None, act=None) -> dict:
     """The whole routed-MoE forward as a chain of the steps above.
 
     ``logits`` (if given) replaces the router product, as in the runner's
     ``forward(hidden_states, router_logits, ...)`` signature (page 2).
     ``latent`` = dict(w_down[L,H], gamma[L], w_up[H,L], eps) and
     ``shared`` = dict(w13[2Is,H], w2[H,Is]) add the latent transform and tail
-    and the shared expert (page 2).  Returns every intermediate."""
+    and the shared expert (page 2).  ``act``: the routed experts' activation
+    (see glu; the shared expert is SwiGLU).  Returns every intermediate."""
     x64 = np.asarray(x, dtype=f64)
     if logits is None:
         logits = router_logits(x64, w_router, router_bias)
@@ -331,7 +376,7 @@ def forward(x, cfg: RouteCfg, w13, w2, *, w_router=None, router_bias=None,
     xin = x64
     if latent is not None:
         xin = x64 @ np.asarray(latent["w_down"], dtype=f64).T
-    y_rows = run_experts(xin, k, offsets, r2p, w13, w2)
+    y_rows = run_experts(xin, k, offsets, r2p, w13, w2, act)
     routed = combine(y_rows, p2r, w)
     res = dict(logits=logits, ids=ids, weights=w, keys=keys, counts=counts,
                offsets=offsets, row_to_pair=r2p, pair_to_row=p2r, y_rows=y_rows,
@@ -351,7 +396,7 @@ def forward(x, cfg: RouteCfg, w13, w2, *, w_router=None, router_bias=None,
 
 
 def forward_tokens(tokens, x, cfg: RouteCfg, w13, w2, *, w_router=None, router_bias=None,
-                   logits=None, corr_bias=None, latent=None, shared=None) -> dict:
+                   logits=None, corr_bias=None, latent=None, shared=None, act=None) -> dict:
     """The same layer evaluated token by token for a list of tokens, without
     the permute (tokens are independent in a routed MoE).  Used to check
     sampled outputs of very large layers, where ``w13[e]``/``w2[e]`` fetch one
@@ -368,7 +413,7 @@ def forward_tokens(tokens, x, cfg: RouteCfg, w13, w2, *, w_router=None, router_b
     for i in range(tokens.shape[0]):
         for j in range(cfg.top_k):
             e = int(ids[i, j])
-            y = expert_mlp(xin[i:i + 1], w13[e], w2[e])[0]
+            y = expert_mlp(xin[i:i + 1], w13[e], w2[e], act)[0]
             routed[i] += w[i, j] * y
     sh = shared_expert(xs, shared["w13"], shared["w2"]) if shared is not None else None
     if latent is not None:

@@ -24,6 +24,7 @@ STAGES = ["router", "downproj", "route", "permute", "gemm1", "gemm2", "combine",
 MOE_NUM_STAGES = len(STAGES)
 
 MOE_WEIGHT_DTYPE, MOE_WEIGHT_FP8_E4M3 = 0, 1
+ACTIVATIONS = {"silu": 0, "gelu": 1, "gelu_tanh": 2, "swiglu_clip": 3}
 
 EXPORTS = ["moe_route", "moe_permute_workspace", "moe_permute", "moe_experts_workspace",
            "moe_experts", "moe_combine", "moe_forward_workspace", "moe_forward",
@@ -50,7 +51,9 @@ class moe_shared_t(ctypes.Structure):
 
 class moe_expert_weights_t(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
-                ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
+                ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
+                ("activation", ctypes.c_int32), ("act_alpha", ctypes.c_float),
+                ("act_limit", ctypes.c_float)]
 
 
 class moe_placement_t(ctypes.Structure):
@@ -250,13 +253,19 @@ class ExpertWeights:
     ``ExpertWeights(w13, w2)``: weights in the layer dtype.
     ``ExpertWeights.fp8(w13, w2, w13_scale, w2_scale)``: OCP e4m3 codes
     (torch.uint8 or torch.float8_e4m3fn) [E, 2I, D] / [E, D, I] with one fp32
-    scale per weight row, [E, 2I] / [E, D]."""
+    scale per weight row, [E, 2I] / [E, D].
+    ``activation``: "silu" (SwiGLU, default), "gelu", "gelu_tanh" or
+    "swiglu_clip" (with ``alpha`` and ``limit``)."""
 
     def __init__(self, w13: torch.Tensor, w2: torch.Tensor, w13_scale=None, w2_scale=None,
-                 fmt: int = MOE_WEIGHT_DTYPE):
+                 fmt: int = MOE_WEIGHT_DTYPE, activation: str = "silu", alpha: float = 1.702,
+                 limit: float = 7.0):
         self.w13, self.w2 = w13, w2
         self.w13_scale, self.w2_scale = w13_scale, w2_scale
         self.format = fmt
+        if activation not in ACTIVATIONS:
+            raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}")
+        self.activation, self.alpha, self.limit = activation, float(alpha), float(limit)
         E, twoI, D = w13.shape
         self.E, self.I, self.D = E, twoI // 2, D
         if tuple(w2.shape) != (E, D, self.I):
@@ -273,12 +282,13 @@ class ExpertWeights:
                 raise ValueError("w13_scale must be [E, 2I] and w2_scale [E, D]")
 
     @classmethod
-    def fp8(cls, w13, w2, w13_scale, w2_scale) -> "ExpertWeights":
-        return cls(w13, w2, w13_scale, w2_scale, MOE_WEIGHT_FP8_E4M3)
+    def fp8(cls, w13, w2, w13_scale, w2_scale, **act) -> "ExpertWeights":
+        return cls(w13, w2, w13_scale, w2_scale, MOE_WEIGHT_FP8_E4M3, **act)
 
     def c(self) -> moe_expert_weights_t:
         return moe_expert_weights_t(self.format, _ptr(self.w13), _ptr(self.w2),
-                                    _ptr(self.w13_scale), _ptr(self.w2_scale))
+                                    _ptr(self.w13_scale), _ptr(self.w2_scale),
+                                    ACTIVATIONS[self.activation], self.alpha, self.limit)
 
     def check_dtype(self, dtype: torch.dtype):
         if self.format == MOE_WEIGHT_DTYPE:

@@ -35,10 +35,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-__device__ __forceinline__ float silu_f32(float g) {
-    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-}
-
 // Tile-list entry of a grouped GEMM: rows [row0, row1) of group g; the
 // group's tiles are the contiguous entries [first, first + count).
 struct Tile {
@@ -85,7 +81,40 @@ struct GemmArgs {
     int32_t b_fp8;
     const float* b_scale;
     int64_t b_scale_gstride;
+    // gate/up activation of EPI_SWIGLU (GluAct) and its parameters
+    int32_t act;
+    float act_alpha, act_limit;
 };
+
+// Gate/up activations h = act(gate, up) ("vLLM-Ascend Kimi K3 MoE Forward
+// Insight", Stage 4: the MLP's activation branches): SwiGLU silu(g) * u;
+// GELU (erf form) and its tanh approximation, gelu(g) * u; and the clipped
+// SwiGLU min(g, L) * sigmoid(alpha * min(g, L)) * (clamp(u, -L, L) + 1).
+enum GluAct { ACT_SILU = 0, ACT_GELU = 1, ACT_GELU_TANH = 2, ACT_SWIGLU_CLIP = 3 };
+
+// PRECISE: exact division for the fp32 layer; otherwise the hardware
+// reciprocal.
+template <bool PRECISE = false>
+__device__ __forceinline__ float glu_f32(float gt, float up, const GemmArgs& a) {
+    auto sigmoid = [](float v) {
+        return PRECISE ? 1.0f / (1.0f + expf(-v)) : __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+    };
+    switch (a.act) {
+        case ACT_GELU:
+            return 0.5f * gt * (1.0f + erff(gt * 0.70710678118654752f)) * up;
+        case ACT_GELU_TANH: {
+            const float z = 0.79788456080286536f * (gt + 0.044715f * gt * gt * gt);
+            return 0.5f * gt * (1.0f + tanhf(z)) * up;
+        }
+        case ACT_SWIGLU_CLIP: {
+            const float gc = fminf(gt, a.act_limit);
+            const float uc = fminf(fmaxf(up, -a.act_limit), a.act_limit);
+            return gc * sigmoid(a.act_alpha * gc) * (uc + 1.0f);
+        }
+        default:
+            return PRECISE ? gt / (1.0f + expf(-gt)) * up : gt * sigmoid(gt) * up;
+    }
+}
 
 // ----- launchers (return hipSuccess or the launch error) -----
 struct RouteArgs {

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
             if (SW) {
                 const int hc = tc.nt * 64 + wn * 32 + fr;
                 if (hc < g.N) {
-                    const float h = silu_f32(acc[mi][0][j] * cs[0]) * (acc[mi][1][j] * cs[1]);
+                    const float h = glu_f32(acc[mi][0][j] * cs[0], acc[mi][1][j] * cs[1], g);
                     ((bf16_t*)g.C)[(int64_t)r * g.ldc + hc] = f32_to_bf16(h);
                 }
             } else {
@@ -428,10 +428,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
                     const f32x4_t u0 = *(const f32x4_t*)(src + 32 + eh * 16 + q * 8);
                     const f32x4_t u1 = *(const f32x4_t*)(src + 32 + eh * 16 + q * 8 + 4);
                     u32x4_t o;
-                    o[0] = pack_bf16x2(silu_f32(g0[0]) * u0[0], silu_f32(g0[1]) * u0[1]);
-                    o[1] = pack_bf16x2(silu_f32(g0[2]) * u0[2], silu_f32(g0[3]) * u0[3]);
-                    o[2] = pack_bf16x2(silu_f32(g1[0]) * u1[0], silu_f32(g1[1]) * u1[1]);
-                    o[3] = pack_bf16x2(silu_f32(g1[2]) * u1[2], silu_f32(g1[3]) * u1[3]);
+                    o[0] = pack_bf16x2(glu_f32(g0[0], u0[0], g), glu_f32(g0[1], u0[1], g));
+                    o[1] = pack_bf16x2(glu_f32(g0[2], u0[2], g), glu_f32(g0[3], u0[3], g));
+                    o[2] = pack_bf16x2(glu_f32(g1[0], u1[0], g), glu_f32(g1[1], u1[1], g));
+                    o[3] = pack_bf16x2(glu_f32(g1[2], u1[2], g), glu_f32(g1[3], u1[3], g));
                     if (hc0 + q * 8 < g.N) *(u32x4_t*)(dst + q * 8) = o;
                 }
             } else {
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(256) void gemm_f32_tiled(GemmArgs g) {
                 const int hc = tc.nt * 32 + tx * 2 + j;
                 if (hc < g.N) {
                     const float gt = acc[i][j], up = acc[i][j + 2];
-                    ((float*)g.C)[(int64_t)r * g.ldc + hc] = gt / (1.0f + expf(-gt)) * up;
+                    ((float*)g.C)[(int64_t)r * g.ldc + hc] = glu_f32<true>(gt, up, g);
                 }
             }
         } else {

@@ -152,7 +152,7 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& g, const TileCoord& 
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int hc = tc.nt * 32 + q * 16 + wr + j;
-                        if (hc < g.N) crow[hc] = f32_to_bf16(silu_f32(gsum[j]) * usum[j]);
+                        if (hc < g.N) crow[hc] = f32_to_bf16(glu_f32(gsum[j], usum[j], g));
                     }
                 }
             }
@@ -397,7 +397,7 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     if (hc0 + j < g.N)
-                        crow[hc0 + j] = f32_to_bf16(silu_f32(acc[tb][j] * rs[j]) * up[j]);
+                        crow[hc0 + j] = f32_to_bf16(glu_f32(acc[tb][j] * rs[j], up[j], g));
             }
         } else if (r < tc.row1) {
             const int c0 = tc.nt * SRN + wave * 16 + g4 * 4;

@@ -22,6 +22,10 @@ namespace {
 
 constexpr size_t kAlign = 256;
 
+static_assert(MOE_ACT_SILU == ACT_SILU && MOE_ACT_GELU == ACT_GELU &&
+                  MOE_ACT_GELU_TANH == ACT_GELU_TANH && MOE_ACT_SWIGLU_CLIP == ACT_SWIGLU_CLIP,
+              "activation codes of the ABI and the kernels agree");
+
 // Bump allocator over the caller's workspace.  With base == nullptr it only
 // measures, so sizing and carving share one code path.
 struct Carve {
@@ -108,6 +112,8 @@ struct ExpertWeights {
     const void* w2;
     const float* s13;  // [E, 2I] row scales (fp8)
     const float* s2;   // [E, D]
+    int act = ACT_SILU;
+    float act_alpha = 0.0f, act_limit = 0.0f;
 };
 
 struct ExpertsWs {
@@ -217,6 +223,9 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
     g1.b_fp8 = ew.fp8;
     g1.b_scale = ew.s13;
     g1.b_scale_gstride = (int64_t)2 * I;
+    g1.act = ew.act;
+    g1.act_alpha = ew.act_alpha;
+    g1.act_limit = ew.act_limit;
     g1.K = D;
     g1.N = I;
     g1.epi = EPI_SWIGLU;
@@ -460,6 +469,12 @@ moe_status_t expert_weights(moe_dtype_t dtype, const moe_expert_weights_t* d, Ex
     ew->w2 = d->w2;
     ew->s13 = ew->fp8 ? d->w13_scale : nullptr;
     ew->s2 = ew->fp8 ? d->w2_scale : nullptr;
+    if (d->activation < MOE_ACT_SILU || d->activation > MOE_ACT_SWIGLU_CLIP) return MOE_EINVAL;
+    ew->act = d->activation;
+    ew->act_alpha = d->act_alpha;
+    ew->act_limit = d->act_limit;
+    if (ew->act == MOE_ACT_SWIGLU_CLIP && !(d->act_alpha > 0.0f && d->act_limit > 0.0f))
+        return MOE_EINVAL;
     if (ew->fp8 && dtype != MOE_DTYPE_BF16) return MOE_ENOTSUP;
     return MOE_OK;
 }
@@ -496,7 +511,7 @@ moe_status_t moe_experts(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, int
                          int32_t I, const void* x, const int32_t* expert_offsets,
                          const int32_t* row_to_pair, const void* w13, const void* w2,
                          float* y_rows, void* ws, size_t ws_bytes, void* stream) {
-    const ExpertWeights ew = {false, w13, w2, nullptr, nullptr};
+    const ExpertWeights ew = {false, w13, w2, nullptr, nullptr, ACT_SILU, 0.0f, 0.0f};
     return experts_impl(dtype, T, k, E, D, I, x, expert_offsets, row_to_pair, ew, y_rows, ws,
                         ws_bytes, stream);
 }
@@ -727,7 +742,7 @@ moe_status_t moe_forward(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t 
                          int32_t* topk_ids_out, float* topk_weights_out,
                          int32_t* expert_counts_out, void* const* stage_events, void* ws,
                          size_t ws_bytes, void* stream) {
-    const ExpertWeights ew = {false, w13, w2, nullptr, nullptr};
+    const ExpertWeights ew = {false, w13, w2, nullptr, nullptr, ACT_SILU, 0.0f, 0.0f};
     return forward_impl(cfg, dtype, T, H, I, x, w_router, router_bias, router_logits,
                         correction_bias, ew, nullptr, latent, shared, out, logits_out,
                         topk_ids_out, topk_weights_out, expert_counts_out, stage_events, ws,

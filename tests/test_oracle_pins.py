@@ -433,3 +433,61 @@ def test_map_to_physical_moves_counts_with_the_table():
 def test_accumulate_load_adds_counts():
     assert np.array_equal(O.accumulate_load(np.array([5, 0, 2]), np.array([1, 2, 3])),
                           np.array([6, 2, 5]))
+
+
+# ------------------------------------------------- gate/up activations ---
+
+def test_gelu_closed_forms():
+    # x * Phi(x): Phi(0) = 1/2, odd part x (gelu(x) - gelu(-x) = x), Phi(1) from math.erf
+    assert O.gelu(np.array([0.0]))[0] == 0.0
+    v = np.array([0.3, 1.0, 2.5, -4.0])
+    np.testing.assert_allclose(O.gelu(v) - O.gelu(-v), v, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(O.gelu(np.array([1.0]))[0], 0.5 * (1 + math.erf(1 / math.sqrt(2))),
+                               rtol=1e-15)
+    assert abs(O.gelu(np.array([-10.0]))[0]) < 1e-20      # Phi(-10) ~ 7.6e-24
+
+
+def test_gelu_tanh_closed_forms_and_closeness():
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+    v = np.array([1.0])
+    ref = 0.5 * (1 + math.tanh(math.sqrt(2 / math.pi) * (1 + 0.044715)))
+    np.testing.assert_allclose(O.gelu_tanh(v)[0], ref, rtol=1e-15)
+    x = np.linspace(-5, 5, 2001)
+    assert np.abs(O.gelu_tanh(x) - O.gelu(x)).max() < 1e-3   # the approximation's known accuracy
+
+
+def test_glu_swiglu_clip_special_cases():
+    act = dict(kind="swiglu_clip", alpha=1.702, limit=7.0)
+    sig = lambda z: 1 / (1 + math.exp(-z))
+    # inside the limits: g * sigmoid(alpha g) * (u + 1)
+    got = O.glu(np.array([0.5]), np.array([2.0]), act)[0]
+    assert abs(got - 0.5 * sig(1.702 * 0.5) * 3.0) < 1e-15
+    # the gate clips at +limit only; the up value clips at both ends
+    got = O.glu(np.array([10.0, -10.0]), np.array([-9.0, 9.0]), act)
+    assert abs(got[0] - 7.0 * sig(1.702 * 7.0) * (-6.0)) < 1e-13
+    assert abs(got[1] - (-10.0) * sig(-17.02) * 8.0) < 1e-13
+
+
+def test_glu_default_is_swiglu():
+    g, u = np.array([-2.0, 0.0, 3.0]), np.array([1.5, 2.0, -1.0])
+    np.testing.assert_allclose(O.glu(g, u), g / (1 + np.exp(-g)) * u, rtol=1e-15)
+
+
+def test_glu_swiglu_clip_reduces_to_swiglu_without_clipping():
+    # alpha = 1 and a limit never reached: silu(g) * (u + 1) = swiglu(g, u) + silu(g)
+    rng = np.random.default_rng(9)
+    g, u = rng.standard_normal(50) * 3, rng.standard_normal(50) * 3
+    got = O.glu(g, u, dict(kind="swiglu_clip", alpha=1.0, limit=1e9))
+    np.testing.assert_allclose(got, O.glu(g, u) + O.silu(g), rtol=1e-13, atol=1e-13)
+
+
+def test_glu_swiglu_clip_saturates_beyond_the_limit():
+    # past the limit the output no longer depends on the clipped input
+    act = dict(kind="swiglu_clip", alpha=1.702, limit=2.0)
+    g = np.array([2.0, 3.0, 50.0, 1e6])
+    assert np.ptp(O.glu(g, np.full(4, 0.7), act)) == 0.0
+    u = np.array([2.0, 5.0, 1e3])
+    assert np.ptp(O.glu(np.full(3, 0.3), u, act)) == 0.0
+    assert np.ptp(O.glu(np.full(3, 0.3), -u, act)) == 0.0
+    # below it, strictly increasing in u for a positive gate
+    assert np.all(np.diff(O.glu(np.full(5, 0.3), np.linspace(-1.9, 1.9, 5), act)) > 0)
