@@ -271,8 +271,8 @@ def main():
                    "parallelism": "none (1 GPU holds all experts)"},
         "roofline": {"bound": "hbm", "achieved": g1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": g1_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gate/up + SwiGLU stage: gemm_bf16_stream<3, false> (experts <= 64 rows)"
-                               " + gemm_bf16_big<3, false> (larger experts)",
+                     "kernel": "gate/up + SwiGLU stage: gemm_bf16_stream<3, false, false> (experts <= 64"
+                               " rows) + gemm_bf16_big<3, false> (larger experts)",
                      "kernel_ms": g1_ms, "algorithmic_bytes": g1b},
         "layer": {"hbm_GBps": abytes / t_s / 1e9, "hbm_frac": abytes / t_s / 1e9 / HBM_PEAK_GBS,
                   "mfma_frac": aflops / t_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
@@ -320,7 +320,8 @@ def main():
             "value": wf.T / (fms * 1e-3), "unit": "tokens/s", "ms_per_step": fms,
             "steps": args.steps, "hbm_frac": fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "gemm1": {"kernel": "gemm_bf16_stream<3, false, true>", "kernel_ms": fstage["gemm1"],
-                      "algorithmic_bytes": f1b, "achieved_GBps": f1, "frac": f1 / HBM_PEAK_GBS},
+                      "algorithmic_bytes": f1b, "achieved_GBps": f1, "frac": f1 / HBM_PEAK_GBS,
+                      "traffic": profiled_traffic(wf.name)},
             "stages_ms": fstage}
         del frun, fin
     if args.copy_probe:
