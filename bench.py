@@ -39,10 +39,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill_zipf", "grouped_sqrtsoftplus", "latent_shared",
-                             "decode_fp8"])
+                             "decode_fp8", "decode_mxfp4"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill line")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the decode line with FP8 E4M3 expert weights")
+    ap.add_argument("--no-mxfp4", action="store_true",
+                    help="skip the decode line with MXFP4 expert weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=64)
     ap.add_argument("--copy-probe", action="store_true",
@@ -76,6 +78,8 @@ def layer_work(w, counts):
     P = w.T * w.k
     if w.weights == "fp8_e4m3":   # one byte per weight plus an fp32 scale per row
         wbytes = touched * (3 * w.I * D + 4 * (2 * w.I + D)) + w.E * w.H * es
+    elif w.weights == "mxfp4":    # half a byte per weight plus a byte per 32
+        wbytes = touched * (3 * w.I * D // 2 + 3 * w.I * D // 32) + w.E * w.H * es
     else:
         wbytes = touched * 3 * w.I * D * es + w.E * w.H * es
     flops = 2.0 * P * 3 * D * w.I + 2.0 * w.T * w.H * w.E
@@ -123,6 +127,8 @@ def gemm1_bytes(w, counts):
     touched = int((counts > 0).sum())
     if w.weights == "fp8_e4m3":
         wb = touched * (2 * w.I * w.D + 4 * 2 * w.I)
+    elif w.weights == "mxfp4":
+        wb = touched * (2 * w.I * w.D // 2 + 2 * w.I * w.D // 32)
     else:
         wb = touched * 2 * w.I * w.D * es
     return wb + w.T * w.D * es + w.T * w.k * w.I * es, touched
@@ -144,9 +150,13 @@ class Runner:
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.out = torch.empty((w.T, w.H), dtype=inp["x"].dtype, device=dev)
         self.counts = torch.empty((w.E,), dtype=torch.int32, device=dev)
-        self.experts = (moe.ExpertWeights.fp8(inp["w13"], inp["w2"], inp["w13_scale"],
-                                              inp["w2_scale"])
-                        if w.weights == "fp8_e4m3" else None)
+        self.experts = None
+        if w.weights == "fp8_e4m3":
+            self.experts = moe.ExpertWeights.fp8(inp["w13"], inp["w2"], inp["w13_scale"],
+                                                 inp["w2_scale"])
+        elif w.weights == "mxfp4":
+            self.experts = moe.ExpertWeights.mxfp4(inp["w13"], inp["w2"], inp["w13_scale"],
+                                                   inp["w2_scale"])
 
     def step(self, events=None):
         i = self.inp
@@ -205,11 +215,12 @@ def cpu_baseline(w, inp, torch, ntok):
     ids, _, _ = O.route(O.router_logits(x, wr, rb), cfg, cb)
     used = sorted(set(ids.reshape(-1).tolist()))
     # host copies (fp32, exact for bf16) of just the experts the sample touches;
-    # FP8 codes are decoded by the oracle (outside the timed region)
-    if w.weights == "fp8_e4m3":
-        w13 = {e: O.dequantize_rows(inp["w13"][e].cpu().numpy(), inp["w13_scale"][e].cpu().numpy())
+    # FP8 / MXFP4 codes are decoded by the oracle (outside the timed region)
+    if w.weights in ("fp8_e4m3", "mxfp4"):
+        dq = O.dequantize_rows if w.weights == "fp8_e4m3" else O.dequantize_mxfp4
+        w13 = {e: dq(inp["w13"][e].cpu().numpy(), inp["w13_scale"][e].cpu().numpy())
                for e in used}
-        w2 = {e: O.dequantize_rows(inp["w2"][e].cpu().numpy(), inp["w2_scale"][e].cpu().numpy())
+        w2 = {e: dq(inp["w2"][e].cpu().numpy(), inp["w2_scale"][e].cpu().numpy())
               for e in used}
     else:
         w13 = {e: inp["w13"][e].float().cpu().numpy() for e in used}
@@ -271,7 +282,7 @@ def main():
                    "parallelism": "none (1 GPU holds all experts)"},
         "roofline": {"bound": "hbm", "achieved": g1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": g1_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gate/up + SwiGLU stage: gemm_bf16_stream<3, false, false> (experts <= 64"
+                     "kernel": "gate/up + SwiGLU stage: gemm_bf16_stream<3, false, 0> (experts <= 64"
                                " rows) + gemm_bf16_big<3, false> (larger experts)",
                      "kernel_ms": g1_ms, "algorithmic_bytes": g1b},
         "layer": {"hbm_GBps": abytes / t_s / 1e9, "hbm_frac": abytes / t_s / 1e9 / HBM_PEAK_GBS,
@@ -319,11 +330,35 @@ def main():
             "workload": describe(wf) + " weights=fp8_e4m3 (per-row fp32 scales)",
             "value": wf.T / (fms * 1e-3), "unit": "tokens/s", "ms_per_step": fms,
             "steps": args.steps, "hbm_frac": fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "gemm1": {"kernel": "gemm_bf16_stream<3, false, true>", "kernel_ms": fstage["gemm1"],
+            "gemm1": {"kernel": "gemm_bf16_stream<3, false, 1>", "kernel_ms": fstage["gemm1"],
                       "algorithmic_bytes": f1b, "achieved_GBps": f1, "frac": f1 / HBM_PEAK_GBS,
                       "traffic": profiled_traffic(wf.name)},
             "stages_ms": fstage}
         del frun, fin
+    if args.workload == "decode" and not args.no_mxfp4:
+        # the same layer with the same weight draws quantised to MXFP4 (E2M1
+        # codes, one E8M0 exponent per 32 elements of a row)
+        wm = WORKLOADS["decode_mxfp4"]
+        print("[bench] decode with MXFP4 expert weights", file=sys.stderr, flush=True)
+        from routed_mixture_experts_amd.synth import mxfp4_rows
+        mxin = dict(inp)
+        mxin["w13"], mxin["w13_scale"] = mxfp4_rows(inp["w13"])
+        mxin["w2"], mxin["w2_scale"] = mxfp4_rows(inp["w2"])
+        mrun = Runner(wm, mxin, torch, moe, stream)
+        mms, _, mstage = mrun.timed(args.steps, args.warmup)
+        mc = mrun.counts.cpu().numpy()
+        mbytes, _, _ = layer_work(wm, mc)
+        m1b, _ = gemm1_bytes(wm, mc)
+        m1 = m1b / (mstage["gemm1"] * 1e-3) / 1e9
+        res["mxfp4_decode"] = {
+            "workload": describe(wm) + " weights=mxfp4 (E2M1, E8M0 exponent per 32)",
+            "value": wm.T / (mms * 1e-3), "unit": "tokens/s", "ms_per_step": mms,
+            "steps": args.steps, "hbm_frac": mbytes / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "gemm1": {"kernel": "gemm_bf16_stream<3, false, 2>", "kernel_ms": mstage["gemm1"],
+                      "algorithmic_bytes": m1b, "achieved_GBps": m1, "frac": m1 / HBM_PEAK_GBS,
+                      "traffic": profiled_traffic(wm.name)},
+            "stages_ms": mstage}
+        del mrun, mxin
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -252,8 +252,25 @@ moe_status_t moe_forward(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t 
  *                        w13_scale [E, 2I] f32, w2_scale [E, D] f32.  Needs
  *                        layer dtype bf16.  Activations (x, h) stay bf16 and
  *                        every sum is fp32, as in the bf16 layer.
+ *   MOE_WEIGHT_MXFP4     OCP microscaling FP4: w13 [E, 2I, D/2] and
+ *                        w2 [E, D, I/2] bytes hold two E2M1 codes each
+ *                        (element 2j of a row in the low nibble of byte j;
+ *                        1 sign, 2 exponent bits with bias 1, 1 mantissa
+ *                        bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), and
+ *                        every 32 consecutive elements of a row share one
+ *                        E8M0 scale byte s, 2^(s - 127): w13_scale
+ *                        [E, 2I, D/32] and w2_scale [E, D, I/32] uint8.  The
+ *                        expert uses W[e, n, 32b + i] = decode(code) *
+ *                        2^(s[e, n, b] - 127).  Scale bytes 0 and 255 (NaN)
+ *                        are outside what the kernels handle.  Needs layer
+ *                        dtype bf16 and D, I multiples of 128 (MOE_ENOTSUP
+ *                        otherwise); activations and sums as for FP8.
  * ---------------------------------------------------------------------- */
-typedef enum { MOE_WEIGHT_DTYPE = 0, MOE_WEIGHT_FP8_E4M3 = 1 } moe_weight_format_t;
+typedef enum {
+    MOE_WEIGHT_DTYPE = 0,
+    MOE_WEIGHT_FP8_E4M3 = 1,
+    MOE_WEIGHT_MXFP4 = 2
+} moe_weight_format_t;
 
 /* Gate/up activation of the routed experts, h = act(gate, up) (page 1,
  * Stage 4: the activation branches of the grouped MLP; the pages name them
@@ -277,8 +294,8 @@ typedef struct {
     int32_t format;           /* moe_weight_format_t */
     const void* w13;          /* [E, 2I, D] */
     const void* w2;           /* [E, D, I] */
-    const float* w13_scale;   /* [E, 2I] f32 (FP8 only) */
-    const float* w2_scale;    /* [E, D] f32 (FP8 only) */
+    const void* w13_scale;    /* FP8: [E, 2I] f32; MXFP4: [E, 2I, D/32] u8 */
+    const void* w2_scale;     /* FP8: [E, D] f32; MXFP4: [E, D, I/32] u8 */
     int32_t activation;       /* moe_activation_t (0 = SwiGLU) */
     float act_alpha;          /* MOE_ACT_SWIGLU_CLIP only */
     float act_limit;          /* MOE_ACT_SWIGLU_CLIP only */
@@ -287,7 +304,8 @@ typedef struct {
 /* moe_experts with the expert weights and activation described by `w` (same
  * workspace as moe_experts).  MOE_EINVAL for an unknown format or activation,
  * missing pointers, or clip parameters that are not positive; MOE_ENOTSUP
- * for FP8 weights with an fp32 layer.  A shared expert always uses SwiGLU. */
+ * for FP8 or MXFP4 weights with an fp32 layer, and for MXFP4 weights with D
+ * or I not a multiple of 128.  A shared expert always uses SwiGLU. */
 moe_status_t moe_experts_ex(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, int32_t D,
                             int32_t I, const void* x, const int32_t* expert_offsets,
                             const int32_t* row_to_pair, const moe_expert_weights_t* w,

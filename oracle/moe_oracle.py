@@ -50,7 +50,11 @@ the grouped-matmul paths include W8A8FP, W4A8 and MXFP variants with the
 dequantisation fused into the matmul; the pages give no format).  Reading:
 OCP FP8 E4M3 codes with one fp32 scale per weight row, the expert using
 decode(code) * scale; activations and every sum stay as in the unquantised
-layer.
+layer.  For the MXFP variant the reading is the OCP Microscaling MXFP4
+format: E2M1 codes (two per byte, element 2j in the low nibble of byte j of
+a row) and one E8M0 exponent byte s per 32 consecutive elements of a row,
+the weight being decode(code) * 2^(s - 127); activations and sums again as
+in the unquantised layer.
 
 Parity pins: every function here is checked in the CPU test suite against
 something other than itself (closed forms, brute force over all subsets,
@@ -234,6 +238,36 @@ def dequantize_rows(codes, scale) -> np.ndarray:
     """Weights from FP8 codes with one scale per row (the last axis is the
     input width): W[..., n, :] = decode(codes[..., n, :]) * scale[..., n]."""
     return fp8_e4m3_decode(codes) * np.asarray(scale, dtype=f64)[..., None]
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Values of 4-bit OCP E2M1 codes (the element format of MXFP4, per the
+    reading in the header): bit 3 is the sign, bits 2..1 the exponent field e
+    with bias 1, bit 0 the mantissa m.  e > 0 gives (1 + m/2) * 2^(e-1); e = 0
+    gives the subnormal m/2.  Every code is finite."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign, e, m = (c >> 3) & 1, (c >> 1) & 3, c & 1
+    mag = np.where(e == 0, m / 2.0, (1.0 + m / 2.0) * np.exp2(e - 1.0))
+    return np.where(sign == 1, -mag, mag).astype(f64)
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """Values of OCP E8M0 scale bytes: 2^(s - 127); s = 255 is NaN."""
+    s = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(s == 255, np.nan, np.exp2(s - 127.0)).astype(f64)
+
+
+def dequantize_mxfp4(codes, scales) -> np.ndarray:
+    """Weights from MXFP4 storage: codes [..., K/2] bytes with element 2j of
+    a row in the low nibble of byte j and 2j+1 in the high nibble; scales
+    [..., K/32] E8M0 bytes, one per 32 consecutive elements.  Returns
+    [..., K] float64: W[..., 32b + i] = e2m1(code) * 2^(s[..., b] - 127)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    elems = np.stack([c & 15, c >> 4], axis=-1).reshape(*c.shape[:-1], 2 * c.shape[-1])
+    sc = e8m0_decode(scales)
+    if sc.shape[-1] * 32 != elems.shape[-1]:
+        raise ValueError("one scale byte per 32 elements")
+    return e2m1_decode(elems) * np.repeat(sc, 32, axis=-1)
 
 
 def map_to_physical(ids, log2phy) -> np.ndarray:

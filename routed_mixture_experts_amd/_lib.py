@@ -23,7 +23,7 @@ GROUP_SCORES = {"max": 0, "top2sum": 1}
 STAGES = ["router", "downproj", "route", "permute", "gemm1", "gemm2", "combine", "shared", "tail"]
 MOE_NUM_STAGES = len(STAGES)
 
-MOE_WEIGHT_DTYPE, MOE_WEIGHT_FP8_E4M3 = 0, 1
+MOE_WEIGHT_DTYPE, MOE_WEIGHT_FP8_E4M3, MOE_WEIGHT_MXFP4 = 0, 1, 2
 ACTIVATIONS = {"silu": 0, "gelu": 1, "gelu_tanh": 2, "swiglu_clip": 3}
 
 EXPORTS = ["moe_route", "moe_permute_workspace", "moe_permute", "moe_experts_workspace",
@@ -254,6 +254,10 @@ class ExpertWeights:
     ``ExpertWeights.fp8(w13, w2, w13_scale, w2_scale)``: OCP e4m3 codes
     (torch.uint8 or torch.float8_e4m3fn) [E, 2I, D] / [E, D, I] with one fp32
     scale per weight row, [E, 2I] / [E, D].
+    ``ExpertWeights.mxfp4(w13, w2, w13_scale, w2_scale)``: OCP MXFP4, uint8
+    [E, 2I, D/2] / [E, D, I/2] E2M1 code pairs (even element in the low
+    nibble) with one uint8 E8M0 exponent per 32 elements of a row,
+    [E, 2I, D/32] / [E, D, I/32].
     ``activation``: "silu" (SwiGLU, default), "gelu", "gelu_tanh" or
     "swiglu_clip" (with ``alpha`` and ``limit``)."""
 
@@ -267,8 +271,23 @@ class ExpertWeights:
             raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}")
         self.activation, self.alpha, self.limit = activation, float(alpha), float(limit)
         E, twoI, D = w13.shape
+        if fmt == MOE_WEIGHT_MXFP4:
+            D = 2 * D  # two codes per byte
         self.E, self.I, self.D = E, twoI // 2, D
-        if tuple(w2.shape) != (E, D, self.I):
+        if fmt == MOE_WEIGHT_MXFP4:
+            if tuple(w2.shape) != (E, D, self.I // 2):
+                raise ValueError("MXFP4 w13 must be [E, 2I, D/2] and w2 [E, D, I/2]")
+            for name, t in (("w13", w13), ("w2", w2)):
+                if t.dtype != torch.uint8 or not t.is_contiguous():
+                    raise ValueError(f"{name} must be contiguous uint8 code pairs")
+            if w13_scale is None or w2_scale is None:
+                raise ValueError("MXFP4 weights need w13_scale and w2_scale")
+            _need(w13_scale, torch.uint8, "w13_scale")
+            _need(w2_scale, torch.uint8, "w2_scale")
+            if (tuple(w13_scale.shape) != (E, 2 * self.I, D // 32)
+                    or tuple(w2_scale.shape) != (E, D, self.I // 32)):
+                raise ValueError("w13_scale must be [E, 2I, D/32] and w2_scale [E, D, I/32]")
+        elif tuple(w2.shape) != (E, D, self.I):
             raise ValueError("w13 must be [E, 2I, D] and w2 [E, D, I]")
         if fmt == MOE_WEIGHT_FP8_E4M3:
             for name, t in (("w13", w13), ("w2", w2)):
@@ -284,6 +303,10 @@ class ExpertWeights:
     @classmethod
     def fp8(cls, w13, w2, w13_scale, w2_scale, **act) -> "ExpertWeights":
         return cls(w13, w2, w13_scale, w2_scale, MOE_WEIGHT_FP8_E4M3, **act)
+
+    @classmethod
+    def mxfp4(cls, w13, w2, w13_scale, w2_scale, **act) -> "ExpertWeights":
+        return cls(w13, w2, w13_scale, w2_scale, MOE_WEIGHT_MXFP4, **act)
 
     def c(self) -> moe_expert_weights_t:
         return moe_expert_weights_t(self.format, _ptr(self.w13), _ptr(self.w2),

@@ -10,6 +10,7 @@ namespace moe {
 typedef uint16_t bf16_t;   // IEEE bfloat16 bit pattern
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -76,15 +77,22 @@ struct GemmArgs {
     void* C;
     int64_t ldc;
     const float* bias;
-    // B as OCP e4m3 codes (one byte per element) with one fp32 scale per B
-    // row: row n of group g is scaled by b_scale[g * b_scale_gstride + n]
-    int32_t b_fp8;
-    const float* b_scale;
+    // Storage of B (WeightFmt).  WF_FP8: OCP e4m3 codes, one byte per
+    // element, and one fp32 scale per B row: row n of group g is scaled by
+    // ((const float*)b_scale)[g * b_scale_gstride + n].  WF_MXFP4: OCP E2M1
+    // codes, two per byte (element 2j in the low nibble of byte j of the row),
+    // and one E8M0 byte per 32 elements of a row: block b of row n of group g
+    // is scaled by 2^(e - 127), e = ((const uint8_t*)b_scale)[g *
+    // b_scale_gstride + n * (K / 32) + b].  b_gstride counts elements.
+    int32_t b_fmt;
+    const void* b_scale;
     int64_t b_scale_gstride;
     // gate/up activation of EPI_SWIGLU (GluAct) and its parameters
     int32_t act;
     float act_alpha, act_limit;
 };
+
+enum WeightFmt { WF_BF16 = 0, WF_FP8 = 1, WF_MXFP4 = 2 };
 
 // Gate/up activations h = act(gate, up) ("vLLM-Ascend Kimi K3 MoE Forward
 // Insight", Stage 4: the MLP's activation branches): SwiGLU silu(g) * u;

@@ -41,9 +41,12 @@ constexpr int TBM = 128, TBN = 128, TBK = 64, TLD = TBK + 8;  // LDS row stride 
 // With FP8 weights (OCP e4m3 codes, one fp32 scale per weight row; grouped
 // products only) each lane loads 8 codes per row segment and turns them into
 // bf16 (exactly) on the way to LDS; the row scale multiplies the fp32 sums in
-// the epilogue.
-template <int EPI, bool FP8>
+// the epilogue.  With MXFP4 weights (E2M1 codes, two per byte, one E8M0
+// exponent per 32 codes) a lane's 8 codes are 4 bytes inside one scale
+// block; the conversion on the way to LDS applies the block scale.
+template <int EPI, int WF>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
+    constexpr bool FP8 = WF == WF_FP8, FP4 = WF == WF_MXFP4;
     constexpr bool SW = EPI == EPI_SWIGLU;
     const int ntn = SW ? (g.N + 63) / 64 : (g.N + TBN - 1) / TBN;
     TileCoord tc;
@@ -63,7 +66,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
 
     const bf16_t* ap[4];
     const bf16_t* bp[4];
-    const uint8_t* bp8[4];
+    const uint8_t* bp8[4];  // FP8 / MXFP4 codes of this lane's row segment
+    const uint8_t* sp4[4];  // MXFP4 block exponents of the row
     const bf16_t* ap2[4];
     const bf16_t* bp2[4];
 #pragma unroll
@@ -80,7 +84,11 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
             wrow = min(tc.nt * TBN + rho, g.N - 1);
         }
         bp[i] = Bg + (int64_t)wrow * g.K + lcol;
-        bp8[i] = (const uint8_t*)g.B + (int64_t)tc.group * g.b_gstride + (int64_t)wrow * g.K + lcol;
+        bp8[i] = FP4 ? (const uint8_t*)g.B + ((int64_t)tc.group * g.b_gstride + (int64_t)wrow * g.K + lcol) / 2
+                     : (const uint8_t*)g.B + (int64_t)tc.group * g.b_gstride + (int64_t)wrow * g.K + lcol;
+        sp4[i] = FP4 ? (const uint8_t*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride +
+                           (int64_t)wrow * (g.K / 32) + lcol / 32
+                     : nullptr;
         bp2[i] = B2 ? B2 + (int64_t)wrow * g.K2 + lcol : nullptr;
     }
 
@@ -88,7 +96,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
     const int nk = nk1 + (A2 ? g.K2 / TBK : 0);
 
     u32x4_t ra[4], rb[4];
-    uint32_t rb8[4][2];  // FP8: raw codes, converted when stored to LDS
+    uint32_t rb8[4][2];  // FP8 / MXFP4: raw codes, converted when stored to LDS
+    uint32_t se[4];      // MXFP4: the block exponent of each segment
     auto gload = [&](int kt) {
         if (kt < nk1) {
             const int ko = kt * TBK;
@@ -99,6 +108,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
                     const uint64_t q = *(const uint64_t*)(bp8[i] + ko);
                     rb8[i][0] = (uint32_t)q;
                     rb8[i][1] = (uint32_t)(q >> 32);
+                } else if (FP4) {
+                    rb8[i][0] = *(const uint32_t*)(bp8[i] + ko / 2);
+                    se[i] = sp4[i][ko / 32];
                 } else {
                     rb[i] = *(const u32x4_t*)(bp[i] + ko);
                 }
@@ -116,6 +128,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (FP8) rb[i] = fp8x8_to_bf16x8(rb8[i][0], rb8[i][1]);
+            if (FP4) rb[i] = fp4x8_to_bf16x8(rb8[i][0], e8m0_scale(se[i]));
             *(u32x4_t*)(&smem[buf][0][(lrow + 32 * i) * TLD + lcol]) = ra[i];
             *(u32x4_t*)(&smem[buf][1][(lrow + 32 * i) * TLD + lcol]) = rb[i];
         }
@@ -165,7 +178,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
     // FP8 row scales of the two weight rows (output columns) of this lane
     float cs[2] = {1.f, 1.f};
     if (FP8) {
-        const float* sc = g.b_scale + (int64_t)tc.group * g.b_scale_gstride;
+        const float* sc = (const float*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride;
         if (SW) {
             const int hc = min(tc.nt * 64 + wn * 32 + fr, g.N - 1);
             cs[0] = sc[hc];
@@ -613,14 +626,15 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
         case EPI_OUT: KERNEL<EPI_OUT><<<gd, bd, 0, s>>>(g); break;                \
         default: KERNEL<EPI_SWIGLU><<<gd, bd, 0, s>>>(g); break;                  \
     }
-#define MOE_TILED_SWITCH(FP8)                                                         \
-    switch (g.epi) {                                                                  \
-        case EPI_F32: gemm_bf16_tiled<EPI_F32, FP8><<<gd, bd, 0, s>>>(g); break;           \
-        case EPI_F32_BIAS: gemm_bf16_tiled<EPI_F32_BIAS, FP8><<<gd, bd, 0, s>>>(g); break; \
-        case EPI_OUT: gemm_bf16_tiled<EPI_OUT, FP8><<<gd, bd, 0, s>>>(g); break;           \
-        default: gemm_bf16_tiled<EPI_SWIGLU, FP8><<<gd, bd, 0, s>>>(g); break;             \
+#define MOE_TILED_SWITCH(WF)                                                              \
+    switch (g.epi) {                                                                      \
+        case EPI_F32: gemm_bf16_tiled<EPI_F32, WF><<<gd, bd, 0, s>>>(g); break;           \
+        case EPI_F32_BIAS: gemm_bf16_tiled<EPI_F32_BIAS, WF><<<gd, bd, 0, s>>>(g); break; \
+        case EPI_OUT: gemm_bf16_tiled<EPI_OUT, WF><<<gd, bd, 0, s>>>(g); break;           \
+        default: gemm_bf16_tiled<EPI_SWIGLU, WF><<<gd, bd, 0, s>>>(g); break;             \
     }
-    if (g.b_fp8 && (dtype == 0 || path == GEMM_BIG || g.A2)) return hipErrorInvalidValue;
+    if (g.b_fmt != WF_BF16 && (dtype == 0 || path == GEMM_BIG || g.A2)) return hipErrorInvalidValue;
+    if (g.b_fmt == WF_MXFP4 && g.K % 128 != 0) return hipErrorInvalidValue;
     if (dtype == 0) {
         MOE_GEMM_SWITCH(gemm_f32_tiled)
     } else if (path == GEMM_STREAM) {
@@ -628,10 +642,12 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
     } else if (path == GEMM_BIG) {
         if (g.A2) launch_big<true>(g, gd, s);
         else launch_big<false>(g, gd, s);
-    } else if (g.b_fp8) {
-        MOE_TILED_SWITCH(true)
+    } else if (g.b_fmt == WF_FP8) {
+        MOE_TILED_SWITCH(WF_FP8)
+    } else if (g.b_fmt == WF_MXFP4) {
+        MOE_TILED_SWITCH(WF_MXFP4)
     } else {
-        MOE_TILED_SWITCH(false)
+        MOE_TILED_SWITCH(WF_BF16)
     }
 #undef MOE_GEMM_SWITCH
 #undef MOE_TILED_SWITCH

@@ -216,29 +216,42 @@ constexpr int SRN = 16 * SRW;        // weight rows per workgroup (SwiGLU: SRN /
 // With FP8 weights (OCP e4m3 codes, one fp32 scale per weight row) each
 // 16-byte weight load holds 16 codes, i.e. two 32-deep k-steps: lane g4 of a
 // 64-deep block takes k 16*g4 .. +15, its first 8 for the even step and the
-// rest for the odd one.  The token operand is staged with the same k order,
-// the codes become bf16 exactly in registers, and the row scale multiplies
+// rest for the odd one.  With MXFP4 weights (OCP E2M1 codes, two per byte,
+// one E8M0 exponent per 32 codes of a row) a 16-byte load holds 32 codes --
+// one scale block -- i.e. four k-steps: lane g4 of a 128-deep block takes k
+// 32*g4 .. +31, 8 per step, and the 4 block exponents of a load unit come
+// in one dword beside it.  The token operand is staged with the same k order
+// as the weights, the codes become bf16 exactly in registers (MXFP4: with
+// the block scale applied by the conversion), and FP8's row scale multiplies
 // the fp32 sums in the epilogue.
-template <int EPI, int NB, bool KCAT, bool FP8>
+template <int EPI, int NB, bool KCAT, int WF>
 __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCoord& tc,
                                                  char* xs) {
     constexpr bool SW = EPI == EPI_SWIGLU;
-    constexpr int CS = NB == 4 ? 8 : 16;   // k-steps (of 32) per token chunk
-    constexpr int UNIT = FP8 ? 2 : 1;      // k-steps per weight load
+    constexpr bool FP8 = WF == WF_FP8, FP4 = WF == WF_MXFP4, QW = WF != WF_BF16;
+    constexpr int CS = NB == 4 ? 8 : 16;       // k-steps (of 32) per token chunk
+    constexpr int UNIT = FP4 ? 4 : FP8 ? 2 : 1;  // k-steps per weight load
     constexpr int PD = FP8 && NB == 4 ? 4 : 8;  // weight loads in flight
-    constexpr int XI = CS * NB / SRW;      // 1 KB token blocks per wave per chunk
-    constexpr int CHUNK = CS * NB * 1024;  // bytes of one token chunk
-    constexpr int WB = FP8 ? 1 : 2;        // bytes per weight element
-    static_assert(!(FP8 && KCAT), "FP8 weights are grouped products only");
-    static_assert(2 * CHUNK <= SX_BYTES && CS % (PD * UNIT) == 0 && XI % NB == 0,
+    constexpr int UPC = CS / UNIT;             // weight loads per chunk
+    // chunks per loop iteration: the ring of PD loads turns a whole number
+    // of times per iteration, so every slot index is static
+    constexpr int RC = PD > UPC ? PD / UPC : 1;
+    constexpr int TU = RC * UPC;               // weight loads per ring turn
+    constexpr int XI = CS * NB / SRW;          // 1 KB token blocks per wave per chunk
+    constexpr int CHUNK = CS * NB * 1024;      // bytes of one token chunk
+    static_assert(!(QW && KCAT), "quantised weights are grouped products only");
+    static_assert(2 * CHUNK <= SX_BYTES && CS % UNIT == 0 && TU % PD == 0 && XI % NB == 0,
                   "stream tiling");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
 
     // 32-bit byte offsets from wave-uniform bases; every operand of one group
-    // fits in 4 GiB (checked on the host)
-    const char* Bb = (const char*)g.B + (int64_t)tc.group * g.b_gstride * WB;
+    // fits in 4 GiB (checked on the host).  Row bytes: K * 2 (bf16), K (FP8),
+    // K / 2 (MXFP4).
+    const int64_t wrow_bytes = FP4 ? g.K / 2 : FP8 ? g.K : (int64_t)g.K * 2;
+    const int64_t group_bytes = FP4 ? g.b_gstride / 2 : FP8 ? g.b_gstride : g.b_gstride * 2;
+    const char* Bb = (const char*)g.B + tc.group * group_bytes;
     const char* B2b = (const char*)g.B2;
     const char* Ab = (const char*)g.A;
     const char* A2b = (const char*)g.A2;
@@ -249,25 +262,32 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     } else {
         wrow = min(tc.nt * SRN + wave * 16 + l16, g.N - 1);
     }
-    const uint32_t wo = (uint32_t)((int64_t)wrow * g.K * WB) + g4 * 16;
+    const uint32_t wo = (uint32_t)(wrow * wrow_bytes) + g4 * 16;
     const uint32_t wo2 = KCAT ? (uint32_t)((int64_t)wrow * g.K2 * 2) + g4 * 16 : 0u;
+    // MXFP4 block exponents of this row: K / 32 bytes, 4 per load unit
+    const char* Sb = FP4 ? (const char*)g.b_scale + tc.group * g.b_scale_gstride +
+                               (int64_t)wrow * (g.K / 32)
+                         : nullptr;
     // token rows past the tile's end load its last row (never stored)
     uint32_t xo[NB], xo2[NB];
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
         const int r = min(tc.row0 + tb * 16 + l16, tc.row1 - 1);
-        xo[tb] = (uint32_t)(a_row_of(g, r) * g.lda * 2) + g4 * (FP8 ? 32 : 16);
+        xo[tb] = (uint32_t)(a_row_of(g, r) * g.lda * 2) + g4 * (FP4 ? 64 : FP8 ? 32 : 16);
         xo2[tb] = KCAT ? (uint32_t)((int64_t)r * g.lda2 * 2) + g4 * 16 : 0u;
     }
 
     const int ns1 = g.K / 32;
     const int ns = ns1 + (KCAT ? g.K2 / 32 : 0);
     const int nch = (ns + CS - 1) / CS;
+    const int nu = ns / UNIT;  // weight load units
+    uint32_t sxn[FP4 ? UPC : 1], sxc[FP4 ? UPC : 1];  // MXFP4 exponents: next / current chunk
 
     // Token chunk c lives in LDS buffer c & 1 as 1 KB blocks b = (k-step
     // b / NB, 16-row block b % NB), each in MFMA operand order (lane l holds
-    // row l % 16, k 8 * (l / 16) .. +7 of the step).  This wave moves blocks
-    // wave * XI .. +XI-1; steps past K re-read the last step (never used).
+    // row l % 16 and the 8 k of the step that lane l / 16 takes).  This wave
+    // moves blocks wave * XI .. +XI-1; steps past K re-read the last step
+    // (never used).
     u32x4_t xr[XI];
     auto load_x = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
@@ -276,22 +296,39 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
             const int tb = i % NB;
             const int st = min(c * CS + b / NB, ns - 1);
             const bool seg1 = !KCAT || st < ns1;
-            // byte offset of step st's 8 elements for this lane (FP8: the
-            // k order of the weight loads)
-            const uint32_t ko = FP8 ? (uint32_t)(st >> 1) * 128 + (uint32_t)(st & 1) * 16
-                                    : (uint32_t)st * 64;
+            // byte offset of step st's 8 elements for this lane (the k order
+            // of the weight loads)
+            const uint32_t ko = FP4   ? (uint32_t)(st >> 2) * 256 + (uint32_t)(st & 3) * 16
+                                : FP8 ? (uint32_t)(st >> 1) * 128 + (uint32_t)(st & 1) * 16
+                                      : (uint32_t)st * 64;
             const char* src = seg1 ? Ab + (xo[tb] + ko)
                                    : A2b + (xo2[tb] + (uint32_t)(st - ns1) * 64);
             xr[i] = *(const u32x4_t*)src;
+        }
+        // MXFP4: the block exponents of the chunk's UPC load units travel
+        // with its tokens (one dword per unit, byte g4 for this lane), so
+        // every weight load unit is a single load
+        if constexpr (FP4) {
+#pragma unroll
+            for (int j = 0; j < UPC; ++j)
+                sxn[j] = *(const uint32_t*)(Sb + 4 * min(c * UPC + j, nu - 1));
         }
     };
     auto store_x = [&](int c) __attribute__((always_inline)) {
         char* dst = xs + (c & 1) * CHUNK + lane * 16;
 #pragma unroll
-        for (int i = 0; i < XI; ++i) *(u32x4_t*)(dst + (wave * XI + i) * 1024) = xr[i];
+        for (int i = 0; i < XI; ++i) {
+            // MXFP4: steps past K get zero tokens (once per chunk, in place
+            // of a select per step on the weights)
+            if (FP4 && c * CS + (wave * XI + i) / NB >= ns) xr[i] = u32x4_t{0u, 0u, 0u, 0u};
+            *(u32x4_t*)(dst + (wave * XI + i) * 1024) = xr[i];
+        }
+        if constexpr (FP4) {
+#pragma unroll
+            for (int j = 0; j < UPC; ++j) sxc[j] = sxn[j];
+        }
     };
     // weight load unit u covers k-steps UNIT*u .. +UNIT-1, 64 bytes of the row
-    const int nu = ns / UNIT;
     auto load_w = [&](int u) __attribute__((always_inline)) {
         u = min(u, nu - 1);
         const bool seg1 = !KCAT || u < ns1;
@@ -300,14 +337,17 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
         return *(const u32x4_t*)src;
     };
 
-    f32x4_t acc[NB];
+    // MXFP4 single-block tiles alternate two accumulators so that
+    // consecutive MFMAs do not wait on each other
+    constexpr int NACC = FP4 && NB == 1 ? 2 : 1;
+    f32x4_t acc[NB], acc2[NB];
 #pragma unroll
-    for (int tb = 0; tb < NB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int tb = 0; tb < NB; ++tb) acc[tb] = acc2[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     u32x4_t w[PD];
 
     // The first weight fragments go out before the wait for chunk 0.  Order
     // is pinned (empty asm with a memory clobber) so that on both paths into
-    // the store of chunk c + 1 the token loads are followed by exactly the CS
+    // the store of chunk c + 1 the token loads are followed by exactly the
     // weight loads of chunk c: the compiler's wait for the token registers
     // then leaves the newest weight loads in flight.
     load_x(0);
@@ -320,55 +360,118 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     load_x(1);
     asm volatile("" ::: "memory");
 
-    for (int c = 0; c < nch; ++c) {
-        // this wave's LDS writes of chunk c are done, and its LDS reads of
-        // chunk c - 1; after the barrier every wave's part of chunk c is
-        // visible and no wave reads buffer (c + 1) & 1 any more.  (A
-        // __syncthreads fence would also drain the weight loads in flight.)
+    // Chunk c starts once this wave's LDS writes of chunk c are done, and
+    // its LDS reads of chunk c - 1; after the barrier every wave's part of
+    // chunk c is visible and no wave reads buffer (c + 1) & 1 any more.  (A
+    // __syncthreads fence would also drain the weight loads in flight.)
+    auto chunk_begin = [&](int c) __attribute__((always_inline)) {
         wait_lgkm0();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        const char* xc = xs + (c & 1) * CHUNK + lane * 16;
+        return (const char*)(xs + (c & 1) * CHUNK + lane * 16);
+    };
+    // Load unit j of chunk c, held in ring slot v: its UNIT k-steps against
+    // every token block, then the refill of the slot PD units ahead.
+    auto unit = [&](int c, const char* xc, int j, int v) __attribute__((always_inline)) {
+        if constexpr (FP4) {
+            // token fragments 4 at a time (XG steps of NB blocks) ahead of
+            // their MFMAs, so their LDS latency overlaps; zero tokens
+            // already cover steps past K
+            constexpr int XG = 4 / NB;
+            const float bs = e8m0_scale((sxc[j] >> (8 * g4)) & 0xffu);
 #pragma unroll
-        for (int u = 0; u < CS; u += PD * UNIT) {
+            for (int h0 = 0; h0 < UNIT; h0 += XG) {
+                u32x4_t xv[XG][NB];
 #pragma unroll
-            for (int v = 0; v < PD; ++v) {
-                const int ul = (c * CS + u) / UNIT + v;  // weight load unit
+                for (int hh = 0; hh < XG; ++hh)
 #pragma unroll
-                for (int hh = 0; hh < UNIT; ++hh) {
-                    const int sl = u + v * UNIT + hh;  // step within the chunk
-                    const int st = c * CS + sl;
-                    u32x4_t wv = w[v];
-                    if (FP8) wv = fp8x8_to_bf16x8(w[v][2 * hh], w[v][2 * hh + 1]);
-                    // steps past K (the ragged last chunk) multiply zero weights
-                    const u32x4_t wz = st < ns ? wv : u32x4_t{0u, 0u, 0u, 0u};
-                    const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, wz);
+                    for (int tb = 0; tb < NB; ++tb)
+                        xv[hh][tb] =
+                            *(const u32x4_t*)(xc + ((j * UNIT + h0 + hh) * NB + tb) * 1024);
+#pragma unroll
+                for (int hh = 0; hh < XG; ++hh) {
+                    const bf16x8_t wf =
+                        __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16x8(w[v][h0 + hh], bs));
 #pragma unroll
                     for (int tb = 0; tb < NB; ++tb) {
-                        const u32x4_t xv = *(const u32x4_t*)(xc + (sl * NB + tb) * 1024);
-                        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            wf, __builtin_bit_cast(bf16x8_t, xv), acc[tb], 0, 0, 0);
+                        f32x4_t& a = NACC == 2 && (hh & 1) ? acc2[tb] : acc[tb];
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            wf, __builtin_bit_cast(bf16x8_t, xv[hh][tb]), a, 0, 0, 0);
                     }
                 }
-                w[v] = load_w(ul + PD);
-                // keep each refill where its slot frees up (the scheduler
-                // otherwise sinks them all to the end of the chunk)
-                if (FP8) asm volatile("" ::: "memory");
+            }
+            w[v] = load_w(c * UPC + j + PD);
+            asm volatile("" ::: "memory");
+            return;
+        }
+#pragma unroll
+        for (int hh = 0; hh < UNIT; ++hh) {
+            const int sl = j * UNIT + hh;  // step within the chunk
+            const int st = c * CS + sl;
+            u32x4_t wv = w[v];
+            if (FP8) wv = fp8x8_to_bf16x8(w[v][2 * hh], w[v][2 * hh + 1]);
+            // steps past K (the ragged last chunk) multiply zero weights
+            const u32x4_t wz = st < ns ? wv : u32x4_t{0u, 0u, 0u, 0u};
+            const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, wz);
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) {
+                const u32x4_t xv = *(const u32x4_t*)(xc + (sl * NB + tb) * 1024);
+                acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    wf, __builtin_bit_cast(bf16x8_t, xv), acc[tb], 0, 0, 0);
             }
         }
+        const int ul = c * UPC + j;
+        w[v] = load_w(ul + PD);
+        // keep each refill where its slot frees up (the scheduler otherwise
+        // sinks them all to the end of the chunk)
+        if (QW) asm volatile("" ::: "memory");
+    };
+    // chunk c + 1 has had a whole chunk to arrive; chunks past the end only
+    // touch the idle buffer, which keeps this branch-free
+    auto chunk_end = [&](int c) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
-        // chunk c + 1 has had a whole chunk to arrive; chunks past the end
-        // only touch the idle buffer, which keeps this branch-free
         store_x(c + 1);
         asm volatile("" ::: "memory");
         load_x(c + 2);
         asm volatile("" ::: "memory");
+    };
+
+    if constexpr (RC == 1) {
+        // one chunk turns the ring of PD loads a whole number of times
+        for (int c = 0; c < nch; ++c) {
+            const char* xc = chunk_begin(c);
+#pragma unroll
+            for (int u = 0; u < UPC; u += PD)
+#pragma unroll
+                for (int v = 0; v < PD; ++v) unit(c, xc, u + v, v);
+            chunk_end(c);
+        }
+    } else {
+        // MXFP4: a chunk holds fewer than PD loads; RC chunks turn the ring
+        // once (unit c * UPC + j of chunk c = c0 + r sits in slot r * UPC + j).
+        // Chunks past the end (when RC does not divide nch) multiply zero
+        // weights and stage clamped, in-bounds token steps.
+        for (int c0 = 0; c0 < nch; c0 += RC) {
+#pragma unroll
+            for (int r = 0; r < RC; ++r) {
+                const int c = c0 + r;
+                const char* xc = chunk_begin(c);
+#pragma unroll
+                for (int j = 0; j < UPC; ++j) unit(c, xc, j, r * UPC + j);
+                chunk_end(c);
+            }
+        }
+    }
+
+    if constexpr (NACC == 2) {
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) acc[tb] += acc2[tb];
     }
 
     // row scales of FP8 weights, for the 4 weight rows this lane's sums belong to
     float rs[4] = {1.f, 1.f, 1.f, 1.f};
     if (FP8) {
-        const float* sc = g.b_scale + (int64_t)tc.group * g.b_scale_gstride;
+        const float* sc = (const float*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             int n;
@@ -418,7 +521,7 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
 
 // Grouped tiles here hold one whole group of at most 64 rows; dense products
 // are cut into 16-row tiles.
-template <int EPI, bool KCAT, bool FP8>
+template <int EPI, bool KCAT, int WF>
 __global__ __launch_bounds__(64 * SRW, 4) void gemm_bf16_stream(GemmArgs g) {
     constexpr bool SW = EPI == EPI_SWIGLU;
     const int ntn = SW ? (g.N + SRN / 2 - 1) / (SRN / 2) : (g.N + SRN - 1) / SRN;
@@ -426,22 +529,22 @@ __global__ __launch_bounds__(64 * SRW, 4) void gemm_bf16_stream(GemmArgs g) {
     if (!fetch_tile(g, SROWS, ntn, tc)) return;
     __shared__ __attribute__((aligned(1024))) char xs[SX_BYTES];
     const int rows = tc.row1 - tc.row0;
-    if (rows <= 16) stream_rows_tile<EPI, 1, KCAT, FP8>(g, tc, xs);
-    else if (rows <= 32) stream_rows_tile<EPI, 2, KCAT, FP8>(g, tc, xs);
-    else stream_rows_tile<EPI, 4, KCAT, FP8>(g, tc, xs);
+    if (rows <= 16) stream_rows_tile<EPI, 1, KCAT, WF>(g, tc, xs);
+    else if (rows <= 32) stream_rows_tile<EPI, 2, KCAT, WF>(g, tc, xs);
+    else stream_rows_tile<EPI, 4, KCAT, WF>(g, tc, xs);
 }
 
 // Dense products with fewer workgroups than this split K over the waves.
 constexpr int64_t kStreamRowsMinGrid = 1024;
 
-template <bool KC, bool FP8>
+template <bool KC, int WF>
 void launch_stream_rows(const GemmArgs& g, dim3 gd, hipStream_t s) {
     const dim3 bd(64 * SRW);
     switch (g.epi) {
-        case EPI_F32: gemm_bf16_stream<EPI_F32, KC, FP8><<<gd, bd, 0, s>>>(g); break;
-        case EPI_F32_BIAS: gemm_bf16_stream<EPI_F32_BIAS, KC, FP8><<<gd, bd, 0, s>>>(g); break;
-        case EPI_OUT: gemm_bf16_stream<EPI_OUT, KC, FP8><<<gd, bd, 0, s>>>(g); break;
-        default: gemm_bf16_stream<EPI_SWIGLU, KC, FP8><<<gd, bd, 0, s>>>(g); break;
+        case EPI_F32: gemm_bf16_stream<EPI_F32, KC, WF><<<gd, bd, 0, s>>>(g); break;
+        case EPI_F32_BIAS: gemm_bf16_stream<EPI_F32_BIAS, KC, WF><<<gd, bd, 0, s>>>(g); break;
+        case EPI_OUT: gemm_bf16_stream<EPI_OUT, KC, WF><<<gd, bd, 0, s>>>(g); break;
+        default: gemm_bf16_stream<EPI_SWIGLU, KC, WF><<<gd, bd, 0, s>>>(g); break;
     }
 }
 
@@ -457,7 +560,7 @@ hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
     const bool sw = g.epi == EPI_SWIGLU;
     const int64_t grid_ks = (int64_t)nm * (sw ? (g.N + 31) / 32 : (g.N + SNW - 1) / SNW);
     if (grid_ks <= 0) return hipSuccess;
-    if (!g.tiles && grid_ks < kStreamRowsMinGrid && !g.b_fp8) {
+    if (!g.tiles && grid_ks < kStreamRowsMinGrid && g.b_fmt == WF_BF16) {
         const dim3 gd((unsigned)grid_ks), bd(256);
         switch (g.epi) {
             case EPI_F32: gemm_bf16_stream_ksplit<EPI_F32><<<gd, bd, 0, s>>>(g); break;
@@ -467,13 +570,16 @@ hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
         }
     } else {
         const dim3 gd((unsigned)((int64_t)nm * stream_col_tiles(g.epi, g.N)));
-        if (g.b_fp8) {
-            if (g.A2) return hipErrorInvalidValue;
-            launch_stream_rows<false, true>(g, gd, s);
+        if (g.b_fmt != WF_BF16 && g.A2) return hipErrorInvalidValue;
+        if (g.b_fmt == WF_MXFP4 && g.K % 128 != 0) return hipErrorInvalidValue;
+        if (g.b_fmt == WF_FP8) {
+            launch_stream_rows<false, WF_FP8>(g, gd, s);
+        } else if (g.b_fmt == WF_MXFP4) {
+            launch_stream_rows<false, WF_MXFP4>(g, gd, s);
         } else if (g.A2) {
-            launch_stream_rows<true, false>(g, gd, s);
+            launch_stream_rows<true, WF_BF16>(g, gd, s);
         } else {
-            launch_stream_rows<false, false>(g, gd, s);
+            launch_stream_rows<false, WF_BF16>(g, gd, s);
         }
     }
     return hipGetLastError();

@@ -93,7 +93,9 @@ __device__ __forceinline__ void wait_lgkm0() {
 // Eight OCP e4m3 codes (code 0 in the low byte of lo) as eight bf16 values.
 // e4m3 keeps 3 mantissa bits and exponents 2^-9 .. 2^8, so every finite code
 // is exact in bf16: v_cvt_pk_f32_fp8 gives its fp32 value (checked against
-// all 256 codes) and the top half of that is the bf16 pattern.
+// all 256 codes) and the top half of that is the bf16 pattern.  (The scaled
+// single-instruction conversion to bf16 pairs gives the same values, but in
+// the streaming kernel the compiler then holds far more registers.)
 __device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
     u32x4_t r;
@@ -105,6 +107,30 @@ __device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
         r[2 * q] = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
         r[2 * q + 1] = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
     }
+    return r;
+}
+
+__device__ __forceinline__ uint32_t bf16x2_bits(bf16x2_t v) {
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// The fp32 that carries an E8M0 block exponent e into the scaled
+// conversions: they use only the exponent field of their fp32 scale
+// (checked: a scale of 3.0 multiplies by 2), so e << 23 stands for 2^(e-127).
+// Codes 1 .. 254; 0 and the NaN code 255 are outside what the kernels handle.
+__device__ __forceinline__ float e8m0_scale(uint32_t e) { return __uint_as_float(e << 23); }
+
+// Eight OCP E2M1 codes (code 0 in the low nibble of byte 0) times the block
+// scale as eight bf16 values.  An E2M1 value (at most 1.5 * 2^2, one mantissa
+// bit) times a power of two is exact in bf16 for block exponents the weights
+// use; v_cvt_scalef32_pk_bf16_fp4 converts the two codes of byte j (low
+// nibble into the low half), checked against all 256 bytes and byte selects.
+__device__ __forceinline__ u32x4_t fp4x8_to_bf16x8(uint32_t codes, float scale) {
+    u32x4_t r;
+    r[0] = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
+    r[1] = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
+    r[2] = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
+    r[3] = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
     return r;
 }
 

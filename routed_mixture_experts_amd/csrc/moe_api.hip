@@ -107,11 +107,11 @@ int64_t big_capacity_ws(moe_dtype_t dt, int64_t P, int E) {
 
 // Routed expert weights as the kernels take them.
 struct ExpertWeights {
-    bool fp8;
+    int fmt;           // WeightFmt
     const void* w13;
     const void* w2;
-    const float* s13;  // [E, 2I] row scales (fp8)
-    const float* s2;   // [E, D]
+    const void* s13;   // FP8: fp32 [E, 2I] row scales; MXFP4: E8M0 [E, 2I, D/32]
+    const void* s2;    // FP8: fp32 [E, D]; MXFP4: E8M0 [E, D, I/32]
     int act = ACT_SILU;
     float act_alpha = 0.0f, act_limit = 0.0f;
 };
@@ -151,19 +151,19 @@ moe_status_t small_groups_gemm(GemmArgs g, const ExpertsWs& w, int E, hipStream_
 }
 
 // Rows per tile of the large-group list.
-int large_rows(moe_dtype_t dt, bool fp8) {
-    return dt == MOE_DTYPE_F32 ? kF32Rows : fp8 ? kTiledRows : kBigRows;
+int large_rows(moe_dtype_t dt, int fmt) {
+    return dt == MOE_DTYPE_F32 ? kF32Rows : fmt != WF_BF16 ? kTiledRows : kBigRows;
 }
 
 moe_status_t large_groups_gemm(moe_dtype_t dt, GemmArgs g, const ExpertsWs& w, int64_t P, int E,
                                hipStream_t s) {
     const bool f32 = dt == MOE_DTYPE_F32;
-    const int rows = large_rows(dt, g.b_fp8 != 0);
+    const int rows = large_rows(dt, g.b_fmt);
     g.tiles = w.big_tiles;
     g.num_tiles = w.counts + 1;
     g.max_tiles = (int32_t)big_capacity(dt, P, E, rows);
     g.tile_m = rows;
-    const int path = f32 || g.b_fp8 ? GEMM_TILED : GEMM_BIG;
+    const int path = f32 || g.b_fmt != WF_BF16 ? GEMM_TILED : GEMM_BIG;
     return hip_status(launch_gemm(f32 ? 0 : 1, path, g, s));
 }
 
@@ -209,7 +209,7 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
                          hipStream_t s, hipEvent_t* ev) {
     const int64_t P = T * k;
     const bool f32 = dt == MOE_DTYPE_F32;
-    MOE_HIP(launch_build_tiles(offsets, E, f32 ? 0 : kStreamMaxRows, large_rows(dt, ew.fp8),
+    MOE_HIP(launch_build_tiles(offsets, E, f32 ? 0 : kStreamMaxRows, large_rows(dt, ew.fmt),
                                w.small_tiles, w.counts, w.big_tiles, w.counts + 1, s));
     if (ev) MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM1], s));
 
@@ -220,9 +220,9 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
     g1.a_div = k;
     g1.B = ew.w13;
     g1.b_gstride = (int64_t)2 * I * D;
-    g1.b_fp8 = ew.fp8;
+    g1.b_fmt = ew.fmt;
     g1.b_scale = ew.s13;
-    g1.b_scale_gstride = (int64_t)2 * I;
+    g1.b_scale_gstride = ew.fmt == WF_MXFP4 ? (int64_t)2 * I * (D / 32) : (int64_t)2 * I;
     g1.act = ew.act;
     g1.act_alpha = ew.act_alpha;
     g1.act_limit = ew.act_limit;
@@ -237,9 +237,9 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
     g2.lda = I;
     g2.B = ew.w2;
     g2.b_gstride = (int64_t)D * I;
-    g2.b_fp8 = ew.fp8;
+    g2.b_fmt = ew.fmt;
     g2.b_scale = ew.s2;
-    g2.b_scale_gstride = D;
+    g2.b_scale_gstride = ew.fmt == WF_MXFP4 ? (int64_t)D * (I / 32) : D;
     g2.K = I;
     g2.N = D;
     g2.epi = EPI_F32;
@@ -463,24 +463,34 @@ namespace {
 // point.
 moe_status_t expert_weights(moe_dtype_t dtype, const moe_expert_weights_t* d, ExpertWeights* ew) {
     if (!d) return MOE_EINVAL;
-    if (d->format != MOE_WEIGHT_DTYPE && d->format != MOE_WEIGHT_FP8_E4M3) return MOE_EINVAL;
-    ew->fp8 = d->format == MOE_WEIGHT_FP8_E4M3;
+    if (d->format != MOE_WEIGHT_DTYPE && d->format != MOE_WEIGHT_FP8_E4M3 &&
+        d->format != MOE_WEIGHT_MXFP4)
+        return MOE_EINVAL;
+    ew->fmt = d->format == MOE_WEIGHT_FP8_E4M3 ? WF_FP8
+              : d->format == MOE_WEIGHT_MXFP4  ? WF_MXFP4
+                                               : WF_BF16;
     ew->w13 = d->w13;
     ew->w2 = d->w2;
-    ew->s13 = ew->fp8 ? d->w13_scale : nullptr;
-    ew->s2 = ew->fp8 ? d->w2_scale : nullptr;
+    ew->s13 = ew->fmt != WF_BF16 ? d->w13_scale : nullptr;
+    ew->s2 = ew->fmt != WF_BF16 ? d->w2_scale : nullptr;
     if (d->activation < MOE_ACT_SILU || d->activation > MOE_ACT_SWIGLU_CLIP) return MOE_EINVAL;
     ew->act = d->activation;
     ew->act_alpha = d->act_alpha;
     ew->act_limit = d->act_limit;
     if (ew->act == MOE_ACT_SWIGLU_CLIP && !(d->act_alpha > 0.0f && d->act_limit > 0.0f))
         return MOE_EINVAL;
-    if (ew->fp8 && dtype != MOE_DTYPE_BF16) return MOE_ENOTSUP;
+    if (ew->fmt != WF_BF16 && dtype != MOE_DTYPE_BF16) return MOE_ENOTSUP;
     return MOE_OK;
 }
 
 bool weights_present(const ExpertWeights& ew) {
-    return ew.w13 && ew.w2 && (!ew.fp8 || (ew.s13 && ew.s2));
+    return ew.w13 && ew.w2 && (ew.fmt == WF_BF16 || (ew.s13 && ew.s2));
+}
+
+// MXFP4 weights are read 128 elements (64 bytes, 4 scale blocks) per load
+// along both reduction widths.
+bool weights_fit(const ExpertWeights& ew, int64_t D, int64_t I) {
+    return ew.fmt != WF_MXFP4 || (D % 128 == 0 && I % 128 == 0);
 }
 
 moe_status_t experts_impl(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, int32_t D,
@@ -489,7 +499,7 @@ moe_status_t experts_impl(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, in
                           void* ws, size_t ws_bytes, void* stream) {
     if (bad_dtype(dtype) || T < 0 || k < 1 || E < 1 || k > E) return MOE_EINVAL;
     if (E > kMaxExperts || k > kMaxTopK) return MOE_ENOTSUP;
-    if (!width_ok(D) || !width_ok(I)) return MOE_ENOTSUP;
+    if (!width_ok(D) || !width_ok(I) || !weights_fit(ew, D, I)) return MOE_ENOTSUP;
     if (T * (int64_t)k > INT32_MAX / 2) return MOE_ENOTSUP;
     if (!fits_u32(T, D, dtype) || !fits_u32(T * k, I, dtype) || !fits_u32(2 * (int64_t)I, D, dtype))
         return MOE_ENOTSUP;
@@ -511,7 +521,7 @@ moe_status_t moe_experts(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, int
                          int32_t I, const void* x, const int32_t* expert_offsets,
                          const int32_t* row_to_pair, const void* w13, const void* w2,
                          float* y_rows, void* ws, size_t ws_bytes, void* stream) {
-    const ExpertWeights ew = {false, w13, w2, nullptr, nullptr, ACT_SILU, 0.0f, 0.0f};
+    const ExpertWeights ew = {WF_BF16, w13, w2, nullptr, nullptr, ACT_SILU, 0.0f, 0.0f};
     return experts_impl(dtype, T, k, E, D, I, x, expert_offsets, row_to_pair, ew, y_rows, ws,
                         ws_bytes, stream);
 }
@@ -598,6 +608,7 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
                           int32_t* expert_counts_out, void* const* stage_events, void* ws,
                           size_t ws_bytes, void* stream) {
     MOE_TRY(check_forward_shapes(cfg, dtype, T, H, I, latent, shared));
+    if (!weights_fit(ew, latent ? latent->latent : H, I)) return MOE_ENOTSUP;
     if (T == 0) return MOE_OK;
     if (!x || !weights_present(ew) || !out) return MOE_EINVAL;
     if (!router_logits && !w_router) return MOE_EINVAL;
@@ -742,7 +753,7 @@ moe_status_t moe_forward(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t 
                          int32_t* topk_ids_out, float* topk_weights_out,
                          int32_t* expert_counts_out, void* const* stage_events, void* ws,
                          size_t ws_bytes, void* stream) {
-    const ExpertWeights ew = {false, w13, w2, nullptr, nullptr, ACT_SILU, 0.0f, 0.0f};
+    const ExpertWeights ew = {WF_BF16, w13, w2, nullptr, nullptr, ACT_SILU, 0.0f, 0.0f};
     return forward_impl(cfg, dtype, T, H, I, x, w_router, router_bias, router_logits,
                         correction_bias, ew, nullptr, latent, shared, out, logits_out,
                         topk_ids_out, topk_weights_out, expert_counts_out, stage_events, ws,

@@ -63,7 +63,7 @@ class Workload:
     shared_inter: Optional[int] = None   # shared expert intermediate width
     rms_eps: float = 1e-6
     gamma_std: float = 0.0               # RMSNorm gamma = 1 + N(0, gamma_std^2)
-    weights: str = "dtype"               # routed expert weights: "dtype" | "fp8_e4m3"
+    weights: str = "dtype"               # routed expert weights: "dtype" | "fp8_e4m3" | "mxfp4"
 
     @property
     def D(self) -> int:
@@ -94,6 +94,9 @@ WORKLOADS = {
     # the decode layer with FP8 E4M3 expert weights (one fp32 scale per row)
     "decode_fp8": Workload("decode_fp8", T=128, H=7168, E=384, k=8, I=2048,
                            routed_scaling=2.5, weights="fp8_e4m3"),
+    # ... and with MXFP4 expert weights (E2M1 codes, one E8M0 exponent per 32)
+    "decode_mxfp4": Workload("decode_mxfp4", T=128, H=7168, E=384, k=8, I=2048,
+                             routed_scaling=2.5, weights="mxfp4"),
 }
 
 FP8_E4M3_MAX = 448.0  # largest finite E4M3 value
@@ -117,6 +120,45 @@ def fp8_rows(w: torch.Tensor, chunk: int = 16):
         codes[e0:e0 + chunk] = (blk / sc[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
         scales[e0:e0 + chunk] = sc
         del blk
+    return codes, scales
+
+
+E2M1_MAX = 6.0  # largest E2M1 magnitude, 1.5 * 2^2
+# midpoints between consecutive E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6
+_E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def mxfp4_rows(w: torch.Tensor, chunk: int = 16):
+    """MXFP4 codes and E8M0 block exponents of a weight tensor [E, n, in]
+    (in a multiple of 32).
+
+    Each block of 32 consecutive inputs of a row gets the exponent x =
+    floor(log2(max|w|)) - 2 (so the block maximum lands in [4, 8)), stored as
+    the byte s = clamp(x + 127, 1, 254) (127 for an all-zero block).  Each
+    w / 2^(s-127) is rounded to the nearest E2M1 magnitude (a tie goes to
+    the smaller one, values past 6 saturate at 6) and encoded as sign << 3 |
+    magnitude index; element 2j of a row goes to the low nibble of byte j,
+    2j + 1 to the high nibble.  Returns (codes [E, n, in/2] uint8, scales
+    [E, n, in/32] uint8).  Input construction only: the layer and the oracle
+    decode the codes themselves.  Works through ``chunk`` experts at a time
+    to bound temporary memory."""
+    E, n, K = w.shape
+    if K % 32:
+        raise ValueError("the input width must be a multiple of 32")
+    codes = torch.empty((E, n, K // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((E, n, K // 32), dtype=torch.uint8, device=w.device)
+    mids = torch.tensor(_E2M1_MIDPOINTS, dtype=torch.float32, device=w.device)
+    for e0 in range(0, E, chunk):
+        blk = w[e0:e0 + chunk].float().reshape(-1, n, K // 32, 32)
+        amax = blk.abs().amax(dim=-1)
+        xe = torch.where(amax > 0, torch.floor(torch.log2(amax)) - 2.0, torch.zeros_like(amax))
+        sb = (xe + 127.0).clamp(1.0, 254.0)
+        y = blk / torch.exp2(sb - 127.0)[..., None]
+        code = torch.bucketize(y.abs(), mids).to(torch.uint8) | ((y < 0).to(torch.uint8) << 3)
+        code = code.reshape(-1, n, K // 2, 2)
+        codes[e0:e0 + chunk] = code[..., 0] | (code[..., 1] << 4)
+        scales[e0:e0 + chunk] = sb.to(torch.uint8)
+        del blk, y, code
     return codes, scales
 
 
@@ -180,7 +222,9 @@ def make_inputs(w: Workload, device="cpu", chunk_rows: int = 8) -> dict:
 
     Keys: x[T,H], w_router[E,H], router_bias[E] (fp32) or None,
     corr_bias[E] (fp32) or None, w13[E,2I,D], w2[E,D,I] (for FP8 weights:
-    uint8 E4M3 codes plus w13_scale[E,2I], w2_scale[E,D] fp32), and for the latent
+    uint8 E4M3 codes plus w13_scale[E,2I], w2_scale[E,D] fp32; for MXFP4
+    weights: w13[E,2I,D/2], w2[E,D,I/2] uint8 code pairs plus
+    w13_scale[E,2I,D/32], w2_scale[E,D,I/32] uint8 exponents), and for the latent
     layer w_down[L,H], gamma[L], w_up[H,L]; for a shared expert
     w13_sh[2Is,H], w2_sh[H,Is].  Weights are row-major [out, in].
     """
@@ -202,6 +246,11 @@ def make_inputs(w: Workload, device="cpu", chunk_rows: int = 8) -> dict:
         # the same draws, quantised per row (the bf16 tensors are dropped)
         for name in ("w13", "w2"):
             codes, scales = fp8_rows(inp[name])
+            inp[name] = codes
+            inp[name + "_scale"] = scales
+    elif w.weights == "mxfp4":
+        for name in ("w13", "w2"):
+            codes, scales = mxfp4_rows(inp[name])
             inp[name] = codes
             inp[name + "_scale"] = scales
     if w.latent:

@@ -64,6 +64,18 @@ class ExpertFetchFP8:
         return O.dequantize_rows(self.codes[e].cpu().numpy(), self.scales[e].cpu().numpy())
 
 
+class ExpertFetchMXFP4:
+    """w[e] -> expert e's weights decoded by the oracle from its MXFP4 codes
+    and E8M0 block exponents (copied from the device one expert at a time)."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor):
+        self.codes, self.scales = codes, scales
+
+    def __getitem__(self, e):
+        e = int(e)
+        return O.dequantize_mxfp4(self.codes[e].cpu().numpy(), self.scales[e].cpu().numpy())
+
+
 def latent_np(inp: dict, w: Workload):
     if not w.latent:
         return None
