@@ -224,7 +224,7 @@ constexpr int SRN = 16 * SRW;        // weight rows per workgroup (SwiGLU: SRN /
 // as the weights, the codes become bf16 exactly in registers (MXFP4: with
 // the block scale applied by the conversion), and FP8's row scale multiplies
 // the fp32 sums in the epilogue.
-template <int EPI, int NB, bool KCAT, int WF>
+template <int EPI, int NB, bool KCAT, int WF, bool SV>
 __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCoord& tc,
                                                  char* xs) {
     constexpr bool SW = EPI == EPI_SWIGLU;
@@ -308,7 +308,21 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
         // MXFP4: the block exponents of the chunk's UPC load units travel
         // with its tokens (one dword per unit, byte g4 for this lane), so
         // every weight load unit is a single load
-        if constexpr (FP4) {
+        if constexpr (FP4 && SV) {
+            // K a multiple of 512: the chunk's UPC exponent dwords are one
+            // aligned vector of the row (chunks past the end re-read the last)
+            const int cl = min(c, nu / UPC - 1);
+            if constexpr (UPC == 4) {
+                const u32x4_t v4 = *(const u32x4_t*)(Sb + 16 * cl);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sxn[j] = v4[j];
+            } else {
+                typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+                const u32x2_t v2 = *(const u32x2_t*)(Sb + 8 * cl);
+                sxn[0] = v2[0];
+                sxn[1] = v2[1];
+            }
+        } else if constexpr (FP4) {
 #pragma unroll
             for (int j = 0; j < UPC; ++j)
                 sxn[j] = *(const uint32_t*)(Sb + 4 * min(c * UPC + j, nu - 1));
@@ -521,7 +535,8 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
 
 // Grouped tiles here hold one whole group of at most 64 rows; dense products
 // are cut into 16-row tiles.
-template <int EPI, bool KCAT, int WF>
+// SV (MXFP4 with K a multiple of 512): block exponents in vector loads.
+template <int EPI, bool KCAT, int WF, bool SV = false>
 __global__ __launch_bounds__(64 * SRW, 4) void gemm_bf16_stream(GemmArgs g) {
     constexpr bool SW = EPI == EPI_SWIGLU;
     const int ntn = SW ? (g.N + SRN / 2 - 1) / (SRN / 2) : (g.N + SRN - 1) / SRN;
@@ -529,22 +544,22 @@ __global__ __launch_bounds__(64 * SRW, 4) void gemm_bf16_stream(GemmArgs g) {
     if (!fetch_tile(g, SROWS, ntn, tc)) return;
     __shared__ __attribute__((aligned(1024))) char xs[SX_BYTES];
     const int rows = tc.row1 - tc.row0;
-    if (rows <= 16) stream_rows_tile<EPI, 1, KCAT, WF>(g, tc, xs);
-    else if (rows <= 32) stream_rows_tile<EPI, 2, KCAT, WF>(g, tc, xs);
-    else stream_rows_tile<EPI, 4, KCAT, WF>(g, tc, xs);
+    if (rows <= 16) stream_rows_tile<EPI, 1, KCAT, WF, SV>(g, tc, xs);
+    else if (rows <= 32) stream_rows_tile<EPI, 2, KCAT, WF, SV>(g, tc, xs);
+    else stream_rows_tile<EPI, 4, KCAT, WF, SV>(g, tc, xs);
 }
 
 // Dense products with fewer workgroups than this split K over the waves.
 constexpr int64_t kStreamRowsMinGrid = 1024;
 
-template <bool KC, int WF>
+template <bool KC, int WF, bool SV = false>
 void launch_stream_rows(const GemmArgs& g, dim3 gd, hipStream_t s) {
     const dim3 bd(64 * SRW);
     switch (g.epi) {
-        case EPI_F32: gemm_bf16_stream<EPI_F32, KC, WF><<<gd, bd, 0, s>>>(g); break;
-        case EPI_F32_BIAS: gemm_bf16_stream<EPI_F32_BIAS, KC, WF><<<gd, bd, 0, s>>>(g); break;
-        case EPI_OUT: gemm_bf16_stream<EPI_OUT, KC, WF><<<gd, bd, 0, s>>>(g); break;
-        default: gemm_bf16_stream<EPI_SWIGLU, KC, WF><<<gd, bd, 0, s>>>(g); break;
+        case EPI_F32: gemm_bf16_stream<EPI_F32, KC, WF, SV><<<gd, bd, 0, s>>>(g); break;
+        case EPI_F32_BIAS: gemm_bf16_stream<EPI_F32_BIAS, KC, WF, SV><<<gd, bd, 0, s>>>(g); break;
+        case EPI_OUT: gemm_bf16_stream<EPI_OUT, KC, WF, SV><<<gd, bd, 0, s>>>(g); break;
+        default: gemm_bf16_stream<EPI_SWIGLU, KC, WF, SV><<<gd, bd, 0, s>>>(g); break;
     }
 }
 
@@ -574,6 +589,8 @@ hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
         if (g.b_fmt == WF_MXFP4 && g.K % 128 != 0) return hipErrorInvalidValue;
         if (g.b_fmt == WF_FP8) {
             launch_stream_rows<false, WF_FP8>(g, gd, s);
+        } else if (g.b_fmt == WF_MXFP4 && g.K % 512 == 0) {
+            launch_stream_rows<false, WF_MXFP4, true>(g, gd, s);
         } else if (g.b_fmt == WF_MXFP4) {
             launch_stream_rows<false, WF_MXFP4>(g, gd, s);
         } else if (g.A2) {
