@@ -19,8 +19,10 @@
  *     in as a caller-owned workspace sized from a capacity (max_T), so one
  *     workspace serves every T <= max_T.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
- *     enqueues kernels on it and returns; results are ready when the stream
- *     reaches them.
+ *     enqueues work on it and returns; results are ready when the stream
+ *     reaches them.  With buffers and workspace allocated beforehand, a call
+ *     can be captured in a HIP graph and replayed: it records no memset, no
+ *     host synchronisation and no allocation.
  *   - Weights are [out, in] row-major (the nn.Linear layout).  bf16 values
  *     are IEEE bfloat16 bit patterns (uint16); f32 is IEEE binary32.
  *   - Pair index p = t*k + j names slot j of token t.
@@ -33,7 +35,12 @@
  *     MOE_ENOSPACE (workspace too small).  A failed launch returns MOE_EHIP.
  *     T == 0 is valid and launches nothing.  No C++ exception crosses the ABI.
  *   - Preconditions the kernels do not check: logits finite; topk_ids in [0,E).
- *   - The calls keep no global mutable state and may be issued from several
+ *   - The only state the library keeps is, per device, one stream of its
+ *     own (default priority, created on first use) with two events: when a
+ *     batch splits the experts into many small and some large groups, the
+ *     small groups' chain runs there, forked from and joined back into
+ *     `stream` with events (a graph capture takes it in).  A mutex keeps
+ *     concurrent callers' forks apart, so calls may be issued from several
  *     host threads on different streams.
  */
 #ifndef ROUTED_MOE_MI355X_H
