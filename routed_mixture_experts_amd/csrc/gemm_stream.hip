@@ -209,9 +209,20 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_ksplit(GemmArgs g) {
 // why it is staged.  Every vector-memory operation here is a register load,
 // so the compiler's in-order vmcnt bookkeeping stays exact (LDS-DMA loads
 // mixed with register loads make it fall back to draining the counter).
-constexpr int SX_BYTES = 64 * 1024;  // token-chunk double buffer
-constexpr int SRW = 8;               // waves per workgroup
-constexpr int SRN = 16 * SRW;        // weight rows per workgroup (SwiGLU: SRN / 2 columns)
+// NW waves per workgroup (8 or 16), 16 weight rows each: SRN = 16 * NW weight
+// rows per workgroup (SwiGLU: SRN / 2 columns).  Token bytes per k-step are
+// the same for any NW and weight bytes grow with it, so 16 waves halve the
+// share of token loads among the loads in flight; but one 16-wave workgroup
+// fills a CU (it takes a 128 KB token buffer and chunks twice as deep) and
+// its barriers span 16 waves.  Alone, 8 waves are faster for every format;
+// beside the 256x256 chain of a large batch, 16 are (bf16 only).
+template <int NW>
+constexpr int sx_bytes() { return NW == 16 ? 128 * 1024 : 64 * 1024; }
+
+int stream_col_tiles_nw(int epi, int N, int nw) {
+    const int srn = 16 * nw;
+    return epi == EPI_SWIGLU ? (N + srn / 2 - 1) / (srn / 2) : (N + srn - 1) / srn;
+}
 
 // With FP8 weights (OCP e4m3 codes, one fp32 scale per weight row) each
 // 16-byte weight load holds 16 codes, i.e. two 32-deep k-steps: lane g4 of a
@@ -224,12 +235,13 @@ constexpr int SRN = 16 * SRW;        // weight rows per workgroup (SwiGLU: SRN /
 // as the weights, the codes become bf16 exactly in registers (MXFP4: with
 // the block scale applied by the conversion), and FP8's row scale multiplies
 // the fp32 sums in the epilogue.
-template <int EPI, int NB, bool KCAT, int WF, bool SV>
+template <int EPI, int NB, bool KCAT, int WF, bool SV, int NW>
 __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCoord& tc,
                                                  char* xs) {
     constexpr bool SW = EPI == EPI_SWIGLU;
     constexpr bool FP8 = WF == WF_FP8, FP4 = WF == WF_MXFP4, QW = WF != WF_BF16;
-    constexpr int CS = NB == 4 ? 8 : 16;       // k-steps (of 32) per token chunk
+    constexpr int SRN = 16 * NW;
+    constexpr int CS = (NB == 4 ? 8 : 16) * (NW / 8);  // k-steps (of 32) per token chunk
     constexpr int UNIT = FP4 ? 4 : FP8 ? 2 : 1;  // k-steps per weight load
     constexpr int PD = FP8 && NB == 4 ? 4 : 8;  // weight loads in flight
     constexpr int UPC = CS / UNIT;             // weight loads per chunk
@@ -237,10 +249,10 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     // of times per iteration, so every slot index is static
     constexpr int RC = PD > UPC ? PD / UPC : 1;
     constexpr int TU = RC * UPC;               // weight loads per ring turn
-    constexpr int XI = CS * NB / SRW;          // 1 KB token blocks per wave per chunk
+    constexpr int XI = CS * NB / NW;           // 1 KB token blocks per wave per chunk
     constexpr int CHUNK = CS * NB * 1024;      // bytes of one token chunk
     static_assert(!(QW && KCAT), "quantised weights are grouped products only");
-    static_assert(2 * CHUNK <= SX_BYTES && CS % UNIT == 0 && TU % PD == 0 && XI % NB == 0,
+    static_assert(2 * CHUNK <= sx_bytes<NW>() && CS % UNIT == 0 && TU % PD == 0 && XI % NB == 0,
                   "stream tiling");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -312,6 +324,7 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
             // K a multiple of 512: the chunk's UPC exponent dwords are one
             // aligned vector of the row (chunks past the end re-read the last)
             const int cl = min(c, nu / UPC - 1);
+            static_assert(UPC == 4 || UPC == 2, "exponent vector of a chunk");
             if constexpr (UPC == 4) {
                 const u32x4_t v4 = *(const u32x4_t*)(Sb + 16 * cl);
 #pragma unroll
@@ -536,40 +549,46 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
 // Grouped tiles here hold one whole group of at most 64 rows; dense products
 // are cut into 16-row tiles.
 // SV (MXFP4 with K a multiple of 512): block exponents in vector loads.
-template <int EPI, bool KCAT, int WF, bool SV = false>
-__global__ __launch_bounds__(64 * SRW, 4) void gemm_bf16_stream(GemmArgs g) {
+template <int EPI, bool KCAT, int WF, bool SV, int NW>
+__global__ __launch_bounds__(64 * NW, 4) void gemm_bf16_stream(GemmArgs g) {
     constexpr bool SW = EPI == EPI_SWIGLU;
+    constexpr int SRN = 16 * NW;
     const int ntn = SW ? (g.N + SRN / 2 - 1) / (SRN / 2) : (g.N + SRN - 1) / SRN;
     TileCoord tc;
     if (!fetch_tile(g, SROWS, ntn, tc)) return;
-    __shared__ __attribute__((aligned(1024))) char xs[SX_BYTES];
+    __shared__ __attribute__((aligned(1024))) char xs[sx_bytes<NW>()];
     const int rows = tc.row1 - tc.row0;
-    if (rows <= 16) stream_rows_tile<EPI, 1, KCAT, WF, SV>(g, tc, xs);
-    else if (rows <= 32) stream_rows_tile<EPI, 2, KCAT, WF, SV>(g, tc, xs);
-    else stream_rows_tile<EPI, 4, KCAT, WF, SV>(g, tc, xs);
+    if (rows <= 16) stream_rows_tile<EPI, 1, KCAT, WF, SV, NW>(g, tc, xs);
+    else if (rows <= 32) stream_rows_tile<EPI, 2, KCAT, WF, SV, NW>(g, tc, xs);
+    else stream_rows_tile<EPI, 4, KCAT, WF, SV, NW>(g, tc, xs);
 }
 
 // Dense products with fewer workgroups than this split K over the waves.
 constexpr int64_t kStreamRowsMinGrid = 1024;
 
-template <bool KC, int WF, bool SV = false>
-void launch_stream_rows(const GemmArgs& g, dim3 gd, hipStream_t s) {
-    const dim3 bd(64 * SRW);
+template <bool KC, int WF, bool SV, int NW>
+void launch_stream_rows(const GemmArgs& g, int nm, hipStream_t s) {
+    const dim3 gd((unsigned)((int64_t)nm * stream_col_tiles_nw(g.epi, g.N, NW))), bd(64 * NW);
     switch (g.epi) {
-        case EPI_F32: gemm_bf16_stream<EPI_F32, KC, WF, SV><<<gd, bd, 0, s>>>(g); break;
-        case EPI_F32_BIAS: gemm_bf16_stream<EPI_F32_BIAS, KC, WF, SV><<<gd, bd, 0, s>>>(g); break;
-        case EPI_OUT: gemm_bf16_stream<EPI_OUT, KC, WF, SV><<<gd, bd, 0, s>>>(g); break;
-        default: gemm_bf16_stream<EPI_SWIGLU, KC, WF, SV><<<gd, bd, 0, s>>>(g); break;
+        case EPI_F32: gemm_bf16_stream<EPI_F32, KC, WF, SV, NW><<<gd, bd, 0, s>>>(g); break;
+        case EPI_F32_BIAS:
+            gemm_bf16_stream<EPI_F32_BIAS, KC, WF, SV, NW><<<gd, bd, 0, s>>>(g);
+            break;
+        case EPI_OUT: gemm_bf16_stream<EPI_OUT, KC, WF, SV, NW><<<gd, bd, 0, s>>>(g); break;
+        default: gemm_bf16_stream<EPI_SWIGLU, KC, WF, SV, NW><<<gd, bd, 0, s>>>(g); break;
     }
 }
+
+// Waves per workgroup of a grouped bf16 weight-streaming product: 8, or 16
+// when the caller asks for it (the small-group chain of a large batch, which
+// runs beside the 256x256 chain: measured 2% faster there, and slower alone).
+int stream_waves(const GemmArgs& g) { return g.stream_nw == 16 ? 16 : 8; }
 
 }  // namespace
 
 int stream_row_tile() { return SROWS; }
 
-int stream_col_tiles(int epi, int N) {
-    return epi == EPI_SWIGLU ? (N + SRN / 2 - 1) / (SRN / 2) : (N + SRN - 1) / SRN;
-}
+int stream_col_tiles(int epi, int N) { return stream_col_tiles_nw(epi, N, 8); }
 
 hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
     const bool sw = g.epi == EPI_SWIGLU;
@@ -584,19 +603,21 @@ hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
             default: gemm_bf16_stream_ksplit<EPI_SWIGLU><<<gd, bd, 0, s>>>(g); break;
         }
     } else {
-        const dim3 gd((unsigned)((int64_t)nm * stream_col_tiles(g.epi, g.N)));
         if (g.b_fmt != WF_BF16 && g.A2) return hipErrorInvalidValue;
         if (g.b_fmt == WF_MXFP4 && g.K % 128 != 0) return hipErrorInvalidValue;
+        const bool w16 = g.tiles && stream_waves(g) == 16;
         if (g.b_fmt == WF_FP8) {
-            launch_stream_rows<false, WF_FP8>(g, gd, s);
+            launch_stream_rows<false, WF_FP8, false, 8>(g, nm, s);
         } else if (g.b_fmt == WF_MXFP4 && g.K % 512 == 0) {
-            launch_stream_rows<false, WF_MXFP4, true>(g, gd, s);
+            launch_stream_rows<false, WF_MXFP4, true, 8>(g, nm, s);
         } else if (g.b_fmt == WF_MXFP4) {
-            launch_stream_rows<false, WF_MXFP4>(g, gd, s);
+            launch_stream_rows<false, WF_MXFP4, false, 8>(g, nm, s);
         } else if (g.A2) {
-            launch_stream_rows<true, WF_BF16>(g, gd, s);
+            launch_stream_rows<true, WF_BF16, false, 8>(g, nm, s);
+        } else if (w16) {
+            launch_stream_rows<false, WF_BF16, false, 16>(g, nm, s);
         } else {
-            launch_stream_rows<false, WF_BF16>(g, gd, s);
+            launch_stream_rows<false, WF_BF16, false, 8>(g, nm, s);
         }
     }
     return hipGetLastError();

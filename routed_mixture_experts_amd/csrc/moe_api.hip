@@ -259,8 +259,11 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
         MOE_TRY(side_stream(&ss));
         MOE_HIP(hipEventRecord(ss->fork, s));
         MOE_HIP(hipStreamWaitEvent(ss->s, ss->fork, 0));
-        moe_status_t st = small_groups_gemm(g1, w, E, ss->s);
-        if (st == MOE_OK) st = small_groups_gemm(g2, w, E, ss->s);
+        // beside the 256-row chain, 16-wave streaming workgroups do better
+        GemmArgs s1 = g1, s2 = g2;
+        s1.stream_nw = s2.stream_nw = 16;
+        moe_status_t st = small_groups_gemm(s1, w, E, ss->s);
+        if (st == MOE_OK) st = small_groups_gemm(s2, w, E, ss->s);
         // the caller's stream joins the side stream even after an error
         const moe_status_t sj = hip_status(hipEventRecord(ss->join, ss->s));
         if (st == MOE_OK) st = large_groups_gemm(dt, g1, w, P, E, s);

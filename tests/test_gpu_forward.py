@@ -192,6 +192,30 @@ def test_forward_is_deterministic():
         assert torch.equal(a, b)
 
 
+def test_forward_two_chains_every_tile_shape():
+    """A skewed batch large enough for the two-stream split: large groups in
+    256-row tiles on the caller's stream, small ones (1, 2 and 4 token blocks
+    of 16 rows) in 16-wave streaming workgroups on the library's stream."""
+    w = Workload("t", T=640, H=256, E=16, k=4, I=192, routed_scaling=1.5)
+    inp = make_inputs(w, DEV)
+    lg = random_logits(w.T, w.E, seed=21)
+    # experts 0-3 take most tokens; 4-15 get graded small loads
+    lg[:, :4] += 3.0
+    lg[:, 4:] += torch.linspace(-2.5, 0.5, w.E - 4)
+    logits = lg.to(DEV)
+    res = _gpu_forward(w, inp, router_logits=logits)
+    ref = _oracle_forward(w, inp, logits=np64(logits))
+    counts = npi(res["counts"])
+    log(f"  counts {sorted(counts.tolist())}")
+    assert w.T * w.k >= 16 * w.E                        # the two-stream split
+    assert counts.max() > 64
+    small = counts[(counts > 0) & (counts <= 64)]
+    assert (small <= 16).any() and ((small > 16) & (small <= 32)).any() and (small > 32).any()
+    assert (npi(res["ids"]) == ref["ids"]).all()
+    assert (counts == ref["counts"]).all()
+    check_float(np64(res["out"]), ref["out"], True, "out two chains")
+
+
 def test_forward_empty_batch():
     w = SMALL["decode_like"]
     inp = make_inputs(w, DEV)
