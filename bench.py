@@ -282,7 +282,7 @@ def main():
                    "parallelism": "none (1 GPU holds all experts)"},
         "roofline": {"bound": "hbm", "achieved": g1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": g1_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gate/up + SwiGLU stage: gemm_bf16_stream<3, false, 0, false> (experts <= 64"
+                     "kernel": "gate/up + SwiGLU stage: gemm_bf16_stream<3, false, 0, false, 8> (experts <= 64"
                                " rows) + gemm_bf16_big<3, false> (larger experts)",
                      "kernel_ms": g1_ms, "algorithmic_bytes": g1b},
         "layer": {"hbm_GBps": abytes / t_s / 1e9, "hbm_frac": abytes / t_s / 1e9 / HBM_PEAK_GBS,
@@ -330,7 +330,7 @@ def main():
             "workload": describe(wf) + " weights=fp8_e4m3 (per-row fp32 scales)",
             "value": wf.T / (fms * 1e-3), "unit": "tokens/s", "ms_per_step": fms,
             "steps": args.steps, "hbm_frac": fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "gemm1": {"kernel": "gemm_bf16_stream<3, false, 1, false>", "kernel_ms": fstage["gemm1"],
+            "gemm1": {"kernel": "gemm_bf16_stream<3, false, 1, false, 8>", "kernel_ms": fstage["gemm1"],
                       "algorithmic_bytes": f1b, "achieved_GBps": f1, "frac": f1 / HBM_PEAK_GBS,
                       "traffic": profiled_traffic(wf.name)},
             "stages_ms": fstage}
@@ -354,7 +354,7 @@ def main():
             "workload": describe(wm) + " weights=mxfp4 (E2M1, E8M0 exponent per 32)",
             "value": wm.T / (mms * 1e-3), "unit": "tokens/s", "ms_per_step": mms,
             "steps": args.steps, "hbm_frac": mbytes / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "gemm1": {"kernel": "gemm_bf16_stream<3, false, 2, true>", "kernel_ms": mstage["gemm1"],
+            "gemm1": {"kernel": "gemm_bf16_stream<3, false, 2, true, 8>", "kernel_ms": mstage["gemm1"],
                       "algorithmic_bytes": m1b, "achieved_GBps": m1, "frac": m1 / HBM_PEAK_GBS,
                       "traffic": profiled_traffic(wm.name)},
             "stages_ms": mstage}
