@@ -345,9 +345,9 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
         char* dst = xs + (c & 1) * CHUNK + lane * 16;
 #pragma unroll
         for (int i = 0; i < XI; ++i) {
-            // MXFP4: steps past K get zero tokens (once per chunk, in place
-            // of a select per step on the weights)
-            if (FP4 && c * CS + (wave * XI + i) / NB >= ns) xr[i] = u32x4_t{0u, 0u, 0u, 0u};
+            // FP8 / MXFP4: steps past K get zero tokens (once per chunk, in
+            // place of a select per step on the converted weights)
+            if (QW && c * CS + (wave * XI + i) / NB >= ns) xr[i] = u32x4_t{0u, 0u, 0u, 0u};
             *(u32x4_t*)(dst + (wave * XI + i) * 1024) = xr[i];
         }
         if constexpr (FP4) {
@@ -437,8 +437,8 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
             const int st = c * CS + sl;
             u32x4_t wv = w[v];
             if (FP8) wv = fp8x8_to_bf16x8(w[v][2 * hh], w[v][2 * hh + 1]);
-            // steps past K (the ragged last chunk) multiply zero weights
-            const u32x4_t wz = st < ns ? wv : u32x4_t{0u, 0u, 0u, 0u};
+            // bf16: steps past K (the ragged last chunk) multiply zero weights
+            const u32x4_t wz = FP8 || st < ns ? wv : u32x4_t{0u, 0u, 0u, 0u};
             const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, wz);
 #pragma unroll
             for (int tb = 0; tb < NB; ++tb) {

@@ -90,28 +90,22 @@ __device__ __forceinline__ void wait_lgkm0() {
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
-// Eight OCP e4m3 codes (code 0 in the low byte of lo) as eight bf16 values.
-// e4m3 keeps 3 mantissa bits and exponents 2^-9 .. 2^8, so every finite code
-// is exact in bf16: v_cvt_pk_f32_fp8 gives its fp32 value (checked against
-// all 256 codes) and the top half of that is the bf16 pattern.  (The scaled
-// single-instruction conversion to bf16 pairs gives the same values, but in
-// the streaming kernel the compiler then holds far more registers.)
-__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-    typedef float f32x2_t __attribute__((ext_vector_type(2)));
-    u32x4_t r;
-    const uint32_t w[2] = {lo, hi};
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], false);  // bytes 0, 1
-        const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], true);   // bytes 2, 3
-        r[2 * q] = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
-        r[2 * q + 1] = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
-    }
-    return r;
-}
-
 __device__ __forceinline__ uint32_t bf16x2_bits(bf16x2_t v) {
     return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight OCP e4m3 codes (code 0 in the low byte of lo) as eight bf16 values.
+// e4m3 keeps 3 mantissa bits and exponents 2^-9 .. 2^8, so every finite code
+// is exact in bf16.  v_cvt_scalef32_pk_bf16_fp8 with a unit scale converts
+// two codes (bytes 0-1, or 2-3 with the high select) in one instruction;
+// checked against all 256 codes, the two NaN codes included.
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    u32x4_t r;
+    r[0] = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+    r[1] = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+    r[2] = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+    r[3] = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+    return r;
 }
 
 // The fp32 that carries an E8M0 block exponent e into the scaled
