@@ -119,6 +119,33 @@ def profiled_traffic(workload: str):
     return None
 
 
+def binding_frac(nbytes, flops, ms):
+    """Fraction of the binding roofline: max(t_HBM, t_MFMA) / t at the chip's
+    peaks (8 TB/s, 2.5 PFLOP/s bf16)."""
+    return max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3)
+
+
+SEEDS = {"x": 0, "w_router": 1, "w13": 2, "w2": 3, "router_bias": 4, "corr_bias": 5,
+         "w_down": 6, "w_up": 7, "w13_sh": 8, "w2_sh": 9, "x_cal": 10, "rank_perm": 11}
+
+
+def checksums(inp, torch):
+    """Sum of every input tensor in float64 (bf16 / fp32 values; FP8 and MXFP4
+    weights as their integer codes), taken in slabs: a fingerprint of the
+    seeded inputs, outside the timed region."""
+    out = {}
+    for name, t in inp.items():
+        if t is None or not hasattr(t, "dtype"):
+            continue
+        flat = t.reshape(-1)
+        acc = 0.0
+        step = 1 << 28
+        for i in range(0, flat.numel(), step):
+            acc += float(flat[i:i + step].to(torch.float64).sum())
+        out[name] = acc
+    return out
+
+
 def gemm1_bytes(w, counts):
     """Algorithmic bytes of one gate/up + SwiGLU launch: gate/up weights of the
     touched experts (unit: one expert, 2*I*D elements), the token activations
@@ -287,9 +314,11 @@ def main():
                      "kernel_ms": g1_ms, "algorithmic_bytes": g1b},
         "layer": {"hbm_GBps": abytes / t_s / 1e9, "hbm_frac": abytes / t_s / 1e9 / HBM_PEAK_GBS,
                   "mfma_frac": aflops / t_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                  "binding_frac": binding_frac(abytes, aflops, ms),
                   "algorithmic_bytes": abytes, "algorithmic_flops": aflops,
                   "host_wall_ms_per_step": wall_ms},
         "stages_ms": stage,
+        "inputs": {"seeds": SEEDS, "checksums": checksums(inp, torch)},
     }
     if args.workload == "decode" and not args.no_prefill:
         wp = WORKLOADS["prefill_zipf"]
@@ -308,7 +337,12 @@ def main():
             "ms_per_step": pms, "steps": psteps,
             "hbm_frac": pbytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "mfma_frac": pflops / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "load": {"max": int(pc.max()), "min": int(pc.min()), "empty": int((pc == 0).sum())},
+            "binding_frac": binding_frac(pbytes, pflops, pms),
+            "algorithmic_bytes": pbytes, "algorithmic_flops": pflops,
+            "load": {"max": int(pc.max()), "min": int(pc.min()), "empty": int((pc == 0).sum()),
+                     "histogram": [int(v) for v in pc]},
+            "input_checksums": {"x": checksums({"x": pin["x"]}, torch)["x"],
+                                "router_bias": checksums({"b": pin["router_bias"]}, torch)["b"]},
             "stages_ms": pstage}
         del prun, pin
     if args.workload == "decode" and not args.no_fp8:
