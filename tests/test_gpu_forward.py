@@ -216,6 +216,47 @@ def test_forward_two_chains_every_tile_shape():
     check_float(np64(res["out"]), ref["out"], True, "out two chains")
 
 
+def test_forward_groups_just_above_the_streaming_limit():
+    """Groups of 65..128 rows (one partly filled 256-row tile each) beside
+    larger groups and streaming groups in the same layer."""
+    w = Workload("t", T=600, H=256, E=16, k=2, I=192)
+    inp = make_inputs(w, DEV)
+    lg = random_logits(w.T, w.E, seed=31)
+    lg[:, 0] += 1.5
+    lg[:, 1] += 1.0
+    lg[:, 12:] -= 1.2
+    logits = lg.to(DEV)
+    res = _gpu_forward(w, inp, router_logits=logits)
+    ref = _oracle_forward(w, inp, logits=np64(logits))
+    counts = npi(res["counts"])
+    log(f"  counts {counts.tolist()}")
+    assert ((counts > 64) & (counts <= 128)).sum() >= 2 and (counts > 128).sum() >= 2
+    assert ((counts > 0) & (counts <= 64)).sum() >= 2
+    assert (npi(res["ids"]) == ref["ids"]).all()
+    check_float(np64(res["out"]), ref["out"], True, "out groups above 64 rows")
+
+
+def test_experts_group_sizes_at_tile_class_boundaries():
+    """Group sizes on the boundaries of the size classes (streaming up to 64
+    rows, 256-row tiles above; one and two tiles around 256; an empty group),
+    through moe_experts, element by element against the oracle."""
+    sizes = [64, 65, 128, 129, 1, 256, 257, 0]
+    E, k, D, I = len(sizes), 2, 256, 128
+    labels = np.repeat(np.arange(E), sizes)          # sorted expert labels
+    T = len(labels) // k
+    ids = np.stack([labels[:T], labels[T:]], 1)       # distinct per token
+    assert (ids[:, 0] != ids[:, 1]).all()
+    w = Workload("t", T=T, H=D, E=E, k=k, I=I)
+    inp = make_inputs(w, DEV)
+    c, off, r2p, p2r = moe.moe_permute(torch.from_numpy(ids.astype(np.int32)).to(DEV), E)
+    assert npi(c).tolist() == sizes
+    y = moe.moe_experts(inp["x"], off, r2p, inp["w13"], inp["w2"], k)
+    torch.cuda.synchronize()
+    _, roff, rr2p, _ = O.permute(ids, E)
+    ref = O.run_experts(np64(inp["x"]), k, roff, rr2p, np64(inp["w13"]), np64(inp["w2"]))
+    check_float(np64(y), ref, True, "y_rows size-class boundaries")
+
+
 def test_forward_empty_batch():
     w = SMALL["decode_like"]
     inp = make_inputs(w, DEV)
