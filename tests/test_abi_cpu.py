@@ -134,3 +134,82 @@ def test_experts_and_combine_validation(lib):
     assert lib.moe_combine(L.MOE_DTYPE_BF16, 0, 2, 8, None, None, None, None, None) == L.MOE_OK
     assert lib.moe_permute(4, 9, 8, p, p, p, p, p, p, 1 << 20, None) == L.MOE_EINVAL
     assert lib.moe_permute(4, 2, 8, p, p, p, p, p, p, 0, None) == L.MOE_ENOSPACE
+
+
+# ---------------------------------------------------- widened entry points ---
+# Host-side validation only: every case below returns before anything is
+# launched (T = 0 is valid and launches nothing), so no GPU is needed.
+
+def _ew(fmt=L.MOE_WEIGHT_DTYPE, scales=True, act=0, alpha=1.702, limit=7.0):
+    p = ctypes.c_void_p(256)
+    s = p if scales else None
+    return L.moe_expert_weights_t(fmt, p, p, s, s, act, alpha, limit)
+
+
+def _experts_ex(lib, desc, dtype=L.MOE_DTYPE_BF16, T=4, D=128, I=128):
+    p = ctypes.c_void_p(256)
+    return lib.moe_experts_ex(dtype, T, 2, 8, D, I, p, p, p,
+                              ctypes.byref(desc) if desc is not None else None, p, p, 16, None)
+
+
+def test_experts_ex_rejects_bad_descriptions(lib):
+    assert _experts_ex(lib, None) == L.MOE_EINVAL
+    assert _experts_ex(lib, _ew(fmt=9)) == L.MOE_EINVAL
+    assert _experts_ex(lib, _ew(act=4)) == L.MOE_EINVAL
+    assert _experts_ex(lib, _ew(act=-1)) == L.MOE_EINVAL
+    clip = L.ACTIVATIONS["swiglu_clip"]
+    assert _experts_ex(lib, _ew(act=clip, alpha=0.0)) == L.MOE_EINVAL
+    assert _experts_ex(lib, _ew(act=clip, limit=-1.0)) == L.MOE_EINVAL
+    # quantised weights need a bf16 layer
+    assert _experts_ex(lib, _ew(L.MOE_WEIGHT_FP8_E4M3), L.MOE_DTYPE_F32) == L.MOE_ENOTSUP
+    assert _experts_ex(lib, _ew(L.MOE_WEIGHT_MXFP4), L.MOE_DTYPE_F32) == L.MOE_ENOTSUP
+    # MXFP4 reads 128 elements per load unit along both reduction widths
+    assert _experts_ex(lib, _ew(L.MOE_WEIGHT_MXFP4), D=192) == L.MOE_ENOTSUP
+    assert _experts_ex(lib, _ew(L.MOE_WEIGHT_MXFP4), I=192) == L.MOE_ENOTSUP
+    # missing scales of a quantised format
+    assert _experts_ex(lib, _ew(L.MOE_WEIGHT_FP8_E4M3, scales=False)) == L.MOE_EINVAL
+    assert _experts_ex(lib, _ew(L.MOE_WEIGHT_MXFP4, scales=False)) == L.MOE_EINVAL
+    # workspace too small, after the description passed
+    assert _experts_ex(lib, _ew(L.MOE_WEIGHT_MXFP4)) == L.MOE_ENOSPACE
+
+
+def test_experts_ex_accepts_valid_descriptions_with_no_tokens(lib):
+    for fmt in (L.MOE_WEIGHT_DTYPE, L.MOE_WEIGHT_FP8_E4M3, L.MOE_WEIGHT_MXFP4):
+        for act in L.ACTIVATIONS.values():
+            assert _experts_ex(lib, _ew(fmt, act=act), T=0) == L.MOE_OK, (fmt, act)
+
+
+def test_placement_validation_and_workspace(lib):
+    c = _cfg(num_experts=8, top_k=2)
+    table = ctypes.c_void_p(256)
+    base = lib.moe_forward_workspace_ex(ctypes.byref(c), L.MOE_DTYPE_BF16, 64, 128, 64, None,
+                                        None, None)
+    more = L.moe_placement_t(12, table, None)
+    with_pl = lib.moe_forward_workspace_ex(ctypes.byref(c), L.MOE_DTYPE_BF16, 64, 128, 64, None,
+                                           None, ctypes.byref(more))
+    assert base > 0 and with_pl > base   # slot ids, and per-slot buffers for 12 slots
+    plain = lib.moe_forward_workspace(ctypes.byref(c), L.MOE_DTYPE_BF16, 64, 128, 64, None, None)
+    assert plain == base
+    p = ctypes.c_void_p(256)
+    ew = _ew()
+
+    def fwd(pl):
+        return lib.moe_forward_ex(ctypes.byref(c), L.MOE_DTYPE_BF16, 4, 128, 64, p, p, None,
+                                  None, None, ctypes.byref(ew), ctypes.byref(pl), None, None, p,
+                                  None, None, None, None, None, p, 1 << 30, None)
+
+    assert fwd(L.moe_placement_t(0, table, None)) == L.MOE_EINVAL       # no slots
+    assert fwd(L.moe_placement_t(12, None, None)) == L.MOE_EINVAL       # no table
+    assert fwd(L.moe_placement_t(2000, table, None)) == L.MOE_ENOTSUP   # > 1024 slots
+
+
+def test_log2phy_and_load_accumulate_validation(lib):
+    p = ctypes.c_void_p(256)
+    assert lib.moe_log2phy(0, 2, 8, 8, None, None, None, None) == L.MOE_OK
+    assert lib.moe_log2phy(4, 2, 8, 8, None, p, p, None) == L.MOE_EINVAL
+    assert lib.moe_log2phy(4, 0, 8, 8, p, p, p, None) == L.MOE_EINVAL
+    assert lib.moe_log2phy(4, 2, 8, 0, p, p, p, None) == L.MOE_EINVAL
+    assert lib.moe_log2phy(4, 2, 2000, 8, p, p, p, None) == L.MOE_ENOTSUP
+    assert lib.moe_load_accumulate(0, None, None, None) == L.MOE_OK
+    assert lib.moe_load_accumulate(-1, p, p, None) == L.MOE_EINVAL
+    assert lib.moe_load_accumulate(4, None, p, None) == L.MOE_EINVAL
