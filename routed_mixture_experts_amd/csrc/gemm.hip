@@ -297,10 +297,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     const int nk1 = g.K / GBK;
     const int nk = nk1 + (KCAT ? g.K2 / GBK : 0);
 
-    // Issue stage kt (clamped to the last stage) into its ring slot: 8 DMA
-    // instructions per wave.  The K segment of a K-concatenated product is
-    // picked with selects.
-    auto issue = [&](int kt) __attribute__((always_inline)) {
+    // Issue DMA blocks i0 .. i1-1 of stage kt (clamped to the last stage)
+    // into its ring slot: 2 DMA instructions per block.  The K segment of a
+    // K-concatenated product is picked with selects.
+    auto issue_blocks = [&](int kt, int i0, int i1) __attribute__((always_inline)) {
         const int slot = kt & (GSLOTS - 1);
         kt = min(kt, nk - 1);
         const bool seg1 = !KCAT || kt < nk1;
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         const char* bbase = seg1 ? Bb : B2b;
         const uint32_t ko = (uint32_t)(seg1 ? kt : kt - nk1) * GBK * 2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = i0; i < i1; ++i) {
             const int blk = (32 * wave + 8 * i) * GBK;
             __builtin_amdgcn_global_load_lds(
                 (const void*)(abase + ((seg1 ? ao[i] : ao2[KCAT ? i : 0]) + ko)),
@@ -318,6 +318,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
                 (lds_ptr_t)&smem[slot][1][blk], 16, 0, 0);
         }
     };
+    auto issue = [&](int kt) __attribute__((always_inline)) { issue_blocks(kt, 0, 4); };
 
     f32x16_t acc[4][2];
 #pragma unroll
@@ -365,15 +366,18 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
             for (int mi = 0; mi < 4; ++mi) f.a[s2][mi] = *(const bf16x8_t*)(&a[aoffs[ks][mi]]);
         }
     };
+    // the MFMAs of one 16-deep step of a half stage
+    auto mma_step = [&](const Frags& f, int s2) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int nj = 0; nj < 2; ++nj)
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    f.a[s2][mi], f.b[s2][nj], acc[mi][nj], 0, 0, 0);
+    };
     auto mma = [&](const Frags& f) __attribute__((always_inline)) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int nj = 0; nj < 2; ++nj)
-                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        f.a[s2][mi], f.b[s2][nj], acc[mi][nj], 0, 0, 0);
+        mma_step(f, 0);
+        mma_step(f, 1);
     };
 
     issue(0);
@@ -395,11 +399,18 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         wait_vmcnt_lgkm0<0>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue(kt + 2);
+        // stage kt+2's DMA goes out in two halves, the second after the
+        // first step's MFMAs, so the whole workgroup's DMA does not queue at
+        // once (5% faster on a dense 8192-row expert)
+        issue_blocks(kt + 2, 0, 2);
         if (active) {
             read_half(kt + 1, 0, f0);
-            mma(f1);
+            mma_step(f1, 0);
         }
+        asm volatile("" ::: "memory");
+        issue_blocks(kt + 2, 2, 4);
+        asm volatile("" ::: "memory");
+        if (active) mma_step(f1, 1);
         asm volatile("" ::: "memory");
     }
     // The ring's trailing DMAs must land before the LDS is reused below.

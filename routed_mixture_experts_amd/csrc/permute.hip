@@ -6,7 +6,7 @@
 // Stage 6: that list is per-expert counts or cumulative -- both are produced.
 //
 // Three small kernels, deterministic by construction (LDS atomics only count;
-// no atomic decides a position):
+// no atomic decides a position), or one block for small batches (perm_small):
 //   count   -- one block per chunk of 1024 pairs builds the chunk's histogram;
 //   scan    -- one block turns the chunk histograms into per-(chunk, expert)
 //              base rows, and writes counts and offsets;
@@ -114,6 +114,80 @@ __global__ __launch_bounds__(64) void perm_scatter(const int32_t* __restrict__ i
     }
 }
 
+// The whole permute of a small batch (P <= kSmallPairs) in one block of 16
+// waves.  Wave w owns the contiguous pair segment [w * seg, (w + 1) * seg):
+// it counts its pairs per expert (LDS atomics only count); one thread per
+// expert turns the 16 segment counts into running bases, the block scans
+// the expert totals into offsets, and each wave then scatters its segment
+// in order with the ballot multi-split of perm_scatter, from its own
+// per-expert cursors.  Segments are ordered by pair index, so rows inside
+// an expert stay in ascending pair order -- the same result as the three
+// kernels above.
+constexpr int kSmallWaves = 16;
+constexpr int64_t kSmallPairs = 4096;
+
+__global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ ids, int P, int E,
+                                                   int nbits, int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ row_to_pair,
+                                                   int32_t* __restrict__ pair_to_row) {
+    __shared__ int cur[kSmallWaves][kMaxExperts];
+    __shared__ int sh[1024];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < kSmallWaves * E; i += 1024) cur[i / E][i % E] = 0;
+    __syncthreads();
+    // segment of whole 64-pair steps per wave
+    const int seg = ((P + kSmallWaves * 64 - 1) / (kSmallWaves * 64)) * 64;
+    const int p0 = wave * seg, p1 = min(p0 + seg, P);
+    for (int p = p0 + lane; p < p1; p += 64) atomicAdd(&cur[wave][ids[p]], 1);
+    __syncthreads();
+    int run = 0;
+    if (tid < E) {
+#pragma unroll
+        for (int w = 0; w < kSmallWaves; ++w) {
+            const int c = cur[w][tid];
+            cur[w][tid] = run;
+            run += c;
+        }
+    }
+    int total;
+    const int off = block_exclusive_scan(tid < E ? run : 0, sh, total);
+    if (tid < E) {
+        counts[tid] = run;
+        offsets[tid] = off;
+#pragma unroll
+        for (int w = 0; w < kSmallWaves; ++w) cur[w][tid] += off;
+    }
+    if (tid == 0) offsets[E] = total;
+    __syncthreads();
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int s = p0; s < p1; s += 64) {
+        const int p = s + lane;
+        const bool valid = p < p1;
+        const int id = valid ? ids[p] : 0;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (id >> b) & 1;
+            const uint64_t bb = __ballot(valid && bit);
+            peers &= bit ? bb : ~bb;
+        }
+        const int rank = __popcll(peers & below);
+        const int cnt = __popcll(peers);
+        // every lane reads its expert's cursor before the lowest peer moves
+        // it (one LDS read, then one LDS write, in order within the wave)
+        const int b0 = valid ? cur[wave][id] : 0;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            const int row = b0 + rank;
+            row_to_pair[row] = p;
+            pair_to_row[p] = row;
+            if (rank == 0) cur[wave][id] = b0 + cnt;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 // Groups with 1..small_max rows get one tile each in the small list; larger
 // groups are cut into big_m-row tiles in the big list.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
@@ -204,6 +278,11 @@ hipError_t launch_permute(int64_t P, int32_t E, const int32_t* ids, int32_t* cou
     const int nchunk = permute_chunks(P);
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
+    if (P <= kSmallPairs) {
+        perm_small<<<1, 1024, 0, s>>>(ids, (int)P, E, nbits, counts, offsets, row_to_pair,
+                                      pair_to_row);
+        return hipGetLastError();
+    }
     if (nchunk > 0) perm_count<<<nchunk, 256, 0, s>>>(ids, P, E, chunk_scratch);
     perm_scan<<<1, 1024, 0, s>>>(nchunk, E, chunk_scratch, counts, offsets);
     if (nchunk > 0)

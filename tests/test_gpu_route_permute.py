@@ -139,6 +139,19 @@ def test_permute_matches_oracle(T, E, k):
     _compare_permute(ids, E, f"random_{T}_{E}_{k}")
 
 
+# Batches of up to 4096 pairs take the single-block permute: sizes around
+# that limit, partly filled and empty wave segments, the largest expert
+# count, and one hot expert group.
+@pytest.mark.parametrize("T,E,k", [(512, 384, 8), (513, 384, 8), (129, 384, 8), (3, 384, 8),
+                                   (100, 1024, 32), (4096, 2, 1), (4097, 2, 1), (65, 7, 7)])
+def test_permute_single_block_sizes(T, E, k):
+    logits = random_logits(T, E, seed=11 * T + E).numpy()
+    ids, _, _ = O.route(logits, O.RouteCfg(num_experts=E, top_k=k))
+    _compare_permute(ids, E, f"small_{T}_{E}_{k}")
+    hot = np.tile(np.arange(k), (T, 1))
+    _compare_permute(hot, E, f"small_hot_{T}_{E}_{k}")
+
+
 def test_permute_extreme_imbalance():
     # every token picks experts 0..k-1: k hot experts hold all rows
     T, E, k = 5000, 384, 8
@@ -165,8 +178,9 @@ def test_permute_empty():
     assert (npi(c) == 0).all() and (npi(off) == 0).all()
 
 
-def test_permute_is_deterministic():
-    T, E, k = 8192, 384, 8
+@pytest.mark.parametrize("T", [8192, 128])
+def test_permute_is_deterministic(T):
+    E, k = 384, 8
     logits = random_logits(T, E, seed=3).numpy()
     ids, _, _ = O.route(logits, O.RouteCfg(num_experts=E, top_k=k))
     it = torch.from_numpy(ids.astype(np.int32)).to(DEV)
