@@ -15,6 +15,7 @@
 
 #include "../../include/moe.h"
 #include "common.h"
+#include "router.h"
 
 using namespace moe;
 
@@ -322,6 +323,7 @@ struct ForwardWs {
     void* h_sh;     // shared intermediate [T, Is]
     float* sh;      // shared output [T, H] (no latent)
     int32_t* phys;  // physical slots of the pairs (with a placement)
+    float* rpart;   // K-slice partial router sums (bf16 batches of <= kRouterSplitMaxT)
 };
 
 // E: experts the permute and expert stages run over (the physical slots
@@ -350,6 +352,10 @@ ForwardWs carve_forward(Carve& c, const moe_route_cfg_t* cfg, moe_dtype_t dt, in
     w.h_sh = sh ? c.take<char>((size_t)max_T * sh->inter * es) : nullptr;
     w.sh = (sh && !lat) ? c.take<float>((size_t)max_T * H) : nullptr;
     w.phys = placed ? c.take<int32_t>((size_t)P) : nullptr;
+    w.rpart = dt == MOE_DTYPE_BF16
+                  ? c.take<float>((size_t)router_splits(El, H) *
+                                  (size_t)std::min<int64_t>(max_T, kRouterSplitMaxT) * El)
+                  : nullptr;
     return w;
 }
 
@@ -644,8 +650,14 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
     if (!logits) {
         float* lo = logits_out ? logits_out : w.logits;
         MOE_TRY(mark(MOE_STAGE_ROUTER, 0));
-        MOE_TRY(dense_gemm(dtype, T, x, H, w_router, H, nullptr, 0, nullptr, 0, E, EPI_F32_BIAS,
-                           lo, E, router_bias, s));
+        if (dtype == MOE_DTYPE_BF16 && T <= kRouterSplitMaxT) {
+            // few tokens: K split over workgroups, slices summed in order
+            MOE_HIP(launch_router_split((const bf16_t*)x, T, H, (const bf16_t*)w_router, E,
+                                        router_bias, w.rpart, lo, s));
+        } else {
+            MOE_TRY(dense_gemm(dtype, T, x, H, w_router, H, nullptr, 0, nullptr, 0, E,
+                               EPI_F32_BIAS, lo, E, router_bias, s));
+        }
         MOE_TRY(mark(MOE_STAGE_ROUTER, 1));
         logits = lo;
     } else {

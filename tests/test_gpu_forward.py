@@ -13,7 +13,7 @@ import torch
 
 import oracle as O
 import routed_mixture_experts_amd as moe
-from routed_mixture_experts_amd.synth import WORKLOADS, Workload, make_inputs, random_logits
+from routed_mixture_experts_amd.synth import WORKLOADS, Workload, make_inputs, random_logits, uniform
 from tests.helpers import (WEIGHT_ATOL, ExpertFetch, check_float, check_ids_allowing_near_ties,
                            latent_np, lib_cfg, log, np64, npi, oracle_cfg, shared_np)
 
@@ -128,6 +128,33 @@ def _gpu_forward(w: Workload, inp: dict, router_logits=None):
     torch.cuda.synchronize()
     res["out"] = out
     return res
+
+
+# Router logits of small bf16 batches come from the K-split router product
+# (up to 256 tokens); 257 tokens take the dense streaming path.  Checked
+# against the oracle's float64 product at the bar of the parity protocol,
+# with and without the bias row, for expert counts that do and do not fill
+# whole 16-expert blocks.
+@pytest.mark.parametrize("T,H,E", [(1, 256, 16), (17, 512, 1000), (100, 7168, 384),
+                                   (128, 7168, 384), (200, 1024, 72), (256, 4096, 256),
+                                   (257, 512, 384)])
+@pytest.mark.parametrize("biased", [False, True])
+def test_router_logits_small_batches(T, H, E, biased):
+    log(f"router logits T={T} H={H} E={E} bias={biased}")
+    w = Workload("router", T=T, H=H, E=E, k=2, I=64)
+    inp = make_inputs(w, DEV)
+    bias = uniform((E,), 2.0, 99, DEV) if biased else None
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    moe.moe_forward(lib_cfg(w), inp["x"], inp["w13"], inp["w2"], w_router=inp["w_router"],
+                    router_bias=bias, logits_out=logits)
+    torch.cuda.synchronize()
+    ref = O.router_logits(np64(inp["x"]), np64(inp["w_router"]),
+                          None if bias is None else np64(bias))
+    got = np64(logits)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    mx = np.abs(got - ref).max() / np.sqrt(np.mean(ref * ref))
+    log(f"  rel_l2={rel:.2e} max_abs/rms={mx:.2e}")
+    assert rel <= 1e-5 and mx <= 1e-4, (rel, mx)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
