@@ -26,6 +26,7 @@
 // taken in bands of row tiles so that the workgroups resident on one XCD share
 // both operands' K slices in its L2.
 #include "gemm_tiles.h"
+#include "router.h"
 
 namespace moe {
 
@@ -94,6 +95,11 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
 
     const int nk1 = g.K / TBK;
     const int nk = nk1 + (A2 ? g.K2 / TBK : 0);
+    // K slices (dense fp32 products, gridDim.y > 1): slice blockIdx.y takes
+    // stages [kt0, kt1) and writes its partial sums to its own M x N block
+    const int kt0 = (int)((int64_t)blockIdx.y * nk / gridDim.y);
+    const int kt1 = (int)((int64_t)(blockIdx.y + 1) * nk / gridDim.y);
+    float* cslice = (float*)g.C + (int64_t)blockIdx.y * g.M * g.ldc;
 
     u32x4_t ra[4], rb[4];
     uint32_t rb8[4][2];  // FP8 / MXFP4: raw codes, converted when stored to LDS
@@ -147,12 +153,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
 #pragma unroll
     for (int nj = 0; nj < 2; ++nj) brow[nj] = SW ? (nj * 64 + wn * 32) : (wn * 64 + nj * 32);
 
-    gload(0);
+    gload(kt0);
     sstore(0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int buf = (kt - kt0) & 1;
+        if (kt + 1 < kt1) gload(kt + 1);
         const bf16_t* sa = smem[buf][0];
         const bf16_t* sb = smem[buf][1];
 #pragma unroll
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
                     acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[nj],
                                                                            acc[mi][nj], 0, 0, 0);
         }
-        if (kt + 1 < nk) sstore(buf ^ 1);
+        if (kt + 1 < kt1) sstore(buf ^ 1);
         __syncthreads();
     }
 
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
                     if (EPI == EPI_OUT)
                         ((bf16_t*)g.C)[(int64_t)r * g.ldc + c] = f32_to_bf16(v);
                     else
-                        ((float*)g.C)[(int64_t)r * g.ldc + c] = v;
+                        cslice[(int64_t)r * g.ldc + c] = v;
                 }
             }
         }
@@ -605,6 +611,20 @@ void launch_big(const GemmArgs& g, dim3 gd, hipStream_t s) {
         default: gemm_bf16_big<EPI_SWIGLU, KC><<<gd, bd, 0, s>>>(g); break;
     }
 }
+
+}  // namespace
+
+hipError_t launch_tiled_kslices(const GemmArgs& g, int kslices, hipStream_t s) {
+    if (g.tiles || g.A2 || g.b_fmt != WF_BF16 || g.epi != EPI_F32 || kslices < 1 ||
+        kslices > g.K / TBK)
+        return hipErrorInvalidValue;
+    const int nm = (g.M + TBM - 1) / TBM;
+    const dim3 gd((unsigned)((int64_t)nm * ((g.N + TBN - 1) / TBN)), (unsigned)kslices), bd(256);
+    if (nm > 0) gemm_bf16_tiled<EPI_F32, WF_BF16><<<gd, bd, 0, s>>>(g);
+    return hipGetLastError();
+}
+
+namespace {
 
 int col_tiles(int path, int dtype, int epi, int N) {
     const bool sw = epi == EPI_SWIGLU;

@@ -354,10 +354,7 @@ ForwardWs carve_forward(Carve& c, const moe_route_cfg_t* cfg, moe_dtype_t dt, in
     w.h_sh = sh ? c.take<char>((size_t)max_T * sh->inter * es) : nullptr;
     w.sh = (sh && !lat) ? c.take<float>((size_t)max_T * H) : nullptr;
     w.phys = placed ? c.take<int32_t>((size_t)P) : nullptr;
-    w.rpart = dt == MOE_DTYPE_BF16
-                  ? c.take<float>((size_t)router_splits(El, H) *
-                                  (size_t)std::min<int64_t>(max_T, kRouterSplitMaxT) * El)
-                  : nullptr;
+    w.rpart = dt == MOE_DTYPE_BF16 ? c.take<float>(router_part_floats(max_T, El, H)) : nullptr;
     return w;
 }
 
@@ -655,6 +652,10 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
         if (dtype == MOE_DTYPE_BF16 && T <= kRouterSplitMaxT) {
             // few tokens: K split over workgroups, slices summed in order
             MOE_HIP(launch_router_split((const bf16_t*)x, T, H, (const bf16_t*)w_router, E,
+                                        router_bias, w.rpart, lo, s));
+        } else if (dtype == MOE_DTYPE_BF16 && router_tiled_splits(T, E, H) > 1) {
+            // a 128x128 grid too small for the chip: K split over slices
+            MOE_HIP(launch_router_tiled((const bf16_t*)x, T, H, (const bf16_t*)w_router, E,
                                         router_bias, w.rpart, lo, s));
         } else {
             MOE_TRY(dense_gemm(dtype, T, x, H, w_router, H, nullptr, 0, nullptr, 0, E,

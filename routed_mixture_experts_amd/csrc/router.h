@@ -20,4 +20,22 @@ int router_splits(int E, int H);
 hipError_t launch_router_split(const bf16_t* x, int64_t T, int H, const bf16_t* w, int E,
                                const float* bias, float* part, float* logits, hipStream_t s);
 
+// Larger batches whose 128x128 tile grid would leave CUs idle: K split over
+// the second grid dimension of the 128x128 kernel (1 when the grid is large
+// enough).
+int router_tiled_splits(int64_t T, int E, int H);
+
+// The same product with router_tiled_splits(T, E, H) > 1 slices, the slices
+// summed in order with the bias; part holds that many T x E floats.
+hipError_t launch_router_tiled(const bf16_t* x, int64_t T, int H, const bf16_t* w, int E,
+                               const float* bias, float* part, float* logits, hipStream_t s);
+
+// Floats of partial sums either split product needs for any T <= max_T.
+size_t router_part_floats(int64_t max_T, int E, int H);
+
+// A dense fp32 product (g.epi == EPI_F32, no tile list) in 128x128 tiles
+// with K split into kslices: slice s writes its partial sums to
+// C + s * M * ldc.  Defined with the kernel in gemm.hip.
+hipError_t launch_tiled_kslices(const GemmArgs& g, int kslices, hipStream_t s);
+
 }  // namespace moe

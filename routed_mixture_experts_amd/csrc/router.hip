@@ -14,6 +14,8 @@
 // scheduling.
 #include "router.h"
 
+#include <string.h>
+
 #include <algorithm>
 
 namespace moe {
@@ -141,6 +143,53 @@ hipError_t launch_router_split(const bf16_t* x, int64_t T, int H, const bf16_t* 
     else if (T <= 128) launch_partial<8>(x, t, H, w, E, part, bias, logits, s);
     else launch_partial<16>(x, t, H, w, E, part, bias, logits, s);
     return hipGetLastError();
+}
+
+int router_tiled_splits(int64_t T, int E, int H) {
+    const int64_t tiles = ((T + 127) / 128) * ((E + 127) / 128);
+    if (tiles >= 256) return 1;
+    // about two workgroups per CU, at least 8 stages of 64 per slice
+    const int64_t by_cus = (512 + tiles - 1) / tiles;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(by_cus, (H / 64) / 8));
+}
+
+hipError_t launch_router_tiled(const bf16_t* x, int64_t T, int H, const bf16_t* w, int E,
+                               const float* bias, float* part, float* logits, hipStream_t s) {
+    const int nsplit = router_tiled_splits(T, E, H);
+    if (T <= 0 || T > INT32_MAX || nsplit < 2) return hipErrorInvalidValue;
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.A = x;
+    g.lda = H;
+    g.a_div = 1;
+    g.B = w;
+    g.K = H;
+    g.N = E;
+    g.M = (int32_t)T;
+    g.epi = EPI_F32;
+    g.C = part;
+    g.ldc = E;
+    const hipError_t e = launch_tiled_kslices(g, nsplit, s);
+    if (e != hipSuccess) return e;
+    const int64_t n = T * E;
+    router_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, nsplit, n, E, bias,
+                                                                     logits);
+    return hipGetLastError();
+}
+
+size_t router_part_floats(int64_t max_T, int E, int H) {
+    size_t n = (size_t)router_splits(E, H) * (size_t)std::min<int64_t>(max_T, kRouterSplitMaxT) *
+               (size_t)E;
+    // the sliced 128x128 product: slices x T peaks at the top of a band of
+    // 128 rows; only grids under 256 tiles (T < 32768) are sliced
+    for (int64_t hi = kRouterSplitMaxT + 128; ; hi += 128) {
+        const int64_t t = std::min(hi, max_T);
+        if (t <= kRouterSplitMaxT) break;
+        const int ks = router_tiled_splits(t, E, H);
+        if (ks > 1) n = std::max(n, (size_t)ks * (size_t)t * (size_t)E);
+        if (t == max_T || ks == 1) break;
+    }
+    return n;
 }
 
 }  // namespace moe

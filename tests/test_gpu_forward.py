@@ -130,14 +130,16 @@ def _gpu_forward(w: Workload, inp: dict, router_logits=None):
     return res
 
 
-# Router logits of small bf16 batches come from the K-split router product
-# (up to 256 tokens); 257 tokens take the dense streaming path.  Checked
-# against the oracle's float64 product at the bar of the parity protocol,
-# with and without the bias row, for expert counts that do and do not fill
-# whole 16-expert blocks.
+# Router logits of bf16 batches: up to 256 tokens the K-split router
+# product; above, 128x128 tiles with K split over slices while their grid is
+# under 256 tiles (300..8192 tokens here), else the dense path (257 tokens
+# with K = 512 is too short to slice).  Checked against the oracle's float64
+# product at the bar of the parity protocol, with and without the bias row,
+# for expert counts that do and do not fill whole 16-expert blocks.
 @pytest.mark.parametrize("T,H,E", [(1, 256, 16), (17, 512, 1000), (100, 7168, 384),
                                    (128, 7168, 384), (200, 1024, 72), (256, 4096, 256),
-                                   (257, 512, 384)])
+                                   (257, 512, 384), (300, 7168, 384), (1000, 1024, 72),
+                                   (2048, 7168, 256), (4096, 4096, 256), (8192, 7168, 384)])
 @pytest.mark.parametrize("biased", [False, True])
 def test_router_logits_small_batches(T, H, E, biased):
     log(f"router logits T={T} H={H} E={E} bias={biased}")
