@@ -354,7 +354,12 @@ ForwardWs carve_forward(Carve& c, const moe_route_cfg_t* cfg, moe_dtype_t dt, in
     w.h_sh = sh ? c.take<char>((size_t)max_T * sh->inter * es) : nullptr;
     w.sh = (sh && !lat) ? c.take<float>((size_t)max_T * H) : nullptr;
     w.phys = placed ? c.take<int32_t>((size_t)P) : nullptr;
-    w.rpart = dt == MOE_DTYPE_BF16 ? c.take<float>(router_part_floats(max_T, El, H)) : nullptr;
+    // partial sums of the K-sliced products: the router, and the latent
+    // down-projection (one after the other, so they share the buffer)
+    w.rpart = dt == MOE_DTYPE_BF16
+                  ? c.take<float>(std::max(router_part_floats(max_T, El, H),
+                                           lat ? dense_part_floats(max_T, D, H) : (size_t)0))
+                  : nullptr;
     return w;
 }
 
@@ -674,8 +679,16 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
     const void* xin = x;
     if (latent) {
         MOE_TRY(mark(MOE_STAGE_DOWNPROJ, 0));
-        MOE_TRY(dense_gemm(dtype, T, x, H, latent->w_down, H, nullptr, 0, nullptr, 0, D, EPI_OUT,
-                           w.z, D, nullptr, s));
+        if (dtype == MOE_DTYPE_BF16 && T > kRouterSplitMaxT &&
+            dense_path(dtype, T, D, EPI_OUT) == GEMM_TILED && dense_tiled_splits(T, D, H) > 1) {
+            // a 128x128 grid that leaves CUs idle: K split over slices
+            MOE_HIP(launch_dense_sliced_bf16((const bf16_t*)x, T, H,
+                                             (const bf16_t*)latent->w_down, D, w.rpart,
+                                             (bf16_t*)w.z, s));
+        } else {
+            MOE_TRY(dense_gemm(dtype, T, x, H, latent->w_down, H, nullptr, 0, nullptr, 0, D,
+                               EPI_OUT, w.z, D, nullptr, s));
+        }
         MOE_TRY(mark(MOE_STAGE_DOWNPROJ, 1));
         xin = w.z;
     } else {

@@ -33,6 +33,16 @@ hipError_t launch_router_tiled(const bf16_t* x, int64_t T, int H, const bf16_t* 
 // Floats of partial sums either split product needs for any T <= max_T.
 size_t router_part_floats(int64_t max_T, int E, int H);
 
+// Dense bf16 products C[T, N] = A[T, K] . B[N, K]^T whose 128x128 grid would
+// leave CUs idle (under 384 tiles): K split into dense_tiled_splits(T, N, K)
+// slices (1: not split), the slices summed in order and rounded once to
+// bf16.  part holds that many T x N floats; dense_part_floats bounds it for
+// any T <= max_T.  N a multiple of 4.
+int dense_tiled_splits(int64_t T, int N, int K);
+hipError_t launch_dense_sliced_bf16(const bf16_t* A, int64_t T, int K, const bf16_t* B, int N,
+                                    float* part, bf16_t* out, hipStream_t s);
+size_t dense_part_floats(int64_t max_T, int N, int K);
+
 // A dense fp32 product (g.epi == EPI_F32, no tile list) in 128x128 tiles
 // with K split into kslices: slice s writes its partial sums to
 // C + s * M * ldc.  Defined with the kernel in gemm.hip.

@@ -107,6 +107,22 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restr
     logits[i] = v;
 }
 
+// The same in-order sum of the slices, rounded once to bf16, four outputs
+// per thread (n a multiple of 4).
+__global__ __launch_bounds__(256) void slices_to_bf16_kernel(const float* __restrict__ part,
+                                                             int nsplit, int64_t n,
+                                                             bf16_t* __restrict__ out) {
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i >= n) return;
+    f32x4_t v = *(const f32x4_t*)(part + i);
+    for (int s = 1; s < nsplit; ++s) {
+        const f32x4_t u = *(const f32x4_t*)(part + (int64_t)s * n + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += u[q];
+    }
+    *(uint2*)(out + i) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+
 // K slices for a batch of ntb token blocks (whole k-steps, at most
 // 4 * steps_per_wave(ntb) per slice)
 int splits_for(int H, int ntb) {
@@ -175,6 +191,48 @@ hipError_t launch_router_tiled(const bf16_t* x, int64_t T, int H, const bf16_t* 
     router_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, nsplit, n, E, bias,
                                                                      logits);
     return hipGetLastError();
+}
+
+int dense_tiled_splits(int64_t T, int N, int K) {
+    const int64_t tiles = ((T + 127) / 128) * ((N + 127) / 128);
+    if (tiles >= 384) return 1;
+    const int64_t by_cus = (512 + tiles - 1) / tiles;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(by_cus, (K / 64) / 8));
+}
+
+hipError_t launch_dense_sliced_bf16(const bf16_t* A, int64_t T, int K, const bf16_t* B, int N,
+                                    float* part, bf16_t* out, hipStream_t s) {
+    const int nsplit = dense_tiled_splits(T, N, K);
+    if (T <= 0 || T > INT32_MAX || nsplit < 2 || N % 4 != 0) return hipErrorInvalidValue;
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.A = A;
+    g.lda = K;
+    g.a_div = 1;
+    g.B = B;
+    g.K = K;
+    g.N = N;
+    g.M = (int32_t)T;
+    g.epi = EPI_F32;
+    g.C = part;
+    g.ldc = N;
+    const hipError_t e = launch_tiled_kslices(g, nsplit, s);
+    if (e != hipSuccess) return e;
+    const int64_t n = T * N;
+    slices_to_bf16_kernel<<<(unsigned)((n / 4 + 255) / 256), 256, 0, s>>>(part, nsplit, n, out);
+    return hipGetLastError();
+}
+
+size_t dense_part_floats(int64_t max_T, int N, int K) {
+    size_t n = 0;
+    for (int64_t hi = 128; ; hi += 128) {
+        const int64_t t = std::min(hi, max_T);
+        if (t <= 0) break;
+        const int ks = dense_tiled_splits(t, N, K);
+        if (ks > 1) n = std::max(n, (size_t)ks * (size_t)t * (size_t)N);
+        if (t == max_T || ks == 1) break;
+    }
+    return n;
 }
 
 size_t router_part_floats(int64_t max_T, int E, int H) {

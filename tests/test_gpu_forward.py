@@ -90,6 +90,10 @@ SMALL = {
     "latent_like": Workload("latent_like", T=200, H=512, E=16, k=4, I=128, latent=256,
                             shared_inter=192, gamma_std=0.1),
     "latent_noshared": Workload("latent_noshared", T=130, H=256, E=8, k=2, I=128, latent=192),
+    # over 256 tokens with K = 1024: the router and the latent down-projection
+    # take the K-sliced 128x128 products
+    "latent_sliced": Workload("latent_sliced", T=520, H=1024, E=16, k=4, I=128, latent=320,
+                              shared_inter=128, gamma_std=0.1),
     "shared_only": Workload("shared_only", T=90, H=256, E=8, k=2, I=128, shared_inter=128),
     "sigmoid_decode": Workload("sigmoid_decode", T=7, H=256, E=64, k=8, I=128,
                                score="sigmoid", renormalize=False, corr_bias=0.2),
