@@ -7,14 +7,16 @@
 //
 // Three small kernels, deterministic by construction (LDS atomics only count;
 // no atomic decides a position), or one block for small batches (perm_small):
-//   count   -- one block per chunk of 1024 pairs builds the chunk's histogram;
+//   count   -- one block per chunk of 4096 pairs builds the chunk's histogram;
 //   scan    -- one block turns the chunk histograms into per-(chunk, expert)
 //              base rows, and writes counts and offsets;
-//   scatter -- one wavefront per chunk walks its pairs in order, 64 at a
-//              time; lanes holding the same expert find each other with one
-//              ballot per id bit (a wave-wide multi-split), take their rank
-//              among lower lanes, and the lowest of them advances the
-//              expert's running row in LDS.
+//   scatter -- one block of 16 waves per chunk: each wave owns a contiguous
+//              segment of the chunk and counts it per expert, the block
+//              turns the chunk's base rows into per-wave bases, and each wave
+//              walks its segment in order, 64 pairs at a time; lanes holding
+//              the same expert find each other with one ballot per id bit (a
+//              wave-wide multi-split), take their rank among lower lanes, and
+//              the lowest of them advances the expert's running row in LDS.
 // A fourth kernel turns the offsets into the tile list of a grouped GEMM.
 #include "common.h"
 
@@ -22,7 +24,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kChunk = 1024;
+constexpr int kChunk = 4096;
 
 __global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ ids, int64_t P,
                                                    int E, int32_t* __restrict__ chunk_counts) {
@@ -79,91 +81,24 @@ __global__ __launch_bounds__(1024) void perm_scan(int nchunk, int E, int32_t* __
     if (e == 0) offsets[E] = total;
 }
 
-__global__ __launch_bounds__(64) void perm_scatter(const int32_t* __restrict__ ids, int64_t P,
-                                                   int E, int nbits,
-                                                   const int32_t* __restrict__ chunk_base,
-                                                   int32_t* __restrict__ row_to_pair,
-                                                   int32_t* __restrict__ pair_to_row) {
-    __shared__ int cur[kMaxExperts];
-    const int lane = threadIdx.x;
-    for (int e = lane; e < E; e += 64) cur[e] = chunk_base[(int64_t)blockIdx.x * E + e];
-    __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kChunk;
-    const uint64_t below = (1ull << lane) - 1ull;
-    for (int s = 0; s < kChunk && base + s < P; s += 64) {
-        const int64_t p = base + s + lane;
-        const bool valid = p < P;
-        const int id = valid ? ids[p] : 0;
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (id >> b) & 1;
-            const uint64_t bb = __ballot(valid && bit);
-            peers &= bit ? bb : ~bb;
-        }
-        const int rank = __popcll(peers & below);
-        const int cnt = __popcll(peers);
-        const int b0 = valid ? cur[id] : 0;
-        __syncthreads();
-        if (valid) {
-            const int row = b0 + rank;
-            row_to_pair[row] = (int32_t)p;
-            pair_to_row[p] = row;
-            if (rank == 0) cur[id] = b0 + cnt;
-        }
-        __syncthreads();
-    }
+constexpr int kScatterWaves = 16;
+
+// Per-wave segments of a chunk: whole 64-pair steps.
+__device__ __forceinline__ int segment_len(int n) {
+    return ((n + kScatterWaves * 64 - 1) / (kScatterWaves * 64)) * 64;
 }
 
-// The whole permute of a small batch (P <= kSmallPairs) in one block of 16
-// waves.  Wave w owns the contiguous pair segment [w * seg, (w + 1) * seg):
-// it counts its pairs per expert (LDS atomics only count); one thread per
-// expert turns the 16 segment counts into running bases, the block scans
-// the expert totals into offsets, and each wave then scatters its segment
-// in order with the ballot multi-split of perm_scatter, from its own
-// per-expert cursors.  Segments are ordered by pair index, so rows inside
-// an expert stay in ascending pair order -- the same result as the three
-// kernels above.
-constexpr int kSmallWaves = 16;
-constexpr int64_t kSmallPairs = 4096;
-
-__global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ ids, int P, int E,
-                                                   int nbits, int32_t* __restrict__ counts,
-                                                   int32_t* __restrict__ offsets,
-                                                   int32_t* __restrict__ row_to_pair,
-                                                   int32_t* __restrict__ pair_to_row) {
-    __shared__ int cur[kSmallWaves][kMaxExperts];
-    __shared__ int sh[1024];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int i = tid; i < kSmallWaves * E; i += 1024) cur[i / E][i % E] = 0;
-    __syncthreads();
-    // segment of whole 64-pair steps per wave
-    const int seg = ((P + kSmallWaves * 64 - 1) / (kSmallWaves * 64)) * 64;
-    const int p0 = wave * seg, p1 = min(p0 + seg, P);
-    for (int p = p0 + lane; p < p1; p += 64) atomicAdd(&cur[wave][ids[p]], 1);
-    __syncthreads();
-    int run = 0;
-    if (tid < E) {
-#pragma unroll
-        for (int w = 0; w < kSmallWaves; ++w) {
-            const int c = cur[w][tid];
-            cur[w][tid] = run;
-            run += c;
-        }
-    }
-    int total;
-    const int off = block_exclusive_scan(tid < E ? run : 0, sh, total);
-    if (tid < E) {
-        counts[tid] = run;
-        offsets[tid] = off;
-#pragma unroll
-        for (int w = 0; w < kSmallWaves; ++w) cur[w][tid] += off;
-    }
-    if (tid == 0) offsets[E] = total;
-    __syncthreads();
+// Wave `wave` scatters pairs [p0, p1) in order from its cursors cur[id]
+// (advanced as it goes): row = cursor + rank among lower lanes with the same
+// id, found by one ballot per id bit.
+__device__ __forceinline__ void scatter_segment(const int32_t* __restrict__ ids, int64_t p0,
+                                                int64_t p1, int nbits, int* cur,
+                                                int32_t* __restrict__ row_to_pair,
+                                                int32_t* __restrict__ pair_to_row) {
+    const int lane = threadIdx.x & 63;
     const uint64_t below = (1ull << lane) - 1ull;
-    for (int s = p0; s < p1; s += 64) {
-        const int p = s + lane;
+    for (int64_t s = p0; s < p1; s += 64) {
+        const int64_t p = s + lane;
         const bool valid = p < p1;
         const int id = valid ? ids[p] : 0;
         uint64_t peers = __ballot(valid);
@@ -176,16 +111,93 @@ __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ i
         const int cnt = __popcll(peers);
         // every lane reads its expert's cursor before the lowest peer moves
         // it (one LDS read, then one LDS write, in order within the wave)
-        const int b0 = valid ? cur[wave][id] : 0;
+        const int b0 = valid ? cur[id] : 0;
         __builtin_amdgcn_wave_barrier();
         if (valid) {
             const int row = b0 + rank;
-            row_to_pair[row] = p;
+            row_to_pair[row] = (int32_t)p;
             pair_to_row[p] = row;
-            if (rank == 0) cur[wave][id] = b0 + cnt;
+            if (rank == 0) cur[id] = b0 + cnt;
         }
         __builtin_amdgcn_wave_barrier();
     }
+}
+
+__global__ __launch_bounds__(1024) void perm_scatter(const int32_t* __restrict__ ids, int64_t P,
+                                                     int E, int nbits,
+                                                     const int32_t* __restrict__ chunk_base,
+                                                     int32_t* __restrict__ row_to_pair,
+                                                     int32_t* __restrict__ pair_to_row) {
+    __shared__ int cur[kScatterWaves][kMaxExperts];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < kScatterWaves * E; i += 1024) cur[i / E][i % E] = 0;
+    __syncthreads();
+    const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+    const int n = (int)min((int64_t)kChunk, P - c0);
+    const int seg = segment_len(n);
+    const int64_t p0 = c0 + min(wave * seg, n), p1 = c0 + min((wave + 1) * seg, n);
+    for (int64_t p = p0 + lane; p < p1; p += 64) atomicAdd(&cur[wave][ids[p]], 1);
+    __syncthreads();
+    if (tid < E) {
+        int run = chunk_base[(int64_t)blockIdx.x * E + tid];
+#pragma unroll
+        for (int w = 0; w < kScatterWaves; ++w) {
+            const int c = cur[w][tid];
+            cur[w][tid] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    scatter_segment(ids, p0, p1, nbits, cur[wave], row_to_pair, pair_to_row);
+}
+
+// The whole permute of a small batch (P <= kSmallPairs) in one block of 16
+// waves.  Wave w owns the contiguous pair segment [w * seg, (w + 1) * seg):
+// it counts its pairs per expert (LDS atomics only count); one thread per
+// expert turns the 16 segment counts into running bases, the block scans
+// the expert totals into offsets, and each wave then scatters its segment
+// in order with the ballot multi-split of perm_scatter, from its own
+// per-expert cursors.  Segments are ordered by pair index, so rows inside
+// an expert stay in ascending pair order -- the same result as the three
+// kernels above.
+constexpr int64_t kSmallPairs = kChunk;
+
+__global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ ids, int P, int E,
+                                                   int nbits, int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ row_to_pair,
+                                                   int32_t* __restrict__ pair_to_row) {
+    __shared__ int cur[kScatterWaves][kMaxExperts];
+    __shared__ int sh[1024];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < kScatterWaves * E; i += 1024) cur[i / E][i % E] = 0;
+    __syncthreads();
+    const int seg = segment_len(P);
+    const int p0 = min(wave * seg, P), p1 = min((wave + 1) * seg, P);
+    for (int p = p0 + lane; p < p1; p += 64) atomicAdd(&cur[wave][ids[p]], 1);
+    __syncthreads();
+    int run = 0;
+    if (tid < E) {
+#pragma unroll
+        for (int w = 0; w < kScatterWaves; ++w) {
+            const int c = cur[w][tid];
+            cur[w][tid] = run;
+            run += c;
+        }
+    }
+    int total;
+    const int off = block_exclusive_scan(tid < E ? run : 0, sh, total);
+    if (tid < E) {
+        counts[tid] = run;
+        offsets[tid] = off;
+#pragma unroll
+        for (int w = 0; w < kScatterWaves; ++w) cur[w][tid] += off;
+    }
+    if (tid == 0) offsets[E] = total;
+    __syncthreads();
+    scatter_segment(ids, p0, p1, nbits, cur[wave], row_to_pair, pair_to_row);
 }
 
 // Groups with 1..small_max rows get one tile each in the small list; larger
@@ -286,8 +298,8 @@ hipError_t launch_permute(int64_t P, int32_t E, const int32_t* ids, int32_t* cou
     if (nchunk > 0) perm_count<<<nchunk, 256, 0, s>>>(ids, P, E, chunk_scratch);
     perm_scan<<<1, 1024, 0, s>>>(nchunk, E, chunk_scratch, counts, offsets);
     if (nchunk > 0)
-        perm_scatter<<<nchunk, 64, 0, s>>>(ids, P, E, nbits, chunk_scratch, row_to_pair,
-                                           pair_to_row);
+        perm_scatter<<<nchunk, 1024, 0, s>>>(ids, P, E, nbits, chunk_scratch, row_to_pair,
+                                             pair_to_row);
     return hipGetLastError();
 }
 
