@@ -99,6 +99,29 @@ def test_workspace_sizes_grow_with_capacity(lib):
     assert lib.moe_forward_workspace(ctypes.byref(c), 7, 128, 7168, 2048, None, None) == 0
 
 
+@pytest.mark.parametrize("E,H,latent", [(384, 7168, None), (256, 4096, None), (16, 1024, 320),
+                                         (256, 7168, 2048), (1000, 512, None)])
+def test_forward_workspace_never_shrinks_with_capacity(lib, E, H, latent):
+    # A workspace sized for max_T must be accepted for every T <= max_T: the
+    # forward checks ws_bytes against the size for its own T.  The partial
+    # sums of the K-sliced router and latent products peak at different
+    # batch sizes, so the size is checked at every batch size up to 2100 and
+    # at the band edges of larger ones.
+    c = _cfg(num_experts=E, top_k=8)
+    lat = None
+    if latent:
+        # the size query checks the description but reads no weights
+        lat = L.moe_latent_t(w_down=256, gamma=256, w_up=256, latent=latent, rms_eps=1e-6)
+    sizes = []
+    Ts = list(range(1, 2101)) + [4095, 4096, 4097, 8191, 8192, 8193, 16384, 32768, 40000]
+    for T in Ts:
+        n = lib.moe_forward_workspace(ctypes.byref(c), L.MOE_DTYPE_BF16, T, H, 256,
+                                      ctypes.byref(lat) if lat else None, None)
+        assert n > 0, T
+        sizes.append(n)
+    assert all(b >= a for a, b in zip(sizes, sizes[1:]))
+
+
 def test_forward_rejects_unaligned_and_missing(lib):
     c = _cfg(num_experts=8, top_k=2)
     # H not a multiple of 64
