@@ -28,6 +28,8 @@
 #include "gemm_tiles.h"
 #include "router.h"
 
+#include <type_traits>
+
 namespace moe {
 
 namespace {
@@ -353,8 +355,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         }
     }
 
-    // does this wave's 128-row half hold any row of the tile (wave-uniform)
+    // does this wave's 128-row half hold any row of the tile (wave-uniform),
+    // and how many of its 32-row blocks do
     const bool active = tc.row1 - tc.row0 > wm * 128;
+    const int nact = min(max((tc.row1 - tc.row0 - wm * 128 + 31) / 32, 0), 4);
 
     // Fragments of one half stage (two 16-deep steps).
     struct Frags {
@@ -386,6 +390,63 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         mma_step(f, 1);
     };
 
+    // A wave with 1..3 of its 32-row blocks inside the tile (the last tile
+    // of a group) runs the same loop over those blocks only: the blocks past
+    // the tile's end cost neither LDS reads nor MFMAs.
+    auto partial_loop = [&](auto NA) __attribute__((always_inline)) {
+        constexpr int na = decltype(NA)::value;
+        auto rd = [&](int kt, int h, Frags& f) __attribute__((always_inline)) {
+            const bf16_t* a = smem[kt & (GSLOTS - 1)][0];
+            const bf16_t* b = smem[kt & (GSLOTS - 1)][1];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int ks = 2 * h + s2;
+#pragma unroll
+                for (int nj = 0; nj < 2; ++nj)
+                    f.b[s2][nj] = *(const bf16x8_t*)(&b[boffs[ks][nj]]);
+#pragma unroll
+                for (int mi = 0; mi < na; ++mi)
+                    f.a[s2][mi] = *(const bf16x8_t*)(&a[aoffs[ks][mi]]);
+            }
+        };
+        auto step = [&](const Frags& f, int s2) __attribute__((always_inline)) {
+#pragma unroll
+            for (int mi = 0; mi < na; ++mi)
+#pragma unroll
+                for (int nj = 0; nj < 2; ++nj)
+                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        f.a[s2][mi], f.b[s2][nj], acc[mi][nj], 0, 0, 0);
+        };
+        issue(0);
+        issue(1);
+        wait_vmcnt_lgkm0<8>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        Frags g0, g1;
+        rd(0, 0, g0);
+        for (int kt = 0; kt < nk; ++kt) {
+            rd(kt, 1, g1);
+            step(g0, 0);
+            step(g0, 1);
+            asm volatile("" ::: "memory");
+            wait_vmcnt_lgkm0<0>();
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            issue_blocks(kt + 2, 0, 2);
+            rd(kt + 1, 0, g0);
+            step(g1, 0);
+            asm volatile("" ::: "memory");
+            issue_blocks(kt + 2, 2, 4);
+            asm volatile("" ::: "memory");
+            step(g1, 1);
+            asm volatile("" ::: "memory");
+        }
+    };
+    // (not in the K-concatenated form, whose registers it would spill)
+    if (!KCAT && nact == 1) partial_loop(std::integral_constant<int, 1>{});
+    else if (!KCAT && nact == 2) partial_loop(std::integral_constant<int, 2>{});
+    else if (!KCAT && nact == 3) partial_loop(std::integral_constant<int, 3>{});
+    else {
     issue(0);
     issue(1);
     wait_vmcnt_lgkm0<8>();  // this wave's part of stage 0 has landed
@@ -418,6 +479,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         asm volatile("" ::: "memory");
         if (active) mma_step(f1, 1);
         asm volatile("" ::: "memory");
+    }
     }
     // The ring's trailing DMAs must land before the LDS is reused below.
     wait_vmcnt<0>();
