@@ -15,6 +15,7 @@
 
 #include "../../include/moe.h"
 #include "common.h"
+#include "permute.h"
 #include "router.h"
 
 using namespace moe;
@@ -209,14 +210,17 @@ moe_status_t side_stream(SideStream** out) {
 // GEMM2 covers the rest of both chains.
 constexpr int64_t kOverlapMinRows = 16;
 
+// tiles_built: the tile lists in w already match offsets (the forward's
+// single-block permute writes them).
 moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, const void* x,
                          const int32_t* offsets, const int32_t* row_to_pair,
                          const ExpertWeights& ew, float* y_rows, const ExpertsWs& w,
-                         hipStream_t s, hipEvent_t* ev) {
+                         hipStream_t s, hipEvent_t* ev, bool tiles_built = false) {
     const int64_t P = T * k;
     const bool f32 = dt == MOE_DTYPE_F32;
-    MOE_HIP(launch_build_tiles(offsets, E, f32 ? 0 : kStreamMaxRows, large_rows(dt, ew.fmt),
-                               w.small_tiles, w.counts, w.big_tiles, w.counts + 1, s));
+    if (!tiles_built)
+        MOE_HIP(launch_build_tiles(offsets, E, f32 ? 0 : kStreamMaxRows, large_rows(dt, ew.fmt),
+                                   w.small_tiles, w.counts, w.big_tiles, w.counts + 1, s));
     if (ev) MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM1], s));
 
     GemmArgs g1 = gemm_defaults();
@@ -712,13 +716,23 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
         MOE_HIP(launch_log2phy(T * k, ids, placement->log2phy, E, Es, w.phys, s));
         disp = w.phys;
     }
-    MOE_HIP(launch_permute(T * k, Es, disp, counts, w.offsets, w.r2p, w.p2r, w.chunks, s));
+    // small batches: one block permutes and writes the GEMM tile lists
+    const bool tiles_built = T * k <= kSmallPermutePairs;
+    if (tiles_built) {
+        MOE_HIP(launch_permute_small_with_tiles(
+            T * k, Es, disp, counts, w.offsets, w.r2p, w.p2r,
+            dtype == MOE_DTYPE_F32 ? 0 : kStreamMaxRows, large_rows(dtype, ew.fmt),
+            w.ex.small_tiles, w.ex.counts, w.ex.big_tiles, w.ex.counts + 1, s));
+    } else {
+        MOE_HIP(launch_permute(T * k, Es, disp, counts, w.offsets, w.r2p, w.p2r, w.chunks, s));
+    }
     if (placement && placement->load)
         MOE_HIP(launch_load_accumulate(Es, counts, placement->load, s));
     MOE_TRY(mark(MOE_STAGE_PERMUTE, 1));
 
     // routed experts
-    MOE_TRY(run_experts(dtype, T, k, Es, D, I, xin, w.offsets, w.r2p, ew, w.y_rows, w.ex, s, ev));
+    MOE_TRY(run_experts(dtype, T, k, Es, D, I, xin, w.offsets, w.r2p, ew, w.y_rows, w.ex, s, ev,
+                        tiles_built));
 
     // shared expert without a latent tail: its output is the combine addend
     if (shared && !latent) {

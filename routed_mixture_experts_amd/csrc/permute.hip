@@ -18,7 +18,7 @@
 //              wave-wide multi-split), take their rank among lower lanes, and
 //              the lowest of them advances the expert's running row in LDS.
 // A fourth kernel turns the offsets into the tile list of a grouped GEMM.
-#include "common.h"
+#include "permute.h"
 
 namespace moe {
 
@@ -162,12 +162,23 @@ __global__ __launch_bounds__(1024) void perm_scatter(const int32_t* __restrict__
 // an expert stay in ascending pair order -- the same result as the three
 // kernels above.
 constexpr int64_t kSmallPairs = kChunk;
+static_assert(kSmallPairs == kSmallPermutePairs, "single-block permute limit");
+
+// Tile lists of the grouped GEMMs, written by perm_small when tiles != null.
+struct TileOut {
+    int32_t small_max, big_m;
+    Tile* small_tiles;
+    int32_t* num_small;
+    Tile* big_tiles;
+    int32_t* num_big;
+};
 
 __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ ids, int P, int E,
                                                    int nbits, int32_t* __restrict__ counts,
                                                    int32_t* __restrict__ offsets,
                                                    int32_t* __restrict__ row_to_pair,
-                                                   int32_t* __restrict__ pair_to_row) {
+                                                   int32_t* __restrict__ pair_to_row,
+                                                   TileOut tiles) {
     __shared__ int cur[kScatterWaves][kMaxExperts];
     __shared__ int sh[1024];
     const int tid = threadIdx.x;
@@ -196,6 +207,36 @@ __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ i
         for (int w = 0; w < kScatterWaves; ++w) cur[w][tid] += off;
     }
     if (tid == 0) offsets[E] = total;
+    if (tiles.small_tiles) {
+        // the tile lists of build_tiles_kernel, from this block's offsets
+        const bool small = run > 0 && run <= tiles.small_max;
+        const int nb = small || tid >= E ? 0 : (run + tiles.big_m - 1) / tiles.big_m;
+        int total_s, total_b;
+        const int start_s = block_exclusive_scan(small ? 1 : 0, sh, total_s);
+        const int start_b = block_exclusive_scan(nb, sh, total_b);
+        if (small) {
+            Tile t = {};
+            t.group = tid;
+            t.row0 = off;
+            t.row1 = off + run;
+            t.first = start_s;
+            t.count = 1;
+            tiles.small_tiles[start_s] = t;
+        }
+        for (int i = 0; i < nb; ++i) {
+            Tile t = {};
+            t.group = tid;
+            t.row0 = off + i * tiles.big_m;
+            t.row1 = min(off + (i + 1) * tiles.big_m, off + run);
+            t.first = start_b;
+            t.count = nb;
+            tiles.big_tiles[start_b + i] = t;
+        }
+        if (tid == 0) {
+            *tiles.num_small = total_s;
+            *tiles.num_big = total_b;
+        }
+    }
     __syncthreads();
     scatter_segment(ids, p0, p1, nbits, cur[wave], row_to_pair, pair_to_row);
 }
@@ -292,7 +333,7 @@ hipError_t launch_permute(int64_t P, int32_t E, const int32_t* ids, int32_t* cou
     while ((1 << nbits) < E) ++nbits;
     if (P <= kSmallPairs) {
         perm_small<<<1, 1024, 0, s>>>(ids, (int)P, E, nbits, counts, offsets, row_to_pair,
-                                      pair_to_row);
+                                      pair_to_row, TileOut{});
         return hipGetLastError();
     }
     if (nchunk > 0) perm_count<<<nchunk, 256, 0, s>>>(ids, P, E, chunk_scratch);
@@ -300,6 +341,22 @@ hipError_t launch_permute(int64_t P, int32_t E, const int32_t* ids, int32_t* cou
     if (nchunk > 0)
         perm_scatter<<<nchunk, 1024, 0, s>>>(ids, P, E, nbits, chunk_scratch, row_to_pair,
                                              pair_to_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_small_with_tiles(int64_t P, int32_t E, const int32_t* ids,
+                                           int32_t* counts, int32_t* offsets,
+                                           int32_t* row_to_pair, int32_t* pair_to_row,
+                                           int32_t small_max, int32_t big_m, Tile* small_tiles,
+                                           int32_t* num_small, Tile* big_tiles, int32_t* num_big,
+                                           hipStream_t s) {
+    if (P > kSmallPairs || E > kMaxExperts || !small_tiles || big_m < 1)
+        return hipErrorInvalidValue;
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const TileOut t{small_max, big_m, small_tiles, num_small, big_tiles, num_big};
+    perm_small<<<1, 1024, 0, s>>>(ids, (int)P, E, nbits, counts, offsets, row_to_pair,
+                                  pair_to_row, t);
     return hipGetLastError();
 }
 
