@@ -1,5 +1,7 @@
-// Router logits of small batches with K split over workgroups (internal to
-// the library; not part of the C ABI).
+// Dense products whose natural grids would leave CUs idle, with K split over
+// workgroups and the slices summed in order: the router logits (small
+// batches in a dedicated kernel, larger ones in 128x128 tiles) and the
+// latent down-projection (internal to the library; not part of the C ABI).
 #pragma once
 
 #include "common.h"
