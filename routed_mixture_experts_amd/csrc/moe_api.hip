@@ -103,7 +103,16 @@ int dense_path(moe_dtype_t dt, int64_t T, int N, int epi) {
 
 // Upper bounds of the two tile lists: the large-group list holds tiles of
 // `rows` rows; the workspace is sized for the smallest tile of the dtype.
+// The small-group list holds one tile per group, or two for groups of
+// kStreamMaxRows+1 .. 2*kStreamMaxRows rows when a small batch splits them
+// (at most P / (kStreamMaxRows + 1) such groups).
 int64_t small_capacity(moe_dtype_t dt, int E) { return dt == MOE_DTYPE_F32 ? 1 : E; }
+int64_t small_capacity_split(int64_t P, int E) {
+    return E + std::min<int64_t>(E, P / (kStreamMaxRows + 1));
+}
+// Batches of at most this many tokens (and no placement) put every group in
+// the small-group list: a group has at most T rows.
+constexpr int64_t kAllSmallMaxT = 2 * kStreamMaxRows;
 int64_t big_capacity(moe_dtype_t dt, int64_t P, int E, int rows) {
     if (dt == MOE_DTYPE_F32) return (P + kF32Rows - 1) / kF32Rows + E;
     return (P + rows - 1) / rows + std::min<int64_t>(E, P / (kStreamMaxRows + 1)) + 1;
@@ -133,7 +142,10 @@ struct ExpertsWs {
 ExpertsWs carve_experts(Carve& c, moe_dtype_t dt, int64_t max_T, int k, int E, int I) {
     ExpertsWs w;
     const int64_t P = max_T * k;
-    w.small_tiles = c.take<Tile>((size_t)small_capacity(dt, E));
+    w.small_tiles = c.take<Tile>((size_t)(dt == MOE_DTYPE_F32
+                                              ? small_capacity(dt, E)
+                                              : small_capacity_split(
+                                                    std::min(max_T, kAllSmallMaxT) * k, E)));
     w.big_tiles = c.take<Tile>((size_t)big_capacity_ws(dt, P, E));
     w.counts = c.take<int32_t>(2);
     w.h = c.take<char>((size_t)P * I * elem_size(dt));
@@ -149,10 +161,14 @@ GemmArgs gemm_defaults() {
 
 // The two halves of one grouped product: groups of at most kStreamMaxRows
 // rows (weight streaming) and the rest (256-row MFMA tiles).
-moe_status_t small_groups_gemm(GemmArgs g, const ExpertsWs& w, int E, hipStream_t s) {
+// split_P: the batch's pairs when groups above kStreamMaxRows rows were split
+// into two small tiles (0: one tile per group).
+moe_status_t small_groups_gemm(GemmArgs g, const ExpertsWs& w, int E, hipStream_t s,
+                               int64_t split_P = 0) {
     g.tiles = w.small_tiles;
     g.num_tiles = w.counts;
-    g.max_tiles = (int32_t)small_capacity(MOE_DTYPE_BF16, E);
+    g.max_tiles = (int32_t)(split_P > 0 ? small_capacity_split(split_P, E)
+                                        : small_capacity(MOE_DTYPE_BF16, E));
     g.tile_m = kStreamMaxRows;
     return hip_status(launch_gemm(1, GEMM_STREAM, g, s));
 }
@@ -211,11 +227,13 @@ moe_status_t side_stream(SideStream** out) {
 constexpr int64_t kOverlapMinRows = 16;
 
 // tiles_built: the tile lists in w already match offsets (the forward's
-// single-block permute writes them).
+// single-block permute writes them); all_small: it put every group in the
+// small-group list, so the large-group products are not launched.
 moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, const void* x,
                          const int32_t* offsets, const int32_t* row_to_pair,
                          const ExpertWeights& ew, float* y_rows, const ExpertsWs& w,
-                         hipStream_t s, hipEvent_t* ev, bool tiles_built = false) {
+                         hipStream_t s, hipEvent_t* ev, bool tiles_built = false,
+                         bool all_small = false) {
     const int64_t P = T * k;
     const bool f32 = dt == MOE_DTYPE_F32;
     if (!tiles_built)
@@ -260,6 +278,17 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
         if (ev) MOE_HIP(hipEventRecord(ev[2 * stage + end], s));
         return MOE_OK;
     };
+    if (all_small) {
+        // every group is in the small-group list (split into two tiles above
+        // kStreamMaxRows rows): no large-group launches, one stream
+        GemmArgs s1 = g1, s2 = g2;
+        s1.stream_nw = s2.stream_nw = P >= kOverlapMinRows * E ? 16 : 8;
+        MOE_TRY(small_groups_gemm(s1, w, E, s, P));
+        MOE_TRY(stage_mark(MOE_STAGE_GEMM1, 1));
+        MOE_TRY(stage_mark(MOE_STAGE_GEMM2, 0));
+        MOE_TRY(small_groups_gemm(s2, w, E, s, P));
+        return stage_mark(MOE_STAGE_GEMM2, 1);
+    }
     if (!f32 && P >= kOverlapMinRows * E) {
         std::lock_guard<std::mutex> lock(g_side_mu);
         SideStream* ss = nullptr;
@@ -716,12 +745,16 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
         MOE_HIP(launch_log2phy(T * k, ids, placement->log2phy, E, Es, w.phys, s));
         disp = w.phys;
     }
-    // small batches: one block permutes and writes the GEMM tile lists
+    // small batches: one block permutes and writes the GEMM tile lists; at
+    // most kAllSmallMaxT tokens (no placement: a group has at most T rows)
+    // every group goes to the small-group list
     const bool tiles_built = T * k <= kSmallPermutePairs;
+    const bool all_small =
+        tiles_built && !placement && dtype == MOE_DTYPE_BF16 && T <= kAllSmallMaxT;
     if (tiles_built) {
         MOE_HIP(launch_permute_small_with_tiles(
             T * k, Es, disp, counts, w.offsets, w.r2p, w.p2r,
-            dtype == MOE_DTYPE_F32 ? 0 : kStreamMaxRows, large_rows(dtype, ew.fmt),
+            dtype == MOE_DTYPE_F32 ? 0 : kStreamMaxRows, large_rows(dtype, ew.fmt), all_small,
             w.ex.small_tiles, w.ex.counts, w.ex.big_tiles, w.ex.counts + 1, s));
     } else {
         MOE_HIP(launch_permute(T * k, Es, disp, counts, w.offsets, w.r2p, w.p2r, w.chunks, s));
@@ -732,7 +765,7 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
 
     // routed experts
     MOE_TRY(run_experts(dtype, T, k, Es, D, I, xin, w.offsets, w.r2p, ew, w.y_rows, w.ex, s, ev,
-                        tiles_built));
+                        tiles_built, all_small));
 
     // shared expert without a latent tail: its output is the combine addend
     if (shared && !latent) {

@@ -166,7 +166,7 @@ static_assert(kSmallPairs == kSmallPermutePairs, "single-block permute limit");
 
 // Tile lists of the grouped GEMMs, written by perm_small when tiles != null.
 struct TileOut {
-    int32_t small_max, big_m;
+    int32_t small_max, big_m, split_small;
     Tile* small_tiles;
     int32_t* num_small;
     Tile* big_tiles;
@@ -209,19 +209,22 @@ __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ i
     if (tid == 0) offsets[E] = total;
     if (tiles.small_tiles) {
         // the tile lists of build_tiles_kernel, from this block's offsets
-        const bool small = run > 0 && run <= tiles.small_max;
-        const int nb = small || tid >= E ? 0 : (run + tiles.big_m - 1) / tiles.big_m;
+        const int sm = tiles.small_max;
+        const int ns = run <= 0 ? 0
+                       : run <= sm ? 1
+                       : tiles.split_small && run <= 2 * sm ? 2 : 0;
+        const int nb = ns > 0 || tid >= E ? 0 : (run + tiles.big_m - 1) / tiles.big_m;
         int total_s, total_b;
-        const int start_s = block_exclusive_scan(small ? 1 : 0, sh, total_s);
+        const int start_s = block_exclusive_scan(ns, sh, total_s);
         const int start_b = block_exclusive_scan(nb, sh, total_b);
-        if (small) {
+        for (int i = 0; i < ns; ++i) {
             Tile t = {};
             t.group = tid;
-            t.row0 = off;
-            t.row1 = off + run;
+            t.row0 = off + i * sm;
+            t.row1 = min(off + (i + 1) * sm, off + run);
             t.first = start_s;
-            t.count = 1;
-            tiles.small_tiles[start_s] = t;
+            t.count = ns;
+            tiles.small_tiles[start_s + i] = t;
         }
         for (int i = 0; i < nb; ++i) {
             Tile t = {};
@@ -347,14 +350,15 @@ hipError_t launch_permute(int64_t P, int32_t E, const int32_t* ids, int32_t* cou
 hipError_t launch_permute_small_with_tiles(int64_t P, int32_t E, const int32_t* ids,
                                            int32_t* counts, int32_t* offsets,
                                            int32_t* row_to_pair, int32_t* pair_to_row,
-                                           int32_t small_max, int32_t big_m, Tile* small_tiles,
-                                           int32_t* num_small, Tile* big_tiles, int32_t* num_big,
-                                           hipStream_t s) {
+                                           int32_t small_max, int32_t big_m, bool split_small,
+                                           Tile* small_tiles, int32_t* num_small,
+                                           Tile* big_tiles, int32_t* num_big, hipStream_t s) {
     if (P > kSmallPairs || E > kMaxExperts || !small_tiles || big_m < 1)
         return hipErrorInvalidValue;
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
-    const TileOut t{small_max, big_m, small_tiles, num_small, big_tiles, num_big};
+    const TileOut t{small_max, big_m, split_small ? 1 : 0, small_tiles, num_small, big_tiles,
+                    num_big};
     perm_small<<<1, 1024, 0, s>>>(ids, (int)P, E, nbits, counts, offsets, row_to_pair,
                                   pair_to_row, t);
     return hipGetLastError();

@@ -163,6 +163,24 @@ def test_router_logits_small_batches(T, H, E, biased):
     assert rel <= 1e-5 and mx <= 1e-4, (rel, mx)
 
 
+# At most 128 tokens every group is in the streaming list; a group of 65..128
+# rows (here: every token on the same k experts) becomes two 64-row tiles.
+@pytest.mark.parametrize("T", [65, 100, 128])
+def test_forward_hot_experts_small_batch(T):
+    w = Workload("hot_small", T=T, H=512, E=16, k=4, I=192, routed_scaling=1.5)
+    log(f"forward hot experts T={T}")
+    inp = make_inputs(w, DEV)
+    logits = random_logits(T, w.E, seed=5)
+    logits[:, 3:7] += 20.0   # experts 3..6 win for every token
+    logits = logits.to(DEV)
+    res = _gpu_forward(w, inp, router_logits=logits)
+    ref = _oracle_forward(w, inp, logits=np64(logits))
+    assert (npi(res["ids"]) == ref["ids"]).all()
+    assert (npi(res["counts"]) == ref["counts"]).all()
+    assert sorted(npi(res["counts"])[3:7].tolist()) == [T] * 4
+    check_float(np64(res["out"]), ref["out"], True, f"out hot T={T}")
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_forward_given_logits_matches_oracle(name):
     """Same fp32 logits on both sides: routing bit-exact, output in tolerance."""
