@@ -322,8 +322,8 @@ def main():
                    "parallelism": "none (1 GPU holds all experts)"},
         "roofline": {"bound": "hbm", "achieved": g1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": g1_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gate/up + SwiGLU stage: gemm_bf16_stream<3, false, 0, false, 8> (experts <= 64"
-                               " rows) + gemm_bf16_big<3, false> (larger experts)",
+                     "kernel": "gate/up + SwiGLU stage: gemm_bf16_stream<3, false, 0, false, 8> (at 128"
+                               " tokens every expert's rows, in 64-row tiles)",
                      "kernel_ms": g1_ms, "algorithmic_bytes": g1b},
         "layer": {"hbm_GBps": abytes / t_s / 1e9, "hbm_frac": abytes / t_s / 1e9 / HBM_PEAK_GBS,
                   "mfma_frac": aflops / t_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
