@@ -97,6 +97,12 @@ SMALL = {
     "shared_only": Workload("shared_only", T=90, H=256, E=8, k=2, I=128, shared_inter=128),
     "sigmoid_decode": Workload("sigmoid_decode", T=7, H=256, E=64, k=8, I=128,
                                score="sigmoid", renormalize=False, corr_bias=0.2),
+    # the largest expert count and top-k the library takes, in a small batch
+    # (single-block permute, every group streamed) and a larger one
+    "max_experts_topk": Workload("max_experts_topk", T=64, H=256, E=1024, k=32, I=64),
+    "max_experts_topk_large": Workload("max_experts_topk_large", T=300, H=256, E=1024, k=32,
+                                       I=64, num_groups=16, topk_group=8, score="sigmoid",
+                                       group_score="top2sum", corr_bias=0.01),
     "f32_grouped_latent": Workload("f32_grouped_latent", T=70, H=128, E=16, k=4, I=64,
                                    dtype="f32", num_groups=4, topk_group=2, latent=128,
                                    shared_inter=64, gamma_std=0.1),
