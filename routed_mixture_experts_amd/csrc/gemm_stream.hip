@@ -214,8 +214,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_ksplit(GemmArgs g) {
 // the same for any NW and weight bytes grow with it, so 16 waves halve the
 // share of token loads among the loads in flight; but one 16-wave workgroup
 // fills a CU (it takes a 128 KB token buffer and chunks twice as deep) and
-// its barriers span 16 waves.  Alone, 8 waves are faster for every format;
-// beside the 256x256 chain of a large batch, 16 are (bf16 only).
+// its barriers span 16 waves.  With a few rows per group (decode) 8 waves
+// are faster for every format; from about 16 rows per group on, 16 are
+// (bf16; measured alone and beside the 256x256 chain of a large batch).
 template <int NW>
 constexpr int sx_bytes() { return NW == 16 ? 128 * 1024 : 64 * 1024; }
 
@@ -580,8 +581,8 @@ void launch_stream_rows(const GemmArgs& g, int nm, hipStream_t s) {
 }
 
 // Waves per workgroup of a grouped bf16 weight-streaming product: 8, or 16
-// when the caller asks for it (the small-group chain of a large batch, which
-// runs beside the 256x256 chain: measured 2% faster there, and slower alone).
+// when the caller asks for it (groups averaging at least 16 rows, where 16
+// waves stream faster; slower at decode's few rows per group).
 int stream_waves(const GemmArgs& g) { return g.stream_nw == 16 ? 16 : 8; }
 
 }  // namespace
