@@ -189,6 +189,30 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     if (a.G > 1) {
         const int per = E / a.G;
         double gs_lane = kNegInf;  // lane g keeps group g's score
+        // lanes per group: when a group fills a power-of-two run of whole
+        // lanes (<= 16, inside one DPP row), one segmented top-2 reduction
+        // scores every group at once; lane g then fetches group g's score
+        // from the group's first lane.  The two best values are the same as
+        // the per-group wave reductions below produce.
+        const int lpg = per % VPL == 0 ? per / VPL : 0;
+        if (lpg == 1 || lpg == 2 || lpg == 4 || lpg == 8 || lpg == 16) {
+            double b1 = kNegInf, b2 = kNegInf;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                if (lane * VPL + i < E) {
+                    const double v = key[i];
+                    if (v > b1) { b2 = b1; b1 = v; }
+                    else if (v > b2) { b2 = v; }
+                }
+            }
+            if (lpg >= 2) top2_step<kDppQuadSwap1>(b1, b2);
+            if (lpg >= 4) top2_step<kDppQuadSwap2>(b1, b2);
+            if (lpg >= 8) top2_step<kDppHalfMirror>(b1, b2);
+            if (lpg >= 16) top2_step<kDppMirror>(b1, b2);
+            const double gsc = a.group_score == 0 ? b1 : b1 + b2;
+            const double mine = __shfl(gsc, min(lane * lpg, 63));
+            if (lane < a.G) gs_lane = mine;
+        } else
         for (int g = 0; g < a.G; ++g) {
             double b1 = kNegInf, b2 = kNegInf;
 #pragma unroll

@@ -36,6 +36,10 @@ ROUTE_CASES = [
     ("k_equals_E", 50, 16, 16, 1, 1, "softmax", "max", 0, True, 1.0),
     ("single_expert", 10, 1, 1, 1, 1, "softmax", "max", 0, True, 1.0),
     ("groups_of_one", 90, 32, 4, 32, 8, "sigmoid", "max", 0, True, 1.0),
+    # groups of 3 experts with 2 per lane: a group does not fill whole lanes
+    ("groups_across_lanes", 200, 96, 4, 32, 8, "sigmoid", "top2sum", 0.05, True, 1.0),
+    # groups of 16 lanes (256 experts in 4 groups, 4 per lane)
+    ("groups_of_16_lanes", 150, 256, 8, 4, 2, "sqrtsoftplus", "top2sum", 0.1, True, 1.0),
 ]
 
 
