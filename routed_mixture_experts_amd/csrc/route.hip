@@ -153,9 +153,12 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
         lg[i] = e < E ? lrow[e] : 0.0f;
     }
 
-    // softmax statistics over all E experts
+    // softmax statistics over all E experts.  With renormalisation and the
+    // logits as keys they cancel: w_j = exp(l_j - m) / sum_sel exp(l_i - m)
+    // with m the largest logit, which is the first selected key.
+    const bool sel_softmax = a.score == 0 && a.raw_keys && a.renormalize;
     double smax = 0.0, ssum = 1.0;
-    if (a.score == 0) {
+    if (a.score == 0 && !sel_softmax) {
         double m = kNegInf;
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
@@ -244,6 +247,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     }
 
     int my_id = 0;
+    double top_key = 0.0;  // the first (largest) selected key
     for (int j = 0; j < a.k; ++j) {
         double bk = kNegInf;
         int bi = kNoIndex;
@@ -253,6 +257,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
             if (((elig >> i) & 1u) && ranks_before(key[i], e, bk, bi)) { bk = key[i]; bi = e; }
         }
         wave_argmax(bk, bi);
+        if (j == 0) top_key = bk;
         if (bi / VPL == lane) elig &= ~(1u << (bi - lane * VPL));
         if (lane == j) my_id = bi;
     }
@@ -261,7 +266,9 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     // violated precondition (NaN logits) from reading outside the row.
     my_id = min(max(my_id, 0), E - 1);
     double s = 0.0;
-    if (lane < a.k) s = score_of(a.score, (double)lrow[my_id], smax, ssum);
+    if (lane < a.k)
+        s = sel_softmax ? exp((double)lrow[my_id] - top_key)
+                        : score_of(a.score, (double)lrow[my_id], smax, ssum);
     double tot = wave_sum(s);
     double w = a.renormalize ? s / tot : s;
     w *= (double)a.scaling;
