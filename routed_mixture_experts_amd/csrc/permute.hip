@@ -41,21 +41,30 @@ __global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ id
         chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-// Exclusive scan of one int per thread across a 1024-thread block.
+// Exclusive scan of one int per thread across a block of whole waves (every
+// block here has 1024 threads): a shuffle scan inside each wave, then the
+// wave totals through LDS.  Integer sums, so the result does not depend on
+// the order.  sh holds at least one int per wave.
 __device__ int block_exclusive_scan(int v, int* sh, int& total) {
     const int tid = threadIdx.x;
-    sh[tid] = v;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        int add = tid >= d ? sh[tid - d] : 0;
-        __syncthreads();
-        sh[tid] += add;
-        __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
     }
-    total = sh[1023];
-    int incl = sh[tid];
+    if (lane == 63) sh[wave] = x;
     __syncthreads();
-    return incl - v;
+    int base = 0, all = 0;
+    for (int w = 0; w < nwaves; ++w) {
+        const int t = sh[w];
+        if (w < wave) base += t;
+        all += t;
+    }
+    total = all;
+    __syncthreads();  // sh is free for the next scan
+    return base + x - v;
 }
 
 __global__ __launch_bounds__(1024) void perm_scan(int nchunk, int E, int32_t* __restrict__ cc,
