@@ -227,8 +227,8 @@ moe_status_t side_stream(SideStream** out) {
 constexpr int64_t kOverlapMinRows = 16;
 
 // tiles_built: the tile lists in w already match offsets (the forward's
-// single-block permute writes them); all_small: it put every group in the
-// small-group list, so the large-group products are not launched.
+// permute writes them); all_small: it put every group in the small-group
+// list, so the large-group products are not launched.
 moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, const void* x,
                          const int32_t* offsets, const int32_t* row_to_pair,
                          const ExpertWeights& ew, float* y_rows, const ExpertsWs& w,
@@ -745,27 +745,22 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
         MOE_HIP(launch_log2phy(T * k, ids, placement->log2phy, E, Es, w.phys, s));
         disp = w.phys;
     }
-    // small batches: one block permutes and writes the GEMM tile lists; at
-    // most kAllSmallMaxT tokens (no placement: a group has at most T rows)
-    // every group goes to the small-group list
-    const bool tiles_built = T * k <= kSmallPermutePairs;
-    const bool all_small =
-        tiles_built && !placement && dtype == MOE_DTYPE_BF16 && T <= kAllSmallMaxT;
-    if (tiles_built) {
-        MOE_HIP(launch_permute_small_with_tiles(
-            T * k, Es, disp, counts, w.offsets, w.r2p, w.p2r,
-            dtype == MOE_DTYPE_F32 ? 0 : kStreamMaxRows, large_rows(dtype, ew.fmt), all_small,
-            w.ex.small_tiles, w.ex.counts, w.ex.big_tiles, w.ex.counts + 1, s));
-    } else {
-        MOE_HIP(launch_permute(T * k, Es, disp, counts, w.offsets, w.r2p, w.p2r, w.chunks, s));
-    }
+    // the permute also writes the GEMM tile lists; at most kAllSmallMaxT
+    // tokens (no placement: a group has at most T rows) every group goes to
+    // the small-group list
+    const bool all_small = T * k <= kSmallPermutePairs && !placement &&
+                           dtype == MOE_DTYPE_BF16 && T <= kAllSmallMaxT;
+    MOE_HIP(launch_permute_with_tiles(
+        T * k, Es, disp, counts, w.offsets, w.r2p, w.p2r, w.chunks,
+        dtype == MOE_DTYPE_F32 ? 0 : kStreamMaxRows, large_rows(dtype, ew.fmt), all_small,
+        w.ex.small_tiles, w.ex.counts, w.ex.big_tiles, w.ex.counts + 1, s));
     if (placement && placement->load)
         MOE_HIP(launch_load_accumulate(Es, counts, placement->load, s));
     MOE_TRY(mark(MOE_STAGE_PERMUTE, 1));
 
     // routed experts
     MOE_TRY(run_experts(dtype, T, k, Es, D, I, xin, w.offsets, w.r2p, ew, w.y_rows, w.ex, s, ev,
-                        tiles_built, all_small));
+                        true, all_small));
 
     // shared expert without a latent tail: its output is the combine addend
     if (shared && !latent) {

@@ -67,17 +67,71 @@ __device__ int block_exclusive_scan(int v, int* sh, int& total) {
     return base + x - v;
 }
 
+// Tile lists of the grouped GEMMs (optional kernel output: small_tiles != null).
+struct TileOut {
+    int32_t small_max, big_m, split_small;
+    Tile* small_tiles;
+    int32_t* num_small;
+    Tile* big_tiles;
+    int32_t* num_big;
+};
+
+// The tile lists of build_tiles_kernel, written by a block that has just
+// computed every expert's row count (run) and first row (off), one thread
+// per expert (tid < E).  Groups of 1..small_max rows get one small tile,
+// with split_small groups of small_max+1 .. 2*small_max rows two, and the
+// rest big_m-row big tiles.  Every thread of the block calls it (it scans).
+__device__ void write_tiles(int tid, int E, int run, int off, const TileOut& tiles, int* sh) {
+    if (!tiles.small_tiles) return;  // uniform over the block
+    const int sm = tiles.small_max;
+    const int ns = run <= 0 ? 0
+                   : run <= sm ? 1
+                   : tiles.split_small && run <= 2 * sm ? 2 : 0;
+    const int nb = ns > 0 || tid >= E ? 0 : (run + tiles.big_m - 1) / tiles.big_m;
+    int total_s, total_b;
+    const int start_s = block_exclusive_scan(ns, sh, total_s);
+    const int start_b = block_exclusive_scan(nb, sh, total_b);
+    for (int i = 0; i < ns; ++i) {
+        Tile t = {};
+        t.group = tid;
+        t.row0 = off + i * sm;
+        t.row1 = min(off + (i + 1) * sm, off + run);
+        t.first = start_s;
+        t.count = ns;
+        tiles.small_tiles[start_s + i] = t;
+    }
+    for (int i = 0; i < nb; ++i) {
+        Tile t = {};
+        t.group = tid;
+        t.row0 = off + i * tiles.big_m;
+        t.row1 = min(off + (i + 1) * tiles.big_m, off + run);
+        t.first = start_b;
+        t.count = nb;
+        tiles.big_tiles[start_b + i] = t;
+    }
+    if (tid == 0) {
+        *tiles.num_small = total_s;
+        *tiles.num_big = total_b;
+    }
+}
+
 __global__ __launch_bounds__(1024) void perm_scan(int nchunk, int E, int32_t* __restrict__ cc,
                                                   int32_t* __restrict__ counts,
-                                                  int32_t* __restrict__ offsets) {
+                                                  int32_t* __restrict__ offsets, TileOut tiles) {
     __shared__ int sh[1024];
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
-        for (int c = 0; c < nchunk; ++c) {
-            int v = cc[(int64_t)c * E + e];
-            cc[(int64_t)c * E + e] = run;
-            run += v;
+        // four chunks' counts are loaded before they are summed
+        for (int c0 = 0; c0 < nchunk; c0 += 4) {
+            int v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = c0 + u < nchunk ? cc[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (c0 + u < nchunk) cc[(int64_t)(c0 + u) * E + e] = run;
+                run += v[u];
+            }
         }
     }
     int total;
@@ -88,6 +142,7 @@ __global__ __launch_bounds__(1024) void perm_scan(int nchunk, int E, int32_t* __
         for (int c = 0; c < nchunk; ++c) cc[(int64_t)c * E + e] += off;
     }
     if (e == 0) offsets[E] = total;
+    write_tiles(e, E, e < E ? run : 0, off, tiles, sh);
 }
 
 constexpr int kScatterWaves = 16;
@@ -173,14 +228,6 @@ __global__ __launch_bounds__(1024) void perm_scatter(const int32_t* __restrict__
 constexpr int64_t kSmallPairs = kChunk;
 static_assert(kSmallPairs == kSmallPermutePairs, "single-block permute limit");
 
-// Tile lists of the grouped GEMMs, written by perm_small when tiles != null.
-struct TileOut {
-    int32_t small_max, big_m, split_small;
-    Tile* small_tiles;
-    int32_t* num_small;
-    Tile* big_tiles;
-    int32_t* num_big;
-};
 
 __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ ids, int P, int E,
                                                    int nbits, int32_t* __restrict__ counts,
@@ -216,39 +263,7 @@ __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ i
         for (int w = 0; w < kScatterWaves; ++w) cur[w][tid] += off;
     }
     if (tid == 0) offsets[E] = total;
-    if (tiles.small_tiles) {
-        // the tile lists of build_tiles_kernel, from this block's offsets
-        const int sm = tiles.small_max;
-        const int ns = run <= 0 ? 0
-                       : run <= sm ? 1
-                       : tiles.split_small && run <= 2 * sm ? 2 : 0;
-        const int nb = ns > 0 || tid >= E ? 0 : (run + tiles.big_m - 1) / tiles.big_m;
-        int total_s, total_b;
-        const int start_s = block_exclusive_scan(ns, sh, total_s);
-        const int start_b = block_exclusive_scan(nb, sh, total_b);
-        for (int i = 0; i < ns; ++i) {
-            Tile t = {};
-            t.group = tid;
-            t.row0 = off + i * sm;
-            t.row1 = min(off + (i + 1) * sm, off + run);
-            t.first = start_s;
-            t.count = ns;
-            tiles.small_tiles[start_s + i] = t;
-        }
-        for (int i = 0; i < nb; ++i) {
-            Tile t = {};
-            t.group = tid;
-            t.row0 = off + i * tiles.big_m;
-            t.row1 = min(off + (i + 1) * tiles.big_m, off + run);
-            t.first = start_b;
-            t.count = nb;
-            tiles.big_tiles[start_b + i] = t;
-        }
-        if (tid == 0) {
-            *tiles.num_small = total_s;
-            *tiles.num_big = total_b;
-        }
-    }
+    write_tiles(tid, E, run, off, tiles, sh);
     __syncthreads();
     scatter_segment(ids, p0, p1, nbits, cur[wave], row_to_pair, pair_to_row);
 }
@@ -337,40 +352,49 @@ hipError_t launch_load_accumulate(int32_t n, const int32_t* counts, int64_t* loa
 
 int permute_chunks(int64_t P) { return (int)((P + kChunk - 1) / kChunk); }
 
-hipError_t launch_permute(int64_t P, int32_t E, const int32_t* ids, int32_t* counts,
-                          int32_t* offsets, int32_t* row_to_pair, int32_t* pair_to_row,
-                          int32_t* chunk_scratch, hipStream_t s) {
+namespace {
+
+hipError_t permute_impl(int64_t P, int32_t E, const int32_t* ids, int32_t* counts,
+                        int32_t* offsets, int32_t* row_to_pair, int32_t* pair_to_row,
+                        int32_t* chunk_scratch, const TileOut& tiles, hipStream_t s) {
     const int nchunk = permute_chunks(P);
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     if (P <= kSmallPairs) {
         perm_small<<<1, 1024, 0, s>>>(ids, (int)P, E, nbits, counts, offsets, row_to_pair,
-                                      pair_to_row, TileOut{});
+                                      pair_to_row, tiles);
         return hipGetLastError();
     }
     if (nchunk > 0) perm_count<<<nchunk, 256, 0, s>>>(ids, P, E, chunk_scratch);
-    perm_scan<<<1, 1024, 0, s>>>(nchunk, E, chunk_scratch, counts, offsets);
+    perm_scan<<<1, 1024, 0, s>>>(nchunk, E, chunk_scratch, counts, offsets, tiles);
     if (nchunk > 0)
         perm_scatter<<<nchunk, 1024, 0, s>>>(ids, P, E, nbits, chunk_scratch, row_to_pair,
                                              pair_to_row);
     return hipGetLastError();
 }
 
-hipError_t launch_permute_small_with_tiles(int64_t P, int32_t E, const int32_t* ids,
-                                           int32_t* counts, int32_t* offsets,
-                                           int32_t* row_to_pair, int32_t* pair_to_row,
-                                           int32_t small_max, int32_t big_m, bool split_small,
-                                           Tile* small_tiles, int32_t* num_small,
-                                           Tile* big_tiles, int32_t* num_big, hipStream_t s) {
-    if (P > kSmallPairs || E > kMaxExperts || !small_tiles || big_m < 1)
+}  // namespace
+
+hipError_t launch_permute(int64_t P, int32_t E, const int32_t* ids, int32_t* counts,
+                          int32_t* offsets, int32_t* row_to_pair, int32_t* pair_to_row,
+                          int32_t* chunk_scratch, hipStream_t s) {
+    return permute_impl(P, E, ids, counts, offsets, row_to_pair, pair_to_row, chunk_scratch,
+                        TileOut{}, s);
+}
+
+hipError_t launch_permute_with_tiles(int64_t P, int32_t E, const int32_t* ids, int32_t* counts,
+                                     int32_t* offsets, int32_t* row_to_pair,
+                                     int32_t* pair_to_row, int32_t* chunk_scratch,
+                                     int32_t small_max, int32_t big_m, bool split_small,
+                                     Tile* small_tiles, int32_t* num_small, Tile* big_tiles,
+                                     int32_t* num_big, hipStream_t s) {
+    if (E > kMaxExperts || !small_tiles || !big_tiles || big_m < 1 ||
+        (split_small && P > kSmallPairs))
         return hipErrorInvalidValue;
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
     const TileOut t{small_max, big_m, split_small ? 1 : 0, small_tiles, num_small, big_tiles,
                     num_big};
-    perm_small<<<1, 1024, 0, s>>>(ids, (int)P, E, nbits, counts, offsets, row_to_pair,
-                                  pair_to_row, t);
-    return hipGetLastError();
+    return permute_impl(P, E, ids, counts, offsets, row_to_pair, pair_to_row, chunk_scratch, t,
+                        s);
 }
 
 hipError_t launch_build_tiles(const int32_t* offsets, int32_t E, int32_t small_max,
