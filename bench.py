@@ -265,10 +265,20 @@ def cpu_baseline(w, inp, torch, ntok):
     else:
         w13 = {e: inp["w13"][e].float().cpu().numpy() for e in used}
         w2 = {e: inp["w2"][e].float().cpu().numpy() for e in used}
+    # the latent projections and the shared expert, as fp32 host copies
+    lat = sh = None
+    if w.latent:
+        lat = dict(w_down=inp["w_down"].float().cpu().numpy(),
+                   gamma=inp["gamma"].float().cpu().numpy(),
+                   w_up=inp["w_up"].float().cpu().numpy(), eps=w.rms_eps)
+    if w.shared_inter:
+        sh = dict(w13=inp["w13_sh"].float().cpu().numpy(),
+                  w2=inp["w2_sh"].float().cpu().numpy())
     info = threadpoolctl.threadpool_info()
     cores = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
     t0 = time.perf_counter()
-    O.forward(x, cfg, w13, w2, w_router=wr, router_bias=rb, corr_bias=cb)
+    O.forward(x, cfg, w13, w2, w_router=wr, router_bias=rb, corr_bias=cb, latent=lat,
+              shared=sh)
     dt = time.perf_counter() - t0
     return {"value": ntok / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": (f"first {ntok} of {w.T} tokens of the {w.name} batch ({len(used)} "

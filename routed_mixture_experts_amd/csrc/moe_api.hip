@@ -196,6 +196,7 @@ moe_status_t large_groups_gemm(moe_dtype_t dt, GemmArgs g, const ExpertsWs& w, i
 struct SideStream {
     hipStream_t s = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
+    hipEvent_t shared_done = nullptr;  // the shared expert's products (forward)
 };
 constexpr int kMaxDevices = 64;
 std::mutex g_side_mu;
@@ -210,6 +211,7 @@ moe_status_t side_stream(SideStream** out) {
     if (!ss.s) {
         MOE_HIP(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
         MOE_HIP(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming));
+        MOE_HIP(hipEventCreateWithFlags(&ss.shared_done, hipEventDisableTiming));
         MOE_HIP(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking));
     }
     *out = &ss;
@@ -682,6 +684,31 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
         return mark(stage, 1);
     };
 
+    // The shared expert reads only x: in bf16 layers its products run on the
+    // library's second stream beside routing, dispatch and the routed
+    // experts, and the caller's stream waits for them where they are used.
+    SideStream* sh_ss = nullptr;
+    if (shared && dtype == MOE_DTYPE_BF16) {
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        MOE_TRY(side_stream(&sh_ss));
+        MOE_HIP(hipEventRecord(sh_ss->fork, s));
+        MOE_HIP(hipStreamWaitEvent(sh_ss->s, sh_ss->fork, 0));
+        moe_status_t st = dense_gemm(dtype, T, x, H, shared->w13, H, nullptr, 0, nullptr, 0,
+                                     shared->inter, EPI_SWIGLU, w.h_sh, shared->inter, nullptr,
+                                     sh_ss->s);
+        if (st == MOE_OK && !latent)
+            st = dense_gemm(dtype, T, w.h_sh, shared->inter, shared->w2, shared->inter, nullptr,
+                            0, nullptr, 0, H, EPI_F32, w.sh, H, nullptr, sh_ss->s);
+        // recorded even after an error, so the caller's stream never waits
+        // on a stale record
+        MOE_HIP(hipEventRecord(sh_ss->shared_done, sh_ss->s));
+        MOE_TRY(st);
+    }
+    auto wait_shared = [&]() -> moe_status_t {
+        if (sh_ss) MOE_HIP(hipStreamWaitEvent(s, sh_ss->shared_done, 0));
+        return MOE_OK;
+    };
+
     // router logits (fp32 accumulate, fp32 out, + optional bias row)
     const float* logits = router_logits;
     if (!logits) {
@@ -763,7 +790,10 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
                         true, all_small));
 
     // shared expert without a latent tail: its output is the combine addend
-    if (shared && !latent) {
+    if (shared && !latent && sh_ss) {
+        MOE_TRY(skip(MOE_STAGE_SHARED));
+        MOE_TRY(wait_shared());
+    } else if (shared && !latent) {
         MOE_TRY(mark(MOE_STAGE_SHARED, 0));
         MOE_TRY(dense_gemm(dtype, T, x, H, shared->w13, H, nullptr, 0, nullptr, 0, shared->inter,
                            EPI_SWIGLU, w.h_sh, shared->inter, nullptr, s));
@@ -795,7 +825,10 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
     MOE_TRY(mark(MOE_STAGE_COMBINE, 1));
 
     if (latent) {
-        if (shared) {
+        if (shared && sh_ss) {
+            MOE_TRY(skip(MOE_STAGE_SHARED));
+            MOE_TRY(wait_shared());
+        } else if (shared) {
             MOE_TRY(mark(MOE_STAGE_SHARED, 0));
             MOE_TRY(dense_gemm(dtype, T, x, H, shared->w13, H, nullptr, 0, nullptr, 0,
                                shared->inter, EPI_SWIGLU, w.h_sh, shared->inter, nullptr, s));

@@ -27,17 +27,30 @@ def _skewed_logits(T, E, seed):
     return lg.to(DEV)
 
 
-@pytest.mark.parametrize("case", ["one_stream", "two_streams"])
+# The shared-expert cases fork the shared products onto the second stream at
+# the start of the layer and join them before the combine (plain layer) or
+# before the latent tail.
+@pytest.mark.parametrize("case", ["one_stream", "two_streams", "shared", "latent_shared"])
 def test_forward_graph_replays_match_eager(case):
     if case == "one_stream":
         w = Workload("t", T=64, H=256, E=32, k=4, I=128, routed_scaling=2.5)  # P < 16 E
         logits = random_logits(w.T, w.E, seed=11).to(DEV)
-    else:
+    elif case == "two_streams":
         w = Workload("t", T=600, H=256, E=8, k=2, I=128)                     # P >= 16 E
         logits = _skewed_logits(w.T, w.E, seed=12)
+    elif case == "shared":
+        w = Workload("t", T=600, H=256, E=8, k=2, I=128, shared_inter=192)
+        logits = _skewed_logits(w.T, w.E, seed=13)
+    else:
+        w = Workload("t", T=300, H=512, E=16, k=4, I=128, latent=256, shared_inter=384)
+        logits = random_logits(w.T, w.E, seed=14).to(DEV)
     log(f"graph capture {case}: T={w.T} E={w.E} k={w.k}")
     inp = make_inputs(w, DEV)
     cfg = lib_cfg(w)
+    lat = None
+    if w.latent:
+        lat = dict(w_down=inp["w_down"], gamma=inp["gamma"], w_up=inp["w_up"], eps=w.rms_eps)
+    sh = dict(w13=inp["w13_sh"], w2=inp["w2_sh"]) if w.shared_inter else None
     x = inp["x"].clone()
     x2 = normal((w.T, w.H), 1.0, 77, torch.bfloat16, DEV)
 
@@ -49,16 +62,16 @@ def test_forward_graph_replays_match_eager(case):
 
     def run(xin, bufs, ws):
         moe.moe_forward(cfg, xin, inp["w13"], inp["w2"], router_logits=logits, workspace=ws,
-                        **bufs)
+                        latent=lat, shared=sh, **bufs)
 
-    nbytes = moe.moe_forward_workspace(cfg, torch.bfloat16, w.T, w.H, w.I, None, None)
+    nbytes = moe.moe_forward_workspace(cfg, torch.bfloat16, w.T, w.H, w.I, lat, sh)
     ws_e = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
     ws_g = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
     ref1, ref2 = buffers(), buffers()
     run(x, ref1, ws_e)            # eager (also creates the library's second stream)
     run(x2, ref2, ws_e)
     torch.cuda.synchronize()
-    if case == "two_streams":
+    if case in ("two_streams", "shared"):
         c = ref1["expert_counts_out"].cpu()
         assert c.max() > 64 and c.min() <= 64, c   # both chains are exercised
 
