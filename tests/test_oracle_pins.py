@@ -62,6 +62,45 @@ def test_golden_rmsnorm():
     np.testing.assert_allclose(out, np.array(g["out"]), rtol=1e-14)
 
 
+RB = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "router_bias_case.json")))
+
+
+def test_golden_router_logits_with_bias_row():
+    """The bias row is per expert and added to every token's logits: a dropped,
+    negated or token-indexed bias gives other values (T == E, so a bias
+    broadcast along the token axis would still run)."""
+    x, w_r = np.array(RB["x"], dtype=np.float64), np.array(RB["w_router"], dtype=np.float64)
+    b = np.array(RB["bias"], dtype=np.float32)
+    assert O.router_logits(x, w_r).tolist() == RB["product"]
+    assert O.router_logits(x, w_r, b).tolist() == RB["logits"]
+    # the case tells the plausible slips apart: bias dropped, negated, or
+    # indexed by token instead of expert
+    p = np.array(RB["product"], dtype=np.float64)
+    for wrong in (p, p - b[None, :], p + b[:, None]):
+        assert wrong.tolist() != RB["logits"]
+
+
+def test_golden_forward_with_router_bias_row():
+    """The same case through the whole layer: the router product with the bias
+    row decides ids and weights (without the bias, rows 1 and 2 pick other
+    experts)."""
+    x, w_r = np.array(RB["x"], dtype=np.float64), np.array(RB["w_router"], dtype=np.float64)
+    b = np.array(RB["bias"], dtype=np.float32)
+    cfg = _cfg(RB["cfg"])
+    rng = np.random.default_rng(3)
+    E, H, I = 3, 4, 2
+    w13, w2 = rng.normal(size=(E, 2 * I, H)), rng.normal(size=(E, H, I))
+    res = O.forward(x, cfg, w13, w2, w_router=w_r, router_bias=b)
+    assert res["logits"].tolist() == RB["logits"]
+    assert res["ids"].tolist() == RB["ids"]
+    np.testing.assert_allclose(res["weights"], np.array(RB["weights"]), rtol=0, atol=1e-15)
+    nob = O.forward(x, cfg, w13, w2, w_router=w_r)
+    assert nob["ids"].tolist() == RB["ids_without_bias"]
+    tok = O.forward_tokens(np.array([2, 0]), x, cfg, w13, w2, w_router=w_r, router_bias=b)
+    assert tok["ids"].tolist() == [RB["ids"][2], RB["ids"][0]]
+    np.testing.assert_allclose(tok["out"], res["out"][[2, 0]], rtol=1e-13)
+
+
 # ------------------------------------------------------------ closed forms ---
 
 def test_sqrtsoftplus_closed_forms():
