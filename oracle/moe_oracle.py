@@ -227,11 +227,14 @@ def fp8_e4m3_decode(codes) -> np.ndarray:
     e > 0 gives (1 + m/8) * 2^(e-7); e = 0 gives the subnormal (m/8) * 2^-6;
     e = 15 with m = 7 is NaN (the format has no infinities, so e = 15 with
     m < 7 is an ordinary value, up to 448)."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    # the formula is evaluated once on all 256 codes; the codes then index
+    # that table (the same values, without per-element exp2 on large tensors)
+    c = np.arange(256, dtype=np.int64)
     sign, e, m = (c >> 7) & 1, (c >> 3) & 15, c & 7
     mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
     val = np.where(sign == 1, -mag, mag)
-    return np.where((e == 15) & (m == 7), np.nan, val).astype(f64)
+    table = np.where((e == 15) & (m == 7), np.nan, val).astype(f64)
+    return table[np.asarray(codes, dtype=np.uint8)]
 
 
 def dequantize_rows(codes, scale) -> np.ndarray:
@@ -245,16 +248,21 @@ def e2m1_decode(codes) -> np.ndarray:
     reading in the header): bit 3 is the sign, bits 2..1 the exponent field e
     with bias 1, bit 0 the mantissa m.  e > 0 gives (1 + m/2) * 2^(e-1); e = 0
     gives the subnormal m/2.  Every code is finite."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    c = np.arange(16, dtype=np.int64)        # all codes, then a table lookup
     sign, e, m = (c >> 3) & 1, (c >> 1) & 3, c & 1
     mag = np.where(e == 0, m / 2.0, (1.0 + m / 2.0) * np.exp2(e - 1.0))
-    return np.where(sign == 1, -mag, mag).astype(f64)
+    table = np.where(sign == 1, -mag, mag).astype(f64)
+    codes = np.asarray(codes, dtype=np.uint8)
+    if codes.size and codes.max() > 15:
+        raise ValueError("E2M1 codes are 4-bit")
+    return table[codes]
 
 
 def e8m0_decode(codes) -> np.ndarray:
     """Values of OCP E8M0 scale bytes: 2^(s - 127); s = 255 is NaN."""
-    s = np.asarray(codes, dtype=np.uint8).astype(np.int64)
-    return np.where(s == 255, np.nan, np.exp2(s - 127.0)).astype(f64)
+    s = np.arange(256, dtype=np.int64)       # all bytes, then a table lookup
+    table = np.where(s == 255, np.nan, np.exp2(s - 127.0)).astype(f64)
+    return table[np.asarray(codes, dtype=np.uint8)]
 
 
 def dequantize_mxfp4(codes, scales) -> np.ndarray:
