@@ -41,10 +41,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill_zipf", "grouped_sqrtsoftplus", "latent_shared",
-                             "decode_fp8", "decode_mxfp4"])
+                             "decode_fp8", "decode_mxfp4", "prefill_fp8"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill line")
     ap.add_argument("--no-fp8", action="store_true",
-                    help="skip the decode line with FP8 E4M3 expert weights")
+                    help="skip the decode and prefill lines with FP8 E4M3 expert weights")
     ap.add_argument("--no-mxfp4", action="store_true",
                     help="skip the decode line with MXFP4 expert weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -163,6 +163,16 @@ def gemm1_bytes(w, counts):
     return wb + w.T * w.D * es + w.T * w.k * w.I * es, touched
 
 
+def percentile(sorted_vals, q):
+    """Linear-interpolated q-th percentile of an ascending list."""
+    if len(sorted_vals) == 1:
+        return sorted_vals[0]
+    pos = (len(sorted_vals) - 1) * q / 100.0
+    lo = int(math.floor(pos))
+    hi = min(lo + 1, len(sorted_vals) - 1)
+    return sorted_vals[lo] + (sorted_vals[hi] - sorted_vals[lo]) * (pos - lo)
+
+
 class Runner:
     """Holds inputs, outputs, workspace and events of one workload."""
 
@@ -210,16 +220,23 @@ class Runner:
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         # The headline pass runs the layer as a caller does, with no stage
-        # events between its kernels.
+        # events between its kernels; one event between consecutive steps
+        # gives the per-step times (their median, p10 and p90).
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        for e in marks:
+            e.record(self.stream)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         start.record(self.stream)
+        marks[0].record(self.stream)
         for s in range(steps):
             self.step()
+            marks[s + 1].record(self.stream)
         end.record(self.stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ms = start.elapsed_time(end) / steps
+        per_step = sorted(marks[s].elapsed_time(marks[s + 1]) for s in range(steps))
         # A second pass of as many steps records the library's HIP events
         # between the stages, on the stream its kernels run on.
         start.record(self.stream)
@@ -233,6 +250,9 @@ class Runner:
             d = [evs[s][2 * i].elapsed_time(evs[s][2 * i + 1]) for s in range(steps)]
             stage[name] = sum(d) / steps
         stage["layer_with_stage_events"] = ms_ev
+        self.step_stats = {"median": percentile(per_step, 50), "p10": percentile(per_step, 10),
+                           "p90": percentile(per_step, 90), "min": per_step[0],
+                           "max": per_step[-1]}
         return ms, wall * 1e3 / steps, stage
 
 
@@ -323,6 +343,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "step_ms": run.step_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -357,7 +378,7 @@ def main():
         pbytes, pflops, ptouched = layer_work(wp, pc)
         res["prefill"] = {
             "workload": describe(wp), "value": wp.T / (pms * 1e-3), "unit": "tokens/s",
-            "ms_per_step": pms, "steps": psteps,
+            "ms_per_step": pms, "step_ms": prun.step_stats, "steps": psteps,
             "hbm_frac": pbytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "mfma_frac": pflops / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "binding_frac": binding_frac(pbytes, pflops, pms),
@@ -367,7 +388,7 @@ def main():
             "input_checksums": {"x": checksums({"x": pin["x"]}, torch)["x"],
                                 "router_bias": checksums({"b": pin["router_bias"]}, torch)["b"]},
             "stages_ms": pstage}
-        del prun, pin
+        del prun
     if args.workload == "decode" and not args.no_fp8:
         # the same layer with the same weight draws quantised to FP8 E4M3 (one
         # fp32 scale per weight row): a separate line, not the headline value
@@ -386,12 +407,37 @@ def main():
         res["fp8_decode"] = {
             "workload": describe(wf) + " weights=fp8_e4m3 (per-row fp32 scales)",
             "value": wf.T / (fms * 1e-3), "unit": "tokens/s", "ms_per_step": fms,
+            "step_ms": frun.step_stats,
             "steps": args.steps, "hbm_frac": fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "gemm1": {"kernel": "gemm_bf16_stream<3, false, 1, false, 8>", "kernel_ms": fstage["gemm1"],
                       "algorithmic_bytes": f1b, "achieved_GBps": f1, "frac": f1 / HBM_PEAK_GBS,
                       "traffic": profiled_traffic(wf.name)},
             "stages_ms": fstage}
-        del frun, fin
+        del frun
+        if not args.no_prefill:
+            # the prefill batch (same x and router bias row) on the FP8 weights
+            wpf = WORKLOADS["prefill_fp8"]
+            print("[bench] prefill with FP8 expert weights", file=sys.stderr, flush=True)
+            fpin = dict(fin)
+            fpin["x"], fpin["router_bias"] = pin["x"], pin["router_bias"]
+            fprun = Runner(wpf, fpin, torch, moe, stream)
+            fpsteps = max(3, args.steps // 2)
+            fpms, _, fpstage = fprun.timed(fpsteps, max(1, args.warmup // 2))
+            fpc = fprun.counts.cpu().numpy()
+            fpbytes, fpflops, _ = layer_work(wpf, fpc)
+            res["fp8_prefill"] = {
+                "workload": describe(wpf) + " weights=fp8_e4m3 (per-row fp32 scales)",
+                "value": wpf.T / (fpms * 1e-3), "unit": "tokens/s", "ms_per_step": fpms,
+                "step_ms": fprun.step_stats, "steps": fpsteps,
+                "hbm_frac": fpbytes / (fpms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "mfma_frac": fpflops / (fpms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                "binding_frac": binding_frac(fpbytes, fpflops, fpms),
+                "algorithmic_bytes": fpbytes, "algorithmic_flops": fpflops,
+                "stages_ms": fpstage}
+            del fprun, fpin
+        del fin
+    if args.workload == "decode" and not args.no_prefill:
+        del pin
     if args.workload == "decode" and not args.no_mxfp4:
         # the same layer with the same weight draws quantised to MXFP4 (E2M1
         # codes, one E8M0 exponent per 32 elements of a row)
@@ -410,6 +456,7 @@ def main():
         res["mxfp4_decode"] = {
             "workload": describe(wm) + " weights=mxfp4 (E2M1, E8M0 exponent per 32)",
             "value": wm.T / (mms * 1e-3), "unit": "tokens/s", "ms_per_step": mms,
+            "step_ms": mrun.step_stats,
             "steps": args.steps, "hbm_frac": mbytes / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "gemm1": {"kernel": "gemm_bf16_stream<3, false, 2, true, 8>", "kernel_ms": mstage["gemm1"],
                       "algorithmic_bytes": m1b, "achieved_GBps": m1, "frac": m1 / HBM_PEAK_GBS,

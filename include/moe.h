@@ -35,13 +35,21 @@
  *     MOE_ENOSPACE (workspace too small).  A failed launch returns MOE_EHIP.
  *     T == 0 is valid and launches nothing.  No C++ exception crosses the ABI.
  *   - Preconditions the kernels do not check: logits finite; topk_ids in [0,E).
- *   - The only state the library keeps is, per device, one stream of its
- *     own (default priority, created on first use) with two events: when a
- *     batch splits the experts into many small and some large groups, the
- *     small groups' chain runs there, forked from and joined back into
- *     `stream` with events (a graph capture takes it in).  A mutex keeps
- *     concurrent callers' forks apart, so calls may be issued from several
- *     host threads on different streams.
+ *   - The only state the library keeps is a table of side streams: for each
+ *     (device, caller stream) pair, one stream of its own (default priority,
+ *     created on the first call that needs it) with three events (fork,
+ *     join, shared expert done).  When a batch splits the experts into many
+ *     small and some large groups, the small groups' chain runs there, and
+ *     in bf16 layers so does the shared expert; both are forked from and
+ *     joined back into `stream` with those events, on every return path
+ *     including errors, so a graph capture of `stream` takes them in.
+ *     Because each caller stream has its own side stream and events, calls
+ *     on different streams may be issued from different host threads, and
+ *     one stream may be captured while another runs eagerly.  Calls on one
+ *     stream must come from one host thread at a time (as for any work on
+ *     one stream).  Past 32 caller streams per device, or if a side stream
+ *     cannot be created, a call runs unsplit on `stream` with the same
+ *     results.
  */
 #ifndef ROUTED_MOE_MI355X_H
 #define ROUTED_MOE_MI355X_H
@@ -216,7 +224,12 @@ moe_status_t moe_combine(moe_dtype_t out_dtype, int64_t T, int32_t k, int32_t D,
  *   ws, ws_bytes   at least moe_forward_workspace(...) with the same shapes
  * With a shared expert and no latent, out = routed + shared, summed in fp32
  * and rounded once; with a latent, the up-projection and the shared expert's
- * down-projection accumulate into one fp32 sum rounded once.
+ * down-projection accumulate into one fp32 sum rounded once.  Between the
+ * down product and the combine, the expert rows are kept in fp16 in bf16
+ * layers (IEEE binary16: an 11-bit significand, three bits more than bf16,
+ * which keeps the output within the bf16 bar) and in fp32 in fp32 layers;
+ * the combine sums them in fp32.  Expert outputs must then stay within
+ * fp16's finite range, |y| <= 65504 (larger ones become +-inf in `out`).
  * ---------------------------------------------------------------------- */
 enum {
     MOE_STAGE_ROUTER = 0,   /* router logits */

@@ -7,6 +7,7 @@ the library is missing, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -436,8 +437,6 @@ def _forward(cfg, x, I, experts, w_router, router_bias, router_logits, correctio
     for name, t in (("router_bias", router_bias), ("router_logits", router_logits),
                     ("correction_bias", correction_bias)):
         _need(t, torch.float32, name)
-    if out is None:
-        out = torch.empty((T, H), dtype=x.dtype, device=x.device)
     c = cfg.c()
     lat = _latent_struct(latent)
     sh = _shared_struct(shared)
@@ -448,8 +447,15 @@ def _forward(cfg, x, I, experts, w_router, router_bias, router_logits, correctio
                                           ctypes.byref(pl) if pl else None)
     if nbytes == 0:
         raise MoeError(MOE_EINVAL, "moe_forward_workspace rejected the shapes")
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    # Buffers made here belong to the stream the layer runs on: torch's
+    # caching allocator then hands their blocks to no other stream while the
+    # layer's kernels (on `stream`, and on the side stream joined back into
+    # it) may still use them.
+    with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
+        if out is None:
+            out = torch.empty((T, H), dtype=x.dtype, device=x.device)
+        if workspace is None:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
     ev = None
     if stage_events is not None:
         if len(stage_events) != 2 * MOE_NUM_STAGES:

@@ -6,7 +6,9 @@
 //
 // A gather, not a scatter: every output element is owned by one thread, the
 // k rows are read through the inverse permutation, the sum runs in fp32 in
-// ascending j and is rounded once.  No atomics.  Optional fused extras:
+// ascending j and is rounded once.  No atomics.  The expert rows come in
+// fp32 or fp16 (bf16 layers; every fp16 value is exact in fp32).  Optional
+// fused extras:
 //  * an fp32 addend (the shared expert's output) added before the rounding;
 //  * RMSNorm of the whole row (the latent tail's norm, page
 //    "vllm.models.kimi_k3.nvidia.latent_moe_runner", allreduce_norm_latent_out
@@ -25,6 +27,16 @@ __device__ __forceinline__ void store4(void* out, int out_dtype, int64_t idx, f3
         uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
         *(uint2*)((bf16_t*)out + idx) = make_uint2(lo, hi);
     }
+}
+
+// Four consecutive values of expert row `row` from fp32 or fp16 storage.
+__device__ __forceinline__ f32x4_t load_y4(const CombineArgs& a, int64_t row, int d) {
+    if (a.y_f16) {
+        const uint2 h = *(const uint2*)((const uint16_t*)a.y_rows + row * a.D + d);
+        return f32x4_t{f16_bits_to_f32(h.x & 0xffffu), f16_bits_to_f32(h.x >> 16),
+                       f16_bits_to_f32(h.y & 0xffffu), f16_bits_to_f32(h.y >> 16)};
+    }
+    return *(const f32x4_t*)((const float*)a.y_rows + row * a.D + d);
 }
 
 __device__ __forceinline__ float gamma_at(const void* gamma, int out_dtype, int d) {
@@ -46,7 +58,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     if (d >= a.D) return;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < a.k; ++j) {
-        const f32x4_t v = *(const f32x4_t*)(a.y_rows + (int64_t)rows[j] * a.D + d);
+        const f32x4_t v = load_y4(a, rows[j], d);
         const float w = ws[j];
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, v[i], acc[i]);
@@ -80,7 +92,7 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(CombineArgs a) {
         const int d = (v * 256 + tid) * 4;
         if (d < a.D) {
             for (int j = 0; j < a.k; ++j) {
-                const f32x4_t y = *(const f32x4_t*)(a.y_rows + (int64_t)rows[j] * a.D + d);
+                const f32x4_t y = load_y4(a, rows[j], d);
                 const float w = ws[j];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[v][i] = fmaf(w, y[i], acc[v][i]);

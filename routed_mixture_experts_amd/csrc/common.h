@@ -36,6 +36,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// IEEE binary16 bit patterns: fp32 -> fp16 rounds to nearest even
+// (v_cvt_f16_f32); fp16 -> fp32 is exact.
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    return f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
 // Tile-list entry of a grouped GEMM: rows [row0, row1) of group g; the
 // group's tiles are the contiguous entries [first, first + count).
 struct Tile {
@@ -47,7 +59,8 @@ enum Epilogue : int {
     EPI_F32 = 0,        // C f32 [M, N]
     EPI_F32_BIAS = 1,   // C f32 [M, N] = acc + bias[n]
     EPI_OUT = 2,        // C in the layer dtype [M, N]
-    EPI_SWIGLU = 3      // C in the layer dtype [M, N]: silu(acc_gate) * acc_up
+    EPI_SWIGLU = 3,     // C in the layer dtype [M, N]: silu(acc_gate) * acc_up
+    EPI_F16 = 4         // C fp16 [M, N] (the expert rows of bf16 layers; grouped only)
 };
 
 // One GEMM launch: C[r, n] = sum_k A[arow(r), k] * B_g[n, k]
@@ -156,13 +169,16 @@ hipError_t launch_build_tiles(const int32_t* offsets, int32_t E, int32_t small_m
                               Tile* big_tiles, int32_t* num_big, hipStream_t s);
 
 // dtype: 0 = f32, 1 = bf16.  path: see gemm.hip (chosen by the caller).
-enum GemmPath : int { GEMM_TILED = 0, GEMM_STREAM = 1, GEMM_BIG = 2 };
+enum GemmPath : int { GEMM_TILED = 0, GEMM_STREAM = 1, GEMM_BIG = 2, GEMM_BIG_RW = 3 };
 hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s);
 // The weight-streaming kernels (gemm_stream.hip): rows per tile, column tiles,
 // and the launch over nm row tiles.
 int stream_row_tile();
 int stream_col_tiles(int epi, int N);
 hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s);
+// 256x256 tiles with the weights streamed into registers (gemm_rw.hip): bf16
+// weights, one K segment; nm row tiles.
+hipError_t launch_rw_gemm(const GemmArgs& g, int nm, hipStream_t s);
 // Rows per tile of a kernel (a grouped tile list must be built with it).
 int gemm_row_tile(int dtype, int path);
 // Largest group the streaming kernel takes as a single tile.
@@ -171,7 +187,8 @@ constexpr int kStreamMaxRows = 64;
 struct CombineArgs {
     int64_t T;
     int32_t k, D;
-    const float* y_rows;
+    const void* y_rows;      // [T*k, D] f32, or fp16 when y_f16
+    int32_t y_f16;
     const int32_t* pair_to_row;
     const float* weights;
     const float* addend;     // optional [T, D] f32 added before rounding

@@ -220,6 +220,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
                     if (EPI == EPI_F32_BIAS && g.bias) v += g.bias[c];
                     if (EPI == EPI_OUT)
                         ((bf16_t*)g.C)[(int64_t)r * g.ldc + c] = f32_to_bf16(v);
+                    else if (EPI == EPI_F16)
+                        ((uint16_t*)g.C)[(int64_t)r * g.ldc + c] = (uint16_t)f32_to_f16_bits(v);
                     else
                         cslice[(int64_t)r * g.ldc + c] = v;
                 }
@@ -548,6 +550,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
                         o[2] = pack_bf16x2(v1[0], v1[1]);
                         o[3] = pack_bf16x2(v1[2], v1[3]);
                         *(u32x4_t*)((bf16_t*)g.C + (int64_t)r * g.ldc + c) = o;
+                    } else if (EPI == EPI_F16) {
+                        u32x4_t o;
+                        o[0] = pack_f16x2(v0[0], v0[1]);
+                        o[1] = pack_f16x2(v0[2], v0[3]);
+                        o[2] = pack_f16x2(v1[0], v1[1]);
+                        o[3] = pack_f16x2(v1[2], v1[3]);
+                        *(u32x4_t*)((uint16_t*)g.C + (int64_t)r * g.ldc + c) = o;
                     } else {
                         float* dst = (float*)g.C + (int64_t)r * g.ldc + c;
                         *(f32x4_t*)dst = v0;
@@ -667,6 +676,9 @@ template <bool KC>
 void launch_big(const GemmArgs& g, dim3 gd, hipStream_t s) {
     const dim3 bd(512);
     switch (g.epi) {
+        case EPI_F16:
+            if constexpr (!KC) gemm_bf16_big<EPI_F16, KC><<<gd, bd, 0, s>>>(g);
+            break;
         case EPI_F32: gemm_bf16_big<EPI_F32, KC><<<gd, bd, 0, s>>>(g); break;
         case EPI_F32_BIAS: gemm_bf16_big<EPI_F32_BIAS, KC><<<gd, bd, 0, s>>>(g); break;
         case EPI_OUT: gemm_bf16_big<EPI_OUT, KC><<<gd, bd, 0, s>>>(g); break;
@@ -692,14 +704,14 @@ int col_tiles(int path, int dtype, int epi, int N) {
     const bool sw = epi == EPI_SWIGLU;
     if (dtype == 0) return sw ? (N + 31) / 32 : (N + FBN - 1) / FBN;
     if (path == GEMM_STREAM) return stream_col_tiles(epi, N);
-    if (path == GEMM_BIG) return sw ? (N + 127) / 128 : (N + GBN - 1) / GBN;
+    if (path == GEMM_BIG || path == GEMM_BIG_RW) return sw ? (N + 127) / 128 : (N + GBN - 1) / GBN;
     return sw ? (N + 63) / 64 : (N + TBN - 1) / TBN;
 }
 
 int row_tile(int path, int dtype) {
     if (dtype == 0) return FBM;
     if (path == GEMM_STREAM) return stream_row_tile();
-    return path == GEMM_BIG ? GBM : TBM;
+    return path == GEMM_BIG || path == GEMM_BIG_RW ? GBM : TBM;
 }
 
 }  // namespace
@@ -721,17 +733,22 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
     }
 #define MOE_TILED_SWITCH(WF)                                                              \
     switch (g.epi) {                                                                      \
+        case EPI_F16: gemm_bf16_tiled<EPI_F16, WF><<<gd, bd, 0, s>>>(g); break;           \
         case EPI_F32: gemm_bf16_tiled<EPI_F32, WF><<<gd, bd, 0, s>>>(g); break;           \
         case EPI_F32_BIAS: gemm_bf16_tiled<EPI_F32_BIAS, WF><<<gd, bd, 0, s>>>(g); break; \
         case EPI_OUT: gemm_bf16_tiled<EPI_OUT, WF><<<gd, bd, 0, s>>>(g); break;           \
         default: gemm_bf16_tiled<EPI_SWIGLU, WF><<<gd, bd, 0, s>>>(g); break;             \
     }
     if (g.b_fmt != WF_BF16 && (dtype == 0 || path == GEMM_BIG || g.A2)) return hipErrorInvalidValue;
+    // fp16 expert rows: grouped bf16 products without a second K segment
+    if (g.epi == EPI_F16 && (dtype == 0 || !g.tiles || g.A2)) return hipErrorInvalidValue;
     if (g.b_fmt == WF_MXFP4 && g.K % 128 != 0) return hipErrorInvalidValue;
     if (dtype == 0) {
         MOE_GEMM_SWITCH(gemm_f32_tiled)
     } else if (path == GEMM_STREAM) {
         return launch_stream_gemm(g, nm, s);
+    } else if (path == GEMM_BIG_RW) {
+        return launch_rw_gemm(g, nm, s);
     } else if (path == GEMM_BIG) {
         if (g.A2) launch_big<true>(g, gd, s);
         else launch_big<false>(g, gd, s);

@@ -530,6 +530,14 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
                     if (hc0 + j < g.N)
                         crow[hc0 + j] = f32_to_bf16(glu_f32(acc[tb][j] * rs[j], up[j], g));
             }
+        } else if (EPI == EPI_F16) {
+            // four consecutive fp16 columns in one 8-byte store (N and the
+            // column base are multiples of 4, so they are all in range or none)
+            const int c0 = tc.nt * SRN + wave * 16 + g4 * 4;
+            if (r < tc.row1 && c0 < g.N)
+                *(uint2*)((uint16_t*)g.C + (int64_t)r * g.ldc + c0) =
+                    make_uint2(pack_f16x2(acc[tb][0] * rs[0], acc[tb][1] * rs[1]),
+                               pack_f16x2(acc[tb][2] * rs[2], acc[tb][3] * rs[3]));
         } else if (r < tc.row1) {
             const int c0 = tc.nt * SRN + wave * 16 + g4 * 4;
 #pragma unroll
@@ -571,6 +579,10 @@ template <bool KC, int WF, bool SV, int NW>
 void launch_stream_rows(const GemmArgs& g, int nm, hipStream_t s) {
     const dim3 gd((unsigned)((int64_t)nm * stream_col_tiles_nw(g.epi, g.N, NW))), bd(64 * NW);
     switch (g.epi) {
+        case EPI_F16:
+            // grouped expert rows only (never a K-concatenated product)
+            if constexpr (!KC) gemm_bf16_stream<EPI_F16, KC, WF, SV, NW><<<gd, bd, 0, s>>>(g);
+            break;
         case EPI_F32: gemm_bf16_stream<EPI_F32, KC, WF, SV, NW><<<gd, bd, 0, s>>>(g); break;
         case EPI_F32_BIAS:
             gemm_bf16_stream<EPI_F32_BIAS, KC, WF, SV, NW><<<gd, bd, 0, s>>>(g);
@@ -595,6 +607,7 @@ hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
     const bool sw = g.epi == EPI_SWIGLU;
     const int64_t grid_ks = (int64_t)nm * (sw ? (g.N + 31) / 32 : (g.N + SNW - 1) / SNW);
     if (grid_ks <= 0) return hipSuccess;
+    if (g.epi == EPI_F16 && (!g.tiles || g.A2)) return hipErrorInvalidValue;
     if (!g.tiles && grid_ks < kStreamRowsMinGrid && g.b_fmt == WF_BF16) {
         const dim3 gd((unsigned)grid_ks), bd(256);
         switch (g.epi) {

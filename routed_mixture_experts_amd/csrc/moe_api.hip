@@ -190,32 +190,55 @@ moe_status_t large_groups_gemm(moe_dtype_t dt, GemmArgs g, const ExpertsWs& w, i
     return hip_status(launch_gemm(f32 ? 0 : 1, path, g, s));
 }
 
-// A second stream per device, owned by the library (default priority), on
-// which the small-group chain runs beside the large-group chain.  The mutex
-// also keeps the fork/join events of concurrent host threads apart.
+// Library-owned side streams (default priority) on which the small-group
+// chain and the shared expert run beside the caller's stream.  There is one
+// per (device, caller stream) pair, with its own fork / join / shared_done
+// events, so calls on different caller streams -- from different host
+// threads, eagerly or under graph capture -- never wait on each other's
+// events or pull each other's work into a capture.  Calls on one caller
+// stream are ordered by that stream, as any work on it is.  The table holds
+// kMaxSideCtx pairs per device; past that (or if creating one fails, e.g.
+// under a capture mode that forbids it) a call runs unsplit on the caller's
+// stream, which gives the same results.
 struct SideStream {
+    hipStream_t caller = nullptr;
     hipStream_t s = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
     hipEvent_t shared_done = nullptr;  // the shared expert's products (forward)
 };
 constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
+constexpr int kMaxSideCtx = 32;
+struct DeviceSides {
+    SideStream ctx[kMaxSideCtx];
+    int n = 0;
+};
+std::mutex g_side_mu;  // guards the table only; launches happen outside it
+DeviceSides g_side[kMaxDevices];
 
-// Called with g_side_mu held.
-moe_status_t side_stream(SideStream** out) {
+// The side stream of `caller` on the current device, or nullptr (run
+// unsplit).  Entries are never removed, so the pointer stays valid.
+SideStream* side_stream(hipStream_t caller) {
     int dev = 0;
-    MOE_HIP(hipGetDevice(&dev));
-    if (dev < 0 || dev >= kMaxDevices) return MOE_ENOTSUP;
-    SideStream& ss = g_side[dev];
-    if (!ss.s) {
-        MOE_HIP(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
-        MOE_HIP(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming));
-        MOE_HIP(hipEventCreateWithFlags(&ss.shared_done, hipEventDisableTiming));
-        MOE_HIP(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking));
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    DeviceSides& d = g_side[dev];
+    for (int i = 0; i < d.n; ++i)
+        if (d.ctx[i].caller == caller) return &d.ctx[i];
+    if (d.n == kMaxSideCtx) return nullptr;
+    SideStream ss;
+    ss.caller = caller;
+    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.shared_done, hipEventDisableTiming) != hipSuccess ||
+        hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) {
+        if (ss.fork) (void)hipEventDestroy(ss.fork);
+        if (ss.join) (void)hipEventDestroy(ss.join);
+        if (ss.shared_done) (void)hipEventDestroy(ss.shared_done);
+        (void)hipGetLastError();
+        return nullptr;
     }
-    *out = &ss;
-    return MOE_OK;
+    d.ctx[d.n] = ss;
+    return &d.ctx[d.n++];
 }
 
 // Grouped gate/up + SwiGLU, then grouped down, over expert-sorted rows.
@@ -233,7 +256,7 @@ constexpr int64_t kOverlapMinRows = 16;
 // list, so the large-group products are not launched.
 moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, const void* x,
                          const int32_t* offsets, const int32_t* row_to_pair,
-                         const ExpertWeights& ew, float* y_rows, const ExpertsWs& w,
+                         const ExpertWeights& ew, void* y_rows, int y_epi, const ExpertsWs& w,
                          hipStream_t s, hipEvent_t* ev, bool tiles_built = false,
                          bool all_small = false) {
     const int64_t P = T * k;
@@ -272,7 +295,7 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
     g2.b_scale_gstride = ew.fmt == WF_MXFP4 ? (int64_t)D * (I / 32) : D;
     g2.K = I;
     g2.N = D;
-    g2.epi = EPI_F32;
+    g2.epi = y_epi;
     g2.C = y_rows;
     g2.ldc = D;
 
@@ -292,23 +315,25 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
         return stage_mark(MOE_STAGE_GEMM2, 1);
     }
     if (!f32 && P >= kOverlapMinRows * E) {
-        std::lock_guard<std::mutex> lock(g_side_mu);
-        SideStream* ss = nullptr;
-        MOE_TRY(side_stream(&ss));
-        MOE_HIP(hipEventRecord(ss->fork, s));
-        MOE_HIP(hipStreamWaitEvent(ss->s, ss->fork, 0));
         // beside the 256-row chain, 16-wave streaming workgroups do better
         GemmArgs s1 = g1, s2 = g2;
         s1.stream_nw = s2.stream_nw = 16;
-        moe_status_t st = small_groups_gemm(s1, w, E, ss->s);
-        if (st == MOE_OK) st = small_groups_gemm(s2, w, E, ss->s);
+        SideStream* ss = side_stream(s);
+        hipStream_t sc = s;  // the small-group chain's stream
+        if (ss) {
+            MOE_HIP(hipEventRecord(ss->fork, s));
+            MOE_HIP(hipStreamWaitEvent(ss->s, ss->fork, 0));
+            sc = ss->s;
+        }
+        moe_status_t st = small_groups_gemm(s1, w, E, sc);
+        if (st == MOE_OK) st = small_groups_gemm(s2, w, E, sc);
         // the caller's stream joins the side stream even after an error
-        const moe_status_t sj = hip_status(hipEventRecord(ss->join, ss->s));
+        const moe_status_t sj = ss ? hip_status(hipEventRecord(ss->join, ss->s)) : MOE_OK;
         if (st == MOE_OK) st = large_groups_gemm(dt, g1, w, P, E, s);
         if (st == MOE_OK) st = stage_mark(MOE_STAGE_GEMM1, 1);
         if (st == MOE_OK) st = stage_mark(MOE_STAGE_GEMM2, 0);
         if (st == MOE_OK) st = large_groups_gemm(dt, g2, w, P, E, s);
-        if (sj == MOE_OK) MOE_HIP(hipStreamWaitEvent(s, ss->join, 0));
+        if (ss && sj == MOE_OK) MOE_HIP(hipStreamWaitEvent(s, ss->join, 0));
         MOE_TRY(sj);
         MOE_TRY(st);
         return stage_mark(MOE_STAGE_GEMM2, 1);
@@ -354,7 +379,7 @@ struct ForwardWs {
     int32_t* p2r;
     int32_t* chunks;
     ExpertsWs ex;
-    float* y_rows;
+    void* y_rows;   // expert outputs [T*k, D]: fp16 in bf16 layers, else f32
     void* z;        // latent input [T, L]
     void* normed;   // latent RMSNorm output [T, L]
     void* h_sh;     // shared intermediate [T, Is]
@@ -383,7 +408,7 @@ ForwardWs carve_forward(Carve& c, const moe_route_cfg_t* cfg, moe_dtype_t dt, in
     w.p2r = c.take<int32_t>((size_t)P);
     w.chunks = c.take<int32_t>((size_t)permute_chunks(P) * E);
     w.ex = carve_experts(c, dt, max_T, k, E, I);
-    w.y_rows = c.take<float>((size_t)P * D);
+    w.y_rows = c.take<char>((size_t)P * D * (dt == MOE_DTYPE_BF16 ? 2 : 4));
     w.z = lat ? c.take<char>((size_t)max_T * D * es) : nullptr;
     w.normed = lat ? c.take<char>((size_t)max_T * D * es) : nullptr;
     w.h_sh = sh ? c.take<char>((size_t)max_T * sh->inter * es) : nullptr;
@@ -560,8 +585,8 @@ moe_status_t experts_impl(moe_dtype_t dtype, int64_t T, int32_t k, int32_t E, in
     if (!ws || ws_bytes < moe_experts_workspace(dtype, T, k, E, D, I)) return MOE_ENOSPACE;
     Carve c(ws);
     ExpertsWs w = carve_experts(c, dtype, T, k, E, I);
-    return run_experts(dtype, T, k, E, D, I, x, expert_offsets, row_to_pair, ew, y_rows, w,
-                       (hipStream_t)stream, nullptr);
+    return run_experts(dtype, T, k, E, D, I, x, expert_offsets, row_to_pair, ew, y_rows, EPI_F32,
+                       w, (hipStream_t)stream, nullptr);
 }
 
 }  // namespace
@@ -687,10 +712,22 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
     // The shared expert reads only x: in bf16 layers its products run on the
     // library's second stream beside routing, dispatch and the routed
     // experts, and the caller's stream waits for them where they are used.
-    SideStream* sh_ss = nullptr;
-    if (shared && dtype == MOE_DTYPE_BF16) {
-        std::lock_guard<std::mutex> lock(g_side_mu);
-        MOE_TRY(side_stream(&sh_ss));
+    SideStream* sh_ss = shared && dtype == MOE_DTYPE_BF16 ? side_stream(s) : nullptr;
+    // Once the shared products are forked, the caller's stream waits for
+    // them on every return path, error returns included, so the side stream
+    // is always joined back (a graph capture needs that).
+    struct SharedJoin {
+        hipStream_t s;
+        SideStream* ss = nullptr;
+        moe_status_t wait() {
+            if (!ss) return MOE_OK;
+            SideStream* t = ss;
+            ss = nullptr;
+            return hip_status(hipStreamWaitEvent(s, t->shared_done, 0));
+        }
+        ~SharedJoin() { (void)wait(); }
+    } sh_join{s};
+    if (sh_ss) {
         MOE_HIP(hipEventRecord(sh_ss->fork, s));
         MOE_HIP(hipStreamWaitEvent(sh_ss->s, sh_ss->fork, 0));
         moe_status_t st = dense_gemm(dtype, T, x, H, shared->w13, H, nullptr, 0, nullptr, 0,
@@ -702,12 +739,10 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
         // recorded even after an error, so the caller's stream never waits
         // on a stale record
         MOE_HIP(hipEventRecord(sh_ss->shared_done, sh_ss->s));
+        sh_join.ss = sh_ss;
         MOE_TRY(st);
     }
-    auto wait_shared = [&]() -> moe_status_t {
-        if (sh_ss) MOE_HIP(hipStreamWaitEvent(s, sh_ss->shared_done, 0));
-        return MOE_OK;
-    };
+    auto wait_shared = [&]() -> moe_status_t { return sh_join.wait(); };
 
     // router logits (fp32 accumulate, fp32 out, + optional bias row)
     const float* logits = router_logits;
@@ -786,7 +821,8 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
     MOE_TRY(mark(MOE_STAGE_PERMUTE, 1));
 
     // routed experts
-    MOE_TRY(run_experts(dtype, T, k, Es, D, I, xin, w.offsets, w.r2p, ew, w.y_rows, w.ex, s, ev,
+    MOE_TRY(run_experts(dtype, T, k, Es, D, I, xin, w.offsets, w.r2p, ew, w.y_rows,
+                        dtype == MOE_DTYPE_BF16 ? EPI_F16 : EPI_F32, w.ex, s, ev,
                         true, all_small));
 
     // shared expert without a latent tail: its output is the combine addend
@@ -809,6 +845,7 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
     ca.k = k;
     ca.D = D;
     ca.y_rows = w.y_rows;
+    ca.y_f16 = dtype == MOE_DTYPE_BF16;
     ca.pair_to_row = w.p2r;
     ca.weights = wts;
     ca.out_dtype = dtype == MOE_DTYPE_F32 ? 0 : 1;

@@ -97,6 +97,9 @@ WORKLOADS = {
     # ... and with MXFP4 expert weights (E2M1 codes, one E8M0 exponent per 32)
     "decode_mxfp4": Workload("decode_mxfp4", T=128, H=7168, E=384, k=8, I=2048,
                              routed_scaling=2.5, weights="mxfp4"),
+    # the prefill layer with FP8 E4M3 expert weights
+    "prefill_fp8": Workload("prefill_fp8", T=8192, H=7168, E=384, k=8, I=2048,
+                            zipf_s=1.1, weights="fp8_e4m3"),
 }
 
 FP8_E4M3_MAX = 448.0  # largest finite E4M3 value

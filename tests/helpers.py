@@ -130,3 +130,71 @@ def check_ids_allowing_near_ties(gpu_ids: np.ndarray, ref_ids: np.ndarray, keys:
             assert gap <= eps, (f"token {t} slot {j}: ids {gpu_ids[t]} vs {ref_ids[t]}, "
                                 f"key gap {gap:.3e} > {eps:.1e}")
     return same
+
+
+def full_layer_parity(w: Workload, inp: dict, res: dict, w13f, w2f, out_tokens, tag: str,
+                      act=None):
+    """Parity of a full-size layer run with the GPU's own router product.
+
+    Logits against the oracle's float64 product on every token (relative L2
+    <= 1e-5).  The oracle then routes from the GPU's logits, so ids and
+    weights must match on every token, and counts, offsets and both maps
+    (moe_permute on the GPU ids) bit for bit.  The output is compared element
+    by element on ``out_tokens`` (a list, or a function of the oracle's
+    counts, offsets and row_to_pair that returns one), which the oracle
+    evaluates from the same logits (``w13f`` / ``w2f`` yield one expert's float64 weights at a time)."""
+    import routed_mixture_experts_amd as moe
+    cfg = oracle_cfg(w)
+    corr = None if inp["corr_bias"] is None else np64(inp["corr_bias"])
+    lg = np64(res["logits"])
+    ref_lg = O.router_logits(np64(inp["x"]), np64(inp["w_router"]),
+                             None if inp["router_bias"] is None else np64(inp["router_bias"]))
+    rel = float(np.linalg.norm(lg - ref_lg) / np.linalg.norm(ref_lg))
+    log(f"[{tag}] logits rel_l2={rel:.2e} (bar 1e-5) over {w.T} tokens")
+    assert rel <= 1e-5, rel
+    ids, wts, _ = O.route(lg, cfg, corr)
+    gids = npi(res["ids"])
+    bad = np.nonzero((gids != ids).any(axis=1))[0]
+    assert bad.size == 0, f"ids differ on {bad.size} tokens, first {bad[:4]}"
+    dw = float(np.abs(np64(res["weights"]) - wts).max())
+    assert dw <= WEIGHT_ATOL, dw
+    rc, roff, rr2p, rp2r = O.permute(ids, w.E)
+    assert (npi(res["counts"]) == rc).all()
+    c, off, r2p, p2r = moe.moe_permute(res["ids"], w.E)
+    torch.cuda.synchronize()
+    assert (npi(c) == rc).all() and (npi(off) == roff).all()
+    assert (npi(r2p) == rr2p).all() and (npi(p2r) == rp2r).all()
+    log(f"[{tag}] ids, weights (max diff {dw:.1e}), counts, offsets, maps exact over "
+        f"{w.T} tokens; load max {rc.max()} min {rc.min()} empty {(rc == 0).sum()}")
+    if callable(out_tokens):
+        out_tokens = out_tokens(rc, roff, rr2p)
+    toks = np.asarray(sorted(set(int(t) for t in out_tokens)), dtype=np.int64)
+    ref = O.forward(np64(inp["x"][torch.from_numpy(toks).to(inp["x"].device)]), cfg, w13f, w2f,
+                    logits=lg[toks], corr_bias=corr, latent=latent_np(inp, w),
+                    shared=shared_np(inp, w), act=act)
+    assert (ref["ids"] == ids[toks]).all()
+    check_float(np64(res["out"])[toks], ref["out"], w.dtype == "bf16",
+                f"{tag} out on {toks.size} tokens")
+    return rc, roff, rr2p
+
+
+def parity_tokens(w: Workload, counts, offsets, row_to_pair, n_random: int = 24, seed: int = 0,
+                  big_rows: int = 256, small_max: int = 64, small_block: int = 16,
+                  extra_groups: int = 20):
+    """Tokens whose outputs a full-size check compares: random ones, the
+    first and last token, and for up to ``extra_groups`` groups of each size
+    class the token of the group's last row when that row falls in a partly
+    filled tile (256-row tiles above ``small_max`` rows, 16-row token blocks
+    at or below), plus two tokens of the largest group."""
+    rng = np.random.default_rng(seed)
+    toks = set(rng.choice(w.T, size=min(n_random, w.T), replace=False).tolist())
+    toks |= {0, w.T - 1}
+    big = [e for e in range(w.E) if counts[e] > small_max and counts[e] % big_rows]
+    small = [e for e in range(w.E) if 0 < counts[e] <= small_max and counts[e] % small_block]
+    for grp in (big[:extra_groups], small[:extra_groups]):
+        for e in grp:
+            toks.add(int(row_to_pair[offsets[e + 1] - 1]) // w.k)
+    hot = int(np.argmax(counts))
+    for r in (offsets[hot], offsets[hot + 1] - 1):
+        toks.add(int(row_to_pair[r]) // w.k)
+    return sorted(toks)

@@ -94,8 +94,12 @@ def test_workspace_sizes_grow_with_capacity(lib):
     c = _cfg(num_experts=384, top_k=8)
     f = lib.moe_forward_workspace(ctypes.byref(c), L.MOE_DTYPE_BF16, 8192, 7168, 2048, None,
                                   None)
-    # y_rows in fp32 dominates: P * D * 4 bytes
-    assert f >= 8192 * 8 * 7168 * 4
+    # the expert rows dominate: P * D fp16 values in a bf16 layer, fp32 in an
+    # fp32 one
+    assert f >= 8192 * 8 * 7168 * 2
+    f32 = lib.moe_forward_workspace(ctypes.byref(c), L.MOE_DTYPE_F32, 8192, 7168, 2048, None,
+                                    None)
+    assert f32 >= 8192 * 8 * 7168 * 4
     assert lib.moe_forward_workspace(ctypes.byref(c), 7, 128, 7168, 2048, None, None) == 0
 
 

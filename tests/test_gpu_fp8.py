@@ -6,7 +6,8 @@ The oracle decodes the same codes and row scales into float64 weights
 values; the remaining difference is the bf16 rounding of h and of the output,
 and the bar is the bf16 layer's.  Shapes cover the streaming kernel with 1, 2
 and 4 token blocks and a ragged last K chunk, the 128-row tiled kernel for
-groups above 64 rows, and the full decode layer (sampled tokens).
+groups above 64 rows, both expert chains in one layer, and the full decode
+and prefill layers.
 """
 import ctypes
 
@@ -18,8 +19,8 @@ import oracle as O
 import routed_mixture_experts_amd as moe
 import routed_mixture_experts_amd._lib as L
 from routed_mixture_experts_amd.synth import WORKLOADS, Workload, make_inputs, random_logits
-from tests.helpers import (WEIGHT_ATOL, ExpertFetchFP8, check_float,
-                           check_ids_allowing_near_ties, lib_cfg, log, np64, npi, oracle_cfg)
+from tests.helpers import (ExpertFetchFP8, WEIGHT_ATOL, check_float, full_layer_parity, lib_cfg,
+                           log, np64, npi, oracle_cfg, parity_tokens)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -120,30 +121,84 @@ def test_forward_fp8_given_logits_matches_oracle():
     check_float(np64(out), ref["out"], True, "out fp8 small layer")
 
 
-def test_full_decode_fp8_sampled():
+def test_full_decode_fp8():
+    """The full decode layer: routing, counts and maps over all 128 tokens
+    from the GPU's logits, and the output on 64 tokens against the oracle's
+    decode of the same codes."""
     w = WORKLOADS["decode_fp8"]
     log(f"full workload decode_fp8: T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
     inp = make_inputs(w, DEV, chunk_rows=16)
     T = w.T
-    logits = torch.empty((T, w.E), dtype=torch.float32, device=DEV)
-    ids = torch.empty((T, w.k), dtype=torch.int32, device=DEV)
-    wts = torch.empty((T, w.k), dtype=torch.float32, device=DEV)
-    counts = torch.empty((w.E,), dtype=torch.int32, device=DEV)
-    out = moe.moe_forward_ex(lib_cfg(w), inp["x"], _fp8(inp), w_router=inp["w_router"],
-                             logits_out=logits, topk_ids_out=ids, topk_weights_out=wts,
-                             expert_counts_out=counts)
+    res = dict(logits=torch.empty((T, w.E), dtype=torch.float32, device=DEV),
+               ids=torch.empty((T, w.k), dtype=torch.int32, device=DEV),
+               weights=torch.empty((T, w.k), dtype=torch.float32, device=DEV),
+               counts=torch.empty((w.E,), dtype=torch.int32, device=DEV))
+    res["out"] = moe.moe_forward_ex(lib_cfg(w), inp["x"], _fp8(inp), w_router=inp["w_router"],
+                                    logits_out=res["logits"], topk_ids_out=res["ids"],
+                                    topk_weights_out=res["weights"],
+                                    expert_counts_out=res["counts"])
     torch.cuda.synchronize()
-    assert npi(counts).sum() == T * w.k
-    np.testing.assert_allclose(np64(wts).sum(1), w.routed_scaling, rtol=1e-6)
-    toks = np.sort(np.random.default_rng(0).choice(T, size=8, replace=False))
-    ref = O.forward_tokens(toks, np64(inp["x"]), oracle_cfg(w),
-                           ExpertFetchFP8(inp["w13"], inp["w13_scale"]),
-                           ExpertFetchFP8(inp["w2"], inp["w2_scale"]),
-                           w_router=np64(inp["w_router"]))
-    lg = np64(logits)[toks]
-    assert np.linalg.norm(lg - ref["logits"]) / np.linalg.norm(ref["logits"]) <= 1e-5
-    same = check_ids_allowing_near_ties(npi(ids)[toks], ref["ids"], ref["keys"], 1e-5)
-    assert np.abs(np64(wts)[toks][same] - ref["weights"][same]).max() <= 1e-5
-    check_float(np64(out)[toks][same], ref["out"][same], True, "out decode_fp8 sampled")
-    del inp
+    toks = np.sort(np.random.default_rng(0).choice(T, size=64, replace=False))
+    full_layer_parity(w, inp, res, ExpertFetchFP8(inp["w13"], inp["w13_scale"]),
+                      ExpertFetchFP8(inp["w2"], inp["w2_scale"]), toks, "decode_fp8")
+    del inp, res
+    torch.cuda.empty_cache()
+
+
+def test_forward_fp8_both_expert_chains():
+    """A skewed batch with groups above 64 rows (128-row tiles, fp16 expert
+    rows stored by the tiled kernel) and small groups (streaming, on the
+    second stream) in one layer, against the oracle's decode of the codes."""
+    w = Workload("t", T=640, H=256, E=16, k=4, I=192, routed_scaling=1.5, weights="fp8_e4m3")
+    log("forward fp8, both expert chains")
+    inp = make_inputs(w, DEV)
+    lg = random_logits(w.T, w.E, seed=23)
+    lg[:, :4] += 3.0
+    lg[:, 4:] += torch.linspace(-2.5, 0.5, w.E - 4)
+    logits = lg.to(DEV)
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device=DEV)
+    counts = torch.empty((w.E,), dtype=torch.int32, device=DEV)
+    out = moe.moe_forward_ex(lib_cfg(w), inp["x"], _fp8(inp), router_logits=logits,
+                             topk_ids_out=ids, expert_counts_out=counts)
+    torch.cuda.synchronize()
+    c = npi(counts)
+    log(f"  counts {sorted(c.tolist())}")
+    assert c.max() > 128 and ((c > 0) & (c <= 64)).any()
+    w13, w2 = _dequant(inp)
+    ref = O.forward(np64(inp["x"]), oracle_cfg(w), w13, w2, logits=np64(logits))
+    assert (npi(ids) == ref["ids"]).all()
+    check_float(np64(out), ref["out"], True, "out fp8 both chains")
+
+
+def test_full_prefill_fp8():
+    """The prefill layer (T=8192, Zipf(1.1) load) with FP8 expert weights:
+    routing, counts and maps over every token, the output on at least 64
+    tokens (random, the hottest expert's, tokens ending partly filled
+    128-row tiles and 16-row token blocks)."""
+    w = WORKLOADS["prefill_fp8"]
+    log(f"full workload prefill_fp8: T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
+    inp = make_inputs(w, DEV, chunk_rows=16)
+    T = w.T
+    res = dict(logits=torch.empty((T, w.E), dtype=torch.float32, device=DEV),
+               ids=torch.empty((T, w.k), dtype=torch.int32, device=DEV),
+               weights=torch.empty((T, w.k), dtype=torch.float32, device=DEV),
+               counts=torch.empty((w.E,), dtype=torch.int32, device=DEV))
+    res["out"] = moe.moe_forward_ex(lib_cfg(w), inp["x"], _fp8(inp), w_router=inp["w_router"],
+                                    router_bias=inp["router_bias"], logits_out=res["logits"],
+                                    topk_ids_out=res["ids"], topk_weights_out=res["weights"],
+                                    expert_counts_out=res["counts"])
+    torch.cuda.synchronize()
+
+    def toks(counts, offsets, r2p):
+        t = parity_tokens(w, counts, offsets, r2p, big_rows=128, extra_groups=12)
+        extra = np.random.default_rng(2).permutation(T)
+        i = 0
+        while len(t) < 64:
+            t = sorted(set(t) | {int(extra[i])})
+            i += 1
+        return t
+
+    full_layer_parity(w, inp, res, ExpertFetchFP8(inp["w13"], inp["w13_scale"]),
+                      ExpertFetchFP8(inp["w2"], inp["w2_scale"]), toks, "prefill_fp8")
+    del inp, res
     torch.cuda.empty_cache()

@@ -7,7 +7,7 @@ weight values; the remaining difference is the bf16 rounding of h and of the
 output, and the bar is the bf16 layer's.  Shapes cover the streaming kernel
 with 1, 2 and 4 token blocks (including passes whose last chunks lie past K),
 the 128-row tiled kernel for groups above 64 rows, several turns of the
-weight-load ring, and the full decode layer (sampled tokens).
+weight-load ring, both expert chains in one layer, and the full decode layer.
 """
 import ctypes
 
@@ -19,8 +19,8 @@ import oracle as O
 import routed_mixture_experts_amd as moe
 import routed_mixture_experts_amd._lib as L
 from routed_mixture_experts_amd.synth import WORKLOADS, Workload, make_inputs, random_logits
-from tests.helpers import (WEIGHT_ATOL, ExpertFetchMXFP4, check_float,
-                           check_ids_allowing_near_ties, lib_cfg, log, np64, npi, oracle_cfg)
+from tests.helpers import (ExpertFetchMXFP4, WEIGHT_ATOL, check_float, full_layer_parity,
+                           lib_cfg, log, np64, npi, oracle_cfg)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -121,30 +121,50 @@ def test_forward_mxfp4_given_logits_matches_oracle():
     check_float(np64(out), ref["out"], True, "out mxfp4 small layer")
 
 
-def test_full_decode_mxfp4_sampled():
+def test_full_decode_mxfp4():
+    """The full decode layer: routing, counts and maps over all 128 tokens
+    from the GPU's logits, and the output on 64 tokens against the oracle's
+    decode of the same codes."""
     w = WORKLOADS["decode_mxfp4"]
     log(f"full workload decode_mxfp4: T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
     inp = make_inputs(w, DEV, chunk_rows=16)
     T = w.T
-    logits = torch.empty((T, w.E), dtype=torch.float32, device=DEV)
-    ids = torch.empty((T, w.k), dtype=torch.int32, device=DEV)
-    wts = torch.empty((T, w.k), dtype=torch.float32, device=DEV)
-    counts = torch.empty((w.E,), dtype=torch.int32, device=DEV)
-    out = moe.moe_forward_ex(lib_cfg(w), inp["x"], _mx(inp), w_router=inp["w_router"],
-                             logits_out=logits, topk_ids_out=ids, topk_weights_out=wts,
-                             expert_counts_out=counts)
+    res = dict(logits=torch.empty((T, w.E), dtype=torch.float32, device=DEV),
+               ids=torch.empty((T, w.k), dtype=torch.int32, device=DEV),
+               weights=torch.empty((T, w.k), dtype=torch.float32, device=DEV),
+               counts=torch.empty((w.E,), dtype=torch.int32, device=DEV))
+    res["out"] = moe.moe_forward_ex(lib_cfg(w), inp["x"], _mx(inp), w_router=inp["w_router"],
+                                    logits_out=res["logits"], topk_ids_out=res["ids"],
+                                    topk_weights_out=res["weights"],
+                                    expert_counts_out=res["counts"])
     torch.cuda.synchronize()
-    assert npi(counts).sum() == T * w.k
-    np.testing.assert_allclose(np64(wts).sum(1), w.routed_scaling, rtol=1e-6)
-    toks = np.sort(np.random.default_rng(1).choice(T, size=8, replace=False))
-    ref = O.forward_tokens(toks, np64(inp["x"]), oracle_cfg(w),
-                           ExpertFetchMXFP4(inp["w13"], inp["w13_scale"]),
-                           ExpertFetchMXFP4(inp["w2"], inp["w2_scale"]),
-                           w_router=np64(inp["w_router"]))
-    lg = np64(logits)[toks]
-    assert np.linalg.norm(lg - ref["logits"]) / np.linalg.norm(ref["logits"]) <= 1e-5
-    same = check_ids_allowing_near_ties(npi(ids)[toks], ref["ids"], ref["keys"], 1e-5)
-    assert np.abs(np64(wts)[toks][same] - ref["weights"][same]).max() <= 1e-5
-    check_float(np64(out)[toks][same], ref["out"][same], True, "out decode_mxfp4 sampled")
-    del inp
+    toks = np.sort(np.random.default_rng(1).choice(T, size=64, replace=False))
+    full_layer_parity(w, inp, res, ExpertFetchMXFP4(inp["w13"], inp["w13_scale"]),
+                      ExpertFetchMXFP4(inp["w2"], inp["w2_scale"]), toks, "decode_mxfp4")
+    del inp, res
     torch.cuda.empty_cache()
+
+
+def test_forward_mxfp4_both_expert_chains():
+    """A skewed batch with groups above 64 rows (128-row tiles, fp16 expert
+    rows stored by the tiled kernel) and small groups (streaming, on the
+    second stream) in one layer, against the oracle's decode of the codes."""
+    w = Workload("t", T=640, H=256, E=16, k=4, I=256, routed_scaling=1.5, weights="mxfp4")
+    log("forward mxfp4, both expert chains")
+    inp = make_inputs(w, DEV)
+    lg = random_logits(w.T, w.E, seed=23)
+    lg[:, :4] += 3.0
+    lg[:, 4:] += torch.linspace(-2.5, 0.5, w.E - 4)
+    logits = lg.to(DEV)
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device=DEV)
+    counts = torch.empty((w.E,), dtype=torch.int32, device=DEV)
+    out = moe.moe_forward_ex(lib_cfg(w), inp["x"], _mx(inp), router_logits=logits,
+                             topk_ids_out=ids, expert_counts_out=counts)
+    torch.cuda.synchronize()
+    c = npi(counts)
+    log(f"  counts {sorted(c.tolist())}")
+    assert c.max() > 128 and ((c > 0) & (c <= 64)).any()
+    w13, w2 = _dequant(inp)
+    ref = O.forward(np64(inp["x"]), oracle_cfg(w), w13, w2, logits=np64(logits))
+    assert (npi(ids) == ref["ids"]).all()
+    check_float(np64(out), ref["out"], True, "out mxfp4 both chains")
