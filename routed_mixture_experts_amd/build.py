@@ -17,8 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["route.hip", "permute.hip", "gemm.hip", "gemm_stream.hip", "gemm_rw.hip",
-           "combine.hip", "router.hip", "moe_api.hip"]
+SOURCES = ["route.hip", "permute.hip", "gemm.hip", "gemm_stream.hip", "combine.hip",
+           "router.hip", "moe_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

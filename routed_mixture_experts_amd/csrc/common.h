@@ -169,16 +169,13 @@ hipError_t launch_build_tiles(const int32_t* offsets, int32_t E, int32_t small_m
                               Tile* big_tiles, int32_t* num_big, hipStream_t s);
 
 // dtype: 0 = f32, 1 = bf16.  path: see gemm.hip (chosen by the caller).
-enum GemmPath : int { GEMM_TILED = 0, GEMM_STREAM = 1, GEMM_BIG = 2, GEMM_BIG_RW = 3 };
+enum GemmPath : int { GEMM_TILED = 0, GEMM_STREAM = 1, GEMM_BIG = 2 };
 hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s);
 // The weight-streaming kernels (gemm_stream.hip): rows per tile, column tiles,
 // and the launch over nm row tiles.
 int stream_row_tile();
 int stream_col_tiles(int epi, int N);
 hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s);
-// 256x256 tiles with the weights streamed into registers (gemm_rw.hip): bf16
-// weights, one K segment; nm row tiles.
-hipError_t launch_rw_gemm(const GemmArgs& g, int nm, hipStream_t s);
 // Rows per tile of a kernel (a grouped tile list must be built with it).
 int gemm_row_tile(int dtype, int path);
 // Largest group the streaming kernel takes as a single tile.

@@ -704,14 +704,14 @@ int col_tiles(int path, int dtype, int epi, int N) {
     const bool sw = epi == EPI_SWIGLU;
     if (dtype == 0) return sw ? (N + 31) / 32 : (N + FBN - 1) / FBN;
     if (path == GEMM_STREAM) return stream_col_tiles(epi, N);
-    if (path == GEMM_BIG || path == GEMM_BIG_RW) return sw ? (N + 127) / 128 : (N + GBN - 1) / GBN;
+    if (path == GEMM_BIG) return sw ? (N + 127) / 128 : (N + GBN - 1) / GBN;
     return sw ? (N + 63) / 64 : (N + TBN - 1) / TBN;
 }
 
 int row_tile(int path, int dtype) {
     if (dtype == 0) return FBM;
     if (path == GEMM_STREAM) return stream_row_tile();
-    return path == GEMM_BIG || path == GEMM_BIG_RW ? GBM : TBM;
+    return path == GEMM_BIG ? GBM : TBM;
 }
 
 }  // namespace
@@ -747,8 +747,6 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
         MOE_GEMM_SWITCH(gemm_f32_tiled)
     } else if (path == GEMM_STREAM) {
         return launch_stream_gemm(g, nm, s);
-    } else if (path == GEMM_BIG_RW) {
-        return launch_rw_gemm(g, nm, s);
     } else if (path == GEMM_BIG) {
         if (g.A2) launch_big<true>(g, gd, s);
         else launch_big<false>(g, gd, s);
