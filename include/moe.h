@@ -17,7 +17,8 @@
  *     row-major, at least 16-byte aligned.  Inputs are never written.  The
  *     library allocates, frees and synchronises nothing; scratch memory comes
  *     in as a caller-owned workspace sized from a capacity (max_T), so one
- *     workspace serves every T <= max_T.
+ *     workspace serves every T <= max_T (moe_forward_noalloc instead uses a
+ *     fixed scratch array of the library's device code).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it and returns; results are ready when the stream
  *     reaches them.  With buffers and workspace allocated beforehand, a call
@@ -35,7 +36,8 @@
  *     MOE_ENOSPACE (workspace too small).  A failed launch returns MOE_EHIP.
  *     T == 0 is valid and launches nothing.  No C++ exception crosses the ABI.
  *   - Preconditions the kernels do not check: logits finite; topk_ids in [0,E).
- *   - The only state the library keeps is a table of side streams: for each
+ *   - Besides moe_forward_noalloc's scratch array (see there), the only
+ *     state the library keeps is a table of side streams: for each
  *     (device, caller stream) pair, one stream of its own (default priority,
  *     created on the first call that needs it) with three events (fork,
  *     join, shared expert done).  When a batch splits the experts into many
@@ -385,6 +387,38 @@ moe_status_t moe_forward_ex(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64
                             float* topk_weights_out, int32_t* expert_counts_out,
                             void* const* stage_events, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_forward_noalloc -- moe_forward_ex for callers that cannot allocate:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  It takes no workspace: its scratch memory is a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES in the library's device code, which each GPU the
+ * library runs on holds until the process ends.  The call allocates nothing
+ * (no hipMalloc / hipFree, no side stream: every kernel runs on `stream`);
+ * the caller passes inputs and outputs as for moe_forward_ex, which it
+ * matches result for result.
+ *   Size limit: the layer's scratch need at this T, moe_forward_workspace_ex
+ *   (cfg, dtype, T, H, I, latent, shared, placement), must be at most
+ *   MOE_NOALLOC_SCRATCH_BYTES (64 MiB: the decode layer with H = 7168,
+ *   I = 2048, 384 experts, top-8 fits up to 376 tokens); a larger need
+ *   returns MOE_ENOSPACE before anything is launched.
+ *   Sharing: every call on one GPU uses that GPU's one array, whatever the
+ *   stream or thread, and leaves the last call's contents in it (nothing in
+ *   it needs to start at zero).  Calls that overlap in time on one GPU --
+ *   two streams, or two host threads -- race on it: order them.
+ *   Errors as moe_forward_ex; MOE_EHIP if the array's device address cannot
+ *   be obtained.
+ * ---------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_forward_noalloc(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t T,
+                                 int32_t H, int32_t I, const void* x, const void* w_router,
+                                 const float* router_bias, const float* router_logits,
+                                 const float* correction_bias,
+                                 const moe_expert_weights_t* experts,
+                                 const moe_placement_t* placement, const moe_latent_t* latent,
+                                 const moe_shared_t* shared, void* out, float* logits_out,
+                                 int32_t* topk_ids_out, float* topk_weights_out,
+                                 int32_t* expert_counts_out, void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_string(moe_status_t status);

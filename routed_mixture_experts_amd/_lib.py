@@ -30,7 +30,8 @@ ACTIVATIONS = {"silu": 0, "gelu": 1, "gelu_tanh": 2, "swiglu_clip": 3}
 EXPORTS = ["moe_route", "moe_permute_workspace", "moe_permute", "moe_experts_workspace",
            "moe_experts", "moe_combine", "moe_forward_workspace", "moe_forward",
            "moe_experts_ex", "moe_forward_ex", "moe_forward_workspace_ex", "moe_log2phy",
-           "moe_load_accumulate", "moe_status_string"]
+           "moe_load_accumulate", "moe_forward_noalloc", "moe_status_string"]
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class moe_route_cfg_t(ctypes.Structure):
@@ -141,6 +142,13 @@ def load() -> ctypes.CDLL:
     lib.moe_log2phy.argtypes = [_I64, _I32, _I32, _I32, _P, _P, _P, _P]
     lib.moe_load_accumulate.restype = _I32
     lib.moe_load_accumulate.argtypes = [_I32, _P, _P, _P]
+    lib.moe_forward_noalloc.restype = _I32
+    lib.moe_forward_noalloc.argtypes = [ctypes.POINTER(moe_route_cfg_t), _I32, _I64, _I32, _I32,
+                                        _P, _P, _P, _P, _P,
+                                        ctypes.POINTER(moe_expert_weights_t),
+                                        ctypes.POINTER(moe_placement_t),
+                                        ctypes.POINTER(moe_latent_t),
+                                        ctypes.POINTER(moe_shared_t), _P, _P, _P, _P, _P, _P]
     lib.moe_forward.restype = _I32
     lib.moe_forward.argtypes = [ctypes.POINTER(moe_route_cfg_t), _I32, _I64, _I32, _I32, _P, _P,
                                 _P, _P, _P, _P, _P, ctypes.POINTER(moe_latent_t),
@@ -505,3 +513,37 @@ def moe_forward_ex(cfg: RouteConfig, x: torch.Tensor, experts: ExpertWeights, *,
                     correction_bias, latent, shared, out, logits_out, topk_ids_out,
                     topk_weights_out, expert_counts_out, stage_events, workspace, stream,
                     placement)
+
+
+def moe_forward_noalloc(cfg: RouteConfig, x: torch.Tensor, experts: ExpertWeights,
+                        out: torch.Tensor, *, w_router=None, router_bias=None,
+                        router_logits=None, correction_bias=None, latent: Optional[dict] = None,
+                        shared: Optional[dict] = None, logits_out=None, topk_ids_out=None,
+                        topk_weights_out=None, expert_counts_out=None, stream=None,
+                        placement: Optional[Placement] = None):
+    """moe_forward_ex with no workspace: the library's fixed device scratch
+    array (MOE_NOALLOC_SCRATCH_BYTES per GPU) holds the intermediates.  Nothing
+    is allocated here either: the caller passes ``out`` and any optional
+    outputs.  Calls that overlap in time on one GPU race on the array."""
+    lib = load()
+    T, H = x.shape
+    experts.check_dtype(x.dtype)
+    _need(w_router, x.dtype, "w_router")
+    _need(out, x.dtype, "out")
+    for name, t in (("router_bias", router_bias), ("router_logits", router_logits),
+                    ("correction_bias", correction_bias)):
+        _need(t, torch.float32, name)
+    if tuple(out.shape) != (T, H):
+        raise ValueError("out must be [T, H]")
+    c = cfg.c()
+    lat = _latent_struct(latent)
+    sh = _shared_struct(shared)
+    pl = placement.c() if placement is not None else None
+    wc = experts.c()
+    _check(lib.moe_forward_noalloc(
+        ctypes.byref(c), _dtype_code(x.dtype), T, H, experts.I, _ptr(x), _ptr(w_router),
+        _ptr(router_bias), _ptr(router_logits), _ptr(correction_bias), ctypes.byref(wc),
+        ctypes.byref(pl) if pl else None, ctypes.byref(lat) if lat else None,
+        ctypes.byref(sh) if sh else None, _ptr(out), _ptr(logits_out), _ptr(topk_ids_out),
+        _ptr(topk_weights_out), _ptr(expert_counts_out), _stream(stream)))
+    return out

@@ -258,7 +258,7 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
                          const int32_t* offsets, const int32_t* row_to_pair,
                          const ExpertWeights& ew, void* y_rows, int y_epi, const ExpertsWs& w,
                          hipStream_t s, hipEvent_t* ev, bool tiles_built = false,
-                         bool all_small = false) {
+                         bool all_small = false, bool side_ok = true) {
     const int64_t P = T * k;
     const bool f32 = dt == MOE_DTYPE_F32;
     if (!tiles_built)
@@ -318,7 +318,7 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
         // beside the 256-row chain, 16-wave streaming workgroups do better
         GemmArgs s1 = g1, s2 = g2;
         s1.stream_nw = s2.stream_nw = 16;
-        SideStream* ss = side_stream(s);
+        SideStream* ss = side_ok ? side_stream(s) : nullptr;
         hipStream_t sc = s;  // the small-group chain's stream
         if (ss) {
             MOE_HIP(hipEventRecord(ss->fork, s));
@@ -682,7 +682,7 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
                           float* logits_out,
                           int32_t* topk_ids_out, float* topk_weights_out,
                           int32_t* expert_counts_out, void* const* stage_events, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          size_t ws_bytes, void* stream, bool side_ok = true) {
     MOE_TRY(check_forward_shapes(cfg, dtype, T, H, I, latent, shared));
     if (!weights_fit(ew, latent ? latent->latent : H, I)) return MOE_ENOTSUP;
     if (T == 0) return MOE_OK;
@@ -712,7 +712,7 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
     // The shared expert reads only x: in bf16 layers its products run on the
     // library's second stream beside routing, dispatch and the routed
     // experts, and the caller's stream waits for them where they are used.
-    SideStream* sh_ss = shared && dtype == MOE_DTYPE_BF16 ? side_stream(s) : nullptr;
+    SideStream* sh_ss = side_ok && shared && dtype == MOE_DTYPE_BF16 ? side_stream(s) : nullptr;
     // Once the shared products are forked, the caller's stream waits for
     // them on every return path, error returns included, so the side stream
     // is always joined back (a graph capture needs that).
@@ -823,7 +823,7 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
     // routed experts
     MOE_TRY(run_experts(dtype, T, k, Es, D, I, xin, w.offsets, w.r2p, ew, w.y_rows,
                         dtype == MOE_DTYPE_BF16 ? EPI_F16 : EPI_F32, w.ex, s, ev,
-                        true, all_small));
+                        true, all_small, side_ok));
 
     // shared expert without a latent tail: its output is the combine addend
     if (shared && !latent && sh_ss) {
@@ -922,6 +922,66 @@ moe_status_t moe_forward_ex(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64
                         correction_bias, ew, placement, latent, shared, out, logits_out,
                         topk_ids_out, topk_weights_out, expert_counts_out, stage_events, ws,
                         ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------
+// moe_forward_noalloc: moe_forward_ex without a workspace argument.  The
+// scratch memory comes from a fixed array in the library's device code,
+// whose address on each device is looked up once with that device current.
+// ------------------------------------------------------------------------
+namespace {
+
+static __device__ __attribute__((aligned(256))) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (nullptr on failure).
+void* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_forward_noalloc(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t T,
+                                 int32_t H, int32_t I, const void* x, const void* w_router,
+                                 const float* router_bias, const float* router_logits,
+                                 const float* correction_bias,
+                                 const moe_expert_weights_t* experts,
+                                 const moe_placement_t* placement, const moe_latent_t* latent,
+                                 const moe_shared_t* shared, void* out, float* logits_out,
+                                 int32_t* topk_ids_out, float* topk_weights_out,
+                                 int32_t* expert_counts_out, void* stream) {
+    MOE_TRY(check_forward_shapes(cfg, dtype, T, H, I, latent, shared));
+    ExpertWeights ew;
+    MOE_TRY(expert_weights(dtype, experts, &ew));
+    if (T == 0) return MOE_OK;
+    // the layer's scratch need at this T, checked before any device call
+    const size_t need = moe_forward_workspace_ex(cfg, dtype, T, H, I, latent, shared, placement);
+    if (need == 0) return MOE_EINVAL;
+    if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ENOSPACE;
+    void* ws = scratch_ptr();
+    if (!ws) return MOE_EHIP;
+    // everything on the caller's stream: no side stream is created
+    return forward_impl(cfg, dtype, T, H, I, x, w_router, router_bias, router_logits,
+                        correction_bias, ew, placement, latent, shared, out, logits_out,
+                        topk_ids_out, topk_weights_out, expert_counts_out, nullptr, ws,
+                        MOE_NOALLOC_SCRATCH_BYTES, stream, /*side_ok=*/false);
 }
 
 }  // extern "C"

@@ -240,3 +240,32 @@ def test_log2phy_and_load_accumulate_validation(lib):
     assert lib.moe_load_accumulate(0, None, None, None) == L.MOE_OK
     assert lib.moe_load_accumulate(-1, p, p, None) == L.MOE_EINVAL
     assert lib.moe_load_accumulate(4, None, p, None) == L.MOE_EINVAL
+
+
+def test_noalloc_rejects_a_need_beyond_its_scratch(lib):
+    """moe_forward_noalloc checks the layer's scratch need against its fixed
+    array before any device call: the decode layer at 377 tokens needs more
+    than 64 MiB, so the call returns MOE_ENOSPACE (the pointers are never
+    touched); invalid shapes are rejected as by moe_forward_ex."""
+    assert L.MOE_NOALLOC_SCRATCH_BYTES == 64 << 20
+    c = L.RouteConfig(384, 8).c()
+    need = lib.moe_forward_workspace_ex(ctypes.byref(c), L.MOE_DTYPE_BF16, 377, 7168, 2048,
+                                        None, None, None)
+    assert need > L.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_workspace_ex(ctypes.byref(c), L.MOE_DTYPE_BF16, 376, 7168, 2048,
+                                        None, None, None) <= L.MOE_NOALLOC_SCRATCH_BYTES
+    wc = L.moe_expert_weights_t(L.MOE_WEIGHT_DTYPE, 16, 16, None, None, 0, 0.0, 0.0)
+
+    def call(T, H=7168, cfg=c, w=wc):
+        return lib.moe_forward_noalloc(ctypes.byref(cfg), L.MOE_DTYPE_BF16, T, H, 2048, 16, 16,
+                                       None, None, None, ctypes.byref(w), None, None, None, 16,
+                                       None, None, None, None, None)
+    assert call(377) == L.MOE_ENOSPACE
+    assert call(100000) == L.MOE_ENOSPACE
+    assert call(0) == L.MOE_OK                          # T == 0 launches nothing
+    assert call(8, H=7000) == L.MOE_ENOTSUP             # width not a multiple of 64
+    bad = L.RouteConfig(384, 8).c()
+    bad.top_k = 0
+    assert call(8, cfg=bad) == L.MOE_EINVAL
+    badw = L.moe_expert_weights_t(7, 16, 16, None, None, 0, 0.0, 0.0)
+    assert call(8, w=badw) == L.MOE_EINVAL
