@@ -256,24 +256,38 @@ __device__ __forceinline__ int swz(int row, int chunk) {
     return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
 }
 
-template <int EPI, bool KCAT>
+// With FP8 weights (OCP e4m3 codes, one fp32 scale per weight row; grouped
+// products only) the B stage holds the codes, 64 bytes per weight row (16
+// KB), moved by global_load_lds in 16 rows x 64 bytes per instruction; a
+// fragment read takes a lane's 8 codes (ds_read_b64) and turns them into
+// 8 bf16 values exactly, and the row scales multiply the fp32 sums in the
+// epilogue.  LDS row r of the codes keeps its four 16-byte chunks at chunk ^
+// ((r >> 2) & 3).
+__device__ __forceinline__ int swz8(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
+template <int EPI, bool KCAT, int WF>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     constexpr bool SW = EPI == EPI_SWIGLU;
+    constexpr bool FP8 = WF == WF_FP8;
+    static_assert(WF == WF_BF16 || (FP8 && !KCAT), "FP8 weights: grouped products only");
     const int ntn = SW ? (g.N + 127) / 128 : (g.N + GBN - 1) / GBN;
     TileCoord tc;
     if (!fetch_tile(g, GBM, ntn, tc)) return;
 
-    // one LDS buffer: ring slot s holds the A tile at [s][0] and the B tile at
-    // [s][1]; after the K loop the epilogue reuses it as a flat fp32 buffer
-    __shared__ __attribute__((aligned(1024))) bf16_t smem[GSLOTS][2][GBM * GBK];
+    // one LDS buffer: ring slot s holds the A tile (bf16) and then the B tile
+    // (bf16, or FP8 codes); after the K loop the epilogue reuses it as a flat
+    // fp32 buffer
+    constexpr int A_BYTES = GBM * GBK * 2;
+    constexpr int B_BYTES = FP8 ? GBN * GBK : GBN * GBK * 2;
+    constexpr int SLOT = A_BYTES + B_BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[GSLOTS * SLOT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
 
-    const bf16_t* Bg = (const bf16_t*)g.B + (int64_t)tc.group * g.b_gstride;
     const char* Ab = (const char*)g.A;
-    const char* Bb = (const char*)Bg;
+    const char* Bb = (const char*)g.B + (int64_t)tc.group * g.b_gstride * (FP8 ? 1 : 2);
     const char* A2b = (const char*)g.A2;
     const char* B2b = (const char*)g.B2;
 
@@ -297,11 +311,27 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         } else {
             wrow = min(tc.nt * GBN + row, g.N - 1);
         }
-        bo[i] = (uint32_t)((int64_t)wrow * g.K * 2) + chunk_bytes;
+        bo[i] = (uint32_t)((int64_t)wrow * g.K * 2) + chunk_bytes;  // (bf16 weights)
         if (KCAT) {
             ao2[i] = (uint32_t)((int64_t)rr * g.lda2 * 2) + chunk_bytes;
             bo2[i] = (uint32_t)((int64_t)wrow * g.K2 * 2) + chunk_bytes;
         }
+    }
+    // FP8 codes: DMA block i (0, 1) of this wave covers tile rows 32*wave +
+    // 16*i .. +15 of B; lane l fills row +l/4, slot l%4 (global chunk
+    // (l%4) ^ swz8(row)).
+    uint32_t bo8[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = 32 * wave + 16 * i + (lane >> 2);
+        int wrow;
+        if (SW) {
+            const int c = min(tc.nt * 128 + (row & 127), g.N - 1);
+            wrow = row < 128 ? c : g.N + c;
+        } else {
+            wrow = min(tc.nt * GBN + row, g.N - 1);
+        }
+        bo8[i] = (uint32_t)((int64_t)wrow * g.K) + swz8(row, lane & 3) * 16;
     }
 
     const int nk1 = g.K / GBK;
@@ -319,13 +349,24 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         const uint32_t ko = (uint32_t)(seg1 ? kt : kt - nk1) * GBK * 2;
 #pragma unroll
         for (int i = i0; i < i1; ++i) {
-            const int blk = (32 * wave + 8 * i) * GBK;
+            const int blk = (32 * wave + 8 * i) * GBK * 2;  // bytes
             __builtin_amdgcn_global_load_lds(
                 (const void*)(abase + ((seg1 ? ao[i] : ao2[KCAT ? i : 0]) + ko)),
-                (lds_ptr_t)&smem[slot][0][blk], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(
-                (const void*)(bbase + ((seg1 ? bo[i] : bo2[KCAT ? i : 0]) + ko)),
-                (lds_ptr_t)&smem[slot][1][blk], 16, 0, 0);
+                (lds_ptr_t)(smem + slot * SLOT + blk), 16, 0, 0);
+            if (!FP8)
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(bbase + ((seg1 ? bo[i] : bo2[KCAT ? i : 0]) + ko)),
+                    (lds_ptr_t)(smem + slot * SLOT + A_BYTES + blk), 16, 0, 0);
+        }
+        if (FP8) {
+            // the codes of the blocks' weight rows: one 16-row DMA per two
+            // token blocks
+#pragma unroll
+            for (int i = i0 / 2; i < (i1 + 1) / 2; ++i)
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(Bb + (bo8[i] + (uint32_t)kt * GBK)),
+                    (lds_ptr_t)(smem + slot * SLOT + A_BYTES + (32 * wave + 16 * i) * GBK), 16,
+                    0, 0);
         }
     };
     auto issue = [&](int kt) __attribute__((always_inline)) { issue_blocks(kt, 0, 4); };
@@ -341,6 +382,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     // Operand fragments of v_mfma_f32_32x32x16_bf16: lane (fr, fh) supplies
     // row fr, k 8*fh .. +7 of 16-deep step ks, i.e. LDS chunk 2*ks + fh.
     const int fr = lane & 31, fh = lane >> 5;
+    // (byte offsets inside a slot's A and B tiles)
     int aoffs[4][4], boffs[4][2];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -348,14 +390,25 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             const int row = wm * 128 + mi * 32 + fr;
-            aoffs[ks][mi] = row * GBK + swz(row, ch) * 8;
+            aoffs[ks][mi] = (row * GBK + swz(row, ch) * 8) * 2;
         }
 #pragma unroll
         for (int nj = 0; nj < 2; ++nj) {
             const int row = (SW ? nj * 128 + wn * 32 : wn * 64 + nj * 32) + fr;
-            boffs[ks][nj] = row * GBK + swz(row, ch) * 8;
+            // FP8: the 8 codes of k 16*ks + 8*fh .. +7 are half of chunk ks
+            boffs[ks][nj] = FP8 ? row * GBK + swz8(row, ks) * 16 + fh * 8
+                                : (row * GBK + swz(row, ch) * 8) * 2;
         }
     }
+    // B fragment at byte offset o of a slot's B tile
+    auto bfrag = [&](const char* b, int o) __attribute__((always_inline)) {
+        if constexpr (FP8) {
+            const uint2 q = *(const uint2*)(b + o);
+            return __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(q.x, q.y));
+        } else {
+            return *(const bf16x8_t*)(b + o);
+        }
+    };
 
     // does this wave's 128-row half hold any row of the tile (wave-uniform),
     // and how many of its 32-row blocks do
@@ -367,15 +420,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         bf16x8_t a[2][4], b[2][2];
     };
     auto read_half = [&](int kt, int h, Frags& f) __attribute__((always_inline)) {
-        const bf16_t* a = smem[kt & (GSLOTS - 1)][0];
-        const bf16_t* b = smem[kt & (GSLOTS - 1)][1];
+        const char* a = smem + (kt & (GSLOTS - 1)) * SLOT;
+        const char* b = a + A_BYTES;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const int ks = 2 * h + s2;
 #pragma unroll
-            for (int nj = 0; nj < 2; ++nj) f.b[s2][nj] = *(const bf16x8_t*)(&b[boffs[ks][nj]]);
+            for (int nj = 0; nj < 2; ++nj) f.b[s2][nj] = bfrag(b, boffs[ks][nj]);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) f.a[s2][mi] = *(const bf16x8_t*)(&a[aoffs[ks][mi]]);
+            for (int mi = 0; mi < 4; ++mi) f.a[s2][mi] = *(const bf16x8_t*)(a + aoffs[ks][mi]);
         }
     };
     // the MFMAs of one 16-deep step of a half stage
@@ -398,17 +451,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     auto partial_loop = [&](auto NA) __attribute__((always_inline)) {
         constexpr int na = decltype(NA)::value;
         auto rd = [&](int kt, int h, Frags& f) __attribute__((always_inline)) {
-            const bf16_t* a = smem[kt & (GSLOTS - 1)][0];
-            const bf16_t* b = smem[kt & (GSLOTS - 1)][1];
+            const char* a = smem + (kt & (GSLOTS - 1)) * SLOT;
+            const char* b = a + A_BYTES;
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 const int ks = 2 * h + s2;
 #pragma unroll
-                for (int nj = 0; nj < 2; ++nj)
-                    f.b[s2][nj] = *(const bf16x8_t*)(&b[boffs[ks][nj]]);
+                for (int nj = 0; nj < 2; ++nj) f.b[s2][nj] = bfrag(b, boffs[ks][nj]);
 #pragma unroll
                 for (int mi = 0; mi < na; ++mi)
-                    f.a[s2][mi] = *(const bf16x8_t*)(&a[aoffs[ks][mi]]);
+                    f.a[s2][mi] = *(const bf16x8_t*)(a + aoffs[ks][mi]);
             }
         };
         auto step = [&](const Frags& f, int s2) __attribute__((always_inline)) {
@@ -421,7 +473,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         };
         issue(0);
         issue(1);
-        wait_vmcnt_lgkm0<8>();
+        wait_vmcnt_lgkm0<FP8 ? 6 : 8>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         Frags g0, g1;
@@ -451,7 +503,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     else {
     issue(0);
     issue(1);
-    wait_vmcnt_lgkm0<8>();  // this wave's part of stage 0 has landed
+    wait_vmcnt_lgkm0<FP8 ? 6 : 8>();  // this wave's part of stage 0 has landed
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     Frags f0, f1;
@@ -497,8 +549,27 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     // the reads.
     if (!active) return;
     constexpr int ELD = 72;
-    float* ep = (float*)&smem[0][0][0] + wave * 32 * ELD;
+    float* ep = (float*)smem + wave * 32 * ELD;
     const int er = lane >> 1, eh = lane & 1;
+    // FP8 row scales of the weight rows behind this lane's output columns
+    // (SwiGLU: 16 h columns, gate and up; otherwise 32 columns)
+    float sg[FP8 ? 32 : 1];
+    if constexpr (FP8) {
+        const float* sc = (const float*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride;
+        if (SW) {
+            const int hc0 = tc.nt * 128 + wn * 32 + eh * 16;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int hc = min(hc0 + i, g.N - 1);
+                sg[i] = sc[hc];
+                sg[16 + i] = sc[g.N + hc];
+            }
+        } else {
+            const int c0 = tc.nt * GBN + wn * 64 + eh * 32;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) sg[i] = sc[min(c0 + i, g.N - 1)];
+        }
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -517,10 +588,19 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
                 bf16_t* dst = (bf16_t*)g.C + (int64_t)r * g.ldc + hc0;
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const f32x4_t g0 = *(const f32x4_t*)(src + eh * 16 + q * 8);
-                    const f32x4_t g1 = *(const f32x4_t*)(src + eh * 16 + q * 8 + 4);
-                    const f32x4_t u0 = *(const f32x4_t*)(src + 32 + eh * 16 + q * 8);
-                    const f32x4_t u1 = *(const f32x4_t*)(src + 32 + eh * 16 + q * 8 + 4);
+                    f32x4_t g0 = *(const f32x4_t*)(src + eh * 16 + q * 8);
+                    f32x4_t g1 = *(const f32x4_t*)(src + eh * 16 + q * 8 + 4);
+                    f32x4_t u0 = *(const f32x4_t*)(src + 32 + eh * 16 + q * 8);
+                    f32x4_t u1 = *(const f32x4_t*)(src + 32 + eh * 16 + q * 8 + 4);
+                    if constexpr (FP8) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            g0[t] *= sg[q * 8 + t];
+                            g1[t] *= sg[q * 8 + 4 + t];
+                            u0[t] *= sg[16 + q * 8 + t];
+                            u1[t] *= sg[16 + q * 8 + 4 + t];
+                        }
+                    }
                     u32x4_t o;
                     o[0] = pack_bf16x2(glu_f32(g0[0], u0[0], g), glu_f32(g0[1], u0[1], g));
                     o[1] = pack_bf16x2(glu_f32(g0[2], u0[2], g), glu_f32(g0[3], u0[3], g));
@@ -536,6 +616,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
                     if (c >= g.N) continue;
                     f32x4_t v0 = *(const f32x4_t*)(src + eh * 32 + q * 8);
                     f32x4_t v1 = *(const f32x4_t*)(src + eh * 32 + q * 8 + 4);
+                    if constexpr (FP8) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            v0[t] *= sg[q * 8 + t];
+                            v1[t] *= sg[q * 8 + 4 + t];
+                        }
+                    }
                     if (EPI == EPI_F32_BIAS && g.bias) {
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
@@ -675,14 +762,25 @@ __global__ __launch_bounds__(256) void gemm_f32_tiled(GemmArgs g) {
 template <bool KC>
 void launch_big(const GemmArgs& g, dim3 gd, hipStream_t s) {
     const dim3 bd(512);
+    if (g.b_fmt == WF_FP8) {
+        // grouped expert products only: gate/up, and the down product's rows
+        if constexpr (!KC) {
+            switch (g.epi) {
+                case EPI_F16: gemm_bf16_big<EPI_F16, false, WF_FP8><<<gd, bd, 0, s>>>(g); break;
+                case EPI_F32: gemm_bf16_big<EPI_F32, false, WF_FP8><<<gd, bd, 0, s>>>(g); break;
+                default: gemm_bf16_big<EPI_SWIGLU, false, WF_FP8><<<gd, bd, 0, s>>>(g); break;
+            }
+        }
+        return;
+    }
     switch (g.epi) {
         case EPI_F16:
-            if constexpr (!KC) gemm_bf16_big<EPI_F16, KC><<<gd, bd, 0, s>>>(g);
+            if constexpr (!KC) gemm_bf16_big<EPI_F16, KC, WF_BF16><<<gd, bd, 0, s>>>(g);
             break;
-        case EPI_F32: gemm_bf16_big<EPI_F32, KC><<<gd, bd, 0, s>>>(g); break;
-        case EPI_F32_BIAS: gemm_bf16_big<EPI_F32_BIAS, KC><<<gd, bd, 0, s>>>(g); break;
-        case EPI_OUT: gemm_bf16_big<EPI_OUT, KC><<<gd, bd, 0, s>>>(g); break;
-        default: gemm_bf16_big<EPI_SWIGLU, KC><<<gd, bd, 0, s>>>(g); break;
+        case EPI_F32: gemm_bf16_big<EPI_F32, KC, WF_BF16><<<gd, bd, 0, s>>>(g); break;
+        case EPI_F32_BIAS: gemm_bf16_big<EPI_F32_BIAS, KC, WF_BF16><<<gd, bd, 0, s>>>(g); break;
+        case EPI_OUT: gemm_bf16_big<EPI_OUT, KC, WF_BF16><<<gd, bd, 0, s>>>(g); break;
+        default: gemm_bf16_big<EPI_SWIGLU, KC, WF_BF16><<<gd, bd, 0, s>>>(g); break;
     }
 }
 
@@ -739,7 +837,13 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
         case EPI_OUT: gemm_bf16_tiled<EPI_OUT, WF><<<gd, bd, 0, s>>>(g); break;           \
         default: gemm_bf16_tiled<EPI_SWIGLU, WF><<<gd, bd, 0, s>>>(g); break;             \
     }
-    if (g.b_fmt != WF_BF16 && (dtype == 0 || path == GEMM_BIG || g.A2)) return hipErrorInvalidValue;
+    if (g.b_fmt != WF_BF16 && (dtype == 0 || g.A2)) return hipErrorInvalidValue;
+    // the 256x256 kernel takes bf16 or FP8 weights (FP8: gate/up or expert rows)
+    if (path == GEMM_BIG && (g.b_fmt == WF_MXFP4 ||
+                             (g.b_fmt == WF_FP8 && (!g.tiles || (g.epi != EPI_SWIGLU &&
+                                                                 g.epi != EPI_F16 &&
+                                                                 g.epi != EPI_F32)))))
+        return hipErrorInvalidValue;
     // fp16 expert rows: grouped bf16 products without a second K segment
     if (g.epi == EPI_F16 && (dtype == 0 || !g.tiles || g.A2)) return hipErrorInvalidValue;
     if (g.b_fmt == WF_MXFP4 && g.K % 128 != 0) return hipErrorInvalidValue;

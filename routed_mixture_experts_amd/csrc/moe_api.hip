@@ -82,8 +82,9 @@ bool fits_u32(int64_t rows, int64_t cols, moe_dtype_t dt) {
 // 256-row LDS tiles (gemm_bf16_big).  fp32 layers use 64-row VALU tiles.
 constexpr int kBigRows = 256;
 constexpr int kF32Rows = 64;
-// Experts with FP8 weights and more than kStreamMaxRows rows use the 128-row
-// register-staged tiles (the codes become bf16 on their way to LDS).
+// Experts with MXFP4 weights and more than kStreamMaxRows rows use the
+// 128-row register-staged tiles (the codes become bf16 on their way to LDS);
+// FP8 weights go through the 256-row tiles, which take the codes into LDS.
 constexpr int kTiledRows = 128;
 
 // Dense products: stream the weights for small batches, and where 128x128
@@ -175,7 +176,7 @@ moe_status_t small_groups_gemm(GemmArgs g, const ExpertsWs& w, int E, hipStream_
 
 // Rows per tile of the large-group list.
 int large_rows(moe_dtype_t dt, int fmt) {
-    return dt == MOE_DTYPE_F32 ? kF32Rows : fmt != WF_BF16 ? kTiledRows : kBigRows;
+    return dt == MOE_DTYPE_F32 ? kF32Rows : fmt == WF_MXFP4 ? kTiledRows : kBigRows;
 }
 
 moe_status_t large_groups_gemm(moe_dtype_t dt, GemmArgs g, const ExpertsWs& w, int64_t P, int E,
@@ -186,7 +187,7 @@ moe_status_t large_groups_gemm(moe_dtype_t dt, GemmArgs g, const ExpertsWs& w, i
     g.num_tiles = w.counts + 1;
     g.max_tiles = (int32_t)big_capacity(dt, P, E, rows);
     g.tile_m = rows;
-    const int path = f32 || g.b_fmt != WF_BF16 ? GEMM_TILED : GEMM_BIG;
+    const int path = f32 || g.b_fmt == WF_MXFP4 ? GEMM_TILED : GEMM_BIG;
     return hip_status(launch_gemm(f32 ? 0 : 1, path, g, s));
 }
 

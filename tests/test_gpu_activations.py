@@ -1,7 +1,8 @@
 """GPU parity of the gate/up activation variants (GELU, GELU-tanh, clipped
 SwiGLU) against the oracle, on every kernel that applies them: the streaming
-kernel (small groups), the 256x256 kernel (large groups), the 128x128 tiled
-kernel (FP8 weights, large groups) and the fp32 layer's kernel."""
+kernel (small groups), the 256x256 kernel (large groups, bf16 or FP8
+weights), the 128x128 tiled kernel (MXFP4 weights, large groups) and the fp32
+layer's kernel."""
 import ctypes
 
 import numpy as np
@@ -26,35 +27,41 @@ ACTS = {
 }
 
 
-def _ew(inp, act, fp8=False):
+def _ew(inp, act, fmt="dtype"):
     kw = dict(activation=act["kind"], alpha=act.get("alpha", 1.702), limit=act.get("limit", 7.0))
-    if fp8:
+    if fmt == "fp8_e4m3":
         return moe.ExpertWeights.fp8(inp["w13"], inp["w2"], inp["w13_scale"], inp["w2_scale"], **kw)
+    if fmt == "mxfp4":
+        return moe.ExpertWeights.mxfp4(inp["w13"], inp["w2"], inp["w13_scale"], inp["w2_scale"],
+                                       **kw)
     return moe.ExpertWeights(inp["w13"], inp["w2"], **kw)
 
 
 @pytest.mark.parametrize("act", list(ACTS))
-@pytest.mark.parametrize("dtype,T,E,k,fp8", [
-    ("bf16", 50, 16, 2, False),     # small groups: streaming kernel
-    ("bf16", 1200, 4, 2, False),    # ~600 rows per expert: 256x256 kernel
-    ("bf16", 700, 8, 3, True),      # FP8 weights, large groups: 128x128 tiled kernel
-    ("f32", 300, 8, 2, False),      # fp32 layer
+@pytest.mark.parametrize("dtype,T,E,k,fmt", [
+    ("bf16", 50, 16, 2, "dtype"),      # small groups: streaming kernel
+    ("bf16", 1200, 4, 2, "dtype"),     # ~600 rows per expert: 256x256 kernel
+    ("bf16", 700, 8, 3, "fp8_e4m3"),   # FP8 weights, ~260 rows: 256x256 kernel
+    ("bf16", 700, 8, 3, "mxfp4"),      # MXFP4 weights, ~260 rows: 128x128 tiled kernel
+    ("f32", 300, 8, 2, "dtype"),       # fp32 layer
 ])
-def test_experts_activation_matches_oracle(act, dtype, T, E, k, fp8):
-    D, I = 256, 192
-    log(f"activation {act} {dtype} T={T} E={E} fp8={fp8}")
-    w = Workload("t", T=T, H=D, E=E, k=k, I=I, dtype=dtype,
-                 weights="fp8_e4m3" if fp8 else "dtype")
+def test_experts_activation_matches_oracle(act, dtype, T, E, k, fmt):
+    D, I = 256, 256 if fmt == "mxfp4" else 192
+    log(f"activation {act} {dtype} T={T} E={E} weights={fmt}")
+    w = Workload("t", T=T, H=D, E=E, k=k, I=I, dtype=dtype, weights=fmt)
     inp = make_inputs(w, DEV)
     logits = random_logits(T, E, seed=T + 7).numpy()
     ids, _, _ = O.route(logits, O.RouteCfg(num_experts=E, top_k=k))
     c, off, r2p, p2r = moe.moe_permute(torch.from_numpy(ids.astype(np.int32)).to(DEV), E)
-    y = moe.moe_experts_ex(inp["x"], off, r2p, _ew(inp, ACTS[act], fp8), k)
+    y = moe.moe_experts_ex(inp["x"], off, r2p, _ew(inp, ACTS[act], fmt), k)
     torch.cuda.synchronize()
     _, roff, rr2p, _ = O.permute(ids, E)
-    if fp8:
+    if fmt == "fp8_e4m3":
         w13 = O.dequantize_rows(inp["w13"].cpu().numpy(), inp["w13_scale"].cpu().numpy())
         w2 = O.dequantize_rows(inp["w2"].cpu().numpy(), inp["w2_scale"].cpu().numpy())
+    elif fmt == "mxfp4":
+        w13 = O.dequantize_mxfp4(inp["w13"].cpu().numpy(), inp["w13_scale"].cpu().numpy())
+        w2 = O.dequantize_mxfp4(inp["w2"].cpu().numpy(), inp["w2_scale"].cpu().numpy())
     else:
         w13, w2 = np64(inp["w13"]), np64(inp["w2"])
     ref = O.run_experts(np64(inp["x"]), k, roff, rr2p, w13, w2, ACTS[act])

@@ -5,9 +5,9 @@ The oracle decodes the same codes and row scales into float64 weights
 (oracle.dequantize_rows), so both sides multiply by exactly the same weight
 values; the remaining difference is the bf16 rounding of h and of the output,
 and the bar is the bf16 layer's.  Shapes cover the streaming kernel with 1, 2
-and 4 token blocks and a ragged last K chunk, the 128-row tiled kernel for
-groups above 64 rows, both expert chains in one layer, and the full decode
-and prefill layers.
+and 4 token blocks and a ragged last K chunk, the 256x256 kernel (codes
+staged in LDS) for groups above 64 rows, both expert chains in one layer, and
+the full decode and prefill layers.
 """
 import ctypes
 
@@ -38,7 +38,7 @@ def _dequant(inp):
 @pytest.mark.parametrize("T,E,k,D,I", [
     (50, 16, 2, 256, 192),     # ~6 rows per expert: one 16-row token block
     (200, 8, 2, 320, 256),     # ~50 rows: 2 and 4 token blocks, K = 320 ends mid-chunk
-    (700, 8, 3, 320, 256),     # ~260 rows: 128-row tiles with a ragged last tile
+    (700, 8, 3, 320, 256),     # ~260 rows: a full and a ragged 256-row tile
     (257, 4, 2, 128, 64),      # N smaller than a tile
 ])
 def test_experts_fp8_match_oracle(T, E, k, D, I):
@@ -146,8 +146,8 @@ def test_full_decode_fp8():
 
 
 def test_forward_fp8_both_expert_chains():
-    """A skewed batch with groups above 64 rows (128-row tiles, fp16 expert
-    rows stored by the tiled kernel) and small groups (streaming, on the
+    """A skewed batch with groups above 64 rows (256-row tiles, fp16 expert
+    rows stored by the 256x256 kernel) and small groups (streaming, on the
     second stream) in one layer, against the oracle's decode of the codes."""
     w = Workload("t", T=640, H=256, E=16, k=4, I=192, routed_scaling=1.5, weights="fp8_e4m3")
     log("forward fp8, both expert chains")
@@ -174,7 +174,7 @@ def test_full_prefill_fp8():
     """The prefill layer (T=8192, Zipf(1.1) load) with FP8 expert weights:
     routing, counts and maps over every token, the output on at least 64
     tokens (random, the hottest expert's, tokens ending partly filled
-    128-row tiles and 16-row token blocks)."""
+    256-row tiles and 16-row token blocks)."""
     w = WORKLOADS["prefill_fp8"]
     log(f"full workload prefill_fp8: T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
     inp = make_inputs(w, DEV, chunk_rows=16)
@@ -190,7 +190,7 @@ def test_full_prefill_fp8():
     torch.cuda.synchronize()
 
     def toks(counts, offsets, r2p):
-        t = parity_tokens(w, counts, offsets, r2p, big_rows=128, extra_groups=12)
+        t = parity_tokens(w, counts, offsets, r2p, big_rows=256, extra_groups=12)
         extra = np.random.default_rng(2).permutation(T)
         i = 0
         while len(t) < 64:
