@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
 // the DMA of stage kt+2; while stage kt's second half is multiplied, stage
 // kt+1's first half is read.  A wave whose 128 rows all lie past the tile's
 // end skips its MFMAs.
-constexpr int GBM = 256, GBN = 256, GBK = 64, GSLOTS = 2;
+constexpr int GBM = 256, GBN = 256, GBK = 64, GSLOTS = 2, BSLOTS = 3;
 
 __device__ __forceinline__ int swz(int row, int chunk) {
     return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
@@ -274,13 +274,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     TileCoord tc;
     if (!fetch_tile(g, GBM, ntn, tc)) return;
 
-    // one LDS buffer: ring slot s holds the A tile (bf16) and then the B tile
-    // (bf16, or FP8 codes); after the K loop the epilogue reuses it as a flat
-    // fp32 buffer
+    // one LDS buffer: a 2-slot ring of A tiles (bf16), then a 3-slot ring of
+    // B tiles (bf16, or FP8 codes); after the K loop the epilogue reuses it
+    // as a flat fp32 buffer
     constexpr int A_BYTES = GBM * GBK * 2;
     constexpr int B_BYTES = FP8 ? GBN * GBK : GBN * GBK * 2;
-    constexpr int SLOT = A_BYTES + B_BYTES;
-    __shared__ __attribute__((aligned(1024))) char smem[GSLOTS * SLOT];
+    constexpr int B_RING = GSLOTS * A_BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[B_RING + BSLOTS * B_BYTES];
+    // DMA instructions per wave and stage: A, B
+    constexpr int NA_DMA = 4, NB_DMA = FP8 ? 2 : 4;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -337,39 +339,52 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     const int nk1 = g.K / GBK;
     const int nk = nk1 + (KCAT ? g.K2 / GBK : 0);
 
-    // Issue DMA blocks i0 .. i1-1 of stage kt (clamped to the last stage)
-    // into its ring slot: 2 DMA instructions per block.  The K segment of a
+    // Issue this wave's DMA of stage kt's A tile, or B tile (kt clamped to
+    // the last stage), into its ring slot.  The K segment of a
     // K-concatenated product is picked with selects.
-    auto issue_blocks = [&](int kt, int i0, int i1) __attribute__((always_inline)) {
-        const int slot = kt & (GSLOTS - 1);
+    auto issue_a = [&](int kt) __attribute__((always_inline)) {
+        char* dst = smem + (kt & (GSLOTS - 1)) * A_BYTES;
         kt = min(kt, nk - 1);
         const bool seg1 = !KCAT || kt < nk1;
         const char* abase = seg1 ? Ab : A2b;
-        const char* bbase = seg1 ? Bb : B2b;
         const uint32_t ko = (uint32_t)(seg1 ? kt : kt - nk1) * GBK * 2;
 #pragma unroll
-        for (int i = i0; i < i1; ++i) {
-            const int blk = (32 * wave + 8 * i) * GBK * 2;  // bytes
+        for (int i = 0; i < 4; ++i)
             __builtin_amdgcn_global_load_lds(
                 (const void*)(abase + ((seg1 ? ao[i] : ao2[KCAT ? i : 0]) + ko)),
-                (lds_ptr_t)(smem + slot * SLOT + blk), 16, 0, 0);
-            if (!FP8)
-                __builtin_amdgcn_global_load_lds(
-                    (const void*)(bbase + ((seg1 ? bo[i] : bo2[KCAT ? i : 0]) + ko)),
-                    (lds_ptr_t)(smem + slot * SLOT + A_BYTES + blk), 16, 0, 0);
-        }
-        if (FP8) {
-            // the codes of the blocks' weight rows: one 16-row DMA per two
-            // token blocks
+                (lds_ptr_t)(dst + (32 * wave + 8 * i) * GBK * 2), 16, 0, 0);
+    };
+    auto issue_b = [&](int kt) __attribute__((always_inline)) {
+        char* dst = smem + B_RING + (kt % BSLOTS) * B_BYTES;
+        kt = min(kt, nk - 1);
+        if constexpr (FP8) {
+            // the codes: 16 weight rows per DMA instruction
 #pragma unroll
-            for (int i = i0 / 2; i < (i1 + 1) / 2; ++i)
+            for (int i = 0; i < 2; ++i)
                 __builtin_amdgcn_global_load_lds(
                     (const void*)(Bb + (bo8[i] + (uint32_t)kt * GBK)),
-                    (lds_ptr_t)(smem + slot * SLOT + A_BYTES + (32 * wave + 16 * i) * GBK), 16,
-                    0, 0);
+                    (lds_ptr_t)(dst + (32 * wave + 16 * i) * GBK), 16, 0, 0);
+        } else {
+            const bool seg1 = !KCAT || kt < nk1;
+            const char* bbase = seg1 ? Bb : B2b;
+            const uint32_t ko = (uint32_t)(seg1 ? kt : kt - nk1) * GBK * 2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(bbase + ((seg1 ? bo[i] : bo2[KCAT ? i : 0]) + ko)),
+                    (lds_ptr_t)(dst + (32 * wave + 8 * i) * GBK * 2), 16, 0, 0);
         }
     };
-    auto issue = [&](int kt) __attribute__((always_inline)) { issue_blocks(kt, 0, 4); };
+    // Prologue: A0 B0 B1 A1 B2.  Stage 0 has landed for this wave once only
+    // the last three tiles' DMA may be in flight.
+    auto prologue = [&]() __attribute__((always_inline)) {
+        issue_a(0);
+        issue_b(0);
+        issue_b(1);
+        issue_a(1);
+        issue_b(2);
+        wait_vmcnt_lgkm0<NA_DMA + 2 * NB_DMA>();
+    };
 
     f32x16_t acc[4][2];
 #pragma unroll
@@ -420,8 +435,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         bf16x8_t a[2][4], b[2][2];
     };
     auto read_half = [&](int kt, int h, Frags& f) __attribute__((always_inline)) {
-        const char* a = smem + (kt & (GSLOTS - 1)) * SLOT;
-        const char* b = a + A_BYTES;
+        const char* a = smem + (kt & (GSLOTS - 1)) * A_BYTES;
+        const char* b = smem + B_RING + (kt % BSLOTS) * B_BYTES;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const int ks = 2 * h + s2;
@@ -451,8 +466,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     auto partial_loop = [&](auto NA) __attribute__((always_inline)) {
         constexpr int na = decltype(NA)::value;
         auto rd = [&](int kt, int h, Frags& f) __attribute__((always_inline)) {
-            const char* a = smem + (kt & (GSLOTS - 1)) * SLOT;
-            const char* b = a + A_BYTES;
+            const char* a = smem + (kt & (GSLOTS - 1)) * A_BYTES;
+            const char* b = smem + B_RING + (kt % BSLOTS) * B_BYTES;
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 const int ks = 2 * h + s2;
@@ -471,9 +486,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
                     acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         f.a[s2][mi], f.b[s2][nj], acc[mi][nj], 0, 0, 0);
         };
-        issue(0);
-        issue(1);
-        wait_vmcnt_lgkm0<FP8 ? 6 : 8>();
+        prologue();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         Frags g0, g1;
@@ -483,14 +496,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
             step(g0, 0);
             step(g0, 1);
             asm volatile("" ::: "memory");
-            wait_vmcnt_lgkm0<0>();
+            wait_vmcnt_lgkm0<NB_DMA>();
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            issue_blocks(kt + 2, 0, 2);
+            issue_a(kt + 2);
             rd(kt + 1, 0, g0);
             step(g1, 0);
             asm volatile("" ::: "memory");
-            issue_blocks(kt + 2, 2, 4);
+            issue_b(kt + 3);
             asm volatile("" ::: "memory");
             step(g1, 1);
             asm volatile("" ::: "memory");
@@ -501,9 +514,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     else if (!KCAT && nact == 2) partial_loop(std::integral_constant<int, 2>{});
     else if (!KCAT && nact == 3) partial_loop(std::integral_constant<int, 3>{});
     else {
-    issue(0);
-    issue(1);
-    wait_vmcnt_lgkm0<FP8 ? 6 : 8>();  // this wave's part of stage 0 has landed
+    prologue();  // this wave's part of stage 0 has landed
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     Frags f0, f1;
@@ -514,22 +525,23 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
             mma(f0);
         }
         asm volatile("" ::: "memory");
-        // stage kt+1's DMA (issued a stage ago) has landed for this wave and
-        // its reads of stage kt are retired; after the barrier stage kt+1 is
-        // visible everywhere and stage kt's slot takes stage kt+2
-        wait_vmcnt_lgkm0<0>();
+        // stage kt+1's A tile (issued a stage ago) and B tile (two stages
+        // ago) have landed for this wave, only stage kt+2's B may be in
+        // flight, and its reads of stage kt are retired; after the barrier
+        // stage kt+1 is visible everywhere and stage kt's slots take stage
+        // kt+2's A tile and stage kt+3's B tile
+        wait_vmcnt_lgkm0<NB_DMA>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        // stage kt+2's DMA goes out in two halves, the second after the
-        // first step's MFMAs, so the whole workgroup's DMA does not queue at
-        // once (5% faster on a dense 8192-row expert)
-        issue_blocks(kt + 2, 0, 2);
+        // the A DMA goes out now, the B DMA after the first step's MFMAs, so
+        // the whole workgroup's DMA does not queue at once
+        issue_a(kt + 2);
         if (active) {
             read_half(kt + 1, 0, f0);
             mma_step(f1, 0);
         }
         asm volatile("" ::: "memory");
-        issue_blocks(kt + 2, 2, 4);
+        issue_b(kt + 3);
         asm volatile("" ::: "memory");
         if (active) mma_step(f1, 1);
         asm volatile("" ::: "memory");
