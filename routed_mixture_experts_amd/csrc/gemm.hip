@@ -235,8 +235,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
 // ------------------------------------------------------------------------
 // 8 waves (two per SIMD) in a 2x4 layout; each wave owns a 128x64 block of
 // 4x2 v_mfma_f32_32x32x16_bf16 tiles (128 fp32 accumulators per lane).  K
-// advances 64 at a time through a 2-slot LDS ring (64 KB per stage) filled
-// directly from global memory by global_load_lds_dwordx4.  Each DMA
+// advances 64 at a time through two LDS rings, 2 slots of A tiles and 3 of
+// B tiles (32 KB each), filled directly from global memory by
+// global_load_lds_dwordx4: a stage's A tile is fetched one stage ahead, its
+// B (weight) tile two stages ahead.  Each DMA
 // instruction moves 8 rows x 128 bytes, whole cache lines: with 16 rows x 64
 // bytes per instruction the L2-to-LDS path delivers 2.4x less (measured 12.5
 // against 30 TB/s on L2-resident tiles).  LDS row r (128 bytes) keeps its
@@ -246,24 +248,25 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
 // global chunk whose swizzled slot is its own.  Operand fragments are read
 // half a stage ahead of their MFMAs: while stage kt's first half is
 // multiplied, its second half is read; then one barrier publishes stage kt+1
-// (its DMA was issued a whole stage earlier) and frees stage kt's slot for
-// the DMA of stage kt+2; while stage kt's second half is multiplied, stage
-// kt+1's first half is read.  A wave whose 128 rows all lie past the tile's
-// end skips its MFMAs.
-constexpr int GBM = 256, GBN = 256, GBK = 64, GSLOTS = 2, BSLOTS = 3;
+// and frees stage kt's slots for the A tile of stage kt+2 and the B tile of
+// stage kt+3; while stage kt's second half is multiplied, stage kt+1's first
+// half is read.  A wave whose 128 rows all lie past the tile's end skips its
+// MFMAs.
+constexpr int GBM = 256, GBN = 256, GBK = 64;
 
 __device__ __forceinline__ int swz(int row, int chunk) {
     return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
 }
 
 // With FP8 weights (OCP e4m3 codes, one fp32 scale per weight row; grouped
-// products only) the B stage holds the codes, 64 bytes per weight row (16
-// KB), moved by global_load_lds in 16 rows x 64 bytes per instruction; a
+// products only) a B slot holds the codes, 64 bytes per weight row (16 KB),
+// moved by global_load_lds in 16 rows x 64 bytes per instruction; a
 // fragment read takes a lane's 8 codes (ds_read_b64) and turns them into
 // 8 bf16 values exactly, and the row scales multiply the fp32 sums in the
 // epilogue.  LDS row r of the codes keeps its four 16-byte chunks at chunk ^
 // ((r >> 2) & 3).
 __device__ __forceinline__ int swz8(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
 
 template <int EPI, bool KCAT, int WF>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
@@ -274,15 +277,35 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     TileCoord tc;
     if (!fetch_tile(g, GBM, ntn, tc)) return;
 
-    // one LDS buffer: a 2-slot ring of A tiles (bf16), then a 3-slot ring of
-    // B tiles (bf16, or FP8 codes); after the K loop the epilogue reuses it
-    // as a flat fp32 buffer
+    // one LDS buffer: a ring of AS A tiles (bf16), then a ring of BS B tiles
+    // (bf16, or FP8 codes); after the K loop the epilogue reuses it as a flat
+    // fp32 buffer.  Stage kt's tiles are fetched AS and BS stages ahead.
     constexpr int A_BYTES = GBM * GBK * 2;
     constexpr int B_BYTES = FP8 ? GBN * GBK : GBN * GBK * 2;
-    constexpr int B_RING = GSLOTS * A_BYTES;
-    __shared__ __attribute__((aligned(1024))) char smem[B_RING + BSLOTS * B_BYTES];
-    // DMA instructions per wave and stage: A, B
+    // 2 + 3 slots (bf16: 160 KB).  Measured against it: 2 + 2 slots 4.8%
+    // slower on the prefill layer; 3 + 2 slots 1% slower; with FP8 codes,
+    // 3 + 4 slots 1% slower.
+    constexpr int AS = 2, BS = 3;
+    constexpr int B_RING = AS * A_BYTES;
+    static_assert(B_RING + BS * B_BYTES <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) char smem[B_RING + BS * B_BYTES];
+    // DMA instructions per wave and stage: A, B.  Each loop turn issues the
+    // ring with the shorter lead first (X, lead L1), then the other (Y, L2);
+    // the prologue issues stages 0 .. L2-1 in the same order.  vmcnt counts
+    // in issue order, so before stage kt+1 is published a wave may leave in
+    // flight the DMAs issued after the later of X_{kt+1} and Y_{kt+1}: with
+    // L1 < L2 that is X_{kt+1}, followed by Y_{kt+L2} of the same turn and
+    // L1-2 whole turns; with L1 == L2 it is Y_{kt+1}, followed by L1-2 whole
+    // turns (exact for the ring depths allowed here, prologue included).
     constexpr int NA_DMA = 4, NB_DMA = FP8 ? 2 : 4;
+    constexpr bool A_FIRST = AS <= BS;
+    constexpr int L1 = A_FIRST ? AS : BS, L2 = A_FIRST ? BS : AS;
+    constexpr int NX = A_FIRST ? NA_DMA : NB_DMA, NY = A_FIRST ? NB_DMA : NA_DMA;
+    static_assert((L1 == 2 && L2 == 2) || (L1 == 2 && L2 == 3) || (L1 == 3 && L2 == 3) ||
+                      (L1 == 3 && L2 == 4),
+                  "ring depths whose wait counts were checked");
+    constexpr int WAIT_LOOP = (L1 < L2 ? NY : 0) + (L1 - 2) * (NX + NY);
+    constexpr int WAIT_PRO = (L1 - 1) * NX + (L2 - 1) * NY;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -343,7 +366,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     // the last stage), into its ring slot.  The K segment of a
     // K-concatenated product is picked with selects.
     auto issue_a = [&](int kt) __attribute__((always_inline)) {
-        char* dst = smem + (kt & (GSLOTS - 1)) * A_BYTES;
+        char* dst = smem + (kt % AS) * A_BYTES;
         kt = min(kt, nk - 1);
         const bool seg1 = !KCAT || kt < nk1;
         const char* abase = seg1 ? Ab : A2b;
@@ -355,7 +378,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
                 (lds_ptr_t)(dst + (32 * wave + 8 * i) * GBK * 2), 16, 0, 0);
     };
     auto issue_b = [&](int kt) __attribute__((always_inline)) {
-        char* dst = smem + B_RING + (kt % BSLOTS) * B_BYTES;
+        char* dst = smem + B_RING + (kt % BS) * B_BYTES;
         kt = min(kt, nk - 1);
         if constexpr (FP8) {
             // the codes: 16 weight rows per DMA instruction
@@ -375,15 +398,23 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
                     (lds_ptr_t)(dst + (32 * wave + 8 * i) * GBK * 2), 16, 0, 0);
         }
     };
-    // Prologue: A0 B0 B1 A1 B2.  Stage 0 has landed for this wave once only
-    // the last three tiles' DMA may be in flight.
+    auto issue_x = [&](int kt) __attribute__((always_inline)) {
+        if constexpr (A_FIRST) issue_a(kt);
+        else issue_b(kt);
+    };
+    auto issue_y = [&](int kt) __attribute__((always_inline)) {
+        if constexpr (A_FIRST) issue_b(kt);
+        else issue_a(kt);
+    };
+    // Stage 0 has landed for this wave once only the DMAs after X_0 and Y_0
+    // may be in flight.
     auto prologue = [&]() __attribute__((always_inline)) {
-        issue_a(0);
-        issue_b(0);
-        issue_b(1);
-        issue_a(1);
-        issue_b(2);
-        wait_vmcnt_lgkm0<NA_DMA + 2 * NB_DMA>();
+#pragma unroll
+        for (int st = 0; st < L2; ++st) {
+            if (st < L1) issue_x(st);
+            issue_y(st);
+        }
+        wait_vmcnt_lgkm0<WAIT_PRO>();
     };
 
     f32x16_t acc[4][2];
@@ -435,8 +466,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         bf16x8_t a[2][4], b[2][2];
     };
     auto read_half = [&](int kt, int h, Frags& f) __attribute__((always_inline)) {
-        const char* a = smem + (kt & (GSLOTS - 1)) * A_BYTES;
-        const char* b = smem + B_RING + (kt % BSLOTS) * B_BYTES;
+        const char* a = smem + (kt % AS) * A_BYTES;
+        const char* b = smem + B_RING + (kt % BS) * B_BYTES;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const int ks = 2 * h + s2;
@@ -466,8 +497,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     auto partial_loop = [&](auto NA) __attribute__((always_inline)) {
         constexpr int na = decltype(NA)::value;
         auto rd = [&](int kt, int h, Frags& f) __attribute__((always_inline)) {
-            const char* a = smem + (kt & (GSLOTS - 1)) * A_BYTES;
-            const char* b = smem + B_RING + (kt % BSLOTS) * B_BYTES;
+            const char* a = smem + (kt % AS) * A_BYTES;
+            const char* b = smem + B_RING + (kt % BS) * B_BYTES;
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 const int ks = 2 * h + s2;
@@ -496,14 +527,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
             step(g0, 0);
             step(g0, 1);
             asm volatile("" ::: "memory");
-            wait_vmcnt_lgkm0<NB_DMA>();
+            wait_vmcnt_lgkm0<WAIT_LOOP>();
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            issue_a(kt + 2);
+            issue_x(kt + L1);
             rd(kt + 1, 0, g0);
             step(g1, 0);
             asm volatile("" ::: "memory");
-            issue_b(kt + 3);
+            issue_y(kt + L2);
             asm volatile("" ::: "memory");
             step(g1, 1);
             asm volatile("" ::: "memory");
@@ -525,23 +556,22 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
             mma(f0);
         }
         asm volatile("" ::: "memory");
-        // stage kt+1's A tile (issued a stage ago) and B tile (two stages
-        // ago) have landed for this wave, only stage kt+2's B may be in
-        // flight, and its reads of stage kt are retired; after the barrier
-        // stage kt+1 is visible everywhere and stage kt's slots take stage
-        // kt+2's A tile and stage kt+3's B tile
-        wait_vmcnt_lgkm0<NB_DMA>();
+        // stage kt+1's tiles have landed for this wave and its reads of
+        // stage kt are retired; after the barrier stage kt+1 is visible
+        // everywhere and stage kt's slots take stage kt+AS's A tile and
+        // stage kt+BS's B tile
+        wait_vmcnt_lgkm0<WAIT_LOOP>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        // the A DMA goes out now, the B DMA after the first step's MFMAs, so
-        // the whole workgroup's DMA does not queue at once
-        issue_a(kt + 2);
+        // one ring's DMA goes out now, the other's after the first step's
+        // MFMAs, so the whole workgroup's DMA does not queue at once
+        issue_x(kt + L1);
         if (active) {
             read_half(kt + 1, 0, f0);
             mma_step(f1, 0);
         }
         asm volatile("" ::: "memory");
-        issue_b(kt + 3);
+        issue_y(kt + L2);
         asm volatile("" ::: "memory");
         if (active) mma_step(f1, 1);
         asm volatile("" ::: "memory");

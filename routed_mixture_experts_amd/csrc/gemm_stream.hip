@@ -236,7 +236,17 @@ int stream_col_tiles_nw(int epi, int N, int nw) {
 // as the weights, the codes become bf16 exactly in registers (MXFP4: with
 // the block scale applied by the conversion), and FP8's row scale multiplies
 // the fp32 sums in the epilogue.
-template <int EPI, int NB, bool KCAT, int WF, bool SV, int NW>
+//
+// A tile of at most 16 / QF rows (QF = 2 or 4, one token block) loads its
+// token rows QF k-steps per 1 KB load instead of one: lane l takes row
+// l % (16 / QF) and the 8 elements that operand lane l % (16 / QF) + 16 * g4
+// of k-step l / (64 / QF) holds (g4 = (l / (16 / QF)) % 4), and writes them
+// to that place of the same LDS blocks, so the MFMA side is unchanged.
+// Operand rows past 16 / QF keep whatever the buffer held: they only feed
+// output rows past the tile's end, which are never stored.  At decode most
+// groups have at most 4 rows, and the token loads then take a quarter of
+// the load slots.
+template <int EPI, int NB, bool KCAT, int WF, bool SV, int NW, int QF>
 __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCoord& tc,
                                                  char* xs) {
     constexpr bool SW = EPI == EPI_SWIGLU;
@@ -250,9 +260,13 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     // of times per iteration, so every slot index is static
     constexpr int RC = PD > UPC ? PD / UPC : 1;
     constexpr int TU = RC * UPC;               // weight loads per ring turn
-    constexpr int XI = CS * NB / NW;           // 1 KB token blocks per wave per chunk
+    // 1 KB token loads per wave per chunk; with QF > 1, TL loads per chunk,
+    // one each for waves 0 .. TL-1
+    constexpr int XI = QF == 1 ? CS * NB / NW : 1;
+    constexpr int TL = CS / QF, RB = 16 / QF;
     constexpr int CHUNK = CS * NB * 1024;      // bytes of one token chunk
     static_assert(!(QW && KCAT), "quantised weights are grouped products only");
+    static_assert(QF == 1 || (NB == 1 && !KCAT && CS % QF == 0 && TL <= NW), "token packing");
     static_assert(2 * CHUNK <= sx_bytes<NW>() && CS % UNIT == 0 && TU % PD == 0 && XI % NB == 0,
                   "stream tiling");
     const int lane = threadIdx.x & 63;
@@ -283,11 +297,18 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
                          : nullptr;
     // token rows past the tile's end load its last row (never stored)
     uint32_t xo[NB], xo2[NB];
+    if constexpr (QF == 1) {
 #pragma unroll
-    for (int tb = 0; tb < NB; ++tb) {
-        const int r = min(tc.row0 + tb * 16 + l16, tc.row1 - 1);
-        xo[tb] = (uint32_t)(a_row_of(g, r) * g.lda * 2) + g4 * (FP4 ? 64 : FP8 ? 32 : 16);
-        xo2[tb] = KCAT ? (uint32_t)((int64_t)r * g.lda2 * 2) + g4 * 16 : 0u;
+        for (int tb = 0; tb < NB; ++tb) {
+            const int r = min(tc.row0 + tb * 16 + l16, tc.row1 - 1);
+            xo[tb] = (uint32_t)(a_row_of(g, r) * g.lda * 2) + g4 * (FP4 ? 64 : FP8 ? 32 : 16);
+            xo2[tb] = KCAT ? (uint32_t)((int64_t)r * g.lda2 * 2) + g4 * 16 : 0u;
+        }
+    } else {
+        const int r = min(tc.row0 + lane % RB, tc.row1 - 1);
+        xo[0] = (uint32_t)(a_row_of(g, r) * g.lda * 2) +
+                ((lane / RB) & 3) * (FP4 ? 64 : FP8 ? 32 : 16);
+        xo2[0] = 0u;
     }
 
     const int ns1 = g.K / 32;
@@ -302,21 +323,30 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     // moves blocks wave * XI .. +XI-1; steps past K re-read the last step
     // (never used).
     u32x4_t xr[XI];
+    // byte offset of step st's 8 elements for a lane (the k order of the
+    // weight loads; the lane's g4 part is in xo)
+    auto step_off = [&](int st) __attribute__((always_inline)) {
+        return FP4   ? (uint32_t)(st >> 2) * 256 + (uint32_t)(st & 3) * 16
+               : FP8 ? (uint32_t)(st >> 1) * 128 + (uint32_t)(st & 1) * 16
+                     : (uint32_t)st * 64;
+    };
     auto load_x = [&](int c) __attribute__((always_inline)) {
+        if constexpr (QF > 1) {
+            if (wave < TL) {
+                const int st = min(c * CS + wave * QF + lane / (4 * RB), ns - 1);
+                xr[0] = *(const u32x4_t*)(Ab + (xo[0] + step_off(st)));
+            }
+        } else {
 #pragma unroll
-        for (int i = 0; i < XI; ++i) {
-            const int b = wave * XI + i;
-            const int tb = i % NB;
-            const int st = min(c * CS + b / NB, ns - 1);
-            const bool seg1 = !KCAT || st < ns1;
-            // byte offset of step st's 8 elements for this lane (the k order
-            // of the weight loads)
-            const uint32_t ko = FP4   ? (uint32_t)(st >> 2) * 256 + (uint32_t)(st & 3) * 16
-                                : FP8 ? (uint32_t)(st >> 1) * 128 + (uint32_t)(st & 1) * 16
-                                      : (uint32_t)st * 64;
-            const char* src = seg1 ? Ab + (xo[tb] + ko)
-                                   : A2b + (xo2[tb] + (uint32_t)(st - ns1) * 64);
-            xr[i] = *(const u32x4_t*)src;
+            for (int i = 0; i < XI; ++i) {
+                const int b = wave * XI + i;
+                const int tb = i % NB;
+                const int st = min(c * CS + b / NB, ns - 1);
+                const bool seg1 = !KCAT || st < ns1;
+                const char* src = seg1 ? Ab + (xo[tb] + step_off(st))
+                                       : A2b + (xo2[tb] + (uint32_t)(st - ns1) * 64);
+                xr[i] = *(const u32x4_t*)src;
+            }
         }
         // MXFP4: the block exponents of the chunk's UPC load units travel
         // with its tokens (one dword per unit, byte g4 for this lane), so
@@ -343,13 +373,23 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
         }
     };
     auto store_x = [&](int c) __attribute__((always_inline)) {
-        char* dst = xs + (c & 1) * CHUNK + lane * 16;
+        if constexpr (QF > 1) {
+            if (wave < TL) {
+                const int sl = wave * QF + lane / (4 * RB);  // step within the chunk
+                const int p = lane % RB + 16 * ((lane / RB) & 3);  // its operand lane
+                if (QW && c * CS + sl >= ns) xr[0] = u32x4_t{0u, 0u, 0u, 0u};
+                *(u32x4_t*)(xs + (c & 1) * CHUNK + sl * 1024 + p * 16) = xr[0];
+            }
+        } else {
+            char* dst = xs + (c & 1) * CHUNK + lane * 16;
 #pragma unroll
-        for (int i = 0; i < XI; ++i) {
-            // FP8 / MXFP4: steps past K get zero tokens (once per chunk, in
-            // place of a select per step on the converted weights)
-            if (QW && c * CS + (wave * XI + i) / NB >= ns) xr[i] = u32x4_t{0u, 0u, 0u, 0u};
-            *(u32x4_t*)(dst + (wave * XI + i) * 1024) = xr[i];
+            for (int i = 0; i < XI; ++i) {
+                // FP8 / MXFP4: steps past K get zero tokens (once per chunk,
+                // in place of a select per step on the converted weights)
+                if (QW && c * CS + (wave * XI + i) / NB >= ns)
+                    xr[i] = u32x4_t{0u, 0u, 0u, 0u};
+                *(u32x4_t*)(dst + (wave * XI + i) * 1024) = xr[i];
+            }
         }
         if constexpr (FP4) {
 #pragma unroll
@@ -567,9 +607,21 @@ __global__ __launch_bounds__(64 * NW, 4) void gemm_bf16_stream(GemmArgs g) {
     if (!fetch_tile(g, SROWS, ntn, tc)) return;
     __shared__ __attribute__((aligned(1024))) char xs[sx_bytes<NW>()];
     const int rows = tc.row1 - tc.row0;
-    if (rows <= 16) stream_rows_tile<EPI, 1, KCAT, WF, SV, NW>(g, tc, xs);
-    else if (rows <= 32) stream_rows_tile<EPI, 2, KCAT, WF, SV, NW>(g, tc, xs);
-    else stream_rows_tile<EPI, 4, KCAT, WF, SV, NW>(g, tc, xs);
+    // (not with FP8 weights, whose register budget the packed forms push
+    // into spills inside the 2-block loop)
+    if constexpr (!KCAT && WF != WF_FP8) {
+        if (rows <= 4) {
+            stream_rows_tile<EPI, 1, KCAT, WF, SV, NW, 4>(g, tc, xs);
+            return;
+        }
+        if (rows <= 8) {
+            stream_rows_tile<EPI, 1, KCAT, WF, SV, NW, 2>(g, tc, xs);
+            return;
+        }
+    }
+    if (rows <= 16) stream_rows_tile<EPI, 1, KCAT, WF, SV, NW, 1>(g, tc, xs);
+    else if (rows <= 32) stream_rows_tile<EPI, 2, KCAT, WF, SV, NW, 1>(g, tc, xs);
+    else stream_rows_tile<EPI, 4, KCAT, WF, SV, NW, 1>(g, tc, xs);
 }
 
 // Dense products with fewer workgroups than this split K over the waves.
