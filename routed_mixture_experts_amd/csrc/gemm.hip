@@ -583,35 +583,37 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
 
     // Epilogue through LDS, one 32-row block of each wave at a time: the
     // accumulators are written in MFMA layout (lane = column, 16 rows), then
-    // each lane reads back half a row and stores it with 16-byte writes.  Only
-    // one block's accumulators are live in VGPRs at a time.  Row stride 72
-    // floats keeps the writes free of bank
-    // write conflicts (reads see at most two-way ones).  Each wave uses its
-    // own region, so LDS order within the wave suffices between the writes and
-    // the reads.
+    // read back so that every store instruction writes whole row segments of
+    // the wave's block: 16 rows x 64 bytes (SwiGLU h), 8 rows x 128 bytes
+    // (bf16 / fp16 outputs) or 4 rows x 256 bytes (fp32), i.e. few, fully
+    // written cache lines per instruction (the fp32 output of a 256x256 tile
+    // is 256 KB).  Only one block's accumulators are live in VGPRs at a time.
+    // Row stride 72 floats keeps the writes free of bank conflicts.  Each wave
+    // uses its own region, so LDS order within the wave suffices between the
+    // writes and the reads.
     if (!active) return;
     constexpr int ELD = 72;
     float* ep = (float*)smem + wave * 32 * ELD;
-    const int er = lane >> 1, eh = lane & 1;
-    // FP8 row scales of the weight rows behind this lane's output columns
-    // (SwiGLU: 16 h columns, gate and up; otherwise 32 columns)
-    float sg[FP8 ? 32 : 1];
+    // this lane's columns of the wave block: SwiGLU 8 h columns (gate at c,
+    // up at 32 + c); 16-bit outputs 8 columns; fp32 4 columns
+    constexpr int CW = EPI == EPI_F32 || EPI == EPI_F32_BIAS ? 4 : 8;  // columns per lane
+    constexpr int LPR = SW ? 4 : 64 / CW;                          // lanes per row
+    constexpr int RPI = 64 / LPR;                                  // rows per store
+    const int c = (lane % LPR) * CW;
+    const int col = SW ? tc.nt * 128 + wn * 32 + c : tc.nt * GBN + wn * 64 + c;
+    // FP8 row scales of the weight rows behind the lane's columns (SwiGLU:
+    // gate then up)
+    float sg[FP8 ? (SW ? 16 : CW) : 1];
     if constexpr (FP8) {
         const float* sc = (const float*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride;
-        if (SW) {
-            const int hc0 = tc.nt * 128 + wn * 32 + eh * 16;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int hc = min(hc0 + i, g.N - 1);
-                sg[i] = sc[hc];
-                sg[16 + i] = sc[g.N + hc];
-            }
-        } else {
-            const int c0 = tc.nt * GBN + wn * 64 + eh * 32;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) sg[i] = sc[min(c0 + i, g.N - 1)];
+        for (int t = 0; t < CW; ++t) {
+            const int n = min(col + t, g.N - 1);
+            sg[t] = sc[n];
+            if (SW) sg[CW + t] = sc[g.N + n];
         }
     }
+    const bool col_ok = col < g.N;  // N is a multiple of 8 (SwiGLU, 16-bit) or 4
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -620,78 +622,68 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
             for (int j = 0; j < 16; ++j)
                 ep[(8 * (j >> 2) + 4 * fh + (j & 3)) * ELD + nj * 32 + fr] = acc[mi][nj][j];
         asm volatile("" ::: "memory");
-        const int r = tc.row0 + wm * 128 + mi * 32 + er;
-        const float* src = ep + er * ELD;
-        if (r < tc.row1) {
+        const int rb = tc.row0 + wm * 128 + mi * 32;
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int row = i * RPI + lane / LPR;
+            const int r = rb + row;
+            const float* src = ep + row * ELD + c;
             if (SW) {
-                // columns 0..31 of the wave block are gate, 32..63 up, for the
-                // wave's 32 h columns; this lane takes 16 of them
-                const int hc0 = tc.nt * 128 + wn * 32 + eh * 16;
-                bf16_t* dst = (bf16_t*)g.C + (int64_t)r * g.ldc + hc0;
+                f32x4_t g0 = *(const f32x4_t*)(src);
+                f32x4_t g1 = *(const f32x4_t*)(src + 4);
+                f32x4_t u0 = *(const f32x4_t*)(src + 32);
+                f32x4_t u1 = *(const f32x4_t*)(src + 36);
+                if constexpr (FP8) {
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    f32x4_t g0 = *(const f32x4_t*)(src + eh * 16 + q * 8);
-                    f32x4_t g1 = *(const f32x4_t*)(src + eh * 16 + q * 8 + 4);
-                    f32x4_t u0 = *(const f32x4_t*)(src + 32 + eh * 16 + q * 8);
-                    f32x4_t u1 = *(const f32x4_t*)(src + 32 + eh * 16 + q * 8 + 4);
-                    if constexpr (FP8) {
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            g0[t] *= sg[q * 8 + t];
-                            g1[t] *= sg[q * 8 + 4 + t];
-                            u0[t] *= sg[16 + q * 8 + t];
-                            u1[t] *= sg[16 + q * 8 + 4 + t];
-                        }
+                    for (int t = 0; t < 4; ++t) {
+                        g0[t] *= sg[t];
+                        g1[t] *= sg[4 + t];
+                        u0[t] *= sg[8 + t];
+                        u1[t] *= sg[12 + t];
                     }
-                    u32x4_t o;
-                    o[0] = pack_bf16x2(glu_f32(g0[0], u0[0], g), glu_f32(g0[1], u0[1], g));
-                    o[1] = pack_bf16x2(glu_f32(g0[2], u0[2], g), glu_f32(g0[3], u0[3], g));
-                    o[2] = pack_bf16x2(glu_f32(g1[0], u1[0], g), glu_f32(g1[1], u1[1], g));
-                    o[3] = pack_bf16x2(glu_f32(g1[2], u1[2], g), glu_f32(g1[3], u1[3], g));
-                    if (hc0 + q * 8 < g.N) *(u32x4_t*)(dst + q * 8) = o;
                 }
+                u32x4_t o;
+                o[0] = pack_bf16x2(glu_f32(g0[0], u0[0], g), glu_f32(g0[1], u0[1], g));
+                o[1] = pack_bf16x2(glu_f32(g0[2], u0[2], g), glu_f32(g0[3], u0[3], g));
+                o[2] = pack_bf16x2(glu_f32(g1[0], u1[0], g), glu_f32(g1[1], u1[1], g));
+                o[3] = pack_bf16x2(glu_f32(g1[2], u1[2], g), glu_f32(g1[3], u1[3], g));
+                if (r < tc.row1 && col_ok)
+                    *(u32x4_t*)((bf16_t*)g.C + (int64_t)r * g.ldc + col) = o;
+            } else if (CW == 8) {
+                f32x4_t v0 = *(const f32x4_t*)(src);
+                f32x4_t v1 = *(const f32x4_t*)(src + 4);
+                if constexpr (FP8) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        v0[t] *= sg[t];
+                        v1[t] *= sg[4 + t];
+                    }
+                }
+                u32x4_t o;
+                if (EPI == EPI_F16) {
+                    o[0] = pack_f16x2(v0[0], v0[1]);
+                    o[1] = pack_f16x2(v0[2], v0[3]);
+                    o[2] = pack_f16x2(v1[0], v1[1]);
+                    o[3] = pack_f16x2(v1[2], v1[3]);
+                } else {  // EPI_OUT: bf16
+                    o[0] = pack_bf16x2(v0[0], v0[1]);
+                    o[1] = pack_bf16x2(v0[2], v0[3]);
+                    o[2] = pack_bf16x2(v1[0], v1[1]);
+                    o[3] = pack_bf16x2(v1[2], v1[3]);
+                }
+                if (r < tc.row1 && col_ok)
+                    *(u32x4_t*)((uint16_t*)g.C + (int64_t)r * g.ldc + col) = o;
             } else {
-                const int c0 = tc.nt * GBN + wn * 64 + eh * 32;
+                f32x4_t v = *(const f32x4_t*)(src);
+                if constexpr (FP8) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int c = c0 + q * 8;
-                    if (c >= g.N) continue;
-                    f32x4_t v0 = *(const f32x4_t*)(src + eh * 32 + q * 8);
-                    f32x4_t v1 = *(const f32x4_t*)(src + eh * 32 + q * 8 + 4);
-                    if constexpr (FP8) {
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            v0[t] *= sg[q * 8 + t];
-                            v1[t] *= sg[q * 8 + 4 + t];
-                        }
-                    }
-                    if (EPI == EPI_F32_BIAS && g.bias) {
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            v0[t] += g.bias[c + t];
-                            v1[t] += g.bias[c + 4 + t];
-                        }
-                    }
-                    if (EPI == EPI_OUT) {
-                        u32x4_t o;
-                        o[0] = pack_bf16x2(v0[0], v0[1]);
-                        o[1] = pack_bf16x2(v0[2], v0[3]);
-                        o[2] = pack_bf16x2(v1[0], v1[1]);
-                        o[3] = pack_bf16x2(v1[2], v1[3]);
-                        *(u32x4_t*)((bf16_t*)g.C + (int64_t)r * g.ldc + c) = o;
-                    } else if (EPI == EPI_F16) {
-                        u32x4_t o;
-                        o[0] = pack_f16x2(v0[0], v0[1]);
-                        o[1] = pack_f16x2(v0[2], v0[3]);
-                        o[2] = pack_f16x2(v1[0], v1[1]);
-                        o[3] = pack_f16x2(v1[2], v1[3]);
-                        *(u32x4_t*)((uint16_t*)g.C + (int64_t)r * g.ldc + c) = o;
-                    } else {
-                        float* dst = (float*)g.C + (int64_t)r * g.ldc + c;
-                        *(f32x4_t*)dst = v0;
-                        *(f32x4_t*)(dst + 4) = v1;
-                    }
+                    for (int t = 0; t < 4; ++t) v[t] *= sg[t];
                 }
+                if (EPI == EPI_F32_BIAS && g.bias && col_ok) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] += g.bias[col + t];
+                }
+                if (r < tc.row1 && col_ok) *(f32x4_t*)((float*)g.C + (int64_t)r * g.ldc + col) = v;
             }
         }
         asm volatile("" ::: "memory");
