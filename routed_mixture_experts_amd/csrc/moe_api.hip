@@ -77,9 +77,10 @@ bool fits_u32(int64_t rows, int64_t cols, moe_dtype_t dt) {
     return rows * cols * (int64_t)elem_size(dt) < ((int64_t)1 << 32);
 }
 
-// Experts with at most kStreamMaxRows rows stream their weights once through
-// registers (gemm_bf16_stream, one tile per expert); larger experts use
-// 256-row LDS tiles (gemm_bf16_big).  fp32 layers use 64-row VALU tiles.
+// Experts with few rows (at most split_rows below; in all-small batches
+// kStreamMaxRows) stream their weights once through registers
+// (gemm_bf16_stream, one tile per expert); larger experts use 256-row LDS
+// tiles (gemm_bf16_big).  fp32 layers use 64-row VALU tiles.
 constexpr int kBigRows = 256;
 constexpr int kF32Rows = 64;
 // Experts with MXFP4 weights and more than kStreamMaxRows rows use the
@@ -102,11 +103,26 @@ int dense_path(moe_dtype_t dt, int64_t T, int N, int epi) {
     return (N % 64 == 0 && ((T + 255) / 256) * cols >= 192) ? GEMM_BIG : GEMM_TILED;
 }
 
+// Where the two chains split in a batch that is not all-small: groups of at
+// most this many rows stream their weights, larger ones take 256-row (or,
+// MXFP4, 128-row) tiles.  With bf16 weights a group of 33..64 rows runs
+// faster in one 256-row tile (each weight byte read once per tile, one or
+// two 32-row blocks of MFMAs per wave) than in 16-wave streaming
+// workgroups, which spend four token blocks of LDS reads and MFMAs per
+// weight fragment: latent layer (64 rows per group on average) 1.175
+// against 1.232 ms, prefill and grouped layers unchanged.  With FP8 codes
+// the same move costs the prefill layer 10.16 against 9.50 ms (its down
+// product), so quantised weights stream up to 64 rows.
+int split_rows(int fmt) { return fmt == WF_BF16 ? 32 : kStreamMaxRows; }
+constexpr int kMinSplitRows = 32;
+
 // Upper bounds of the two tile lists: the large-group list holds tiles of
 // `rows` rows; the workspace is sized for the smallest tile of the dtype.
 // The small-group list holds one tile per group, or two for groups of
 // kStreamMaxRows+1 .. 2*kStreamMaxRows rows when a small batch splits them
-// (at most P / (kStreamMaxRows + 1) such groups).
+// (at most P / (kStreamMaxRows + 1) such groups).  The large-group list has
+// at most one partly filled tile per group above the split (at most
+// P / (kMinSplitRows + 1) groups).
 int64_t small_capacity(moe_dtype_t dt, int E) { return dt == MOE_DTYPE_F32 ? 1 : E; }
 int64_t small_capacity_split(int64_t P, int E) {
     return E + std::min<int64_t>(E, P / (kStreamMaxRows + 1));
@@ -116,7 +132,7 @@ int64_t small_capacity_split(int64_t P, int E) {
 constexpr int64_t kAllSmallMaxT = 2 * kStreamMaxRows;
 int64_t big_capacity(moe_dtype_t dt, int64_t P, int E, int rows) {
     if (dt == MOE_DTYPE_F32) return (P + kF32Rows - 1) / kF32Rows + E;
-    return (P + rows - 1) / rows + std::min<int64_t>(E, P / (kStreamMaxRows + 1)) + 1;
+    return (P + rows - 1) / rows + std::min<int64_t>(E, P / (kMinSplitRows + 1)) + 1;
 }
 int64_t big_capacity_ws(moe_dtype_t dt, int64_t P, int E) {
     return big_capacity(dt, P, E, dt == MOE_DTYPE_F32 ? kF32Rows : kTiledRows);
@@ -160,8 +176,8 @@ GemmArgs gemm_defaults() {
     return g;
 }
 
-// The two halves of one grouped product: groups of at most kStreamMaxRows
-// rows (weight streaming) and the rest (256-row MFMA tiles).
+// The two halves of one grouped product: groups of at most split_rows rows
+// (weight streaming) and the rest (256-row MFMA tiles).
 // split_P: the batch's pairs when groups above kStreamMaxRows rows were split
 // into two small tiles (0: one tile per group).
 moe_status_t small_groups_gemm(GemmArgs g, const ExpertsWs& w, int E, hipStream_t s,
@@ -263,7 +279,9 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
     const int64_t P = T * k;
     const bool f32 = dt == MOE_DTYPE_F32;
     if (!tiles_built)
-        MOE_HIP(launch_build_tiles(offsets, E, f32 ? 0 : kStreamMaxRows, large_rows(dt, ew.fmt),
+        MOE_HIP(launch_build_tiles(offsets, E,
+                                   f32 ? 0 : all_small ? kStreamMaxRows : split_rows(ew.fmt),
+                                   large_rows(dt, ew.fmt),
                                    w.small_tiles, w.counts, w.big_tiles, w.counts + 1, s));
     if (ev) MOE_HIP(hipEventRecord(ev[2 * MOE_STAGE_GEMM1], s));
 
@@ -815,7 +833,8 @@ moe_status_t forward_impl(const moe_route_cfg_t* cfg, moe_dtype_t dtype, int64_t
                            dtype == MOE_DTYPE_BF16 && T <= kAllSmallMaxT;
     MOE_HIP(launch_permute_with_tiles(
         T * k, Es, disp, counts, w.offsets, w.r2p, w.p2r, w.chunks,
-        dtype == MOE_DTYPE_F32 ? 0 : kStreamMaxRows, large_rows(dtype, ew.fmt), all_small,
+        dtype == MOE_DTYPE_F32 ? 0 : all_small ? kStreamMaxRows : split_rows(ew.fmt),
+        large_rows(dtype, ew.fmt), all_small,
         w.ex.small_tiles, w.ex.counts, w.ex.big_tiles, w.ex.counts + 1, s));
     if (placement && placement->load)
         MOE_HIP(launch_load_accumulate(Es, counts, placement->load, s));

@@ -252,9 +252,11 @@ def test_forward_is_deterministic():
 
 
 def test_forward_two_chains_every_tile_shape():
-    """A skewed batch large enough for the two-stream split: large groups in
-    256-row tiles on the caller's stream, small ones (1, 2 and 4 token blocks
-    of 16 rows) in 16-wave streaming workgroups on the library's stream."""
+    """A skewed batch large enough for the two-stream split: groups above 32
+    rows in 256-row tiles on the caller's stream (one of 33..64 rows with two
+    of its 32-row blocks live), groups of at most 32 rows (1 and 2 token
+    blocks of 16 rows) in 16-wave streaming workgroups on the library's
+    stream."""
     w = Workload("t", T=640, H=256, E=16, k=4, I=192, routed_scaling=1.5)
     inp = make_inputs(w, DEV)
     lg = random_logits(w.T, w.E, seed=21)
@@ -267,17 +269,17 @@ def test_forward_two_chains_every_tile_shape():
     counts = npi(res["counts"])
     log(f"  counts {sorted(counts.tolist())}")
     assert w.T * w.k >= 16 * w.E                        # the two-stream split
-    assert counts.max() > 64
-    small = counts[(counts > 0) & (counts <= 64)]
-    assert (small <= 16).any() and ((small > 16) & (small <= 32)).any() and (small > 32).any()
+    assert counts.max() > 64 and ((counts > 32) & (counts <= 64)).any()
+    small = counts[(counts > 0) & (counts <= 32)]
+    assert (small <= 16).any() and (small > 16).any()
     assert (npi(res["ids"]) == ref["ids"]).all()
     assert (counts == ref["counts"]).all()
     check_float(np64(res["out"]), ref["out"], True, "out two chains")
 
 
 def test_forward_groups_just_above_the_streaming_limit():
-    """Groups of 65..128 rows (one partly filled 256-row tile each) beside
-    larger groups and streaming groups in the same layer."""
+    """Groups of 33..128 rows (one partly filled 256-row tile each) beside
+    larger groups and streaming groups (at most 32 rows) in the same layer."""
     w = Workload("t", T=600, H=256, E=16, k=2, I=192)
     inp = make_inputs(w, DEV)
     lg = random_logits(w.T, w.E, seed=31)
@@ -290,16 +292,17 @@ def test_forward_groups_just_above_the_streaming_limit():
     counts = npi(res["counts"])
     log(f"  counts {counts.tolist()}")
     assert ((counts > 64) & (counts <= 128)).sum() >= 2 and (counts > 128).sum() >= 2
-    assert ((counts > 0) & (counts <= 64)).sum() >= 2
+    assert ((counts > 32) & (counts <= 64)).sum() >= 2
+    assert ((counts > 0) & (counts <= 32)).sum() >= 2
     assert (npi(res["ids"]) == ref["ids"]).all()
-    check_float(np64(res["out"]), ref["out"], True, "out groups above 64 rows")
+    check_float(np64(res["out"]), ref["out"], True, "out groups above 32 rows")
 
 
 def test_experts_group_sizes_at_tile_class_boundaries():
-    """Group sizes on the boundaries of the size classes (streaming up to 64
+    """Group sizes on the boundaries of the size classes (streaming up to 32
     rows, 256-row tiles above; one and two tiles around 256; an empty group),
     through moe_experts, element by element against the oracle."""
-    sizes = [64, 65, 128, 129, 1, 256, 257, 0]
+    sizes = [32, 33, 64, 65, 128, 129, 1, 256, 257, 0, 3]
     E, k, D, I = len(sizes), 2, 256, 128
     labels = np.repeat(np.arange(E), sizes)          # sorted expert labels
     T = len(labels) // k

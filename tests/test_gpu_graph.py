@@ -21,7 +21,7 @@ DEV = "cuda"
 
 def _skewed_logits(T, E, seed):
     # experts 0 .. E/2-1 get most tokens (groups above 64 rows), the others
-    # few: both expert chains run, and the second stream is used
+    # at most 32: both expert chains run, and the second stream is used
     lg = random_logits(T, E, seed=seed)
     lg[:, : E // 2] += 2.5
     return lg.to(DEV)
@@ -73,7 +73,7 @@ def test_forward_graph_replays_match_eager(case):
     torch.cuda.synchronize()
     if case in ("two_streams", "shared"):
         c = ref1["expert_counts_out"].cpu()
-        assert c.max() > 64 and c.min() <= 64, c   # both chains are exercised
+        assert c.max() > 64 and c.min() <= 32, c   # both chains are exercised
 
     got = buffers()
     g = torch.cuda.CUDAGraph()

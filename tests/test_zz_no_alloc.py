@@ -56,7 +56,7 @@ def test_noalloc_matches_forward_ex_two_calls(case):
         w = Workload("t", T=600, H=256, E=8, k=2, I=128, shared_inter=192)
         inp = make_inputs(w, DEV)
         lg = random_logits(w.T, w.E, seed=29)
-        lg[:, : w.E // 2] += 2.5      # groups above and below 64 rows
+        lg[:, : w.E // 2] += 2.5      # groups above 64 rows and at most 32
         kw = dict(router_logits=lg.to(DEV), shared=dict(w13=inp["w13_sh"], w2=inp["w2_sh"]))
     for T in (w.T, w.T // 3 + 1):
         log(f"noalloc {case} T={T}")
