@@ -7,7 +7,10 @@ gate/up+SwiGLU -> down -> combine) over one batch of synthetic tokens already
 resident in HBM.  The headline workload is the decode-shaped bf16 layer
 (T=128, H=7168, 384 experts, top-8, I=2048, routed scaling 2.5); the
 prefill-shaped layer (T=8192, Zipf(1.1) expert load) runs on the same weights
-and is reported beside it.  Prints ONE JSON line.
+and is reported beside it, and both shapes run again with the same weight
+draws quantised to FP8 E4M3 (per-row scales) and to MXFP4 (E2M1 codes, one
+E8M0 exponent per 32 elements); each is a separate entry, never the headline
+value.  Prints ONE JSON line.
 
 The headline time is a pass with no instrumentation between the kernels.
 Per-stage times come from a second pass of as many steps, with HIP events
@@ -41,7 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill_zipf", "grouped_sqrtsoftplus", "latent_shared",
-                             "decode_fp8", "decode_mxfp4", "prefill_fp8"])
+                             "decode_fp8", "decode_mxfp4", "prefill_fp8", "prefill_mxfp4"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill line")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the decode and prefill lines with FP8 E4M3 expert weights")
@@ -443,8 +446,6 @@ def main():
                 "stages_ms": fpstage}
             del fprun, fpin
         del fin
-    if args.workload == "decode" and not args.no_prefill:
-        del pin
     if args.workload == "decode" and not args.no_mxfp4:
         # the same layer with the same weight draws quantised to MXFP4 (E2M1
         # codes, one E8M0 exponent per 32 elements of a row)
@@ -469,7 +470,31 @@ def main():
                       "algorithmic_bytes": m1b, "achieved_GBps": m1, "frac": m1 / HBM_PEAK_GBS,
                       "traffic": profiled_traffic(wm.name)},
             "stages_ms": mstage}
-        del mrun, mxin
+        del mrun
+        if not args.no_prefill:
+            # the prefill batch (same x and router bias row) on the MXFP4 weights
+            wpm = WORKLOADS["prefill_mxfp4"]
+            print("[bench] prefill with MXFP4 expert weights", file=sys.stderr, flush=True)
+            mpin = dict(mxin)
+            mpin["x"], mpin["router_bias"] = pin["x"], pin["router_bias"]
+            mprun = Runner(wpm, mpin, torch, moe, stream)
+            mpsteps = max(3, args.steps // 2)
+            mpms, _, mpstage = mprun.timed(mpsteps, max(1, args.warmup // 2))
+            mpc = mprun.counts.cpu().numpy()
+            mpbytes, mpflops, _ = layer_work(wpm, mpc)
+            res["mxfp4_prefill"] = {
+                "workload": describe(wpm) + " weights=mxfp4 (E2M1, E8M0 exponent per 32)",
+                "value": wpm.T / (mpms * 1e-3), "unit": "tokens/s", "ms_per_step": mpms,
+                "step_ms": mprun.step_stats, "steps": mpsteps,
+                "hbm_frac": mpbytes / (mpms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "mfma_frac": mpflops / (mpms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                "binding_frac": binding_frac(mpbytes, mpflops, mpms),
+                "algorithmic_bytes": mpbytes, "algorithmic_flops": mpflops,
+                "stages_ms": mpstage}
+            del mprun, mpin
+        del mxin
+    if args.workload == "decode" and not args.no_prefill:
+        del pin
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -267,12 +267,22 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // ((r >> 2) & 3).
 __device__ __forceinline__ int swz8(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
+// With MXFP4 weights (OCP E2M1 codes, two per byte, one E8M0 exponent per 32
+// codes of a row; grouped products only) a B slot holds the codes, 32 bytes
+// per weight row (8 KB, one 32-row DMA instruction per wave; LDS row r keeps
+// its two 16-byte chunks at chunk ^ ((r >> 3) & 1)), and after them one
+// dword of exponents per row: the 4 blocks holding the stage's 2 (a 32-row
+// DMA of 4-byte pieces per wave).  A fragment read takes a lane's 8 codes
+// (ds_read_b32) and its block exponent and turns them into 8 bf16 values,
+// the scale applied by the conversion.
+
 
 template <int EPI, bool KCAT, int WF>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     constexpr bool SW = EPI == EPI_SWIGLU;
-    constexpr bool FP8 = WF == WF_FP8;
-    static_assert(WF == WF_BF16 || (FP8 && !KCAT), "FP8 weights: grouped products only");
+    constexpr bool FP8 = WF == WF_FP8, FP4 = WF == WF_MXFP4;
+    static_assert(WF == WF_BF16 || ((FP8 || FP4) && !KCAT),
+                  "FP8 / MXFP4 weights: grouped products only");
     const int ntn = SW ? (g.N + 127) / 128 : (g.N + GBN - 1) / GBN;
     TileCoord tc;
     if (!fetch_tile(g, GBM, ntn, tc)) return;
@@ -281,7 +291,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     // (bf16, or FP8 codes); after the K loop the epilogue reuses it as a flat
     // fp32 buffer.  Stage kt's tiles are fetched AS and BS stages ahead.
     constexpr int A_BYTES = GBM * GBK * 2;
-    constexpr int B_BYTES = FP8 ? GBN * GBK : GBN * GBK * 2;
+    constexpr int B_CODES = GBN * GBK / 2;  // MXFP4 codes of a B slot
+    constexpr int B_BYTES = FP8 ? GBN * GBK : FP4 ? B_CODES + GBN * 4 : GBN * GBK * 2;
     // 2 + 3 slots (bf16: 160 KB).  Measured against it: 2 + 2 slots 4.8%
     // slower on the prefill layer; 3 + 2 slots 1% slower; with FP8 codes,
     // 3 + 4 slots 1% slower.
@@ -297,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     // L1 < L2 that is X_{kt+1}, followed by Y_{kt+L2} of the same turn and
     // L1-2 whole turns; with L1 == L2 it is Y_{kt+1}, followed by L1-2 whole
     // turns (exact for the ring depths allowed here, prologue included).
-    constexpr int NA_DMA = 4, NB_DMA = FP8 ? 2 : 4;
+    constexpr int NA_DMA = 4, NB_DMA = FP8 || FP4 ? 2 : 4;
     constexpr bool A_FIRST = AS <= BS;
     constexpr int L1 = A_FIRST ? AS : BS, L2 = A_FIRST ? BS : AS;
     constexpr int NX = A_FIRST ? NA_DMA : NB_DMA, NY = A_FIRST ? NB_DMA : NA_DMA;
@@ -312,7 +323,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     const int wm = wave >> 2, wn = wave & 3;
 
     const char* Ab = (const char*)g.A;
-    const char* Bb = (const char*)g.B + (int64_t)tc.group * g.b_gstride * (FP8 ? 1 : 2);
+    const char* Bb = (const char*)g.B + (FP4   ? (int64_t)tc.group * g.b_gstride / 2
+                                         : FP8 ? (int64_t)tc.group * g.b_gstride
+                                               : (int64_t)tc.group * g.b_gstride * 2);
     const char* A2b = (const char*)g.A2;
     const char* B2b = (const char*)g.B2;
 
@@ -358,6 +371,24 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         }
         bo8[i] = (uint32_t)((int64_t)wrow * g.K) + swz8(row, lane & 3) * 16;
     }
+    // MXFP4: the codes' DMA covers tile rows 32*wave .. +31, lane l filling
+    // row +l/2, slot l%2 (global chunk (l%2) ^ ((row >> 3) & 1)); the
+    // exponents' DMA (lanes 0..31) row +l.
+    const char* Sb = FP4 ? (const char*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride
+                         : nullptr;
+    uint32_t bo4 = 0, eo4 = 0;
+    if constexpr (FP4) {
+        auto wrow_of = [&](int row) __attribute__((always_inline)) {
+            if (SW) {
+                const int c = min(tc.nt * 128 + (row & 127), g.N - 1);
+                return row < 128 ? c : g.N + c;
+            }
+            return min(tc.nt * GBN + row, g.N - 1);
+        };
+        const int row = 32 * wave + (lane >> 1);
+        bo4 = (uint32_t)((int64_t)wrow_of(row) * (g.K / 2)) + (((lane & 1) ^ ((row >> 3) & 1)) * 16);
+        eo4 = (uint32_t)((int64_t)wrow_of(32 * wave + (lane & 31)) * (g.K / 32));
+    }
 
     const int nk1 = g.K / GBK;
     const int nk = nk1 + (KCAT ? g.K2 / GBK : 0);
@@ -387,6 +418,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
                 __builtin_amdgcn_global_load_lds(
                     (const void*)(Bb + (bo8[i] + (uint32_t)kt * GBK)),
                     (lds_ptr_t)(dst + (32 * wave + 16 * i) * GBK), 16, 0, 0);
+        } else if constexpr (FP4) {
+            // the codes, then the exponent dword holding blocks 2kt, 2kt+1
+            // (K is a multiple of 128, so that dword is aligned and whole)
+            __builtin_amdgcn_global_load_lds((const void*)(Bb + (bo4 + (uint32_t)kt * 32)),
+                                             (lds_ptr_t)(dst + 32 * wave * 32), 16, 0, 0);
+            if (lane < 32)
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(Sb + (eo4 + (uint32_t)(kt >> 1) * 4)),
+                    (lds_ptr_t)(dst + B_CODES + 32 * wave * 4), 4, 0, 0);
         } else {
             const bool seg1 = !KCAT || kt < nk1;
             const char* bbase = seg1 ? Bb : B2b;
@@ -441,16 +481,27 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
 #pragma unroll
         for (int nj = 0; nj < 2; ++nj) {
             const int row = (SW ? nj * 128 + wn * 32 : wn * 64 + nj * 32) + fr;
-            // FP8: the 8 codes of k 16*ks + 8*fh .. +7 are half of chunk ks
-            boffs[ks][nj] = FP8 ? row * GBK + swz8(row, ks) * 16 + fh * 8
-                                : (row * GBK + swz(row, ch) * 8) * 2;
+            // FP8: the 8 codes of k 16*ks + 8*fh .. +7 are half of chunk ks;
+            // MXFP4: they are bytes 8*ks + 4*fh .. +3 of the row
+            boffs[ks][nj] = FP8   ? row * GBK + swz8(row, ks) * 16 + fh * 8
+                            : FP4 ? row * 32 + (((ks >> 1) ^ ((row >> 3) & 1)) * 16) +
+                                        ((8 * ks + 4 * fh) & 15)
+                                  : (row * GBK + swz(row, ch) * 8) * 2;
         }
     }
-    // B fragment at byte offset o of a slot's B tile
-    auto bfrag = [&](const char* b, int o) __attribute__((always_inline)) {
+    // B fragment (16-deep step ks, block nj) of stage kt in B slot b
+    auto bfrag = [&](const char* b, int kt, int ks, int nj) __attribute__((always_inline)) {
+        const int o = boffs[ks][nj];
         if constexpr (FP8) {
             const uint2 q = *(const uint2*)(b + o);
             return __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(q.x, q.y));
+        } else if constexpr (FP4) {
+            const int row = (SW ? nj * 128 + wn * 32 : wn * 64 + nj * 32) + fr;
+            const uint32_t q = *(const uint32_t*)(b + o);
+            const uint32_t e = *(const uint32_t*)(b + B_CODES + row * 4);
+            // block 2kt + ks/2 is byte 2*(kt & 1) + ks/2 of the dword
+            const uint32_t eb = (e >> (8 * (2 * (kt & 1) + (ks >> 1)))) & 0xffu;
+            return __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16x8(q, e8m0_scale(eb)));
         } else {
             return *(const bf16x8_t*)(b + o);
         }
@@ -472,7 +523,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         for (int s2 = 0; s2 < 2; ++s2) {
             const int ks = 2 * h + s2;
 #pragma unroll
-            for (int nj = 0; nj < 2; ++nj) f.b[s2][nj] = bfrag(b, boffs[ks][nj]);
+            for (int nj = 0; nj < 2; ++nj) f.b[s2][nj] = bfrag(b, kt, ks, nj);
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) f.a[s2][mi] = *(const bf16x8_t*)(a + aoffs[ks][mi]);
         }
@@ -503,7 +554,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
             for (int s2 = 0; s2 < 2; ++s2) {
                 const int ks = 2 * h + s2;
 #pragma unroll
-                for (int nj = 0; nj < 2; ++nj) f.b[s2][nj] = bfrag(b, boffs[ks][nj]);
+                for (int nj = 0; nj < 2; ++nj) f.b[s2][nj] = bfrag(b, kt, ks, nj);
 #pragma unroll
                 for (int mi = 0; mi < na; ++mi)
                     f.a[s2][mi] = *(const bf16x8_t*)(a + aoffs[ks][mi]);
@@ -807,6 +858,16 @@ void launch_big(const GemmArgs& g, dim3 gd, hipStream_t s) {
         }
         return;
     }
+    if (g.b_fmt == WF_MXFP4) {
+        if constexpr (!KC) {
+            switch (g.epi) {
+                case EPI_F16: gemm_bf16_big<EPI_F16, false, WF_MXFP4><<<gd, bd, 0, s>>>(g); break;
+                case EPI_F32: gemm_bf16_big<EPI_F32, false, WF_MXFP4><<<gd, bd, 0, s>>>(g); break;
+                default: gemm_bf16_big<EPI_SWIGLU, false, WF_MXFP4><<<gd, bd, 0, s>>>(g); break;
+            }
+        }
+        return;
+    }
     switch (g.epi) {
         case EPI_F16:
             if constexpr (!KC) gemm_bf16_big<EPI_F16, KC, WF_BF16><<<gd, bd, 0, s>>>(g);
@@ -872,11 +933,10 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
         default: gemm_bf16_tiled<EPI_SWIGLU, WF><<<gd, bd, 0, s>>>(g); break;             \
     }
     if (g.b_fmt != WF_BF16 && (dtype == 0 || g.A2)) return hipErrorInvalidValue;
-    // the 256x256 kernel takes bf16 or FP8 weights (FP8: gate/up or expert rows)
-    if (path == GEMM_BIG && (g.b_fmt == WF_MXFP4 ||
-                             (g.b_fmt == WF_FP8 && (!g.tiles || (g.epi != EPI_SWIGLU &&
-                                                                 g.epi != EPI_F16 &&
-                                                                 g.epi != EPI_F32)))))
+    // the 256x256 kernel takes quantised weights for grouped gate/up or
+    // expert rows only
+    if (path == GEMM_BIG && g.b_fmt != WF_BF16 &&
+        (!g.tiles || (g.epi != EPI_SWIGLU && g.epi != EPI_F16 && g.epi != EPI_F32)))
         return hipErrorInvalidValue;
     // fp16 expert rows: grouped bf16 products without a second K segment
     if (g.epi == EPI_F16 && (dtype == 0 || !g.tiles || g.A2)) return hipErrorInvalidValue;

@@ -83,9 +83,10 @@ bool fits_u32(int64_t rows, int64_t cols, moe_dtype_t dt) {
 // tiles (gemm_bf16_big).  fp32 layers use 64-row VALU tiles.
 constexpr int kBigRows = 256;
 constexpr int kF32Rows = 64;
-// Experts with MXFP4 weights and more than kStreamMaxRows rows use the
-// 128-row register-staged tiles (the codes become bf16 on their way to LDS);
-// FP8 weights go through the 256-row tiles, which take the codes into LDS.
+// Quantised expert weights (FP8 codes, MXFP4 codes with their exponents)
+// go through the same 256-row tiles, which take the codes into LDS and
+// convert them at the fragment read.  The workspace's tile list is sized for
+// 128-row tiles, a bound that also covers them.
 constexpr int kTiledRows = 128;
 
 // Dense products: stream the weights for small batches, and where 128x128
@@ -104,8 +105,7 @@ int dense_path(moe_dtype_t dt, int64_t T, int N, int epi) {
 }
 
 // Where the two chains split in a batch that is not all-small: groups of at
-// most this many rows stream their weights, larger ones take 256-row (or,
-// MXFP4, 128-row) tiles.  With bf16 weights a group of 33..64 rows runs
+// most this many rows stream their weights, larger ones take 256-row tiles.  With bf16 weights a group of 33..64 rows runs
 // faster in one 256-row tile (each weight byte read once per tile, one or
 // two 32-row blocks of MFMAs per wave) than in 16-wave streaming
 // workgroups, which spend four token blocks of LDS reads and MFMAs per
@@ -192,7 +192,7 @@ moe_status_t small_groups_gemm(GemmArgs g, const ExpertsWs& w, int E, hipStream_
 
 // Rows per tile of the large-group list.
 int large_rows(moe_dtype_t dt, int fmt) {
-    return dt == MOE_DTYPE_F32 ? kF32Rows : fmt == WF_MXFP4 ? kTiledRows : kBigRows;
+    return dt == MOE_DTYPE_F32 ? kF32Rows : kBigRows;
 }
 
 moe_status_t large_groups_gemm(moe_dtype_t dt, GemmArgs g, const ExpertsWs& w, int64_t P, int E,
@@ -203,7 +203,7 @@ moe_status_t large_groups_gemm(moe_dtype_t dt, GemmArgs g, const ExpertsWs& w, i
     g.num_tiles = w.counts + 1;
     g.max_tiles = (int32_t)big_capacity(dt, P, E, rows);
     g.tile_m = rows;
-    const int path = f32 || g.b_fmt == WF_MXFP4 ? GEMM_TILED : GEMM_BIG;
+    const int path = f32 ? GEMM_TILED : GEMM_BIG;
     return hip_status(launch_gemm(f32 ? 0 : 1, path, g, s));
 }
 

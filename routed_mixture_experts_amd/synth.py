@@ -100,6 +100,9 @@ WORKLOADS = {
     # the prefill layer with FP8 E4M3 expert weights
     "prefill_fp8": Workload("prefill_fp8", T=8192, H=7168, E=384, k=8, I=2048,
                             zipf_s=1.1, weights="fp8_e4m3"),
+    # ... and with MXFP4 expert weights
+    "prefill_mxfp4": Workload("prefill_mxfp4", T=8192, H=7168, E=384, k=8, I=2048,
+                              zipf_s=1.1, weights="mxfp4"),
 }
 
 FP8_E4M3_MAX = 448.0  # largest finite E4M3 value

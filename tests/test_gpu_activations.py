@@ -1,8 +1,7 @@
 """GPU parity of the gate/up activation variants (GELU, GELU-tanh, clipped
 SwiGLU) against the oracle, on every kernel that applies them: the streaming
-kernel (small groups), the 256x256 kernel (large groups, bf16 or FP8
-weights), the 128x128 tiled kernel (MXFP4 weights, large groups) and the fp32
-layer's kernel."""
+kernel (small groups), the 256x256 kernel (large groups, bf16, FP8 or MXFP4
+weights) and the fp32 layer's kernel."""
 import ctypes
 
 import numpy as np
@@ -42,7 +41,7 @@ def _ew(inp, act, fmt="dtype"):
     ("bf16", 50, 16, 2, "dtype"),      # small groups: streaming kernel
     ("bf16", 1200, 4, 2, "dtype"),     # ~600 rows per expert: 256x256 kernel
     ("bf16", 700, 8, 3, "fp8_e4m3"),   # FP8 weights, ~260 rows: 256x256 kernel
-    ("bf16", 700, 8, 3, "mxfp4"),      # MXFP4 weights, ~260 rows: 128x128 tiled kernel
+    ("bf16", 700, 8, 3, "mxfp4"),      # MXFP4 weights, ~260 rows: 256x256 kernel
     ("f32", 300, 8, 2, "dtype"),       # fp32 layer
 ])
 def test_experts_activation_matches_oracle(act, dtype, T, E, k, fmt):

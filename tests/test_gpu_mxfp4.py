@@ -6,8 +6,10 @@ weights (oracle.dequantize_mxfp4), so both sides multiply by exactly the same
 weight values; the remaining difference is the bf16 rounding of h and of the
 output, and the bar is the bf16 layer's.  Shapes cover the streaming kernel
 with 1, 2 and 4 token blocks (including passes whose last chunks lie past K),
-the 128-row tiled kernel for groups above 64 rows, several turns of the
-weight-load ring, both expert chains in one layer, and the full decode layer.
+the 256x256 kernel for groups above 64 rows (codes and exponents staged in
+LDS, decoded at the fragment read), several turns of the weight-load ring,
+both expert chains in one layer, the full decode layer and the full prefill
+layer.
 """
 import ctypes
 
@@ -20,7 +22,7 @@ import routed_mixture_experts_amd as moe
 import routed_mixture_experts_amd._lib as L
 from routed_mixture_experts_amd.synth import WORKLOADS, Workload, make_inputs, random_logits
 from tests.helpers import (ExpertFetchMXFP4, WEIGHT_ATOL, check_float, full_layer_parity,
-                           lib_cfg, log, np64, npi, oracle_cfg)
+                           lib_cfg, log, np64, npi, oracle_cfg, parity_tokens)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -40,7 +42,7 @@ def _dequant(inp):
     (50, 16, 2, 256, 256),     # ~6 rows per expert: one 16-row token block
     (200, 8, 2, 384, 256),     # ~50 rows: 2 and 4 token blocks; chunks past K
     (300, 16, 2, 1024, 512),   # ~37 rows, K = 1024: several turns of the load ring
-    (700, 8, 3, 384, 256),     # ~260 rows: 128-row tiles with a ragged last tile
+    (700, 8, 3, 384, 256),     # ~260 rows: 256-row tiles with a ragged last tile
     (257, 4, 2, 128, 128),     # N smaller than a tile
 ])
 def test_experts_mxfp4_match_oracle(T, E, k, D, I):
@@ -146,8 +148,8 @@ def test_full_decode_mxfp4():
 
 
 def test_forward_mxfp4_both_expert_chains():
-    """A skewed batch with groups above 64 rows (128-row tiles, fp16 expert
-    rows stored by the tiled kernel) and small groups (streaming, on the
+    """A skewed batch with groups above 64 rows (256x256 tiles, fp16 expert
+    rows stored by that kernel) and small groups (streaming, on the
     second stream) in one layer, against the oracle's decode of the codes."""
     w = Workload("t", T=640, H=256, E=16, k=4, I=256, routed_scaling=1.5, weights="mxfp4")
     log("forward mxfp4, both expert chains")
@@ -168,3 +170,37 @@ def test_forward_mxfp4_both_expert_chains():
     ref = O.forward(np64(inp["x"]), oracle_cfg(w), w13, w2, logits=np64(logits))
     assert (npi(ids) == ref["ids"]).all()
     check_float(np64(out), ref["out"], True, "out mxfp4 both chains")
+
+
+def test_full_prefill_mxfp4():
+    """The prefill layer (T=8192, Zipf(1.1) load) with MXFP4 expert weights:
+    routing, counts and maps over every token, the output on at least 64
+    tokens (random, the hottest expert's, tokens ending partly filled
+    256-row tiles and 16-row token blocks)."""
+    w = WORKLOADS["prefill_mxfp4"]
+    log(f"full workload prefill_mxfp4: T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
+    inp = make_inputs(w, DEV, chunk_rows=16)
+    T = w.T
+    res = dict(logits=torch.empty((T, w.E), dtype=torch.float32, device=DEV),
+               ids=torch.empty((T, w.k), dtype=torch.int32, device=DEV),
+               weights=torch.empty((T, w.k), dtype=torch.float32, device=DEV),
+               counts=torch.empty((w.E,), dtype=torch.int32, device=DEV))
+    res["out"] = moe.moe_forward_ex(lib_cfg(w), inp["x"], _mx(inp), w_router=inp["w_router"],
+                                    router_bias=inp["router_bias"], logits_out=res["logits"],
+                                    topk_ids_out=res["ids"], topk_weights_out=res["weights"],
+                                    expert_counts_out=res["counts"])
+    torch.cuda.synchronize()
+
+    def toks(counts, offsets, r2p):
+        t = parity_tokens(w, counts, offsets, r2p, big_rows=256, extra_groups=12)
+        extra = np.random.default_rng(2).permutation(T)
+        i = 0
+        while len(t) < 64:
+            t = sorted(set(t) | {int(extra[i])})
+            i += 1
+        return t
+
+    full_layer_parity(w, inp, res, ExpertFetchMXFP4(inp["w13"], inp["w13_scale"]),
+                      ExpertFetchMXFP4(inp["w2"], inp["w2_scale"]), toks, "prefill_mxfp4")
+    del inp, res
+    torch.cuda.empty_cache()
