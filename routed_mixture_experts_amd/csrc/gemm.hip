@@ -11,13 +11,13 @@
 // row, layer-dtype store, or SwiGLU silu(gate) * up).
 //
 // Kernels:
-//  * gemm_bf16_big    -- 256x256 tiles, 8 waves, a 2-slot LDS ring of 64-deep
-//    K stages filled by global_load_lds in whole 128-byte lines, operand
-//    fragments read half a stage ahead: groups with more than 64 rows
-//    (prefill) and large dense products.
+//  * gemm_bf16_big    -- 256x256 tiles, 8 waves, LDS rings of 64-deep K
+//    stages (2 A slots, 3 B slots) filled by global_load_lds, operand
+//    fragments read half a stage ahead; bf16, FP8 or MXFP4 weights: the
+//    large expert groups (prefill) and large dense products.
 //  * gemm_bf16_tiled  -- 128x128x64 LDS double-buffered tiles, 4 waves in a
 //    2x2 layout, each wave a 64x64 block of v_mfma_f32_32x32x16_bf16: mid-size
-//    dense products.
+//    dense products (bf16 weights).
 //  * the weight-streaming kernels for groups of at most 64 rows (all of
 //    decode) and small dense products live in gemm_stream.hip.
 //  * gemm_f32_tiled   -- fp32 VALU 64x64 tiles for the fp32 layer.
@@ -41,15 +41,9 @@ using namespace tiles;
 // ------------------------------------------------------------------------
 constexpr int TBM = 128, TBN = 128, TBK = 64, TLD = TBK + 8;  // LDS row stride (elements)
 
-// With FP8 weights (OCP e4m3 codes, one fp32 scale per weight row; grouped
-// products only) each lane loads 8 codes per row segment and turns them into
-// bf16 (exactly) on the way to LDS; the row scale multiplies the fp32 sums in
-// the epilogue.  With MXFP4 weights (E2M1 codes, two per byte, one E8M0
-// exponent per 32 codes) a lane's 8 codes are 4 bytes inside one scale
-// block; the conversion on the way to LDS applies the block scale.
-template <int EPI, int WF>
+// Dense products only (one group, bf16 weights).
+template <int EPI>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
-    constexpr bool FP8 = WF == WF_FP8, FP4 = WF == WF_MXFP4;
     constexpr bool SW = EPI == EPI_SWIGLU;
     const int ntn = SW ? (g.N + 63) / 64 : (g.N + TBN - 1) / TBN;
     TileCoord tc;
@@ -69,8 +63,6 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
 
     const bf16_t* ap[4];
     const bf16_t* bp[4];
-    const uint8_t* bp8[4];  // FP8 / MXFP4 codes of this lane's row segment
-    const uint8_t* sp4[4];  // MXFP4 block exponents of the row
     const bf16_t* ap2[4];
     const bf16_t* bp2[4];
 #pragma unroll
@@ -87,11 +79,6 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
             wrow = min(tc.nt * TBN + rho, g.N - 1);
         }
         bp[i] = Bg + (int64_t)wrow * g.K + lcol;
-        bp8[i] = FP4 ? (const uint8_t*)g.B + ((int64_t)tc.group * g.b_gstride + (int64_t)wrow * g.K + lcol) / 2
-                     : (const uint8_t*)g.B + (int64_t)tc.group * g.b_gstride + (int64_t)wrow * g.K + lcol;
-        sp4[i] = FP4 ? (const uint8_t*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride +
-                           (int64_t)wrow * (g.K / 32) + lcol / 32
-                     : nullptr;
         bp2[i] = B2 ? B2 + (int64_t)wrow * g.K2 + lcol : nullptr;
     }
 
@@ -104,24 +91,13 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
     float* cslice = (float*)g.C + (int64_t)blockIdx.y * g.M * g.ldc;
 
     u32x4_t ra[4], rb[4];
-    uint32_t rb8[4][2];  // FP8 / MXFP4: raw codes, converted when stored to LDS
-    uint32_t se[4];      // MXFP4: the block exponent of each segment
     auto gload = [&](int kt) {
         if (kt < nk1) {
             const int ko = kt * TBK;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 ra[i] = *(const u32x4_t*)(ap[i] + ko);
-                if (FP8) {
-                    const uint64_t q = *(const uint64_t*)(bp8[i] + ko);
-                    rb8[i][0] = (uint32_t)q;
-                    rb8[i][1] = (uint32_t)(q >> 32);
-                } else if (FP4) {
-                    rb8[i][0] = *(const uint32_t*)(bp8[i] + ko / 2);
-                    se[i] = sp4[i][ko / 32];
-                } else {
-                    rb[i] = *(const u32x4_t*)(bp[i] + ko);
-                }
+                rb[i] = *(const u32x4_t*)(bp[i] + ko);
             }
         } else {
             const int ko = (kt - nk1) * TBK;
@@ -135,8 +111,6 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
     auto sstore = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (FP8) rb[i] = fp8x8_to_bf16x8(rb8[i][0], rb8[i][1]);
-            if (FP4) rb[i] = fp4x8_to_bf16x8(rb8[i][0], e8m0_scale(se[i]));
             *(u32x4_t*)(&smem[buf][0][(lrow + 32 * i) * TLD + lcol]) = ra[i];
             *(u32x4_t*)(&smem[buf][1][(lrow + 32 * i) * TLD + lcol]) = rb[i];
         }
@@ -183,21 +157,6 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
         __syncthreads();
     }
 
-    // FP8 row scales of the two weight rows (output columns) of this lane
-    float cs[2] = {1.f, 1.f};
-    if (FP8) {
-        const float* sc = (const float*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride;
-        if (SW) {
-            const int hc = min(tc.nt * 64 + wn * 32 + fr, g.N - 1);
-            cs[0] = sc[hc];
-            cs[1] = sc[g.N + hc];
-        } else {
-#pragma unroll
-            for (int nj = 0; nj < 2; ++nj)
-                cs[nj] = sc[min(tc.nt * TBN + wn * 64 + nj * 32 + fr, g.N - 1)];
-        }
-    }
-
     // epilogue: lane holds column fr of each 32x32 block, rows 8*(j/4)+4*(lane/32)+j%4
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
@@ -208,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
             if (SW) {
                 const int hc = tc.nt * 64 + wn * 32 + fr;
                 if (hc < g.N) {
-                    const float h = glu_f32(acc[mi][0][j] * cs[0], acc[mi][1][j] * cs[1], g);
+                    const float h = glu_f32(acc[mi][0][j], acc[mi][1][j], g);
                     ((bf16_t*)g.C)[(int64_t)r * g.ldc + hc] = f32_to_bf16(h);
                 }
             } else {
@@ -216,12 +175,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
                 for (int nj = 0; nj < 2; ++nj) {
                     const int c = tc.nt * TBN + wn * 64 + nj * 32 + fr;
                     if (c >= g.N) continue;
-                    float v = acc[mi][nj][j] * cs[nj];
+                    float v = acc[mi][nj][j];
                     if (EPI == EPI_F32_BIAS && g.bias) v += g.bias[c];
                     if (EPI == EPI_OUT)
                         ((bf16_t*)g.C)[(int64_t)r * g.ldc + c] = f32_to_bf16(v);
-                    else if (EPI == EPI_F16)
-                        ((uint16_t*)g.C)[(int64_t)r * g.ldc + c] = (uint16_t)f32_to_f16_bits(v);
                     else
                         cslice[(int64_t)r * g.ldc + c] = v;
                 }
@@ -288,8 +245,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
     if (!fetch_tile(g, GBM, ntn, tc)) return;
 
     // one LDS buffer: a ring of AS A tiles (bf16), then a ring of BS B tiles
-    // (bf16, or FP8 codes); after the K loop the epilogue reuses it as a flat
-    // fp32 buffer.  Stage kt's tiles are fetched AS and BS stages ahead.
+    // (bf16, FP8 codes, or MXFP4 codes and exponents); after the K loop the
+    // epilogue reuses it as a flat fp32 buffer.  Stage kt's A and B tiles are
+    // issued while stages kt - AS and kt - BS are multiplied.
     constexpr int A_BYTES = GBM * GBK * 2;
     constexpr int B_CODES = GBN * GBK / 2;  // MXFP4 codes of a B slot
     constexpr int B_BYTES = FP8 ? GBN * GBK : FP4 ? B_CODES + GBN * 4 : GBN * GBK * 2;
@@ -887,7 +845,7 @@ hipError_t launch_tiled_kslices(const GemmArgs& g, int kslices, hipStream_t s) {
         return hipErrorInvalidValue;
     const int nm = (g.M + TBM - 1) / TBM;
     const dim3 gd((unsigned)((int64_t)nm * ((g.N + TBN - 1) / TBN)), (unsigned)kslices), bd(256);
-    if (nm > 0) gemm_bf16_tiled<EPI_F32, WF_BF16><<<gd, bd, 0, s>>>(g);
+    if (nm > 0) gemm_bf16_tiled<EPI_F32><<<gd, bd, 0, s>>>(g);
     return hipGetLastError();
 }
 
@@ -924,14 +882,6 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
         case EPI_OUT: KERNEL<EPI_OUT><<<gd, bd, 0, s>>>(g); break;                \
         default: KERNEL<EPI_SWIGLU><<<gd, bd, 0, s>>>(g); break;                  \
     }
-#define MOE_TILED_SWITCH(WF)                                                              \
-    switch (g.epi) {                                                                      \
-        case EPI_F16: gemm_bf16_tiled<EPI_F16, WF><<<gd, bd, 0, s>>>(g); break;           \
-        case EPI_F32: gemm_bf16_tiled<EPI_F32, WF><<<gd, bd, 0, s>>>(g); break;           \
-        case EPI_F32_BIAS: gemm_bf16_tiled<EPI_F32_BIAS, WF><<<gd, bd, 0, s>>>(g); break; \
-        case EPI_OUT: gemm_bf16_tiled<EPI_OUT, WF><<<gd, bd, 0, s>>>(g); break;           \
-        default: gemm_bf16_tiled<EPI_SWIGLU, WF><<<gd, bd, 0, s>>>(g); break;             \
-    }
     if (g.b_fmt != WF_BF16 && (dtype == 0 || g.A2)) return hipErrorInvalidValue;
     // the 256x256 kernel takes quantised weights for grouped gate/up or
     // expert rows only
@@ -940,6 +890,9 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
         return hipErrorInvalidValue;
     // fp16 expert rows: grouped bf16 products without a second K segment
     if (g.epi == EPI_F16 && (dtype == 0 || !g.tiles || g.A2)) return hipErrorInvalidValue;
+    // the 128x128 kernel takes bf16 weights and stores no fp16 expert rows
+    if (dtype != 0 && path == GEMM_TILED && (g.b_fmt != WF_BF16 || g.epi == EPI_F16))
+        return hipErrorInvalidValue;
     if (g.b_fmt == WF_MXFP4 && g.K % 128 != 0) return hipErrorInvalidValue;
     if (dtype == 0) {
         MOE_GEMM_SWITCH(gemm_f32_tiled)
@@ -948,15 +901,10 @@ hipError_t launch_gemm(int dtype, int path, const GemmArgs& g, hipStream_t s) {
     } else if (path == GEMM_BIG) {
         if (g.A2) launch_big<true>(g, gd, s);
         else launch_big<false>(g, gd, s);
-    } else if (g.b_fmt == WF_FP8) {
-        MOE_TILED_SWITCH(WF_FP8)
-    } else if (g.b_fmt == WF_MXFP4) {
-        MOE_TILED_SWITCH(WF_MXFP4)
     } else {
-        MOE_TILED_SWITCH(WF_BF16)
+        MOE_GEMM_SWITCH(gemm_bf16_tiled)
     }
 #undef MOE_GEMM_SWITCH
-#undef MOE_TILED_SWITCH
     return hipGetLastError();
 }
 
