@@ -2,6 +2,7 @@
 // library (gfx950 only).  Nothing here is part of the C ABI.
 #pragma once
 
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -115,27 +116,48 @@ enum WeightFmt { WF_BF16 = 0, WF_FP8 = 1, WF_MXFP4 = 2 };
 // SwiGLU min(g, L) * sigmoid(alpha * min(g, L)) * (clamp(u, -L, L) + 1).
 enum GluAct { ACT_SILU = 0, ACT_GELU = 1, ACT_GELU_TANH = 2, ACT_SWIGLU_CLIP = 3 };
 
-// PRECISE: exact division for the fp32 layer; otherwise the hardware
-// reciprocal.
-template <bool PRECISE = false>
-__device__ __forceinline__ float glu_f32(float gt, float up, const GemmArgs& a) {
+// One activation, fixed at compile time.  PRECISE: exact division for the
+// fp32 layer; otherwise the hardware reciprocal.
+template <int ACT, bool PRECISE = false>
+__device__ __forceinline__ float glu_act(float gt, float up, const GemmArgs& a) {
     auto sigmoid = [](float v) {
         return PRECISE ? 1.0f / (1.0f + expf(-v)) : __builtin_amdgcn_rcpf(1.0f + __expf(-v));
     };
+    if constexpr (ACT == ACT_GELU) {
+        return 0.5f * gt * (1.0f + erff(gt * 0.70710678118654752f)) * up;
+    } else if constexpr (ACT == ACT_GELU_TANH) {
+        const float z = 0.79788456080286536f * (gt + 0.044715f * gt * gt * gt);
+        return 0.5f * gt * (1.0f + tanhf(z)) * up;
+    } else if constexpr (ACT == ACT_SWIGLU_CLIP) {
+        const float gc = fminf(gt, a.act_limit);
+        const float uc = fminf(fmaxf(up, -a.act_limit), a.act_limit);
+        return gc * sigmoid(a.act_alpha * gc) * (uc + 1.0f);
+    } else {
+        return PRECISE ? gt / (1.0f + expf(-gt)) * up : gt * sigmoid(gt) * up;
+    }
+}
+
+// The activation picked per element from the launch's code (uniform over the
+// launch: one scalar branch per element).  Epilogues with many elements per
+// lane switch once outside their loops and call glu_act instead.
+template <bool PRECISE = false>
+__device__ __forceinline__ float glu_f32(float gt, float up, const GemmArgs& a) {
     switch (a.act) {
-        case ACT_GELU:
-            return 0.5f * gt * (1.0f + erff(gt * 0.70710678118654752f)) * up;
-        case ACT_GELU_TANH: {
-            const float z = 0.79788456080286536f * (gt + 0.044715f * gt * gt * gt);
-            return 0.5f * gt * (1.0f + tanhf(z)) * up;
-        }
-        case ACT_SWIGLU_CLIP: {
-            const float gc = fminf(gt, a.act_limit);
-            const float uc = fminf(fmaxf(up, -a.act_limit), a.act_limit);
-            return gc * sigmoid(a.act_alpha * gc) * (uc + 1.0f);
-        }
-        default:
-            return PRECISE ? gt / (1.0f + expf(-gt)) * up : gt * sigmoid(gt) * up;
+        case ACT_GELU: return glu_act<ACT_GELU, PRECISE>(gt, up, a);
+        case ACT_GELU_TANH: return glu_act<ACT_GELU_TANH, PRECISE>(gt, up, a);
+        case ACT_SWIGLU_CLIP: return glu_act<ACT_SWIGLU_CLIP, PRECISE>(gt, up, a);
+        default: return glu_act<ACT_SILU, PRECISE>(gt, up, a);
+    }
+}
+
+// Calls body(std::integral_constant<int, ACT>{}) for the launch's activation.
+template <typename F>
+__device__ __forceinline__ void with_act(const GemmArgs& a, F&& body) {
+    switch (a.act) {
+        case ACT_GELU: body(std::integral_constant<int, ACT_GELU>{}); break;
+        case ACT_GELU_TANH: body(std::integral_constant<int, ACT_GELU_TANH>{}); break;
+        case ACT_SWIGLU_CLIP: body(std::integral_constant<int, ACT_SWIGLU_CLIP>{}); break;
+        default: body(std::integral_constant<int, ACT_SILU>{}); break;
     }
 }
 

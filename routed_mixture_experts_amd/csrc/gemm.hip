@@ -623,6 +623,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         }
     }
     const bool col_ok = col < g.N;  // N is a multiple of 8 (SwiGLU, 16-bit) or 4
+    // (SwiGLU: one copy of the loop per activation, picked once)
+    auto epilogue = [&](auto ACTC) __attribute__((always_inline)) {
+    constexpr int ACT = decltype(ACTC)::value;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -652,10 +655,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
                     }
                 }
                 u32x4_t o;
-                o[0] = pack_bf16x2(glu_f32(g0[0], u0[0], g), glu_f32(g0[1], u0[1], g));
-                o[1] = pack_bf16x2(glu_f32(g0[2], u0[2], g), glu_f32(g0[3], u0[3], g));
-                o[2] = pack_bf16x2(glu_f32(g1[0], u1[0], g), glu_f32(g1[1], u1[1], g));
-                o[3] = pack_bf16x2(glu_f32(g1[2], u1[2], g), glu_f32(g1[3], u1[3], g));
+                o[0] = pack_bf16x2(glu_act<ACT>(g0[0], u0[0], g), glu_act<ACT>(g0[1], u0[1], g));
+                o[1] = pack_bf16x2(glu_act<ACT>(g0[2], u0[2], g), glu_act<ACT>(g0[3], u0[3], g));
+                o[2] = pack_bf16x2(glu_act<ACT>(g1[0], u1[0], g), glu_act<ACT>(g1[1], u1[1], g));
+                o[3] = pack_bf16x2(glu_act<ACT>(g1[2], u1[2], g), glu_act<ACT>(g1[3], u1[3], g));
                 if (r < tc.row1 && col_ok)
                     *(u32x4_t*)((bf16_t*)g.C + (int64_t)r * g.ldc + col) = o;
             } else if (CW == 8) {
@@ -697,6 +700,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
         }
         asm volatile("" ::: "memory");
     }
+    };
+    if constexpr (SW) with_act(g, epilogue);
+    else epilogue(std::integral_constant<int, ACT_SILU>{});
 }
 
 // ------------------------------------------------------------------------
