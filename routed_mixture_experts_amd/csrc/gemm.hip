@@ -11,10 +11,13 @@
 // row, layer-dtype store, or SwiGLU silu(gate) * up).
 //
 // Kernels:
-//  * gemm_bf16_big    -- 256x256 tiles, 8 waves, LDS rings of 64-deep K
-//    stages (2 A slots, 3 B slots) filled by global_load_lds, operand
-//    fragments read half a stage ahead; bf16, FP8 or MXFP4 weights: the
-//    large expert groups (prefill) and large dense products.
+//  * gemm_bf16_big4   -- 256x256 tiles, 4 waves of 128x128, LDS rings of
+//    64-deep K stages (2 A slots, 3 B slots) filled by global_load_lds,
+//    fragments read one 16-deep step ahead: bf16 weights, the large expert
+//    groups (prefill) and large dense products.
+//  * gemm_bf16_big    -- the same tiles and rings with 8 waves of 128x64:
+//    FP8 or MXFP4 expert weights (converted at the fragment read) and the
+//    K-concatenated dense product.
 //  * gemm_bf16_tiled  -- 128x128x64 LDS double-buffered tiles, 4 waves in a
 //    2x2 layout, each wave a 64x64 block of v_mfma_f32_32x32x16_bf16: mid-size
 //    dense products (bf16 weights).
@@ -706,6 +709,298 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------------
+// 256x256 tiles with 4 waves (one per SIMD), each a 128x128 block of 4x4
+// v_mfma_f32_32x32x16_bf16 tiles (256 fp32 accumulators per lane).  The same
+// LDS rings, swizzle and DMA as gemm_bf16_big; a wave's DMA share is 64 rows
+// of each tile (8 instructions).  Per 16-deep step a wave reads 4 A and 4 B
+// fragments for 16 MFMAs (gemm_bf16_big: 4 + 2 for 8), so a 64-deep stage
+// reads 128 KB of LDS instead of 192 KB.  Fragments are read one step ahead,
+// and each step's reads and DMA instructions are placed one after each MFMA
+// (scheduling fences), so that the one wave of a SIMD keeps its MFMA pipe
+// fed; the stage's one barrier sits between its third and last steps.
+// bf16 weights, no second K segment.
+// ------------------------------------------------------------------------
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_big4(GemmArgs g) {
+    constexpr bool SW = EPI == EPI_SWIGLU;
+    const int ntn = SW ? (g.N + 127) / 128 : (g.N + GBN - 1) / GBN;
+    TileCoord tc;
+    if (!fetch_tile(g, GBM, ntn, tc)) return;
+
+    constexpr int A_BYTES = GBM * GBK * 2, B_BYTES = GBN * GBK * 2;
+    constexpr int AS = 2, BS = 3;
+    constexpr int B_RING = AS * A_BYTES;
+    static_assert(B_RING + BS * B_BYTES <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) char smem[B_RING + BS * B_BYTES];
+    // per wave and stage: 8 DMA instructions for A, 8 for B
+    constexpr int ND = 8;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const char* Ab = (const char*)g.A;
+    const char* Bb = (const char*)g.B + (int64_t)tc.group * g.b_gstride * 2;
+
+    uint32_t ao[ND], bo[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+        const int row = 64 * wave + 8 * i + (lane >> 3);
+        const int chunk_bytes = swz(row, lane & 7) * 16;
+        const int r = tc.row0 + row;
+        const int rr = r < tc.row1 ? r : tc.row0;
+        ao[i] = (uint32_t)(a_row_of(g, rr) * g.lda * 2) + chunk_bytes;
+        int wrow;
+        if (SW) {
+            const int c = min(tc.nt * 128 + (row & 127), g.N - 1);
+            wrow = row < 128 ? c : g.N + c;
+        } else {
+            wrow = min(tc.nt * GBN + row, g.N - 1);
+        }
+        bo[i] = (uint32_t)((int64_t)wrow * g.K * 2) + chunk_bytes;
+    }
+    const int nk = g.K / GBK;
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[mi][nj][j] = 0.0f;
+
+    // fragment (fr, fh): row fr, k 8*fh .. +7 of a 16-deep step, i.e. chunk
+    // 2*ks + fh; rows of the wave's blocks share the low 4 bits, so one
+    // offset per step serves every block (the rest are immediates)
+    const int fr = lane & 31, fh = lane >> 5;
+    const int arow0 = 128 * wm + fr;
+    const int brow0 = (SW ? 64 * wn : 128 * wn) + fr;
+    int aoffs[4], boffs[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int ch = 2 * ks + fh;
+        aoffs[ks] = (arow0 * GBK + swz(arow0, ch) * 8) * 2;
+        boffs[ks] = (brow0 * GBK + swz(brow0, ch) * 8) * 2;
+    }
+    struct Frags {
+        bf16x8_t a[4], b[4];
+    };
+    const int nact = min(max((tc.row1 - tc.row0 - wm * 128 + 31) / 32, 0), 4);
+
+    auto run = [&](auto NAC) __attribute__((always_inline)) {
+        constexpr int NA = decltype(NAC)::value;
+        constexpr int NR = NA > 0 ? 4 + NA : 0;  // fragment reads per step
+        // fragment read i of a step, in the order the step's MFMAs first use
+        // them: A block 0, B blocks 0..3 (SwiGLU: gate rows, then the
+        // matching up rows), then A blocks 1..NA-1
+        auto rd1 = [&](int as, int bs, int ks, Frags& f, int i) __attribute__((always_inline)) {
+            if (i >= 1 && i <= 4) {
+                const int nj = i - 1;
+                const char* b = smem + B_RING + bs + boffs[ks];
+                const int bd = (SW ? ((nj < 2 ? 0 : 128) + 32 * (nj & 1)) : 32 * nj) * GBK * 2;
+                f.b[nj] = *(const bf16x8_t*)(b + bd);
+            } else {
+                const int mi = i == 0 ? 0 : i - 4;
+                const char* a = smem + as + aoffs[ks];
+                f.a[mi] = *(const bf16x8_t*)(a + mi * 32 * GBK * 2);
+            }
+        };
+        // MFMA i of a step: block (i / 4, i % 4)
+        auto mf1 = [&](const Frags& f, int i) __attribute__((always_inline)) {
+            acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                f.a[i >> 2], f.b[i & 3], acc[i >> 2][i & 3], 0, 0, 0);
+        };
+        // one DMA instruction (i of 8) of stage kt's A or B tile
+        auto da1 = [&](int as, int kt, int i) __attribute__((always_inline)) {
+            char* dst = smem + as;
+            const uint32_t ko = (uint32_t)min(kt, nk - 1) * GBK * 2;
+            __builtin_amdgcn_global_load_lds((const void*)(Ab + (ao[i] + ko)),
+                                             (lds_ptr_t)(dst + (64 * wave + 8 * i) * GBK * 2), 16, 0, 0);
+        };
+        auto db1 = [&](int bs, int kt, int i) __attribute__((always_inline)) {
+            char* dst = smem + B_RING + bs;
+            const uint32_t ko = (uint32_t)min(kt, nk - 1) * GBK * 2;
+            __builtin_amdgcn_global_load_lds((const void*)(Bb + (bo[i] + ko)),
+                                             (lds_ptr_t)(dst + (64 * wave + 8 * i) * GBK * 2), 16, 0, 0);
+        };
+
+        // DMA issue order: prologue A0 B0 A1 B1; turn kt issues B_{kt+2}
+        // during its first step and A_{kt+2} during its last, after the
+        // barrier that follows its third step.  Before the barrier of turn kt
+        // (publishing stage kt+1) only B_{kt+2} may still be in flight.
+#pragma unroll
+        for (int i = 0; i < ND; ++i) da1(0, 0, i);
+#pragma unroll
+        for (int i = 0; i < ND; ++i) db1(0, 0, i);
+#pragma unroll
+        for (int i = 0; i < ND; ++i) da1(A_BYTES, 1, i);
+#pragma unroll
+        for (int i = 0; i < ND; ++i) db1(B_BYTES, 1, i);
+        wait_vmcnt_lgkm0<2 * ND>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        Frags f0, f1;
+        if constexpr (NA > 0) {
+#pragma unroll
+            for (int i = 0; i < NR; ++i) rd1(0, 0, 0, f0, i);
+        }
+        // ring slots (byte offsets) of stages kt, kt+1 (A) and kt, kt+1,
+        // kt+2 (B), rotated at the end of each turn
+        int sa0 = 0, sa1 = A_BYTES, sb0 = 0, sb1 = B_BYTES, sb2 = 2 * B_BYTES;
+        for (int kt = 0; kt < nk; ++kt) {
+            __builtin_amdgcn_sched_barrier(0);
+            // step 0: MFMAs of f0, reads of step 1 and the B tile of kt+2,
+            // one instruction after each MFMA
+#pragma unroll
+            for (int i = 0; i < (NA * 4 > NR + ND ? NA * 4 : NR + ND); ++i) {
+                if (i < NA * 4) mf1(f0, i);
+                if (i < NR) rd1(sa0, sb0, 1, f1, i);
+                else if (i < NR + ND) db1(sb2, kt + 2, i - NR);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (NA > 0) {
+                // steps 1 and 2 (a one-block wave has 4 MFMAs for 5 reads)
+                constexpr int N12 = NA * 4 > NR ? NA * 4 : NR;
+#pragma unroll
+                for (int i = 0; i < N12; ++i) {
+                    if (i < NA * 4) mf1(f1, i);
+                    if (i < NR) rd1(sa0, sb0, 2, f0, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int i = 0; i < N12; ++i) {
+                    if (i < NA * 4) mf1(f0, i);
+                    if (i < NR) rd1(sa0, sb0, 3, f1, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            asm volatile("" ::: "memory");
+            // stage kt+1 has landed for this wave and all its reads of stage
+            // kt are retired; after the barrier stage kt+1 is visible and
+            // stage kt's slots are free
+            wait_vmcnt_lgkm0<ND>();
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            // step 3 with the reads of stage kt+1's step 0 and the A tile of
+            // kt+2 (at the last turn the reads take the clamped copy of the
+            // last stage: landed, never used)
+            // (full waves: the A DMA after the even MFMAs, the reads after
+            // the odd ones)
+            constexpr int M3 = NA * 4;
+            if constexpr (M3 >= 2 * NR && M3 >= 2 * ND) {
+#pragma unroll
+                for (int i = 0; i < M3; ++i) {
+                    mf1(f1, i);
+                    if ((i & 1) == 0 && (i >> 1) < ND) da1(sa0, kt + 2, i >> 1);
+                    if ((i & 1) == 1 && (i >> 1) < NR) rd1(sa1, sb1, 0, f0, i >> 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                constexpr int N3 = M3 > NR ? (M3 > ND ? M3 : ND) : (NR > ND ? NR : ND);
+#pragma unroll
+                for (int i = 0; i < N3; ++i) {
+                    if (i < M3) mf1(f1, i);
+                    if (i < NR) rd1(sa1, sb1, 0, f0, i);
+                    if (i < ND) da1(sa0, kt + 2, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            asm volatile("" ::: "memory");
+            {
+                const int t = sa0;
+                sa0 = sa1;
+                sa1 = t;
+                const int u = sb0;
+                sb0 = sb1;
+                sb1 = sb2;
+                sb2 = u;
+            }
+        }
+        // the trailing DMAs must land before the LDS is reused
+        wait_vmcnt<0>();
+        __syncthreads();
+        if constexpr (NA > 0) {
+        // epilogue through LDS, one 32-row block at a time; row stride 136
+        // floats (the two halves of a wave write 4 rows apart: banks +32)
+        constexpr int ELD = 136;
+        float* ep = (float*)smem + wave * 32 * ELD;
+        constexpr int CW = EPI == EPI_F32 || EPI == EPI_F32_BIAS ? 4 : 8;
+        constexpr int WC = SW ? 64 : 128;
+        constexpr int LPR = WC / CW, RPI = 64 / LPR;
+        const int c = (lane % LPR) * CW;
+        const int col = SW ? tc.nt * 128 + 64 * wn + c : tc.nt * GBN + 128 * wn + c;
+        const bool col_ok = col < g.N;
+        auto epi = [&](auto ACTC) __attribute__((always_inline)) {
+            constexpr int ACT = decltype(ACTC)::value;
+#pragma unroll
+            for (int mi = 0; mi < NA; ++mi) {
+#pragma unroll
+                for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        ep[(8 * (j >> 2) + 4 * fh + (j & 3)) * ELD + nj * 32 + fr] = acc[mi][nj][j];
+                asm volatile("" ::: "memory");
+                const int rb = tc.row0 + wm * 128 + mi * 32;
+#pragma unroll
+                for (int i = 0; i < 32 / RPI; ++i) {
+                    const int row = i * RPI + lane / LPR;
+                    const int r = rb + row;
+                    const float* src = ep + row * ELD + c;
+                    if (SW) {
+                        const f32x4_t g0 = *(const f32x4_t*)(src);
+                        const f32x4_t g1 = *(const f32x4_t*)(src + 4);
+                        const f32x4_t u0 = *(const f32x4_t*)(src + 64);
+                        const f32x4_t u1 = *(const f32x4_t*)(src + 68);
+                        u32x4_t o;
+                        o[0] = pack_bf16x2(glu_act<ACT>(g0[0], u0[0], g), glu_act<ACT>(g0[1], u0[1], g));
+                        o[1] = pack_bf16x2(glu_act<ACT>(g0[2], u0[2], g), glu_act<ACT>(g0[3], u0[3], g));
+                        o[2] = pack_bf16x2(glu_act<ACT>(g1[0], u1[0], g), glu_act<ACT>(g1[1], u1[1], g));
+                        o[3] = pack_bf16x2(glu_act<ACT>(g1[2], u1[2], g), glu_act<ACT>(g1[3], u1[3], g));
+                        if (r < tc.row1 && col_ok)
+                            *(u32x4_t*)((bf16_t*)g.C + (int64_t)r * g.ldc + col) = o;
+                    } else if (CW == 8) {
+                        const f32x4_t v0 = *(const f32x4_t*)(src);
+                        const f32x4_t v1 = *(const f32x4_t*)(src + 4);
+                        u32x4_t o;
+                        if (EPI == EPI_F16) {
+                            o[0] = pack_f16x2(v0[0], v0[1]);
+                            o[1] = pack_f16x2(v0[2], v0[3]);
+                            o[2] = pack_f16x2(v1[0], v1[1]);
+                            o[3] = pack_f16x2(v1[2], v1[3]);
+                        } else {
+                            o[0] = pack_bf16x2(v0[0], v0[1]);
+                            o[1] = pack_bf16x2(v0[2], v0[3]);
+                            o[2] = pack_bf16x2(v1[0], v1[1]);
+                            o[3] = pack_bf16x2(v1[2], v1[3]);
+                        }
+                        if (r < tc.row1 && col_ok)
+                            *(u32x4_t*)((uint16_t*)g.C + (int64_t)r * g.ldc + col) = o;
+                    } else {
+                        f32x4_t v = *(const f32x4_t*)(src);
+                        if (EPI == EPI_F32_BIAS && g.bias && col_ok) {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) v[t] += g.bias[col + t];
+                        }
+                        if (r < tc.row1 && col_ok)
+                            *(f32x4_t*)((float*)g.C + (int64_t)r * g.ldc + col) = v;
+                    }
+                }
+                asm volatile("" ::: "memory");
+            }
+        };
+        if constexpr (SW) with_act(g, epi);
+        else epi(std::integral_constant<int, ACT_SILU>{});
+        }
+    };
+    if (nact == 4) run(std::integral_constant<int, 4>{});
+    else if (nact == 3) run(std::integral_constant<int, 3>{});
+    else if (nact == 2) run(std::integral_constant<int, 2>{});
+    else if (nact == 1) run(std::integral_constant<int, 1>{});
+    else run(std::integral_constant<int, 0>{});
+}
+
+
+// ------------------------------------------------------------------------
 // fp32 VALU tiled kernel (64x64 tiles, 4x4 outputs per thread)
 // ------------------------------------------------------------------------
 constexpr int FBM = 64, FBN = 64, FBK = 16;
@@ -832,14 +1127,24 @@ void launch_big(const GemmArgs& g, dim3 gd, hipStream_t s) {
         }
         return;
     }
-    switch (g.epi) {
-        case EPI_F16:
-            if constexpr (!KC) gemm_bf16_big<EPI_F16, KC, WF_BF16><<<gd, bd, 0, s>>>(g);
-            break;
-        case EPI_F32: gemm_bf16_big<EPI_F32, KC, WF_BF16><<<gd, bd, 0, s>>>(g); break;
-        case EPI_F32_BIAS: gemm_bf16_big<EPI_F32_BIAS, KC, WF_BF16><<<gd, bd, 0, s>>>(g); break;
-        case EPI_OUT: gemm_bf16_big<EPI_OUT, KC, WF_BF16><<<gd, bd, 0, s>>>(g); break;
-        default: gemm_bf16_big<EPI_SWIGLU, KC, WF_BF16><<<gd, bd, 0, s>>>(g); break;
+    if constexpr (!KC) {
+        // bf16 weights, one K segment: 4 waves of 128x128
+        const dim3 b4(256);
+        switch (g.epi) {
+            case EPI_F16: gemm_bf16_big4<EPI_F16><<<gd, b4, 0, s>>>(g); break;
+            case EPI_F32: gemm_bf16_big4<EPI_F32><<<gd, b4, 0, s>>>(g); break;
+            case EPI_F32_BIAS: gemm_bf16_big4<EPI_F32_BIAS><<<gd, b4, 0, s>>>(g); break;
+            case EPI_OUT: gemm_bf16_big4<EPI_OUT><<<gd, b4, 0, s>>>(g); break;
+            default: gemm_bf16_big4<EPI_SWIGLU><<<gd, b4, 0, s>>>(g); break;
+        }
+    } else {
+        // the K-concatenated form (dense, no fp16 rows) keeps 8 waves
+        switch (g.epi) {
+            case EPI_F32: gemm_bf16_big<EPI_F32, true, WF_BF16><<<gd, bd, 0, s>>>(g); break;
+            case EPI_F32_BIAS: gemm_bf16_big<EPI_F32_BIAS, true, WF_BF16><<<gd, bd, 0, s>>>(g); break;
+            case EPI_OUT: gemm_bf16_big<EPI_OUT, true, WF_BF16><<<gd, bd, 0, s>>>(g); break;
+            default: gemm_bf16_big<EPI_SWIGLU, true, WF_BF16><<<gd, bd, 0, s>>>(g); break;
+        }
     }
 }
 
