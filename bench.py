@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=64)
     ap.add_argument("--cpu-runs", type=int, default=3)
+    ap.add_argument("--dense-expert", action="store_true",
+                    help="also time one dense expert (8192 token rows, H=7168, I=2048, bf16) "
+                         "through moe_experts: the 256x256 kernels' gate/up and down alone")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run three plain 1 GiB device-to-device copies (a known-size "
                          "reference for HBM byte counters)")
@@ -315,6 +318,41 @@ def cpu_baseline(w, inp, torch, ntok, runs=3):
                        + ", ".join(f"{t:.2f}" for t in times) + " s")}
 
 
+def dense_expert(torch, moe, steps: int, warmup: int) -> dict:
+    """One expert holding all 8192 token rows (H=7168, I=2048, bf16, seeded
+    N(0,1) tokens and N(0,1/fan_in) weights): moe_experts runs the gate/up +
+    SwiGLU product and the down product (fp32 rows) on the 256x256 kernels
+    with every tile full.  Reports the pair's time and executed rate."""
+    from routed_mixture_experts_amd.synth import normal
+    T, D, I = 8192, 7168, 2048
+    dev = "cuda:0"
+    x = normal((T, D), 1.0, 20, torch.bfloat16, dev)
+    w13 = normal((1, 2 * I, D), D ** -0.5, 21, torch.bfloat16, dev)
+    w2 = normal((1, D, I), I ** -0.5, 22, torch.bfloat16, dev)
+    off = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    r2p = torch.arange(T, dtype=torch.int32, device=dev)
+    y = torch.empty((T, D), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        moe.moe_experts(x, off, r2p, w13, w2, 1, y_rows=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(steps):
+        e0.record()
+        moe.moe_experts(x, off, r2p, w13, w2, 1, y_rows=y)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    ms = ts[len(ts) // 2]
+    flops = 2.0 * T * 3 * D * I
+    return {"workload": f"one dense expert: {T} rows, H={D}, I={I}, bf16, fp32 rows out",
+            "ms_median": ms, "steps": steps, "algorithmic_flops": flops,
+            "tflops": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "kernels": "gemm_bf16_big4<3> (gate/up + SwiGLU), gemm_bf16_big4<0> (down, fp32 rows)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -495,6 +533,9 @@ def main():
         del mxin
     if args.workload == "decode" and not args.no_prefill:
         del pin
+    if args.dense_expert:
+        print("[bench] dense expert", file=sys.stderr, flush=True)
+        res["dense_expert"] = dense_expert(torch, moe, max(5, args.steps // 2), 2)
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
