@@ -13,11 +13,10 @@
 // Kernels:
 //  * gemm_bf16_big4   -- 256x256 tiles, 4 waves of 128x128, LDS rings of
 //    64-deep K stages (2 A slots, 3 B slots) filled by global_load_lds,
-//    fragments read one 16-deep step ahead: bf16 weights, the large expert
-//    groups (prefill) and large dense products.
-//  * gemm_bf16_big    -- the same tiles and rings with 8 waves of 128x64:
-//    FP8 or MXFP4 expert weights (converted at the fragment read) and the
-//    K-concatenated dense product.
+//    fragments read one 16-deep step ahead; bf16, FP8 or MXFP4 weights (the
+//    quantised ones converted at the fragment read): the large expert
+//    groups (prefill) and large dense products, with or without a second K
+//    segment.
 //  * gemm_bf16_tiled  -- 128x128x64 LDS double-buffered tiles, 4 waves in a
 //    2x2 layout, each wave a 64x64 block of v_mfma_f32_32x32x16_bf16: mid-size
 //    dense products (bf16 weights).
@@ -38,6 +37,10 @@ namespace moe {
 namespace {
 
 using namespace tiles;
+
+// 8-byte LDS loads as a vector type (a struct type would drop the load's
+// type-based alias information)
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------------
 // bf16 LDS-tiled MFMA kernel
@@ -191,575 +194,129 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------------
-// bf16 256x256 MFMA kernel for grouped products with many rows per group
+// 256x256 MFMA kernel: groups with many rows per group, large dense products
 // ------------------------------------------------------------------------
-// 8 waves (two per SIMD) in a 2x4 layout; each wave owns a 128x64 block of
-// 4x2 v_mfma_f32_32x32x16_bf16 tiles (128 fp32 accumulators per lane).  K
-// advances 64 at a time through two LDS rings, 2 slots of A tiles and 3 of
-// B tiles (32 KB each), filled directly from global memory by
-// global_load_lds_dwordx4: a stage's A tile is fetched one stage ahead, its
-// B (weight) tile two stages ahead.  Each DMA
-// instruction moves 8 rows x 128 bytes, whole cache lines: with 16 rows x 64
-// bytes per instruction the L2-to-LDS path delivers 2.4x less (measured 12.5
-// against 30 TB/s on L2-resident tiles).  LDS row r (128 bytes) keeps its
-// eight 16-byte chunks at chunk ^ ((r & 7) ^ ((r >> 3) & 1)), so the MFMA
-// operand reads (32 rows, one chunk) hit distinct banks for any 8
-// consecutive rows and, per row parity, any 16; a lane therefore fetches the
-// global chunk whose swizzled slot is its own.  Operand fragments are read
-// half a stage ahead of their MFMAs: while stage kt's first half is
-// multiplied, its second half is read; then one barrier publishes stage kt+1
-// and frees stage kt's slots for the A tile of stage kt+2 and the B tile of
-// stage kt+3; while stage kt's second half is multiplied, stage kt+1's first
-// half is read.  A wave whose 128 rows all lie past the tile's end skips its
-// MFMAs.
+// 4 waves (one per SIMD) in a 2x2 layout; each wave owns a 128x128 block of
+// 4x4 v_mfma_f32_32x32x16_bf16 tiles (256 fp32 accumulators per lane, kept
+// in AGPRs).  K advances 64 at a time through two LDS rings, 2 slots of A
+// (token) tiles and 3 of B (weight) tiles, filled directly from global
+// memory by global_load_lds.  Each A DMA instruction moves 8 rows x 128
+// bytes, whole cache lines: with 16 rows x 64 bytes per instruction the
+// L2-to-LDS path delivers 2.4x less (measured 12.5 against 30 TB/s on
+// L2-resident tiles).  LDS row r (128 bytes) keeps its eight 16-byte chunks
+// at chunk ^ ((r & 7) ^ ((r >> 3) & 1)), so the MFMA operand reads (32 rows,
+// one chunk) hit distinct banks for any 8 consecutive rows and, per row
+// parity, any 16; a lane therefore fetches the global chunk whose swizzled
+// slot is its own.  Per 16-deep step a wave reads 4 A and 4 B fragments for
+// 16 MFMAs (a stage reads 128 KB of LDS); fragments are read one step ahead,
+// and each step's reads and DMA instructions are placed one after each MFMA
+// (scheduling fences), so that the one wave of a SIMD keeps its MFMA pipe
+// fed; the stage's one barrier sits between its third and last steps.
+//
+// B slots by weight format:
+//  * bf16: 128 bytes per weight row (32 KB), like A.
+//  * FP8 (OCP e4m3 codes, one fp32 scale per weight row; grouped products
+//    only): 64 bytes per row (16 KB), moved in 16 rows x 64 bytes per DMA
+//    instruction; LDS row r keeps its four 16-byte chunks at chunk ^
+//    ((r >> 2) & 3).  A fragment read takes a lane's 8 codes and turns them
+//    into 8 bf16 values exactly; the row scales multiply the fp32 sums in
+//    the epilogue.
+//  * MXFP4 (OCP E2M1 codes, two per byte, one E8M0 exponent per 32 codes of
+//    a row; grouped products only): 32 bytes per row (8 KB; LDS row r keeps
+//    its two 16-byte chunks at chunk ^ ((r >> 3) & 1)), then one dword of
+//    exponents per row, the 4 blocks holding the stage's 2.  A fragment read
+//    takes a lane's 8 codes and its block exponent and turns them into 8
+//    bf16 values, the scale applied by the conversion.
+// bf16 products may carry a second K segment ([A | A2] . [B | B2]^T).
 constexpr int GBM = 256, GBN = 256, GBK = 64;
 
 __device__ __forceinline__ int swz(int row, int chunk) {
     return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
 }
 
-// With FP8 weights (OCP e4m3 codes, one fp32 scale per weight row; grouped
-// products only) a B slot holds the codes, 64 bytes per weight row (16 KB),
-// moved by global_load_lds in 16 rows x 64 bytes per instruction; a
-// fragment read takes a lane's 8 codes (ds_read_b64) and turns them into
-// 8 bf16 values exactly, and the row scales multiply the fp32 sums in the
-// epilogue.  LDS row r of the codes keeps its four 16-byte chunks at chunk ^
-// ((r >> 2) & 3).
 __device__ __forceinline__ int swz8(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
-// With MXFP4 weights (OCP E2M1 codes, two per byte, one E8M0 exponent per 32
-// codes of a row; grouped products only) a B slot holds the codes, 32 bytes
-// per weight row (8 KB, one 32-row DMA instruction per wave; LDS row r keeps
-// its two 16-byte chunks at chunk ^ ((r >> 3) & 1)), and after them one
-// dword of exponents per row: the 4 blocks holding the stage's 2 (a 32-row
-// DMA of 4-byte pieces per wave).  A fragment read takes a lane's 8 codes
-// (ds_read_b32) and its block exponent and turns them into 8 bf16 values,
-// the scale applied by the conversion.
-
-
-template <int EPI, bool KCAT, int WF>
-__global__ __launch_bounds__(512, 1) void gemm_bf16_big(GemmArgs g) {
-    constexpr bool SW = EPI == EPI_SWIGLU;
-    constexpr bool FP8 = WF == WF_FP8, FP4 = WF == WF_MXFP4;
-    static_assert(WF == WF_BF16 || ((FP8 || FP4) && !KCAT),
-                  "FP8 / MXFP4 weights: grouped products only");
-    const int ntn = SW ? (g.N + 127) / 128 : (g.N + GBN - 1) / GBN;
-    TileCoord tc;
-    if (!fetch_tile(g, GBM, ntn, tc)) return;
-
-    // one LDS buffer: a ring of AS A tiles (bf16), then a ring of BS B tiles
-    // (bf16, FP8 codes, or MXFP4 codes and exponents); after the K loop the
-    // epilogue reuses it as a flat fp32 buffer.  Stage kt's A and B tiles are
-    // issued while stages kt - AS and kt - BS are multiplied.
-    constexpr int A_BYTES = GBM * GBK * 2;
-    constexpr int B_CODES = GBN * GBK / 2;  // MXFP4 codes of a B slot
-    constexpr int B_BYTES = FP8 ? GBN * GBK : FP4 ? B_CODES + GBN * 4 : GBN * GBK * 2;
-    // 2 + 3 slots (bf16: 160 KB).  Measured against it: 2 + 2 slots 4.8%
-    // slower on the prefill layer; 3 + 2 slots 1% slower; with FP8 codes,
-    // 3 + 4 slots 1% slower.
-    constexpr int AS = 2, BS = 3;
-    constexpr int B_RING = AS * A_BYTES;
-    static_assert(B_RING + BS * B_BYTES <= 160 * 1024, "LDS");
-    __shared__ __attribute__((aligned(1024))) char smem[B_RING + BS * B_BYTES];
-    // DMA instructions per wave and stage: A, B.  Each loop turn issues the
-    // ring with the shorter lead first (X, lead L1), then the other (Y, L2);
-    // the prologue issues stages 0 .. L2-1 in the same order.  vmcnt counts
-    // in issue order, so before stage kt+1 is published a wave may leave in
-    // flight the DMAs issued after the later of X_{kt+1} and Y_{kt+1}: with
-    // L1 < L2 that is X_{kt+1}, followed by Y_{kt+L2} of the same turn and
-    // L1-2 whole turns; with L1 == L2 it is Y_{kt+1}, followed by L1-2 whole
-    // turns (exact for the ring depths allowed here, prologue included).
-    constexpr int NA_DMA = 4, NB_DMA = FP8 || FP4 ? 2 : 4;
-    constexpr bool A_FIRST = AS <= BS;
-    constexpr int L1 = A_FIRST ? AS : BS, L2 = A_FIRST ? BS : AS;
-    constexpr int NX = A_FIRST ? NA_DMA : NB_DMA, NY = A_FIRST ? NB_DMA : NA_DMA;
-    static_assert((L1 == 2 && L2 == 2) || (L1 == 2 && L2 == 3) || (L1 == 3 && L2 == 3) ||
-                      (L1 == 3 && L2 == 4),
-                  "ring depths whose wait counts were checked");
-    constexpr int WAIT_LOOP = (L1 < L2 ? NY : 0) + (L1 - 2) * (NX + NY);
-    constexpr int WAIT_PRO = (L1 - 1) * NX + (L2 - 1) * NY;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
-
-    const char* Ab = (const char*)g.A;
-    const char* Bb = (const char*)g.B + (FP4   ? (int64_t)tc.group * g.b_gstride / 2
-                                         : FP8 ? (int64_t)tc.group * g.b_gstride
-                                               : (int64_t)tc.group * g.b_gstride * 2);
-    const char* A2b = (const char*)g.A2;
-    const char* B2b = (const char*)g.B2;
-
-    // DMA block i of this wave covers tile rows 32*wave + 8*i .. +7 of A and
-    // of B; lane l fills row +l/8, slot l%8, i.e. global chunk
-    // (l%8) ^ swizzle(row).  The swizzle reads bits 0..3 of the row: l/8 and
-    // the parity of i.  32-bit byte offsets from wave-uniform bases; rows past
-    // the tile's end load the tile's first row (never stored).
-    uint32_t ao[4], bo[4], ao2[KCAT ? 4 : 1], bo2[KCAT ? 4 : 1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 32 * wave + 8 * i + (lane >> 3);
-        const int chunk_bytes = swz(row, lane & 7) * 16;
-        const int r = tc.row0 + row;
-        const int rr = r < tc.row1 ? r : tc.row0;
-        ao[i] = (uint32_t)(a_row_of(g, rr) * g.lda * 2) + chunk_bytes;
-        int wrow;
-        if (SW) {
-            const int c = min(tc.nt * 128 + (row & 127), g.N - 1);
-            wrow = row < 128 ? c : g.N + c;
-        } else {
-            wrow = min(tc.nt * GBN + row, g.N - 1);
-        }
-        bo[i] = (uint32_t)((int64_t)wrow * g.K * 2) + chunk_bytes;  // (bf16 weights)
-        if (KCAT) {
-            ao2[i] = (uint32_t)((int64_t)rr * g.lda2 * 2) + chunk_bytes;
-            bo2[i] = (uint32_t)((int64_t)wrow * g.K2 * 2) + chunk_bytes;
-        }
-    }
-    // FP8 codes: DMA block i (0, 1) of this wave covers tile rows 32*wave +
-    // 16*i .. +15 of B; lane l fills row +l/4, slot l%4 (global chunk
-    // (l%4) ^ swz8(row)).
-    uint32_t bo8[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = 32 * wave + 16 * i + (lane >> 2);
-        int wrow;
-        if (SW) {
-            const int c = min(tc.nt * 128 + (row & 127), g.N - 1);
-            wrow = row < 128 ? c : g.N + c;
-        } else {
-            wrow = min(tc.nt * GBN + row, g.N - 1);
-        }
-        bo8[i] = (uint32_t)((int64_t)wrow * g.K) + swz8(row, lane & 3) * 16;
-    }
-    // MXFP4: the codes' DMA covers tile rows 32*wave .. +31, lane l filling
-    // row +l/2, slot l%2 (global chunk (l%2) ^ ((row >> 3) & 1)); the
-    // exponents' DMA (lanes 0..31) row +l.
-    const char* Sb = FP4 ? (const char*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride
-                         : nullptr;
-    uint32_t bo4 = 0, eo4 = 0;
-    if constexpr (FP4) {
-        auto wrow_of = [&](int row) __attribute__((always_inline)) {
-            if (SW) {
-                const int c = min(tc.nt * 128 + (row & 127), g.N - 1);
-                return row < 128 ? c : g.N + c;
-            }
-            return min(tc.nt * GBN + row, g.N - 1);
-        };
-        const int row = 32 * wave + (lane >> 1);
-        bo4 = (uint32_t)((int64_t)wrow_of(row) * (g.K / 2)) + (((lane & 1) ^ ((row >> 3) & 1)) * 16);
-        eo4 = (uint32_t)((int64_t)wrow_of(32 * wave + (lane & 31)) * (g.K / 32));
-    }
-
-    const int nk1 = g.K / GBK;
-    const int nk = nk1 + (KCAT ? g.K2 / GBK : 0);
-
-    // Issue this wave's DMA of stage kt's A tile, or B tile (kt clamped to
-    // the last stage), into its ring slot.  The K segment of a
-    // K-concatenated product is picked with selects.
-    auto issue_a = [&](int kt) __attribute__((always_inline)) {
-        char* dst = smem + (kt % AS) * A_BYTES;
-        kt = min(kt, nk - 1);
-        const bool seg1 = !KCAT || kt < nk1;
-        const char* abase = seg1 ? Ab : A2b;
-        const uint32_t ko = (uint32_t)(seg1 ? kt : kt - nk1) * GBK * 2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds(
-                (const void*)(abase + ((seg1 ? ao[i] : ao2[KCAT ? i : 0]) + ko)),
-                (lds_ptr_t)(dst + (32 * wave + 8 * i) * GBK * 2), 16, 0, 0);
-    };
-    auto issue_b = [&](int kt) __attribute__((always_inline)) {
-        char* dst = smem + B_RING + (kt % BS) * B_BYTES;
-        kt = min(kt, nk - 1);
-        if constexpr (FP8) {
-            // the codes: 16 weight rows per DMA instruction
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                __builtin_amdgcn_global_load_lds(
-                    (const void*)(Bb + (bo8[i] + (uint32_t)kt * GBK)),
-                    (lds_ptr_t)(dst + (32 * wave + 16 * i) * GBK), 16, 0, 0);
-        } else if constexpr (FP4) {
-            // the codes, then the exponent dword holding blocks 2kt, 2kt+1
-            // (K is a multiple of 128, so that dword is aligned and whole)
-            __builtin_amdgcn_global_load_lds((const void*)(Bb + (bo4 + (uint32_t)kt * 32)),
-                                             (lds_ptr_t)(dst + 32 * wave * 32), 16, 0, 0);
-            if (lane < 32)
-                __builtin_amdgcn_global_load_lds(
-                    (const void*)(Sb + (eo4 + (uint32_t)(kt >> 1) * 4)),
-                    (lds_ptr_t)(dst + B_CODES + 32 * wave * 4), 4, 0, 0);
-        } else {
-            const bool seg1 = !KCAT || kt < nk1;
-            const char* bbase = seg1 ? Bb : B2b;
-            const uint32_t ko = (uint32_t)(seg1 ? kt : kt - nk1) * GBK * 2;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_global_load_lds(
-                    (const void*)(bbase + ((seg1 ? bo[i] : bo2[KCAT ? i : 0]) + ko)),
-                    (lds_ptr_t)(dst + (32 * wave + 8 * i) * GBK * 2), 16, 0, 0);
-        }
-    };
-    auto issue_x = [&](int kt) __attribute__((always_inline)) {
-        if constexpr (A_FIRST) issue_a(kt);
-        else issue_b(kt);
-    };
-    auto issue_y = [&](int kt) __attribute__((always_inline)) {
-        if constexpr (A_FIRST) issue_b(kt);
-        else issue_a(kt);
-    };
-    // Stage 0 has landed for this wave once only the DMAs after X_0 and Y_0
-    // may be in flight.
-    auto prologue = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int st = 0; st < L2; ++st) {
-            if (st < L1) issue_x(st);
-            issue_y(st);
-        }
-        wait_vmcnt_lgkm0<WAIT_PRO>();
-    };
-
-    f32x16_t acc[4][2];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < 2; ++nj)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) acc[mi][nj][j] = 0.0f;
-
-    // Operand fragments of v_mfma_f32_32x32x16_bf16: lane (fr, fh) supplies
-    // row fr, k 8*fh .. +7 of 16-deep step ks, i.e. LDS chunk 2*ks + fh.
-    const int fr = lane & 31, fh = lane >> 5;
-    // (byte offsets inside a slot's A and B tiles)
-    int aoffs[4][4], boffs[4][2];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int ch = ks * 2 + fh;
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int row = wm * 128 + mi * 32 + fr;
-            aoffs[ks][mi] = (row * GBK + swz(row, ch) * 8) * 2;
-        }
-#pragma unroll
-        for (int nj = 0; nj < 2; ++nj) {
-            const int row = (SW ? nj * 128 + wn * 32 : wn * 64 + nj * 32) + fr;
-            // FP8: the 8 codes of k 16*ks + 8*fh .. +7 are half of chunk ks;
-            // MXFP4: they are bytes 8*ks + 4*fh .. +3 of the row
-            boffs[ks][nj] = FP8   ? row * GBK + swz8(row, ks) * 16 + fh * 8
-                            : FP4 ? row * 32 + (((ks >> 1) ^ ((row >> 3) & 1)) * 16) +
-                                        ((8 * ks + 4 * fh) & 15)
-                                  : (row * GBK + swz(row, ch) * 8) * 2;
-        }
-    }
-    // B fragment (16-deep step ks, block nj) of stage kt in B slot b
-    auto bfrag = [&](const char* b, int kt, int ks, int nj) __attribute__((always_inline)) {
-        const int o = boffs[ks][nj];
-        if constexpr (FP8) {
-            const uint2 q = *(const uint2*)(b + o);
-            return __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(q.x, q.y));
-        } else if constexpr (FP4) {
-            const int row = (SW ? nj * 128 + wn * 32 : wn * 64 + nj * 32) + fr;
-            const uint32_t q = *(const uint32_t*)(b + o);
-            const uint32_t e = *(const uint32_t*)(b + B_CODES + row * 4);
-            // block 2kt + ks/2 is byte 2*(kt & 1) + ks/2 of the dword
-            const uint32_t eb = (e >> (8 * (2 * (kt & 1) + (ks >> 1)))) & 0xffu;
-            return __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16x8(q, e8m0_scale(eb)));
-        } else {
-            return *(const bf16x8_t*)(b + o);
-        }
-    };
-
-    // does this wave's 128-row half hold any row of the tile (wave-uniform),
-    // and how many of its 32-row blocks do
-    const bool active = tc.row1 - tc.row0 > wm * 128;
-    const int nact = min(max((tc.row1 - tc.row0 - wm * 128 + 31) / 32, 0), 4);
-
-    // Fragments of one half stage (two 16-deep steps).
-    struct Frags {
-        bf16x8_t a[2][4], b[2][2];
-    };
-    auto read_half = [&](int kt, int h, Frags& f) __attribute__((always_inline)) {
-        const char* a = smem + (kt % AS) * A_BYTES;
-        const char* b = smem + B_RING + (kt % BS) * B_BYTES;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const int ks = 2 * h + s2;
-#pragma unroll
-            for (int nj = 0; nj < 2; ++nj) f.b[s2][nj] = bfrag(b, kt, ks, nj);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) f.a[s2][mi] = *(const bf16x8_t*)(a + aoffs[ks][mi]);
-        }
-    };
-    // the MFMAs of one 16-deep step of a half stage
-    auto mma_step = [&](const Frags& f, int s2) __attribute__((always_inline)) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int nj = 0; nj < 2; ++nj)
-                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    f.a[s2][mi], f.b[s2][nj], acc[mi][nj], 0, 0, 0);
-    };
-    auto mma = [&](const Frags& f) __attribute__((always_inline)) {
-        mma_step(f, 0);
-        mma_step(f, 1);
-    };
-
-    // A wave with 1..3 of its 32-row blocks inside the tile (the last tile
-    // of a group) runs the same loop over those blocks only: the blocks past
-    // the tile's end cost neither LDS reads nor MFMAs.
-    auto partial_loop = [&](auto NA) __attribute__((always_inline)) {
-        constexpr int na = decltype(NA)::value;
-        auto rd = [&](int kt, int h, Frags& f) __attribute__((always_inline)) {
-            const char* a = smem + (kt % AS) * A_BYTES;
-            const char* b = smem + B_RING + (kt % BS) * B_BYTES;
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int ks = 2 * h + s2;
-#pragma unroll
-                for (int nj = 0; nj < 2; ++nj) f.b[s2][nj] = bfrag(b, kt, ks, nj);
-#pragma unroll
-                for (int mi = 0; mi < na; ++mi)
-                    f.a[s2][mi] = *(const bf16x8_t*)(a + aoffs[ks][mi]);
-            }
-        };
-        auto step = [&](const Frags& f, int s2) __attribute__((always_inline)) {
-#pragma unroll
-            for (int mi = 0; mi < na; ++mi)
-#pragma unroll
-                for (int nj = 0; nj < 2; ++nj)
-                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        f.a[s2][mi], f.b[s2][nj], acc[mi][nj], 0, 0, 0);
-        };
-        prologue();
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        Frags g0, g1;
-        rd(0, 0, g0);
-        for (int kt = 0; kt < nk; ++kt) {
-            rd(kt, 1, g1);
-            step(g0, 0);
-            step(g0, 1);
-            asm volatile("" ::: "memory");
-            wait_vmcnt_lgkm0<WAIT_LOOP>();
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            issue_x(kt + L1);
-            rd(kt + 1, 0, g0);
-            step(g1, 0);
-            asm volatile("" ::: "memory");
-            issue_y(kt + L2);
-            asm volatile("" ::: "memory");
-            step(g1, 1);
-            asm volatile("" ::: "memory");
-        }
-    };
-    // (not in the K-concatenated form, whose registers it would spill)
-    if (!KCAT && nact == 1) partial_loop(std::integral_constant<int, 1>{});
-    else if (!KCAT && nact == 2) partial_loop(std::integral_constant<int, 2>{});
-    else if (!KCAT && nact == 3) partial_loop(std::integral_constant<int, 3>{});
-    else {
-    prologue();  // this wave's part of stage 0 has landed
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    Frags f0, f1;
-    if (active) read_half(0, 0, f0);
-    for (int kt = 0; kt < nk; ++kt) {
-        if (active) {
-            read_half(kt, 1, f1);
-            mma(f0);
-        }
-        asm volatile("" ::: "memory");
-        // stage kt+1's tiles have landed for this wave and its reads of
-        // stage kt are retired; after the barrier stage kt+1 is visible
-        // everywhere and stage kt's slots take stage kt+AS's A tile and
-        // stage kt+BS's B tile
-        wait_vmcnt_lgkm0<WAIT_LOOP>();
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        // one ring's DMA goes out now, the other's after the first step's
-        // MFMAs, so the whole workgroup's DMA does not queue at once
-        issue_x(kt + L1);
-        if (active) {
-            read_half(kt + 1, 0, f0);
-            mma_step(f1, 0);
-        }
-        asm volatile("" ::: "memory");
-        issue_y(kt + L2);
-        asm volatile("" ::: "memory");
-        if (active) mma_step(f1, 1);
-        asm volatile("" ::: "memory");
-    }
-    }
-    // The ring's trailing DMAs must land before the LDS is reused below.
-    wait_vmcnt<0>();
-    __syncthreads();
-
-    // Epilogue through LDS, one 32-row block of each wave at a time: the
-    // accumulators are written in MFMA layout (lane = column, 16 rows), then
-    // read back so that every store instruction writes whole row segments of
-    // the wave's block: 16 rows x 64 bytes (SwiGLU h), 8 rows x 128 bytes
-    // (bf16 / fp16 outputs) or 4 rows x 256 bytes (fp32), i.e. few, fully
-    // written cache lines per instruction (the fp32 output of a 256x256 tile
-    // is 256 KB).  Only one block's accumulators are live in VGPRs at a time.
-    // Row stride 72 floats keeps the writes free of bank conflicts.  Each wave
-    // uses its own region, so LDS order within the wave suffices between the
-    // writes and the reads.
-    if (!active) return;
-    constexpr int ELD = 72;
-    float* ep = (float*)smem + wave * 32 * ELD;
-    // this lane's columns of the wave block: SwiGLU 8 h columns (gate at c,
-    // up at 32 + c); 16-bit outputs 8 columns; fp32 4 columns
-    constexpr int CW = EPI == EPI_F32 || EPI == EPI_F32_BIAS ? 4 : 8;  // columns per lane
-    constexpr int LPR = SW ? 4 : 64 / CW;                          // lanes per row
-    constexpr int RPI = 64 / LPR;                                  // rows per store
-    const int c = (lane % LPR) * CW;
-    const int col = SW ? tc.nt * 128 + wn * 32 + c : tc.nt * GBN + wn * 64 + c;
-    // FP8 row scales of the weight rows behind the lane's columns (SwiGLU:
-    // gate then up)
-    float sg[FP8 ? (SW ? 16 : CW) : 1];
-    if constexpr (FP8) {
-        const float* sc = (const float*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride;
-#pragma unroll
-        for (int t = 0; t < CW; ++t) {
-            const int n = min(col + t, g.N - 1);
-            sg[t] = sc[n];
-            if (SW) sg[CW + t] = sc[g.N + n];
-        }
-    }
-    const bool col_ok = col < g.N;  // N is a multiple of 8 (SwiGLU, 16-bit) or 4
-    // (SwiGLU: one copy of the loop per activation, picked once)
-    auto epilogue = [&](auto ACTC) __attribute__((always_inline)) {
-    constexpr int ACT = decltype(ACTC)::value;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int nj = 0; nj < 2; ++nj)
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-                ep[(8 * (j >> 2) + 4 * fh + (j & 3)) * ELD + nj * 32 + fr] = acc[mi][nj][j];
-        asm volatile("" ::: "memory");
-        const int rb = tc.row0 + wm * 128 + mi * 32;
-#pragma unroll
-        for (int i = 0; i < 32 / RPI; ++i) {
-            const int row = i * RPI + lane / LPR;
-            const int r = rb + row;
-            const float* src = ep + row * ELD + c;
-            if (SW) {
-                f32x4_t g0 = *(const f32x4_t*)(src);
-                f32x4_t g1 = *(const f32x4_t*)(src + 4);
-                f32x4_t u0 = *(const f32x4_t*)(src + 32);
-                f32x4_t u1 = *(const f32x4_t*)(src + 36);
-                if constexpr (FP8) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        g0[t] *= sg[t];
-                        g1[t] *= sg[4 + t];
-                        u0[t] *= sg[8 + t];
-                        u1[t] *= sg[12 + t];
-                    }
-                }
-                u32x4_t o;
-                o[0] = pack_bf16x2(glu_act<ACT>(g0[0], u0[0], g), glu_act<ACT>(g0[1], u0[1], g));
-                o[1] = pack_bf16x2(glu_act<ACT>(g0[2], u0[2], g), glu_act<ACT>(g0[3], u0[3], g));
-                o[2] = pack_bf16x2(glu_act<ACT>(g1[0], u1[0], g), glu_act<ACT>(g1[1], u1[1], g));
-                o[3] = pack_bf16x2(glu_act<ACT>(g1[2], u1[2], g), glu_act<ACT>(g1[3], u1[3], g));
-                if (r < tc.row1 && col_ok)
-                    *(u32x4_t*)((bf16_t*)g.C + (int64_t)r * g.ldc + col) = o;
-            } else if (CW == 8) {
-                f32x4_t v0 = *(const f32x4_t*)(src);
-                f32x4_t v1 = *(const f32x4_t*)(src + 4);
-                if constexpr (FP8) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        v0[t] *= sg[t];
-                        v1[t] *= sg[4 + t];
-                    }
-                }
-                u32x4_t o;
-                if (EPI == EPI_F16) {
-                    o[0] = pack_f16x2(v0[0], v0[1]);
-                    o[1] = pack_f16x2(v0[2], v0[3]);
-                    o[2] = pack_f16x2(v1[0], v1[1]);
-                    o[3] = pack_f16x2(v1[2], v1[3]);
-                } else {  // EPI_OUT: bf16
-                    o[0] = pack_bf16x2(v0[0], v0[1]);
-                    o[1] = pack_bf16x2(v0[2], v0[3]);
-                    o[2] = pack_bf16x2(v1[0], v1[1]);
-                    o[3] = pack_bf16x2(v1[2], v1[3]);
-                }
-                if (r < tc.row1 && col_ok)
-                    *(u32x4_t*)((uint16_t*)g.C + (int64_t)r * g.ldc + col) = o;
-            } else {
-                f32x4_t v = *(const f32x4_t*)(src);
-                if constexpr (FP8) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] *= sg[t];
-                }
-                if (EPI == EPI_F32_BIAS && g.bias && col_ok) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] += g.bias[col + t];
-                }
-                if (r < tc.row1 && col_ok) *(f32x4_t*)((float*)g.C + (int64_t)r * g.ldc + col) = v;
-            }
-        }
-        asm volatile("" ::: "memory");
-    }
-    };
-    if constexpr (SW) with_act(g, epilogue);
-    else epilogue(std::integral_constant<int, ACT_SILU>{});
-}
-
-// ------------------------------------------------------------------------
-// 256x256 tiles with 4 waves (one per SIMD), each a 128x128 block of 4x4
-// v_mfma_f32_32x32x16_bf16 tiles (256 fp32 accumulators per lane).  The same
-// LDS rings, swizzle and DMA as gemm_bf16_big; a wave's DMA share is 64 rows
-// of each tile (8 instructions).  Per 16-deep step a wave reads 4 A and 4 B
-// fragments for 16 MFMAs (gemm_bf16_big: 4 + 2 for 8), so a 64-deep stage
-// reads 128 KB of LDS instead of 192 KB.  Fragments are read one step ahead,
-// and each step's reads and DMA instructions are placed one after each MFMA
-// (scheduling fences), so that the one wave of a SIMD keeps its MFMA pipe
-// fed; the stage's one barrier sits between its third and last steps.
-// bf16 weights, no second K segment.
-// ------------------------------------------------------------------------
-template <int EPI>
+template <int EPI, int WF, bool KCAT>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big4(GemmArgs g) {
     constexpr bool SW = EPI == EPI_SWIGLU;
+    constexpr bool FP8 = WF == WF_FP8, FP4 = WF == WF_MXFP4;
+    static_assert(!KCAT || WF == WF_BF16, "a second K segment: bf16 weights only");
     const int ntn = SW ? (g.N + 127) / 128 : (g.N + GBN - 1) / GBN;
     TileCoord tc;
     if (!fetch_tile(g, GBM, ntn, tc)) return;
 
-    constexpr int A_BYTES = GBM * GBK * 2, B_BYTES = GBN * GBK * 2;
+    // B slot: bf16 rows (128 bytes per stage), FP8 codes (64 bytes), or MXFP4
+    // codes (32 bytes) followed by one exponent dword per row
+    constexpr int A_BYTES = GBM * GBK * 2;
+    constexpr int B_ROW = FP8 ? GBK : FP4 ? GBK / 2 : GBK * 2;  // bytes per weight row
+    constexpr int B_CODES = GBN * B_ROW;
+    constexpr int B_BYTES = FP4 ? B_CODES + GBN * 4 : B_CODES;
     constexpr int AS = 2, BS = 3;
     constexpr int B_RING = AS * A_BYTES;
     static_assert(B_RING + BS * B_BYTES <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(1024))) char smem[B_RING + BS * B_BYTES];
-    // per wave and stage: 8 DMA instructions for A, 8 for B
-    constexpr int ND = 8;
+    // DMA instructions per wave and stage (a wave's share is 64 rows): A 8
+    // (8 rows x 128 B each); B 8 (bf16), 4 (FP8: 16 rows x 64 B), or 3
+    // (MXFP4: 2 x 32 rows x 32 B of codes, 1 x 64 rows x 4 B of exponents)
+    constexpr int NDA = 8, NDB = FP8 ? 4 : FP4 ? 3 : 8;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
     const char* Ab = (const char*)g.A;
-    const char* Bb = (const char*)g.B + (int64_t)tc.group * g.b_gstride * 2;
+    const char* Bb = (const char*)g.B + (FP4   ? (int64_t)tc.group * g.b_gstride / 2
+                                         : FP8 ? (int64_t)tc.group * g.b_gstride
+                                               : (int64_t)tc.group * g.b_gstride * 2);
+    const char* Sb = FP4 ? (const char*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride : nullptr;
+    const char* A2b = (const char*)g.A2;
+    const char* B2b = (const char*)g.B2;
+    auto wrow_of = [&](int row) __attribute__((always_inline)) {
+        if (SW) {
+            const int c = min(tc.nt * 128 + (row & 127), g.N - 1);
+            return row < 128 ? c : g.N + c;
+        }
+        return min(tc.nt * GBN + row, g.N - 1);
+    };
 
-    uint32_t ao[ND], bo[ND];
+    // A: lane l of DMA instruction i fills row 64*wave + 8*i + l/8, slot l%8,
+    // i.e. global chunk (l%8) ^ swizzle(row); B likewise for bf16 rows; FP8:
+    // row 64*wave + 16*i + l/4, slot l%4 (chunk (l%4) ^ swz8(row)); MXFP4:
+    // row 64*wave + 32*i + l/2, slot l%2 (chunk (l%2) ^ ((row >> 3) & 1)),
+    // and the exponent dword of row 64*wave + l
+    // (second K segment: ao2, bo2; its A rows are the tile's rows)
+    uint32_t ao[NDA], bo[NDB], ao2[KCAT ? NDA : 1], bo2[KCAT ? NDB : 1];
 #pragma unroll
-    for (int i = 0; i < ND; ++i) {
+    for (int i = 0; i < NDA; ++i) {
         const int row = 64 * wave + 8 * i + (lane >> 3);
         const int chunk_bytes = swz(row, lane & 7) * 16;
         const int r = tc.row0 + row;
         const int rr = r < tc.row1 ? r : tc.row0;
         ao[i] = (uint32_t)(a_row_of(g, rr) * g.lda * 2) + chunk_bytes;
-        int wrow;
-        if (SW) {
-            const int c = min(tc.nt * 128 + (row & 127), g.N - 1);
-            wrow = row < 128 ? c : g.N + c;
-        } else {
-            wrow = min(tc.nt * GBN + row, g.N - 1);
-        }
-        bo[i] = (uint32_t)((int64_t)wrow * g.K * 2) + chunk_bytes;
+        if constexpr (KCAT) ao2[i] = (uint32_t)((int64_t)rr * g.lda2 * 2) + chunk_bytes;
     }
-    const int nk = g.K / GBK;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+        if constexpr (FP8) {
+            const int row = 64 * wave + 16 * i + (lane >> 2);
+            bo[i] = (uint32_t)((int64_t)wrow_of(row) * g.K) + swz8(row, lane & 3) * 16;
+        } else if constexpr (FP4) {
+            if (i < 2) {
+                const int row = 64 * wave + 32 * i + (lane >> 1);
+                bo[i] = (uint32_t)((int64_t)wrow_of(row) * (g.K / 2)) +
+                        (((lane & 1) ^ ((row >> 3) & 1)) * 16);
+            } else {
+                bo[i] = (uint32_t)((int64_t)wrow_of(64 * wave + lane) * (g.K / 32));
+            }
+        } else {
+            const int row = 64 * wave + 8 * i + (lane >> 3);
+            bo[i] = (uint32_t)((int64_t)wrow_of(row) * g.K * 2) + swz(row, lane & 7) * 16;
+            if constexpr (KCAT)
+                bo2[i] = (uint32_t)((int64_t)wrow_of(row) * g.K2 * 2) + swz(row, lane & 7) * 16;
+        }
+    }
+    const int nk1 = g.K / GBK;
+    const int nk = nk1 + (KCAT ? g.K2 / GBK : 0);
     f32x16_t acc[4][4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
@@ -769,7 +326,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big4(GemmArgs g) {
             for (int j = 0; j < 16; ++j) acc[mi][nj][j] = 0.0f;
 
     // fragment (fr, fh): row fr, k 8*fh .. +7 of a 16-deep step, i.e. chunk
-    // 2*ks + fh; rows of the wave's blocks share the low 4 bits, so one
+    // 2*ks + fh (FP8: half fh of chunk ks; MXFP4: bytes 8*ks + 4*fh .. +3
+    // of the row); rows of the wave's blocks share their low 5 bits, so one
     // offset per step serves every block (the rest are immediates)
     const int fr = lane & 31, fh = lane >> 5;
     const int arow0 = 128 * wm + fr;
@@ -779,10 +337,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big4(GemmArgs g) {
     for (int ks = 0; ks < 4; ++ks) {
         const int ch = 2 * ks + fh;
         aoffs[ks] = (arow0 * GBK + swz(arow0, ch) * 8) * 2;
-        boffs[ks] = (brow0 * GBK + swz(brow0, ch) * 8) * 2;
+        boffs[ks] = FP8   ? brow0 * GBK + swz8(brow0, ks) * 16 + fh * 8
+                    : FP4 ? brow0 * 32 + (((ks >> 1) ^ ((brow0 >> 3) & 1)) * 16) + ((8 * ks + 4 * fh) & 15)
+                          : (brow0 * GBK + swz(brow0, ch) * 8) * 2;
     }
+    // row offset of B block nj from brow0: SwiGLU gate rows (nj 0, 1), then
+    // the matching up rows
+    auto bdrow = [](int nj) constexpr { return SW ? (nj < 2 ? 0 : 128) + 32 * (nj & 1) : 32 * nj; };
+    // raw B fragment: bf16 values, 8 FP8 codes, or 8 E2M1 codes
+    using braw_t = std::conditional_t<FP8, u32x2_t, std::conditional_t<FP4, uint32_t, bf16x8_t>>;
     struct Frags {
-        bf16x8_t a[4], b[4];
+        bf16x8_t a[4];
+        braw_t b[4];
     };
     const int nact = min(max((tc.row1 - tc.row0 - wm * 128 + 31) / 32, 0), 4);
 
@@ -790,37 +356,83 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big4(GemmArgs g) {
         constexpr int NA = decltype(NAC)::value;
         constexpr int NR = NA > 0 ? 4 + NA : 0;  // fragment reads per step
         // fragment read i of a step, in the order the step's MFMAs first use
-        // them: A block 0, B blocks 0..3 (SwiGLU: gate rows, then the
-        // matching up rows), then A blocks 1..NA-1
+        // them: A block 0, B blocks 0..3, then A blocks 1..NA-1
         auto rd1 = [&](int as, int bs, int ks, Frags& f, int i) __attribute__((always_inline)) {
             if (i >= 1 && i <= 4) {
                 const int nj = i - 1;
-                const char* b = smem + B_RING + bs + boffs[ks];
-                const int bd = (SW ? ((nj < 2 ? 0 : 128) + 32 * (nj & 1)) : 32 * nj) * GBK * 2;
-                f.b[nj] = *(const bf16x8_t*)(b + bd);
+                const char* b = smem + B_RING + bs + boffs[ks] + bdrow(nj) * B_ROW;
+                f.b[nj] = *(const braw_t*)b;
             } else {
                 const int mi = i == 0 ? 0 : i - 4;
                 const char* a = smem + as + aoffs[ks];
                 f.a[mi] = *(const bf16x8_t*)(a + mi * 32 * GBK * 2);
             }
         };
-        // MFMA i of a step: block (i / 4, i % 4)
-        auto mf1 = [&](const Frags& f, int i) __attribute__((always_inline)) {
-            acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                f.a[i >> 2], f.b[i & 3], acc[i >> 2][i & 3], 0, 0, 0);
+        // MXFP4: the exponent dword of each B block's row (four blocks, two
+        // of which belong to the stage), read once per stage: stage 0's before
+        // the loop, stage kt+1's during stage kt's last step
+        uint32_t ex[4] = {0, 0, 0, 0};
+        auto rde = [&](int bs, int nj) __attribute__((always_inline)) {
+            ex[nj] = *(const uint32_t*)(smem + B_RING + bs + B_CODES + (brow0 + bdrow(nj)) * 4);
         };
-        // one DMA instruction (i of 8) of stage kt's A or B tile
+        // bf16 B operands of a step, converted where first used
+        bf16x8_t bc[4];
+        auto conv = [&](const Frags& f, int kt, int ks, int nj) __attribute__((always_inline)) {
+            if constexpr (FP8) {
+                bc[nj] = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(f.b[nj][0], f.b[nj][1]));
+            } else if constexpr (FP4) {
+                // block 2kt + ks/2 is byte 2*(kt & 1) + ks/2 of the dword
+                const uint32_t eb = (ex[nj] >> (8 * (2 * (kt & 1) + (ks >> 1)))) & 0xffu;
+                bc[nj] = __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16x8(f.b[nj], e8m0_scale(eb)));
+            }
+        };
+        // MFMA i of a step: block (i / 4, i % 4); the first four MFMAs
+        // convert the B fragment they introduce
+        auto mf1 = [&](const Frags& f, int kt, int ks, int i) __attribute__((always_inline)) {
+            if constexpr (FP8 || FP4) {
+                if (i < 4) conv(f, kt, ks, i);
+                acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    f.a[i >> 2], bc[i & 3], acc[i >> 2][i & 3], 0, 0, 0);
+            } else {
+                acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    f.a[i >> 2], f.b[i & 3], acc[i >> 2][i & 3], 0, 0, 0);
+            }
+        };
+        // one DMA instruction of stage kt's A or B tile
+        // (stage kt clamped to the last; the K segment picked with selects)
         auto da1 = [&](int as, int kt, int i) __attribute__((always_inline)) {
             char* dst = smem + as;
-            const uint32_t ko = (uint32_t)min(kt, nk - 1) * GBK * 2;
-            __builtin_amdgcn_global_load_lds((const void*)(Ab + (ao[i] + ko)),
-                                             (lds_ptr_t)(dst + (64 * wave + 8 * i) * GBK * 2), 16, 0, 0);
+            kt = min(kt, nk - 1);
+            const bool seg1 = !KCAT || kt < nk1;
+            const char* abase = seg1 ? Ab : A2b;
+            const uint32_t ko = (uint32_t)(seg1 ? kt : kt - nk1) * GBK * 2;
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(abase + ((seg1 ? ao[i] : ao2[KCAT ? i : 0]) + ko)),
+                (lds_ptr_t)(dst + (64 * wave + 8 * i) * GBK * 2), 16, 0, 0);
         };
         auto db1 = [&](int bs, int kt, int i) __attribute__((always_inline)) {
             char* dst = smem + B_RING + bs;
-            const uint32_t ko = (uint32_t)min(kt, nk - 1) * GBK * 2;
-            __builtin_amdgcn_global_load_lds((const void*)(Bb + (bo[i] + ko)),
-                                             (lds_ptr_t)(dst + (64 * wave + 8 * i) * GBK * 2), 16, 0, 0);
+            kt = min(kt, nk - 1);
+            if constexpr (FP8) {
+                __builtin_amdgcn_global_load_lds((const void*)(Bb + (bo[i] + (uint32_t)kt * GBK)),
+                                                 (lds_ptr_t)(dst + (64 * wave + 16 * i) * GBK), 16, 0, 0);
+            } else if constexpr (FP4) {
+                // the codes, then the exponent dword holding blocks 2kt, 2kt+1
+                // (K is a multiple of 128, so that dword is aligned and whole)
+                if (i < 2)
+                    __builtin_amdgcn_global_load_lds((const void*)(Bb + (bo[i] + (uint32_t)kt * 32)),
+                                                     (lds_ptr_t)(dst + (64 * wave + 32 * i) * 32), 16, 0, 0);
+                else
+                    __builtin_amdgcn_global_load_lds((const void*)(Sb + (bo[2] + (uint32_t)(kt >> 1) * 4)),
+                                                     (lds_ptr_t)(dst + B_CODES + 64 * wave * 4), 4, 0, 0);
+            } else {
+                const bool seg1 = !KCAT || kt < nk1;
+                const char* bbase = seg1 ? Bb : B2b;
+                const uint32_t ko = (uint32_t)(seg1 ? kt : kt - nk1) * GBK * 2;
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(bbase + ((seg1 ? bo[i] : bo2[KCAT ? i : 0]) + ko)),
+                    (lds_ptr_t)(dst + (64 * wave + 8 * i) * GBK * 2), 16, 0, 0);
+            }
         };
 
         // DMA issue order: prologue A0 B0 A1 B1; turn kt issues B_{kt+2}
@@ -828,20 +440,24 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big4(GemmArgs g) {
         // barrier that follows its third step.  Before the barrier of turn kt
         // (publishing stage kt+1) only B_{kt+2} may still be in flight.
 #pragma unroll
-        for (int i = 0; i < ND; ++i) da1(0, 0, i);
+        for (int i = 0; i < NDA; ++i) da1(0, 0, i);
 #pragma unroll
-        for (int i = 0; i < ND; ++i) db1(0, 0, i);
+        for (int i = 0; i < NDB; ++i) db1(0, 0, i);
 #pragma unroll
-        for (int i = 0; i < ND; ++i) da1(A_BYTES, 1, i);
+        for (int i = 0; i < NDA; ++i) da1(A_BYTES, 1, i);
 #pragma unroll
-        for (int i = 0; i < ND; ++i) db1(B_BYTES, 1, i);
-        wait_vmcnt_lgkm0<2 * ND>();
+        for (int i = 0; i < NDB; ++i) db1(B_BYTES, 1, i);
+        wait_vmcnt_lgkm0<NDA + NDB>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         Frags f0, f1;
         if constexpr (NA > 0) {
 #pragma unroll
             for (int i = 0; i < NR; ++i) rd1(0, 0, 0, f0, i);
+            if constexpr (FP4) {
+#pragma unroll
+                for (int nj = 0; nj < 4; ++nj) rde(0, nj);
+            }
         }
         // ring slots (byte offsets) of stages kt, kt+1 (A) and kt, kt+1,
         // kt+2 (B), rotated at the end of each turn
@@ -850,25 +466,29 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big4(GemmArgs g) {
             __builtin_amdgcn_sched_barrier(0);
             // step 0: MFMAs of f0, reads of step 1 and the B tile of kt+2,
             // one instruction after each MFMA
+            {
+                constexpr int NO = NR + NDB;
+                constexpr int N0 = NA * 4 > NO ? NA * 4 : NO;
 #pragma unroll
-            for (int i = 0; i < (NA * 4 > NR + ND ? NA * 4 : NR + ND); ++i) {
-                if (i < NA * 4) mf1(f0, i);
-                if (i < NR) rd1(sa0, sb0, 1, f1, i);
-                else if (i < NR + ND) db1(sb2, kt + 2, i - NR);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int i = 0; i < N0; ++i) {
+                    if (i < NA * 4) mf1(f0, kt, 0, i);
+                    if (i < NR) rd1(sa0, sb0, 1, f1, i);
+                    else if (i < NO) db1(sb2, kt + 2, i - NR);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             if constexpr (NA > 0) {
                 // steps 1 and 2 (a one-block wave has 4 MFMAs for 5 reads)
                 constexpr int N12 = NA * 4 > NR ? NA * 4 : NR;
 #pragma unroll
                 for (int i = 0; i < N12; ++i) {
-                    if (i < NA * 4) mf1(f1, i);
+                    if (i < NA * 4) mf1(f1, kt, 1, i);
                     if (i < NR) rd1(sa0, sb0, 2, f0, i);
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
                 for (int i = 0; i < N12; ++i) {
-                    if (i < NA * 4) mf1(f0, i);
+                    if (i < NA * 4) mf1(f0, kt, 2, i);
                     if (i < NR) rd1(sa0, sb0, 3, f1, i);
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -877,32 +497,48 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big4(GemmArgs g) {
             // stage kt+1 has landed for this wave and all its reads of stage
             // kt are retired; after the barrier stage kt+1 is visible and
             // stage kt's slots are free
-            wait_vmcnt_lgkm0<ND>();
+            wait_vmcnt_lgkm0<NDB>();
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            // step 3 with the reads of stage kt+1's step 0 and the A tile of
-            // kt+2 (at the last turn the reads take the clamped copy of the
-            // last stage: landed, never used)
+            // step 3 with the reads of stage kt+1's step 0 (and its
+            // exponents) and the A tile of kt+2 (at the last turn the reads
+            // take the clamped copy of the last stage: landed, never used)
             // (full waves: the A DMA after the even MFMAs, the reads after
             // the odd ones)
-            constexpr int M3 = NA * 4;
-            if constexpr (M3 >= 2 * NR && M3 >= 2 * ND) {
+            {
+                constexpr int M3 = NA * 4;
+                // step 3's conversions use this stage's exponents: keep them
+                // until its first four MFMAs have converted their fragments
+                uint32_t exn[4] = {0, 0, 0, 0};
+                auto rde3 = [&](int nj) __attribute__((always_inline)) {
+                    exn[nj] = *(const uint32_t*)(smem + B_RING + sb1 + B_CODES + (brow0 + bdrow(nj)) * 4);
+                };
+                constexpr int NE = FP4 && NA > 0 ? 4 : 0;
+                if constexpr (M3 >= 2 * (NR + NE) && M3 >= 2 * NDA) {
 #pragma unroll
-                for (int i = 0; i < M3; ++i) {
-                    mf1(f1, i);
-                    if ((i & 1) == 0 && (i >> 1) < ND) da1(sa0, kt + 2, i >> 1);
-                    if ((i & 1) == 1 && (i >> 1) < NR) rd1(sa1, sb1, 0, f0, i >> 1);
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int i = 0; i < M3; ++i) {
+                        mf1(f1, kt, 3, i);
+                        if ((i & 1) == 0 && (i >> 1) < NDA) da1(sa0, kt + 2, i >> 1);
+                        if ((i & 1) == 1 && (i >> 1) < NR) rd1(sa1, sb1, 0, f0, i >> 1);
+                        else if ((i & 1) == 1 && (i >> 1) < NR + NE) rde3((i >> 1) - NR);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                } else {
+                    constexpr int NO = NR + NE;
+                    constexpr int N3 = M3 > NO ? (M3 > NDA ? M3 : NDA) : (NO > NDA ? NO : NDA);
+#pragma unroll
+                    for (int i = 0; i < N3; ++i) {
+                        if (i < M3) mf1(f1, kt, 3, i);
+                        if (i < NR) rd1(sa1, sb1, 0, f0, i);
+                        else if (i < NO) rde3(i - NR);
+                        if (i < NDA) da1(sa0, kt + 2, i);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
-            } else {
-                constexpr int N3 = M3 > NR ? (M3 > ND ? M3 : ND) : (NR > ND ? NR : ND);
+                if constexpr (FP4) {
 #pragma unroll
-                for (int i = 0; i < N3; ++i) {
-                    if (i < M3) mf1(f1, i);
-                    if (i < NR) rd1(sa1, sb1, 0, f0, i);
-                    if (i < ND) da1(sa0, kt + 2, i);
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int nj = 0; nj < 4; ++nj) ex[nj] = exn[nj];
                 }
             }
             asm volatile("" ::: "memory");
@@ -919,6 +555,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big4(GemmArgs g) {
         // the trailing DMAs must land before the LDS is reused
         wait_vmcnt<0>();
         __syncthreads();
+        // FP8: the row scale of the weight row behind each block's column,
+        // applied as the sums are written out
+        float sn[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (FP8 && NA > 0) {
+            const float* sc = (const float*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride;
+#pragma unroll
+            for (int nj = 0; nj < 4; ++nj) sn[nj] = sc[wrow_of(brow0 + bdrow(nj))];
+        }
         if constexpr (NA > 0) {
         // epilogue through LDS, one 32-row block at a time; row stride 136
         // floats (the two halves of a wave write 4 rows apart: banks +32)
@@ -938,7 +582,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big4(GemmArgs g) {
                 for (int nj = 0; nj < 4; ++nj)
 #pragma unroll
                     for (int j = 0; j < 16; ++j)
-                        ep[(8 * (j >> 2) + 4 * fh + (j & 3)) * ELD + nj * 32 + fr] = acc[mi][nj][j];
+                        ep[(8 * (j >> 2) + 4 * fh + (j & 3)) * ELD + nj * 32 + fr] =
+                            FP8 ? acc[mi][nj][j] * sn[nj] : acc[mi][nj][j];
                 asm volatile("" ::: "memory");
                 const int rb = tc.row0 + wm * 128 + mi * 32;
 #pragma unroll
@@ -1105,45 +750,35 @@ __global__ __launch_bounds__(256) void gemm_f32_tiled(GemmArgs g) {
 
 template <bool KC>
 void launch_big(const GemmArgs& g, dim3 gd, hipStream_t s) {
-    const dim3 bd(512);
-    if (g.b_fmt == WF_FP8) {
-        // grouped expert products only: gate/up, and the down product's rows
-        if constexpr (!KC) {
-            switch (g.epi) {
-                case EPI_F16: gemm_bf16_big<EPI_F16, false, WF_FP8><<<gd, bd, 0, s>>>(g); break;
-                case EPI_F32: gemm_bf16_big<EPI_F32, false, WF_FP8><<<gd, bd, 0, s>>>(g); break;
-                default: gemm_bf16_big<EPI_SWIGLU, false, WF_FP8><<<gd, bd, 0, s>>>(g); break;
-            }
-        }
-        return;
-    }
-    if (g.b_fmt == WF_MXFP4) {
-        if constexpr (!KC) {
-            switch (g.epi) {
-                case EPI_F16: gemm_bf16_big<EPI_F16, false, WF_MXFP4><<<gd, bd, 0, s>>>(g); break;
-                case EPI_F32: gemm_bf16_big<EPI_F32, false, WF_MXFP4><<<gd, bd, 0, s>>>(g); break;
-                default: gemm_bf16_big<EPI_SWIGLU, false, WF_MXFP4><<<gd, bd, 0, s>>>(g); break;
-            }
-        }
-        return;
-    }
-    if constexpr (!KC) {
-        // bf16 weights, one K segment: 4 waves of 128x128
-        const dim3 b4(256);
+    const dim3 bd(256);
+    if constexpr (KC) {
+        // the K-concatenated dense product (no fp16 rows)
         switch (g.epi) {
-            case EPI_F16: gemm_bf16_big4<EPI_F16><<<gd, b4, 0, s>>>(g); break;
-            case EPI_F32: gemm_bf16_big4<EPI_F32><<<gd, b4, 0, s>>>(g); break;
-            case EPI_F32_BIAS: gemm_bf16_big4<EPI_F32_BIAS><<<gd, b4, 0, s>>>(g); break;
-            case EPI_OUT: gemm_bf16_big4<EPI_OUT><<<gd, b4, 0, s>>>(g); break;
-            default: gemm_bf16_big4<EPI_SWIGLU><<<gd, b4, 0, s>>>(g); break;
+            case EPI_F32: gemm_bf16_big4<EPI_F32, WF_BF16, true><<<gd, bd, 0, s>>>(g); break;
+            case EPI_F32_BIAS: gemm_bf16_big4<EPI_F32_BIAS, WF_BF16, true><<<gd, bd, 0, s>>>(g); break;
+            case EPI_OUT: gemm_bf16_big4<EPI_OUT, WF_BF16, true><<<gd, bd, 0, s>>>(g); break;
+            default: gemm_bf16_big4<EPI_SWIGLU, WF_BF16, true><<<gd, bd, 0, s>>>(g); break;
+        }
+    } else if (g.b_fmt == WF_FP8) {
+        // grouped expert products only: gate/up, and the down product's rows
+        switch (g.epi) {
+            case EPI_F16: gemm_bf16_big4<EPI_F16, WF_FP8, false><<<gd, bd, 0, s>>>(g); break;
+            case EPI_F32: gemm_bf16_big4<EPI_F32, WF_FP8, false><<<gd, bd, 0, s>>>(g); break;
+            default: gemm_bf16_big4<EPI_SWIGLU, WF_FP8, false><<<gd, bd, 0, s>>>(g); break;
+        }
+    } else if (g.b_fmt == WF_MXFP4) {
+        switch (g.epi) {
+            case EPI_F16: gemm_bf16_big4<EPI_F16, WF_MXFP4, false><<<gd, bd, 0, s>>>(g); break;
+            case EPI_F32: gemm_bf16_big4<EPI_F32, WF_MXFP4, false><<<gd, bd, 0, s>>>(g); break;
+            default: gemm_bf16_big4<EPI_SWIGLU, WF_MXFP4, false><<<gd, bd, 0, s>>>(g); break;
         }
     } else {
-        // the K-concatenated form (dense, no fp16 rows) keeps 8 waves
         switch (g.epi) {
-            case EPI_F32: gemm_bf16_big<EPI_F32, true, WF_BF16><<<gd, bd, 0, s>>>(g); break;
-            case EPI_F32_BIAS: gemm_bf16_big<EPI_F32_BIAS, true, WF_BF16><<<gd, bd, 0, s>>>(g); break;
-            case EPI_OUT: gemm_bf16_big<EPI_OUT, true, WF_BF16><<<gd, bd, 0, s>>>(g); break;
-            default: gemm_bf16_big<EPI_SWIGLU, true, WF_BF16><<<gd, bd, 0, s>>>(g); break;
+            case EPI_F16: gemm_bf16_big4<EPI_F16, WF_BF16, false><<<gd, bd, 0, s>>>(g); break;
+            case EPI_F32: gemm_bf16_big4<EPI_F32, WF_BF16, false><<<gd, bd, 0, s>>>(g); break;
+            case EPI_F32_BIAS: gemm_bf16_big4<EPI_F32_BIAS, WF_BF16, false><<<gd, bd, 0, s>>>(g); break;
+            case EPI_OUT: gemm_bf16_big4<EPI_OUT, WF_BF16, false><<<gd, bd, 0, s>>>(g); break;
+            default: gemm_bf16_big4<EPI_SWIGLU, WF_BF16, false><<<gd, bd, 0, s>>>(g); break;
         }
     }
 }
