@@ -106,6 +106,13 @@ def layer_work(w, counts):
 # committed counter summary applies while their hash matches.
 STREAM_KERNEL_SOURCES = ("gemm_stream.hip", "gemm_tiles.h", "common.h")
 
+# The decode gate/up + SwiGLU kernel for each expert weight format
+# (template arguments: epilogue, K-concatenated, weight format, exponent
+# vectors, waves per workgroup, column tiles per workgroup).
+STREAM_GATE_UP = {"dtype": "gemm_bf16_stream<3, false, 0, false, 8, 1>",
+                  "fp8_e4m3": "gemm_bf16_stream<3, false, 1, false, 8, 1>",
+                  "mxfp4": "gemm_bf16_stream<3, false, 2, true, 8, 1>"}
+
 
 def profiled_traffic(workload: str):
     """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
@@ -400,7 +407,7 @@ def main():
                    "parallelism": "none (1 GPU holds all experts)"},
         "roofline": {"bound": "hbm", "achieved": g1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": g1_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": ("gate/up + SwiGLU stage: gemm_bf16_stream<3, false, 0, false, 8> (at "
+                     "kernel": (f"gate/up + SwiGLU stage: {STREAM_GATE_UP[w.weights]} (at "
                                 "128 tokens every expert's rows, in 64-row tiles)" if w.T <= 128 else
                                 "gate/up + SwiGLU stage (both expert chains)"),
                      "kernel_ms": g1_ms, "algorithmic_bytes": g1b},
@@ -457,7 +464,7 @@ def main():
             "value": wf.T / (fms * 1e-3), "unit": "tokens/s", "ms_per_step": fms,
             "step_ms": frun.step_stats,
             "steps": args.steps, "hbm_frac": fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "gemm1": {"kernel": "gemm_bf16_stream<3, false, 1, false, 8>", "kernel_ms": fstage["gemm1"],
+            "gemm1": {"kernel": STREAM_GATE_UP["fp8_e4m3"], "kernel_ms": fstage["gemm1"],
                       "algorithmic_bytes": f1b, "achieved_GBps": f1, "frac": f1 / HBM_PEAK_GBS,
                       "traffic": profiled_traffic(wf.name)},
             "stages_ms": fstage}
@@ -504,7 +511,7 @@ def main():
             "value": wm.T / (mms * 1e-3), "unit": "tokens/s", "ms_per_step": mms,
             "step_ms": mrun.step_stats,
             "steps": args.steps, "hbm_frac": mbytes / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "gemm1": {"kernel": "gemm_bf16_stream<3, false, 2, true, 8>", "kernel_ms": mstage["gemm1"],
+            "gemm1": {"kernel": STREAM_GATE_UP["mxfp4"], "kernel_ms": mstage["gemm1"],
                       "algorithmic_bytes": m1b, "achieved_GBps": m1, "frac": m1 / HBM_PEAK_GBS,
                       "traffic": profiled_traffic(wm.name)},
             "stages_ms": mstage}

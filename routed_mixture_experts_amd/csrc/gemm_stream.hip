@@ -230,7 +230,12 @@ int stream_col_tiles_nw(int epi, int N, int nw) {
 // 64-deep block takes k 16*g4 .. +15, its first 8 for the even step and the
 // rest for the odd one.  With MXFP4 weights (OCP E2M1 codes, two per byte,
 // one E8M0 exponent per 32 codes of a row) a 16-byte load holds 32 codes --
-// one scale block -- i.e. four k-steps: lane g4 of a 128-deep block takes k
+// one scale block -- i.e. four k-steps.  K a multiple of 512: two loads
+// take the 128 bytes of a 256-deep block of the wave's 16 rows as whole
+// cache lines (8 rows each, 8 lanes a row), and a lane exchange gives lane
+// l of row l % 16 the 64 codes k = 64*g4 .. +63 of the block, 8 per step
+// (the memory instructions and cache lines of this stream, rather than its
+// bytes, set its pace).  Otherwise lane g4 of a 128-deep block takes k
 // 32*g4 .. +31, 8 per step, and the 4 block exponents of a load unit come
 // in one dword beside it.  The token operand is staged with the same k order
 // as the weights, the codes become bf16 exactly in registers (MXFP4: with
@@ -246,7 +251,7 @@ int stream_col_tiles_nw(int epi, int N, int nw) {
 // output rows past the tile's end, which are never stored.  At decode most
 // groups have at most 4 rows, and the token loads then take a quarter of
 // the load slots.
-template <int EPI, int NB, bool KCAT, int WF, bool SV, int NW, int QF>
+template <int EPI, int NB, bool KCAT, int WF, bool SV, int NW, int QF, int NT>
 __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCoord& tc,
                                                  char* xs) {
     constexpr bool SW = EPI == EPI_SWIGLU;
@@ -269,6 +274,10 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     static_assert(QF == 1 || (NB == 1 && !KCAT && CS % QF == 0 && TL <= NW), "token packing");
     static_assert(2 * CHUNK <= sx_bytes<NW>() && CS % UNIT == 0 && TU % PD == 0 && XI % NB == 0,
                   "stream tiling");
+    // NT > 1 (MXFP4 with K a multiple of 1024 and N of SRS): NT column tiles
+    // in a row, each a whole number of ring turns
+    static_assert(NT == 1 || (FP4 && SV && RC > 1), "column tiles per workgroup");
+    constexpr int SRS = SW ? SRN / 2 : SRN;  // weight rows from one column tile to the next
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -290,6 +299,27 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
         wrow = min(tc.nt * SRN + wave * 16 + l16, g.N - 1);
     }
     const uint32_t wo = (uint32_t)(wrow * wrow_bytes) + g4 * 16;
+    // MXFP4 with K a multiple of 512 (PL): a load pair covers 128 bytes (256
+    // codes, 8 k-steps) of the wave's 16 rows as whole cache lines: the even
+    // unit of the pair rows 0-7, the odd one rows 8-15, each row read by 8
+    // lanes (lane l: row l % 8, bytes 16 * (l / 8) ..).  wpo[p] is the offset
+    // of unit parity p less p * 64, so that unit u sits at wpo[u & 1] + 64 u.
+    constexpr bool PL = FP4 && SV;
+    uint32_t wpo[2] = {0u, 0u};
+    if constexpr (PL) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int x = p * 8 + (lane & 7);  // wave row
+            int rr;
+            if (SW) {
+                const int c = min(tc.nt * (SRN / 2) + wave * 8 + (x & 7), g.N - 1);
+                rr = x < 8 ? c : g.N + c;
+            } else {
+                rr = min(tc.nt * SRN + wave * 16 + x, g.N - 1);
+            }
+            wpo[p] = (uint32_t)(rr * wrow_bytes) + 16 * (lane >> 3) - (uint32_t)(p * 64);
+        }
+    }
     const uint32_t wo2 = KCAT ? (uint32_t)((int64_t)wrow * g.K2 * 2) + g4 * 16 : 0u;
     // MXFP4 block exponents of this row: K / 32 bytes, 4 per load unit
     const char* Sb = FP4 ? (const char*)g.b_scale + tc.group * g.b_scale_gstride +
@@ -301,13 +331,14 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
             const int r = min(tc.row0 + tb * 16 + l16, tc.row1 - 1);
-            xo[tb] = (uint32_t)(a_row_of(g, r) * g.lda * 2) + g4 * (FP4 ? 64 : FP8 ? 32 : 16);
+            xo[tb] = (uint32_t)(a_row_of(g, r) * g.lda * 2) +
+                     g4 * (PL ? 128 : FP4 ? 64 : FP8 ? 32 : 16);
             xo2[tb] = KCAT ? (uint32_t)((int64_t)r * g.lda2 * 2) + g4 * 16 : 0u;
         }
     } else {
         const int r = min(tc.row0 + lane % RB, tc.row1 - 1);
         xo[0] = (uint32_t)(a_row_of(g, r) * g.lda * 2) +
-                ((lane / RB) & 3) * (FP4 ? 64 : FP8 ? 32 : 16);
+                ((lane / RB) & 3) * (PL ? 128 : FP4 ? 64 : FP8 ? 32 : 16);
         xo2[0] = 0u;
     }
 
@@ -315,7 +346,27 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     const int ns = ns1 + (KCAT ? g.K2 / 32 : 0);
     const int nch = (ns + CS - 1) / CS;
     const int nu = ns / UNIT;  // weight load units
-    uint32_t sxn[FP4 ? UPC : 1], sxc[FP4 ? UPC : 1];  // MXFP4 exponents: next / current chunk
+    // MXFP4 block exponents, one dword per load unit.  K a multiple of 512:
+    // they come in groups of 8 units (32 bytes of each row), one ring turn
+    // and one loop pass, lane (row i, q) holding units 2 q and 2 q + 1 of
+    // the group: one 8-byte load per wave for 8 units rather than a 16-byte
+    // one for each chunk's 4, since the count of memory instructions and of
+    // cache lines, not bytes, is what holds this stream back.  The group in
+    // use (egc) is handed to the lanes that need it with ds_bpermute when a
+    // chunk starts (bsc: the chunk's block scales for this lane); the next
+    // one (egn) is requested when a pass starts, as far ahead as the
+    // weights.  Otherwise (sxn, sxc) a chunk's exponent dwords travel with
+    // its token rows, one chunk ahead, byte g4 of dword j for this lane.
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    uint32_t sxn[FP4 && !SV ? UPC : 1], sxc[FP4 && !SV ? UPC : 1];
+    u32x2_t egc = u32x2_t{0u, 0u}, egn = egc;
+    float bsc[FP4 && SV ? UPC : 1];
+    // NT > 1: unit u of the workgroup's stream is unit u - t * nu of column
+    // tile t, whose rows lie SRS * t rows on; since a row is nu units of 64
+    // bytes, its address is the tile-0 address of unit u shifted by
+    // t * (SRS - 1) rows.  Exponent rows move SRS * K / 32 bytes per tile.
+    const uint32_t tstep = NT > 1 ? (uint32_t)((SRS - 1) * wrow_bytes) : 0u;
+    const uint32_t xstep = NT > 1 ? (uint32_t)(SRS * (g.K / 32)) : 0u;
 
     // Token chunk c lives in LDS buffer c & 1 as 1 KB blocks b = (k-step
     // b / NB, 16-row block b % NB), each in MFMA operand order (lane l holds
@@ -326,11 +377,13 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     // byte offset of step st's 8 elements for a lane (the k order of the
     // weight loads; the lane's g4 part is in xo)
     auto step_off = [&](int st) __attribute__((always_inline)) {
-        return FP4   ? (uint32_t)(st >> 2) * 256 + (uint32_t)(st & 3) * 16
+        return PL    ? (uint32_t)(st >> 3) * 512 + (uint32_t)(st & 7) * 16
+               : FP4 ? (uint32_t)(st >> 2) * 256 + (uint32_t)(st & 3) * 16
                : FP8 ? (uint32_t)(st >> 1) * 128 + (uint32_t)(st & 1) * 16
                      : (uint32_t)st * 64;
     };
-    auto load_x = [&](int c) __attribute__((always_inline)) {
+    // chunk c of column tile xt (tokens do not depend on the tile)
+    auto load_x = [&](int c, int xt) __attribute__((always_inline)) {
         if constexpr (QF > 1) {
             if (wave < TL) {
                 const int st = min(c * CS + wave * QF + lane / (4 * RB), ns - 1);
@@ -348,36 +401,29 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
                 xr[i] = *(const u32x4_t*)src;
             }
         }
-        // MXFP4: the block exponents of the chunk's UPC load units travel
-        // with its tokens (one dword per unit, byte g4 for this lane), so
-        // every weight load unit is a single load
-        if constexpr (FP4 && SV) {
-            // K a multiple of 512: the chunk's UPC exponent dwords are one
-            // aligned vector of the row (chunks past the end re-read the last)
-            const int cl = min(c, nu / UPC - 1);
-            static_assert(UPC == 4 || UPC == 2, "exponent vector of a chunk");
-            if constexpr (UPC == 4) {
-                const u32x4_t v4 = *(const u32x4_t*)(Sb + 16 * cl);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sxn[j] = v4[j];
-            } else {
-                typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-                const u32x2_t v2 = *(const u32x2_t*)(Sb + 8 * cl);
-                sxn[0] = v2[0];
-                sxn[1] = v2[1];
-            }
-        } else if constexpr (FP4) {
+        // MXFP4, K not a multiple of 512: the chunk's exponent dwords
+        if constexpr (FP4 && !SV) {
 #pragma unroll
             for (int j = 0; j < UPC; ++j)
                 sxn[j] = *(const uint32_t*)(Sb + 4 * min(c * UPC + j, nu - 1));
         }
     };
-    auto store_x = [&](int c) __attribute__((always_inline)) {
+    // MXFP4, K a multiple of 512: exponent group gi of column tile xt into
+    // egn (units past the row's end re-read its last 2)
+    auto load_eg = [&](int gi, int xt) __attribute__((always_inline)) {
+        if constexpr (FP4 && SV) {
+            static_assert(UPC * RC == 8 && PD == 8, "one exponent group per pass");
+            const int u0 = min(8 * gi + 2 * g4, nu - 2);
+            egn = *(const u32x2_t*)(Sb + (NT > 1 ? xt * xstep : 0u) + 4 * u0);
+        }
+    };
+    // into LDS buffer c & 1; cl is the chunk's place in its column tile
+    auto store_x = [&](int c, int cl) __attribute__((always_inline)) {
         if constexpr (QF > 1) {
             if (wave < TL) {
                 const int sl = wave * QF + lane / (4 * RB);  // step within the chunk
                 const int p = lane % RB + 16 * ((lane / RB) & 3);  // its operand lane
-                if (QW && c * CS + sl >= ns) xr[0] = u32x4_t{0u, 0u, 0u, 0u};
+                if (QW && cl * CS + sl >= ns) xr[0] = u32x4_t{0u, 0u, 0u, 0u};
                 *(u32x4_t*)(xs + (c & 1) * CHUNK + sl * 1024 + p * 16) = xr[0];
             }
         } else {
@@ -386,19 +432,29 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
             for (int i = 0; i < XI; ++i) {
                 // FP8 / MXFP4: steps past K get zero tokens (once per chunk,
                 // in place of a select per step on the converted weights)
-                if (QW && c * CS + (wave * XI + i) / NB >= ns)
+                if (QW && cl * CS + (wave * XI + i) / NB >= ns)
                     xr[i] = u32x4_t{0u, 0u, 0u, 0u};
                 *(u32x4_t*)(dst + (wave * XI + i) * 1024) = xr[i];
             }
         }
-        if constexpr (FP4) {
+        if constexpr (FP4 && !SV) {
 #pragma unroll
             for (int j = 0; j < UPC; ++j) sxc[j] = sxn[j];
         }
     };
+    // NT > 1: loads run at most PD <= nu units ahead, so unit u lies in the
+    // tile of the MFMAs (shift wsh) or the next one (from unit wu_end on)
+    int wu_end = nu;
+    uint32_t wsh = 0u, wsh_next = tstep;
     // weight load unit u covers k-steps UNIT*u .. +UNIT-1, 64 bytes of the row
     auto load_w = [&](int u) __attribute__((always_inline)) {
+        if constexpr (NT > 1) {
+            u = min(u, NT * nu - 1);
+            const uint32_t sh = u >= wu_end ? wsh_next : wsh;
+            return *(const u32x4_t*)(Bb + (wpo[u & 1] + sh + (uint32_t)u * 64));
+        }
         u = min(u, nu - 1);
+        if constexpr (PL) return *(const u32x4_t*)(Bb + (wpo[u & 1] + (uint32_t)u * 64));
         const bool seg1 = !KCAT || u < ns1;
         const char* src = seg1 ? Bb + (wo + (uint32_t)u * 64)
                                : B2b + (wo2 + (uint32_t)(u - ns1) * 64);
@@ -418,15 +474,20 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     // the store of chunk c + 1 the token loads are followed by exactly the
     // weight loads of chunk c: the compiler's wait for the token registers
     // then leaves the newest weight loads in flight.
-    load_x(0);
+    load_x(0, 0);
+    load_eg(0, 0);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int v = 0; v < PD; ++v) w[v] = load_w(v);
     asm volatile("" ::: "memory");
-    store_x(0);
+    store_x(0, 0);
     asm volatile("" ::: "memory");
-    load_x(1);
+    load_x(1, 0);  // NT > 1 has nch >= RC >= 2
     asm volatile("" ::: "memory");
+    // NT > 1: the place in its tile of the chunk loaded but not stored, and
+    // the place xl2 in tile xt2 of the next chunk to load
+    int xs1 = 1, xl2 = 2, xt2 = 0;
+    if (NT > 1 && xl2 == nch) xl2 = 0, xt2 = 1;
 
     // Chunk c starts once this wave's LDS writes of chunk c are done, and
     // its LDS reads of chunk c - 1; after the barrier every wave's part of
@@ -441,6 +502,55 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     // Load unit j of chunk c, held in ring slot v: its UNIT k-steps against
     // every token block, then the refill of the slot PD units ahead.
     auto unit = [&](int c, const char* xc, int j, int v) __attribute__((always_inline)) {
+        if constexpr (PL) {
+            // a load pair is used with its odd unit: lanes l and l ^ 8 hold
+            // the two halves of the lines of row l % 8 (even unit) and of row
+            // 8 + l % 8 (odd unit); one row-rotate by 8 and three selects per
+            // dword give lane l (row l % 16) its 32 codes a (bytes 32 q ..,
+            // q = l / 16, of the row's 128) and the next 32, b.  Step h of
+            // the 8 takes codes 8 h .. of the 64.
+            if (j & 1) {
+                const int va = v - 1, ja = j - 1;
+                const bool lo = (lane & 8) == 0;
+                u32x4_t wa, wb;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t sv = lo ? w[v][d] : w[va][d];
+                    const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(
+                        0, (int)sv, 0x128 /* row_ror:8 */, 0xf, 0xf, false);
+                    wa[d] = lo ? w[va][d] : t;
+                    wb[d] = lo ? t : w[v][d];
+                }
+                w[va] = load_w(c * UPC + ja + PD);
+                w[v] = load_w(c * UPC + j + PD);
+                asm volatile("" ::: "memory");
+                constexpr int XG = 4 / NB;
+#pragma unroll
+                for (int h0 = 0; h0 < 2 * UNIT; h0 += XG) {
+                    u32x4_t xv[XG][NB];
+#pragma unroll
+                    for (int hh = 0; hh < XG; ++hh)
+#pragma unroll
+                        for (int tb = 0; tb < NB; ++tb)
+                            xv[hh][tb] = *(const u32x4_t*)(xc + ((ja * UNIT + h0 + hh) * NB + tb) *
+                                                                   1024);
+#pragma unroll
+                    for (int hh = 0; hh < XG; ++hh) {
+                        const int h = h0 + hh;
+                        const bf16x8_t wf = __builtin_bit_cast(
+                            bf16x8_t, fp4x8_to_bf16x8(h < 4 ? wa[h] : wb[h - 4],
+                                                      bsc[ja + (h >= 4)]));
+#pragma unroll
+                        for (int tb = 0; tb < NB; ++tb) {
+                            f32x4_t& a = NACC == 2 && (hh & 1) ? acc2[tb] : acc[tb];
+                            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                wf, __builtin_bit_cast(bf16x8_t, xv[hh][tb]), a, 0, 0, 0);
+                        }
+                    }
+                }
+            }
+            return;
+        }
         if constexpr (FP4) {
             // token fragments 4 at a time (XG steps of NB blocks) ahead of
             // their MFMAs, so their LDS latency overlaps; zero tokens
@@ -498,10 +608,83 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     // touch the idle buffer, which keeps this branch-free
     auto chunk_end = [&](int c) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
-        store_x(c + 1);
+        store_x(c + 1, NT > 1 ? xs1 : c + 1);
         asm volatile("" ::: "memory");
-        load_x(c + 2);
+        if constexpr (NT > 1) {
+            // past the last tile: in-bounds re-reads into the idle buffer
+            load_x(xl2, xt2);
+            xs1 = xl2;
+            if (++xl2 == nch) xl2 = 0, xt2 = min(xt2 + 1, NT - 1);
+        } else {
+            load_x(c + 2, 0);
+        }
         asm volatile("" ::: "memory");
+    };
+
+    // Stores column tile nt of the output from acc (+ acc2).
+    auto epilogue = [&](int nt) __attribute__((always_inline)) {
+        if constexpr (NACC == 2) {
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) acc[tb] += acc2[tb];
+        }
+
+        // row scales of FP8 weights, for the 4 weight rows this lane's sums belong to
+        float rs[4] = {1.f, 1.f, 1.f, 1.f};
+        if (FP8) {
+            const float* sc = (const float*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                int n;
+                if (SW) {
+                    const int hc = min(nt * (SRN / 2) + wave * 8 + (g4 & 1) * 4 + j, g.N - 1);
+                    n = g4 < 2 ? hc : g.N + hc;
+                } else {
+                    n = min(nt * SRN + wave * 16 + g4 * 4 + j, g.N - 1);
+                }
+                rs[j] = sc[n];
+            }
+        }
+
+        // acc[tb][j] = C[weight row 4*g4 + j of this wave][token 16*tb + l16]
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+            const int r = tc.row0 + tb * 16 + l16;
+            if (SW) {
+                // lanes 32..63 hold the up rows of lane - 32's gate rows
+                float up[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) up[j] = __shfl_xor(acc[tb][j] * rs[j], 32);
+                if (g4 < 2 && r < tc.row1) {
+                    bf16_t* crow = (bf16_t*)g.C + (int64_t)r * g.ldc;
+                    const int hc0 = nt * (SRN / 2) + wave * 8 + g4 * 4;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (hc0 + j < g.N)
+                            crow[hc0 + j] = f32_to_bf16(glu_f32(acc[tb][j] * rs[j], up[j], g));
+                }
+            } else if (EPI == EPI_F16) {
+                // four consecutive fp16 columns in one 8-byte store (N and the
+                // column base are multiples of 4, so they are all in range or none)
+                const int c0 = nt * SRN + wave * 16 + g4 * 4;
+                if (r < tc.row1 && c0 < g.N)
+                    *(uint2*)((uint16_t*)g.C + (int64_t)r * g.ldc + c0) =
+                        make_uint2(pack_f16x2(acc[tb][0] * rs[0], acc[tb][1] * rs[1]),
+                                   pack_f16x2(acc[tb][2] * rs[2], acc[tb][3] * rs[3]));
+            } else if (r < tc.row1) {
+                const int c0 = nt * SRN + wave * 16 + g4 * 4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = c0 + j;
+                    if (c >= g.N) continue;
+                    float o = acc[tb][j] * rs[j];
+                    if (EPI == EPI_F32_BIAS && g.bias) o += g.bias[c];
+                    if (EPI == EPI_OUT)
+                        ((bf16_t*)g.C)[(int64_t)r * g.ldc + c] = f32_to_bf16(o);
+                    else
+                        ((float*)g.C)[(int64_t)r * g.ldc + c] = o;
+                }
+            }
+        }
     };
 
     if constexpr (RC == 1) {
@@ -519,129 +702,132 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
         // once (unit c * UPC + j of chunk c = c0 + r sits in slot r * UPC + j).
         // Chunks past the end (when RC does not divide nch) multiply zero
         // weights and stage clamped, in-bounds token steps.
-        for (int c0 = 0; c0 < nch; c0 += RC) {
+        // NT > 1: when a tile's last chunk is done, its sums are stored
+        // and cleared while the loads of the next tile are in flight
+        int tile = 0, tleft = nch;
+        for (int c0 = 0; c0 < NT * nch; c0 += RC) {
+            if constexpr (FP4 && SV) {
+                // this pass's exponent group comes into use; the next pass's
+                // (the next group of the tile, or the next tile's first)
+                egc = egn;
+                if (NT > 1 && tleft == RC) load_eg(0, min(tile + 1, NT - 1));
+                else load_eg((NT > 1 ? nch - tleft : c0) / RC + 1, tile);
+                asm volatile("" ::: "memory");
+            }
 #pragma unroll
             for (int r = 0; r < RC; ++r) {
                 const int c = c0 + r;
                 const char* xc = chunk_begin(c);
+                if constexpr (FP4 && SV) {
+                    // pair pp of the chunk, units 2 pp and 2 pp + 1 of it
+                    // (blocks 0-3 and 4-7 of its 128 bytes per row), is pair
+                    // k = r * UPC / 2 + pp of the group, held by lane (i, k);
+                    // this lane's codes a and b are blocks 2 q and 2 q + 1
+#pragma unroll
+                    for (int pp = 0; pp < UPC / 2; ++pp) {
+                        const int src = (l16 + 16 * (r * UPC / 2 + pp)) * 4;
+                        const uint32_t d0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)egc[0]);
+                        const uint32_t d1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)egc[1]);
+                        const uint32_t d = g4 < 2 ? d0 : d1;
+                        const uint32_t sh = 16 * (g4 & 1);
+                        bsc[2 * pp] = e8m0_scale((d >> sh) & 0xffu);
+                        bsc[2 * pp + 1] = e8m0_scale((d >> (sh + 8)) & 0xffu);
+                    }
+                    asm volatile("" ::: "memory");
+                }
 #pragma unroll
                 for (int j = 0; j < UPC; ++j) unit(c, xc, j, r * UPC + j);
                 chunk_end(c);
             }
-        }
-    }
-
-    if constexpr (NACC == 2) {
+            if constexpr (NT > 1) {
+                tleft -= RC;
+                if (tleft == 0 && tile < NT - 1) {
+                    epilogue(tc.nt + tile);
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb) acc[tb] += acc2[tb];
-    }
-
-    // row scales of FP8 weights, for the 4 weight rows this lane's sums belong to
-    float rs[4] = {1.f, 1.f, 1.f, 1.f};
-    if (FP8) {
-        const float* sc = (const float*)g.b_scale + (int64_t)tc.group * g.b_scale_gstride;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int n;
-            if (SW) {
-                const int hc = min(tc.nt * (SRN / 2) + wave * 8 + (g4 & 1) * 4 + j, g.N - 1);
-                n = g4 < 2 ? hc : g.N + hc;
-            } else {
-                n = min(tc.nt * SRN + wave * 16 + g4 * 4 + j, g.N - 1);
-            }
-            rs[j] = sc[n];
-        }
-    }
-
-    // acc[tb][j] = C[weight row 4*g4 + j of this wave][token 16*tb + l16]
-#pragma unroll
-    for (int tb = 0; tb < NB; ++tb) {
-        const int r = tc.row0 + tb * 16 + l16;
-        if (SW) {
-            // lanes 32..63 hold the up rows of lane - 32's gate rows
-            float up[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) up[j] = __shfl_xor(acc[tb][j] * rs[j], 32);
-            if (g4 < 2 && r < tc.row1) {
-                bf16_t* crow = (bf16_t*)g.C + (int64_t)r * g.ldc;
-                const int hc0 = tc.nt * (SRN / 2) + wave * 8 + g4 * 4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (hc0 + j < g.N)
-                        crow[hc0 + j] = f32_to_bf16(glu_f32(acc[tb][j] * rs[j], up[j], g));
-            }
-        } else if (EPI == EPI_F16) {
-            // four consecutive fp16 columns in one 8-byte store (N and the
-            // column base are multiples of 4, so they are all in range or none)
-            const int c0 = tc.nt * SRN + wave * 16 + g4 * 4;
-            if (r < tc.row1 && c0 < g.N)
-                *(uint2*)((uint16_t*)g.C + (int64_t)r * g.ldc + c0) =
-                    make_uint2(pack_f16x2(acc[tb][0] * rs[0], acc[tb][1] * rs[1]),
-                               pack_f16x2(acc[tb][2] * rs[2], acc[tb][3] * rs[3]));
-        } else if (r < tc.row1) {
-            const int c0 = tc.nt * SRN + wave * 16 + g4 * 4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = c0 + j;
-                if (c >= g.N) continue;
-                float o = acc[tb][j] * rs[j];
-                if (EPI == EPI_F32_BIAS && g.bias) o += g.bias[c];
-                if (EPI == EPI_OUT)
-                    ((bf16_t*)g.C)[(int64_t)r * g.ldc + c] = f32_to_bf16(o);
-                else
-                    ((float*)g.C)[(int64_t)r * g.ldc + c] = o;
+                    for (int tb = 0; tb < NB; ++tb) acc[tb] = acc2[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    ++tile;
+                    tleft = nch;
+                    wsh = wsh_next;
+                    wsh_next += tstep;
+                    wu_end += nu;
+                }
             }
         }
+        epilogue(tc.nt + tile);
+        return;
     }
+    epilogue(tc.nt);
 }
 
 // Grouped tiles here hold one whole group of at most 64 rows; dense products
 // are cut into 16-row tiles.
-// SV (MXFP4 with K a multiple of 512): block exponents in vector loads.
-template <int EPI, bool KCAT, int WF, bool SV, int NW>
+// SV (MXFP4 with K a multiple of 512): whole-line weight loads and exponent
+// groups.
+// NT: column tiles per workgroup, streamed back to back (ntn a multiple of NT).
+template <int EPI, bool KCAT, int WF, bool SV, int NW, int NT>
 __global__ __launch_bounds__(64 * NW, 4) void gemm_bf16_stream(GemmArgs g) {
     constexpr bool SW = EPI == EPI_SWIGLU;
     constexpr int SRN = 16 * NW;
     const int ntn = SW ? (g.N + SRN / 2 - 1) / (SRN / 2) : (g.N + SRN - 1) / SRN;
     TileCoord tc;
-    if (!fetch_tile(g, SROWS, ntn, tc)) return;
+    if (!fetch_tile(g, SROWS, ntn / NT, tc)) return;
+    tc.nt *= NT;
     __shared__ __attribute__((aligned(1024))) char xs[sx_bytes<NW>()];
     const int rows = tc.row1 - tc.row0;
     // (not with FP8 weights, whose register budget the packed forms push
     // into spills inside the 2-block loop)
     if constexpr (!KCAT && WF != WF_FP8) {
         if (rows <= 4) {
-            stream_rows_tile<EPI, 1, KCAT, WF, SV, NW, 4>(g, tc, xs);
+            stream_rows_tile<EPI, 1, KCAT, WF, SV, NW, 4, NT>(g, tc, xs);
             return;
         }
         if (rows <= 8) {
-            stream_rows_tile<EPI, 1, KCAT, WF, SV, NW, 2>(g, tc, xs);
+            stream_rows_tile<EPI, 1, KCAT, WF, SV, NW, 2, NT>(g, tc, xs);
             return;
         }
     }
-    if (rows <= 16) stream_rows_tile<EPI, 1, KCAT, WF, SV, NW, 1>(g, tc, xs);
-    else if (rows <= 32) stream_rows_tile<EPI, 2, KCAT, WF, SV, NW, 1>(g, tc, xs);
-    else stream_rows_tile<EPI, 4, KCAT, WF, SV, NW, 1>(g, tc, xs);
+    if (rows <= 16) stream_rows_tile<EPI, 1, KCAT, WF, SV, NW, 1, NT>(g, tc, xs);
+    else if (rows <= 32) stream_rows_tile<EPI, 2, KCAT, WF, SV, NW, 1, NT>(g, tc, xs);
+    else stream_rows_tile<EPI, 4, KCAT, WF, SV, NW, 1, NT>(g, tc, xs);
 }
 
 // Dense products with fewer workgroups than this split K over the waves.
 constexpr int64_t kStreamRowsMinGrid = 1024;
 
-template <bool KC, int WF, bool SV, int NW>
+template <bool KC, int WF, bool SV, int NW, int NT = 1>
 void launch_stream_rows(const GemmArgs& g, int nm, hipStream_t s) {
-    const dim3 gd((unsigned)((int64_t)nm * stream_col_tiles_nw(g.epi, g.N, NW))), bd(64 * NW);
-    switch (g.epi) {
-        case EPI_F16:
-            // grouped expert rows only (never a K-concatenated product)
-            if constexpr (!KC) gemm_bf16_stream<EPI_F16, KC, WF, SV, NW><<<gd, bd, 0, s>>>(g);
-            break;
-        case EPI_F32: gemm_bf16_stream<EPI_F32, KC, WF, SV, NW><<<gd, bd, 0, s>>>(g); break;
-        case EPI_F32_BIAS:
-            gemm_bf16_stream<EPI_F32_BIAS, KC, WF, SV, NW><<<gd, bd, 0, s>>>(g);
-            break;
-        case EPI_OUT: gemm_bf16_stream<EPI_OUT, KC, WF, SV, NW><<<gd, bd, 0, s>>>(g); break;
-        default: gemm_bf16_stream<EPI_SWIGLU, KC, WF, SV, NW><<<gd, bd, 0, s>>>(g); break;
+    const dim3 gd((unsigned)((int64_t)nm * (stream_col_tiles_nw(g.epi, g.N, NW) / NT))),
+        bd(64 * NW);
+    if constexpr (NT > 1) {
+        // only the expert down product's fp16 rows take several tiles
+        if (g.epi == EPI_F16) gemm_bf16_stream<EPI_F16, KC, WF, SV, NW, NT><<<gd, bd, 0, s>>>(g);
+    } else {
+        switch (g.epi) {
+            case EPI_F16:
+                // grouped expert rows only (never a K-concatenated product)
+                if constexpr (!KC) gemm_bf16_stream<EPI_F16, KC, WF, SV, NW, NT><<<gd, bd, 0, s>>>(g);
+                break;
+            case EPI_F32: gemm_bf16_stream<EPI_F32, KC, WF, SV, NW, NT><<<gd, bd, 0, s>>>(g); break;
+            case EPI_F32_BIAS:
+                gemm_bf16_stream<EPI_F32_BIAS, KC, WF, SV, NW, NT><<<gd, bd, 0, s>>>(g);
+                break;
+            case EPI_OUT: gemm_bf16_stream<EPI_OUT, KC, WF, SV, NW, NT><<<gd, bd, 0, s>>>(g); break;
+            default: gemm_bf16_stream<EPI_SWIGLU, KC, WF, SV, NW, NT><<<gd, bd, 0, s>>>(g); break;
+        }
     }
+}
+
+// Column tiles per workgroup of an MXFP4 expert down product (fp16 rows)
+// whose block exponents come in vectors: with short rows (K = 2048 is 16
+// load units per row) one tile's stream is mostly the filling and draining
+// of the loads in flight, so a workgroup streams several tiles back to back,
+// each a whole number of ring turns (K a multiple of 1024) of whole tiles
+// (N a multiple of 128).  Gate/up rows (K = 7168) gain nothing from it.
+int stream_tiles_per_group(const GemmArgs& g) {
+    if (g.epi != EPI_F16 || g.K % 1024 != 0 || g.N % 128 != 0) return 1;
+    const int ntn = g.N / 128;
+    // 2 tiles (32 units per row at K = 2048) measured faster than 4 or 1
+    return g.K <= 4096 && ntn % 2 == 0 ? 2 : 1;
 }
 
 // Waves per workgroup of a grouped bf16 weight-streaming product: 8, or 16
@@ -675,7 +861,10 @@ hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
         if (g.b_fmt == WF_FP8) {
             launch_stream_rows<false, WF_FP8, false, 8>(g, nm, s);
         } else if (g.b_fmt == WF_MXFP4 && g.K % 512 == 0) {
-            launch_stream_rows<false, WF_MXFP4, true, 8>(g, nm, s);
+            if (stream_tiles_per_group(g) == 2)
+                launch_stream_rows<false, WF_MXFP4, true, 8, 2>(g, nm, s);
+            else
+                launch_stream_rows<false, WF_MXFP4, true, 8>(g, nm, s);
         } else if (g.b_fmt == WF_MXFP4) {
             launch_stream_rows<false, WF_MXFP4, false, 8>(g, nm, s);
         } else if (g.A2) {

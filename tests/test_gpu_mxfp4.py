@@ -44,6 +44,9 @@ def _dequant(inp):
     (300, 16, 2, 1024, 512),   # ~37 rows, K = 1024: several turns of the load ring
     (700, 8, 3, 384, 256),     # ~260 rows: 256-row tiles with a ragged last tile
     (257, 4, 2, 128, 128),     # N smaller than a tile
+    # K a multiple of 1024: workgroups stream 4 column tiles back to back
+    (120, 16, 2, 2048, 1024),  # ~15 rows: packed token rows and 1 block
+    (400, 16, 2, 1024, 1024),  # ~50 rows: 2 and 4 token blocks
 ])
 def test_experts_mxfp4_match_oracle(T, E, k, D, I):
     log(f"experts mxfp4 T={T} E={E} k={k} D={D} I={I}")
