@@ -447,14 +447,22 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     int wu_end = nu;
     uint32_t wsh = 0u, wsh_next = tstep;
     // weight load unit u covers k-steps UNIT*u .. +UNIT-1, 64 bytes of the row
+    // Whole-line (PL) weight loads are non-temporal: each weight line is
+    // read once, and L2 keeps the token rows and exponents the workgroups of
+    // an expert share (MXFP4 gate/up: HBM fetch 1.08x -> 1.03x of its
+    // algorithmic bytes).  The half-line loads of the other forms stay
+    // ordinary: their two halves of a line come from two instructions, and
+    // non-temporal reads of them ran 22% slower.
     auto load_w = [&](int u) __attribute__((always_inline)) {
         if constexpr (NT > 1) {
             u = min(u, NT * nu - 1);
             const uint32_t sh = u >= wu_end ? wsh_next : wsh;
-            return *(const u32x4_t*)(Bb + (wpo[u & 1] + sh + (uint32_t)u * 64));
+            return __builtin_nontemporal_load(
+                (const u32x4_t*)(Bb + (wpo[u & 1] + sh + (uint32_t)u * 64)));
         }
         u = min(u, nu - 1);
-        if constexpr (PL) return *(const u32x4_t*)(Bb + (wpo[u & 1] + (uint32_t)u * 64));
+        if constexpr (PL)
+            return __builtin_nontemporal_load((const u32x4_t*)(Bb + (wpo[u & 1] + (uint32_t)u * 64)));
         const bool seg1 = !KCAT || u < ns1;
         const char* src = seg1 ? Bb + (wo + (uint32_t)u * 64)
                                : B2b + (wo2 + (uint32_t)(u - ns1) * 64);
