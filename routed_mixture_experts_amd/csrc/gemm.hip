@@ -330,7 +330,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big4(GemmArgs g) {
     // of the row); rows of the wave's blocks share their low 5 bits, so one
     // offset per step serves every block (the rest are immediates)
     const int fr = lane & 31, fh = lane >> 5;
-    const int arow0 = 128 * wm + fr;
+    // Rows per compute wave: a tile of at most 128 (64) live rows gives each
+    // wave 64 (32) of them, so that all four SIMDs share its MFMAs instead
+    // of two (the DMA rows do not change)
+    const int tile_rows = tc.row1 - tc.row0;
+    const int wrows = tile_rows <= 64 ? 32 : tile_rows <= 128 ? 64 : 128;
+    const int wrb = wrows * wm;  // the wave's first row in the tile
+    const int arow0 = wrb + fr;
     const int brow0 = (SW ? 64 * wn : 128 * wn) + fr;
     int aoffs[4], boffs[4];
 #pragma unroll
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big4(GemmArgs g) {
         bf16x8_t a[4];
         braw_t b[4];
     };
-    const int nact = min(max((tc.row1 - tc.row0 - wm * 128 + 31) / 32, 0), 4);
+    const int nact = min(max((tile_rows - wrb + 31) / 32, 0), wrows / 32);
 
     auto run = [&](auto NAC) __attribute__((always_inline)) {
         constexpr int NA = decltype(NAC)::value;
@@ -585,7 +591,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big4(GemmArgs g) {
                         ep[(8 * (j >> 2) + 4 * fh + (j & 3)) * ELD + nj * 32 + fr] =
                             FP8 ? acc[mi][nj][j] * sn[nj] : acc[mi][nj][j];
                 asm volatile("" ::: "memory");
-                const int rb = tc.row0 + wm * 128 + mi * 32;
+                const int rb = tc.row0 + wrb + mi * 32;
 #pragma unroll
                 for (int i = 0; i < 32 / RPI; ++i) {
                     const int row = i * RPI + lane / LPR;
