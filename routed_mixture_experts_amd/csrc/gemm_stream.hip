@@ -446,11 +446,11 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     // tile of the MFMAs (shift wsh) or the next one (from unit wu_end on)
     int wu_end = nu;
     uint32_t wsh = 0u, wsh_next = tstep;
-    // weight load unit u covers k-steps UNIT*u .. +UNIT-1, 64 bytes of the row
-    // Whole-line (PL) weight loads are non-temporal: each weight line is
-    // read once, and L2 keeps the token rows and exponents the workgroups of
-    // an expert share (MXFP4 gate/up: HBM fetch 1.08x -> 1.03x of its
-    // algorithmic bytes).  The half-line loads of the other forms stay
+    // Weight load unit u covers k-steps UNIT*u .. +UNIT-1, 64 bytes of the
+    // row.  Whole-line (PL) weight loads are non-temporal: each weight line
+    // is read once, and L2 keeps the token rows that the workgroups of an
+    // expert's column tiles share (MXFP4 gate/up: HBM fetch 1.08x -> 1.03x
+    // of its algorithmic bytes).  The half-line loads of the other forms stay
     // ordinary: their two halves of a line come from two instructions, and
     // non-temporal reads of them ran 22% slower.
     auto load_w = [&](int u) __attribute__((always_inline)) {
