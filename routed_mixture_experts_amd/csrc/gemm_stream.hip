@@ -299,12 +299,17 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
         wrow = min(tc.nt * SRN + wave * 16 + l16, g.N - 1);
     }
     const uint32_t wo = (uint32_t)(wrow * wrow_bytes) + g4 * 16;
-    // MXFP4 with K a multiple of 512 (PL): a load pair covers 128 bytes (256
-    // codes, 8 k-steps) of the wave's 16 rows as whole cache lines: the even
-    // unit of the pair rows 0-7, the odd one rows 8-15, each row read by 8
-    // lanes (lane l: row l % 8, bytes 16 * (l / 8) ..).  wpo[p] is the offset
-    // of unit parity p less p * 64, so that unit u sits at wpo[u & 1] + 64 u.
-    constexpr bool PL = FP4 && SV;
+    // PL (SV: K a multiple of 512 for MXFP4, 128 for FP8, 64 for bf16): a
+    // load pair covers 128 bytes of the wave's 16 rows (2 * UNIT k-steps) as
+    // whole cache lines: the even unit of the pair rows 0-7, the odd one rows
+    // 8-15, each row read by 8 lanes (lane l: row l % 8, bytes 16 * (l / 8)
+    // ..).  wpo[p] is the offset of unit parity p less p * 64, so that unit u
+    // sits at wpo[u & 1] + 64 u.
+    static_assert(!(SV && KCAT), "load pairs: one K segment");
+    constexpr bool PL = SV;
+    // k-steps of a lane's contiguous 16 * W bytes of a row: a lane takes
+    // elements 8 * W * g4 .. of each 32 * W-deep block, 8 per step
+    constexpr int W = PL ? 2 * UNIT : UNIT;
     uint32_t wpo[2] = {0u, 0u};
     if constexpr (PL) {
 #pragma unroll
@@ -332,13 +337,13 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
         for (int tb = 0; tb < NB; ++tb) {
             const int r = min(tc.row0 + tb * 16 + l16, tc.row1 - 1);
             xo[tb] = (uint32_t)(a_row_of(g, r) * g.lda * 2) +
-                     g4 * (PL ? 128 : FP4 ? 64 : FP8 ? 32 : 16);
+                     g4 * (16 * W);
             xo2[tb] = KCAT ? (uint32_t)((int64_t)r * g.lda2 * 2) + g4 * 16 : 0u;
         }
     } else {
         const int r = min(tc.row0 + lane % RB, tc.row1 - 1);
         xo[0] = (uint32_t)(a_row_of(g, r) * g.lda * 2) +
-                ((lane / RB) & 3) * (PL ? 128 : FP4 ? 64 : FP8 ? 32 : 16);
+                ((lane / RB) & 3) * (16 * W);
         xo2[0] = 0u;
     }
 
@@ -377,10 +382,7 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     // byte offset of step st's 8 elements for a lane (the k order of the
     // weight loads; the lane's g4 part is in xo)
     auto step_off = [&](int st) __attribute__((always_inline)) {
-        return PL    ? (uint32_t)(st >> 3) * 512 + (uint32_t)(st & 7) * 16
-               : FP4 ? (uint32_t)(st >> 2) * 256 + (uint32_t)(st & 3) * 16
-               : FP8 ? (uint32_t)(st >> 1) * 128 + (uint32_t)(st & 1) * 16
-                     : (uint32_t)st * 64;
+        return (uint32_t)(st / W) * (64 * W) + (uint32_t)(st % W) * 16;
     };
     // chunk c of column tile xt (tokens do not depend on the tile)
     auto load_x = [&](int c, int xt) __attribute__((always_inline)) {
@@ -450,9 +452,10 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     // row.  Whole-line (PL) weight loads are non-temporal: each weight line
     // is read once, and L2 keeps the token rows that the workgroups of an
     // expert's column tiles share (MXFP4 gate/up: HBM fetch 1.08x -> 1.03x
-    // of its algorithmic bytes).  The half-line loads of the other forms stay
-    // ordinary: their two halves of a line come from two instructions, and
-    // non-temporal reads of them ran 22% slower.
+    // of its algorithmic bytes).  Half-line loads (the 16-wave form, the
+    // second K segment, unaligned K) stay ordinary: the two halves of a line
+    // come from two instructions, and non-temporal reads of them ran 22%
+    // slower.
     auto load_w = [&](int u) __attribute__((always_inline)) {
         if constexpr (NT > 1) {
             u = min(u, NT * nu - 1);
@@ -509,50 +512,82 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     };
     // Load unit j of chunk c, held in ring slot v: its UNIT k-steps against
     // every token block, then the refill of the slot PD units ahead.
+    // A load pair (slots va = v - 1 and v) is used with its odd unit: lanes
+    // l and l ^ 8 hold the two halves of the lines of row l % 8 (even unit)
+    // and of row 8 + l % 8 (odd unit); one row-rotate by 8 and three selects
+    // per dword give lane l (row l % 16) bytes 32 q .. +15 (q = l / 16) of
+    // the row's 128 in a and the next 16 in b.
+    struct Pair {
+        u32x4_t a, b;
+    };
+    auto exchange = [&](int va, int v) __attribute__((always_inline)) {
+        const bool lo = (lane & 8) == 0;
+        Pair p;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t sv = lo ? w[v][d] : w[va][d];
+            const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(
+                0, (int)sv, 0x128 /* row_ror:8 */, 0xf, 0xf, false);
+            p.a[d] = lo ? w[va][d] : t;
+            p.b[d] = lo ? t : w[v][d];
+        }
+        return p;
+    };
     auto unit = [&](int c, const char* xc, int j, int v) __attribute__((always_inline)) {
         if constexpr (PL) {
-            // a load pair is used with its odd unit: lanes l and l ^ 8 hold
-            // the two halves of the lines of row l % 8 (even unit) and of row
-            // 8 + l % 8 (odd unit); one row-rotate by 8 and three selects per
-            // dword give lane l (row l % 16) its 32 codes a (bytes 32 q ..,
-            // q = l / 16, of the row's 128) and the next 32, b.  Step h of
-            // the 8 takes codes 8 h .. of the 64.
             if (j & 1) {
                 const int va = v - 1, ja = j - 1;
-                const bool lo = (lane & 8) == 0;
-                u32x4_t wa, wb;
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint32_t sv = lo ? w[v][d] : w[va][d];
-                    const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(
-                        0, (int)sv, 0x128 /* row_ror:8 */, 0xf, 0xf, false);
-                    wa[d] = lo ? w[va][d] : t;
-                    wb[d] = lo ? t : w[v][d];
-                }
+                const Pair p = exchange(va, v);
                 w[va] = load_w(c * UPC + ja + PD);
                 w[v] = load_w(c * UPC + j + PD);
                 asm volatile("" ::: "memory");
-                constexpr int XG = 4 / NB;
+                if constexpr (FP4) {
+                    // 32 codes in a, 32 in b; step h of the 8 takes codes
+                    // 8 h .. of the 64, with the block scale of a or b
+                    constexpr int XG = 4 / NB;
 #pragma unroll
-                for (int h0 = 0; h0 < 2 * UNIT; h0 += XG) {
-                    u32x4_t xv[XG][NB];
+                    for (int h0 = 0; h0 < 2 * UNIT; h0 += XG) {
+                        u32x4_t xv[XG][NB];
 #pragma unroll
-                    for (int hh = 0; hh < XG; ++hh)
+                        for (int hh = 0; hh < XG; ++hh)
 #pragma unroll
-                        for (int tb = 0; tb < NB; ++tb)
-                            xv[hh][tb] = *(const u32x4_t*)(xc + ((ja * UNIT + h0 + hh) * NB + tb) *
-                                                                   1024);
+                            for (int tb = 0; tb < NB; ++tb)
+                                xv[hh][tb] = *(const u32x4_t*)(xc + ((ja * UNIT + h0 + hh) * NB + tb) *
+                                                                       1024);
 #pragma unroll
-                    for (int hh = 0; hh < XG; ++hh) {
-                        const int h = h0 + hh;
-                        const bf16x8_t wf = __builtin_bit_cast(
-                            bf16x8_t, fp4x8_to_bf16x8(h < 4 ? wa[h] : wb[h - 4],
-                                                      bsc[ja + (h >= 4)]));
+                        for (int hh = 0; hh < XG; ++hh) {
+                            const int h = h0 + hh;
+                            const bf16x8_t wf = __builtin_bit_cast(
+                                bf16x8_t, fp4x8_to_bf16x8(h < 4 ? p.a[h] : p.b[h - 4],
+                                                          bsc[ja + (h >= 4)]));
+#pragma unroll
+                            for (int tb = 0; tb < NB; ++tb) {
+                                f32x4_t& a = NACC == 2 && (hh & 1) ? acc2[tb] : acc[tb];
+                                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    wf, __builtin_bit_cast(bf16x8_t, xv[hh][tb]), a, 0, 0, 0);
+                            }
+                        }
+                    }
+                } else {
+                    // FP8: 16 codes in a, 16 in b, step h of the 4 takes codes
+                    // 8 h ..; bf16: step 0 takes a, step 1 b (steps past K,
+                    // the ragged last chunk, multiply zero weights)
+#pragma unroll
+                    for (int h = 0; h < 2 * UNIT; ++h) {
+                        const int sl = ja * UNIT + h;  // step within the chunk
+                        u32x4_t wf;
+                        if constexpr (FP8) {
+                            const u32x4_t& q = h < 2 ? p.a : p.b;
+                            wf = fp8x8_to_bf16x8(q[2 * (h & 1)], q[2 * (h & 1) + 1]);
+                        } else {
+                            wf = c * CS + sl < ns ? (h == 0 ? p.a : p.b) : u32x4_t{0u, 0u, 0u, 0u};
+                        }
 #pragma unroll
                         for (int tb = 0; tb < NB; ++tb) {
-                            f32x4_t& a = NACC == 2 && (hh & 1) ? acc2[tb] : acc[tb];
-                            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                wf, __builtin_bit_cast(bf16x8_t, xv[hh][tb]), a, 0, 0, 0);
+                            const u32x4_t xv = *(const u32x4_t*)(xc + (sl * NB + tb) * 1024);
+                            acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, wf), __builtin_bit_cast(bf16x8_t, xv),
+                                acc[tb], 0, 0, 0);
                         }
                     }
                 }
@@ -866,7 +901,9 @@ hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
         if (g.b_fmt != WF_BF16 && g.A2) return hipErrorInvalidValue;
         if (g.b_fmt == WF_MXFP4 && g.K % 128 != 0) return hipErrorInvalidValue;
         const bool w16 = g.tiles && stream_waves(g) == 16;
-        if (g.b_fmt == WF_FP8) {
+        if (g.b_fmt == WF_FP8 && g.K % 128 == 0) {
+            launch_stream_rows<false, WF_FP8, true, 8>(g, nm, s);
+        } else if (g.b_fmt == WF_FP8) {
             launch_stream_rows<false, WF_FP8, false, 8>(g, nm, s);
         } else if (g.b_fmt == WF_MXFP4 && g.K % 512 == 0) {
             if (stream_tiles_per_group(g) == 2)
@@ -878,9 +915,11 @@ hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
         } else if (g.A2) {
             launch_stream_rows<true, WF_BF16, false, 8>(g, nm, s);
         } else if (w16) {
+            // (load pairs push the 16-wave form's deeper chunks into spills)
             launch_stream_rows<false, WF_BF16, false, 16>(g, nm, s);
         } else {
-            launch_stream_rows<false, WF_BF16, false, 8>(g, nm, s);
+            if (g.K % 64 == 0) launch_stream_rows<false, WF_BF16, true, 8>(g, nm, s);
+            else launch_stream_rows<false, WF_BF16, false, 8>(g, nm, s);
         }
     }
     return hipGetLastError();

@@ -40,6 +40,9 @@ def _dequant(inp):
     (200, 8, 2, 320, 256),     # ~50 rows: 2 and 4 token blocks, K = 320 ends mid-chunk
     (700, 8, 3, 320, 256),     # ~260 rows: a full and a ragged 256-row tile
     (257, 4, 2, 128, 64),      # N smaller than a tile
+    # K a multiple of 128: whole-line weight load pairs
+    (120, 16, 2, 1024, 512),   # ~15 rows: 1 token block
+    (320, 16, 2, 512, 256),    # ~40 rows: 2 and 4 token blocks
 ])
 def test_experts_fp8_match_oracle(T, E, k, D, I):
     log(f"experts fp8 T={T} E={E} k={k} D={D} I={I}")
