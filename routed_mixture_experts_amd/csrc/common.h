@@ -104,8 +104,6 @@ struct GemmArgs {
     // gate/up activation of EPI_SWIGLU (GluAct) and its parameters
     int32_t act;
     float act_alpha, act_limit;
-    // grouped bf16 weight streaming: 16 asks for 16-wave workgroups
-    int32_t stream_nw;
 };
 
 enum WeightFmt { WF_BF16 = 0, WF_FP8 = 1, WF_MXFP4 = 2 };

@@ -209,16 +209,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_ksplit(GemmArgs g) {
 // why it is staged.  Every vector-memory operation here is a register load,
 // so the compiler's in-order vmcnt bookkeeping stays exact (LDS-DMA loads
 // mixed with register loads make it fall back to draining the counter).
-// NW waves per workgroup (8 or 16), 16 weight rows each: SRN = 16 * NW weight
-// rows per workgroup (SwiGLU: SRN / 2 columns).  Token bytes per k-step are
-// the same for any NW and weight bytes grow with it, so 16 waves halve the
-// share of token loads among the loads in flight; but one 16-wave workgroup
-// fills a CU (it takes a 128 KB token buffer and chunks twice as deep) and
-// its barriers span 16 waves.  With a few rows per group (decode) 8 waves
-// are faster for every format; from about 16 rows per group on, 16 are
-// (bf16; measured alone and beside the 256x256 chain of a large batch).
+// NW = 8 waves per workgroup, 16 weight rows each: SRN = 16 * NW weight rows
+// per workgroup (SwiGLU: SRN / 2 columns), and a 64 KB token buffer.  (A
+// 16-wave form, 256 weight rows per workgroup, streamed groups of 16 or more
+// rows faster while the weights came in half-line loads; with whole-line
+// load pairs 8 waves are faster at every group size measured.)
 template <int NW>
-constexpr int sx_bytes() { return NW == 16 ? 128 * 1024 : 64 * 1024; }
+constexpr int sx_bytes() { return NW * 8 * 1024; }
 
 int stream_col_tiles_nw(int epi, int N, int nw) {
     const int srn = 16 * nw;
@@ -452,10 +449,9 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     // row.  Whole-line (PL) weight loads are non-temporal: each weight line
     // is read once, and L2 keeps the token rows that the workgroups of an
     // expert's column tiles share (MXFP4 gate/up: HBM fetch 1.08x -> 1.03x
-    // of its algorithmic bytes).  Half-line loads (the 16-wave form, the
-    // second K segment, unaligned K) stay ordinary: the two halves of a line
-    // come from two instructions, and non-temporal reads of them ran 22%
-    // slower.
+    // of its algorithmic bytes).  Half-line loads (the second K segment,
+    // unaligned K) stay ordinary: the two halves of a line come from two
+    // instructions, and non-temporal reads of them ran 22% slower.
     auto load_w = [&](int u) __attribute__((always_inline)) {
         if constexpr (NT > 1) {
             u = min(u, NT * nu - 1);
@@ -873,11 +869,6 @@ int stream_tiles_per_group(const GemmArgs& g) {
     return g.K <= 4096 && ntn % 2 == 0 ? 2 : 1;
 }
 
-// Waves per workgroup of a grouped bf16 weight-streaming product: 8, or 16
-// when the caller asks for it (groups averaging at least 16 rows, where 16
-// waves stream faster; slower at decode's few rows per group).
-int stream_waves(const GemmArgs& g) { return g.stream_nw == 16 ? 16 : 8; }
-
 }  // namespace
 
 int stream_row_tile() { return SROWS; }
@@ -900,7 +891,6 @@ hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
     } else {
         if (g.b_fmt != WF_BF16 && g.A2) return hipErrorInvalidValue;
         if (g.b_fmt == WF_MXFP4 && g.K % 128 != 0) return hipErrorInvalidValue;
-        const bool w16 = g.tiles && stream_waves(g) == 16;
         if (g.b_fmt == WF_FP8 && g.K % 128 == 0) {
             launch_stream_rows<false, WF_FP8, true, 8>(g, nm, s);
         } else if (g.b_fmt == WF_FP8) {
@@ -914,12 +904,10 @@ hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
             launch_stream_rows<false, WF_MXFP4, false, 8>(g, nm, s);
         } else if (g.A2) {
             launch_stream_rows<true, WF_BF16, false, 8>(g, nm, s);
-        } else if (w16) {
-            // (load pairs push the 16-wave form's deeper chunks into spills)
-            launch_stream_rows<false, WF_BF16, false, 16>(g, nm, s);
+        } else if (g.K % 64 == 0) {
+            launch_stream_rows<false, WF_BF16, true, 8>(g, nm, s);
         } else {
-            if (g.K % 64 == 0) launch_stream_rows<false, WF_BF16, true, 8>(g, nm, s);
-            else launch_stream_rows<false, WF_BF16, false, 8>(g, nm, s);
+            launch_stream_rows<false, WF_BF16, false, 8>(g, nm, s);
         }
     }
     return hipGetLastError();

@@ -107,10 +107,10 @@ int dense_path(moe_dtype_t dt, int64_t T, int N, int epi) {
 // Where the two chains split in a batch that is not all-small: groups of at
 // most this many rows stream their weights, larger ones take 256-row tiles.  With bf16 weights a group of 33..64 rows runs
 // faster in one 256-row tile (each weight byte read once per tile, one or
-// two 32-row blocks of MFMAs per wave) than in 16-wave streaming
-// workgroups, which spend four token blocks of LDS reads and MFMAs per
-// weight fragment: latent layer (64 rows per group on average) 1.175
-// against 1.232 ms, prefill and grouped layers unchanged.  With FP8 codes
+// two 32-row blocks of MFMAs per wave) than in the streaming kernel, which
+// spends four token blocks of LDS reads and MFMAs per weight fragment:
+// latent layer (64 rows per group on average) 1.175 against 1.232 ms (then
+// with 16-wave streaming workgroups), prefill and grouped layers unchanged.  With FP8 codes
 // the same move costs the prefill layer 10.16 against 9.50 ms (its down
 // product), so quantised weights stream up to 64 rows.
 int split_rows(int fmt) { return fmt == WF_BF16 ? 32 : kStreamMaxRows; }
@@ -325,18 +325,13 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
     if (all_small) {
         // every group is in the small-group list (split into two tiles above
         // kStreamMaxRows rows): no large-group launches, one stream
-        GemmArgs s1 = g1, s2 = g2;
-        s1.stream_nw = s2.stream_nw = P >= kOverlapMinRows * E ? 16 : 8;
-        MOE_TRY(small_groups_gemm(s1, w, E, s, P));
+        MOE_TRY(small_groups_gemm(g1, w, E, s, P));
         MOE_TRY(stage_mark(MOE_STAGE_GEMM1, 1));
         MOE_TRY(stage_mark(MOE_STAGE_GEMM2, 0));
-        MOE_TRY(small_groups_gemm(s2, w, E, s, P));
+        MOE_TRY(small_groups_gemm(g2, w, E, s, P));
         return stage_mark(MOE_STAGE_GEMM2, 1);
     }
     if (!f32 && P >= kOverlapMinRows * E) {
-        // beside the 256-row chain, 16-wave streaming workgroups do better
-        GemmArgs s1 = g1, s2 = g2;
-        s1.stream_nw = s2.stream_nw = 16;
         SideStream* ss = side_ok ? side_stream(s) : nullptr;
         hipStream_t sc = s;  // the small-group chain's stream
         if (ss) {
@@ -344,8 +339,8 @@ moe_status_t run_experts(moe_dtype_t dt, int64_t T, int k, int E, int D, int I, 
             MOE_HIP(hipStreamWaitEvent(ss->s, ss->fork, 0));
             sc = ss->s;
         }
-        moe_status_t st = small_groups_gemm(s1, w, E, sc);
-        if (st == MOE_OK) st = small_groups_gemm(s2, w, E, sc);
+        moe_status_t st = small_groups_gemm(g1, w, E, sc);
+        if (st == MOE_OK) st = small_groups_gemm(g2, w, E, sc);
         // the caller's stream joins the side stream even after an error
         const moe_status_t sj = ss ? hip_status(hipEventRecord(ss->join, ss->s)) : MOE_OK;
         if (st == MOE_OK) st = large_groups_gemm(dt, g1, w, P, E, s);
