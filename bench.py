@@ -107,10 +107,10 @@ def layer_work(w, counts):
 STREAM_KERNEL_SOURCES = ("gemm_stream.hip", "gemm_tiles.h", "common.h")
 
 # The decode gate/up + SwiGLU kernel for each expert weight format
-# (template arguments: epilogue, K-concatenated, weight format, exponent
-# vectors, waves per workgroup, column tiles per workgroup).
-STREAM_GATE_UP = {"dtype": "gemm_bf16_stream<3, false, 0, false, 8, 1>",
-                  "fp8_e4m3": "gemm_bf16_stream<3, false, 1, false, 8, 1>",
+# (template arguments: epilogue, K-concatenated, weight format, whole-line
+# load pairs, waves per workgroup, column tiles per workgroup).
+STREAM_GATE_UP = {"dtype": "gemm_bf16_stream<3, false, 0, true, 8, 1>",
+                  "fp8_e4m3": "gemm_bf16_stream<3, false, 1, true, 8, 1>",
                   "mxfp4": "gemm_bf16_stream<3, false, 2, true, 8, 1>"}
 
 
