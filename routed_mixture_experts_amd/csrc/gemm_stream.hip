@@ -271,9 +271,10 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     static_assert(QF == 1 || (NB == 1 && !KCAT && CS % QF == 0 && TL <= NW), "token packing");
     static_assert(2 * CHUNK <= sx_bytes<NW>() && CS % UNIT == 0 && TU % PD == 0 && XI % NB == 0,
                   "stream tiling");
-    // NT > 1 (MXFP4 with K a multiple of 1024 and N of SRS): NT column tiles
-    // in a row, each a whole number of ring turns
-    static_assert(NT == 1 || (FP4 && SV && RC > 1), "column tiles per workgroup");
+    // NT > 1 (expert down products with fp16 rows and whole-line loads, K a
+    // multiple of 1024 and N of SRS): NT column tiles in a row, each a whole
+    // number of chunks and ring turns
+    static_assert(NT == 1 || (SV && EPI == EPI_F16), "column tiles per workgroup");
     constexpr int SRS = SW ? SRN / 2 : SRN;  // weight rows from one column tile to the next
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -489,7 +490,7 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
     asm volatile("" ::: "memory");
     store_x(0, 0);
     asm volatile("" ::: "memory");
-    load_x(1, 0);  // NT > 1 has nch >= RC >= 2
+    load_x(1, 0);  // NT > 1 has nch >= 2
     asm volatile("" ::: "memory");
     // NT > 1: the place in its tile of the chunk loaded but not stored, and
     // the place xl2 in tile xt2 of the next chunk to load
@@ -576,7 +577,11 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
                             const u32x4_t& q = h < 2 ? p.a : p.b;
                             wf = fp8x8_to_bf16x8(q[2 * (h & 1)], q[2 * (h & 1) + 1]);
                         } else {
-                            wf = c * CS + sl < ns ? (h == 0 ? p.a : p.b) : u32x4_t{0u, 0u, 0u, 0u};
+                            // steps past K (a ragged last chunk) multiply zero
+                            // weights; with NT > 1, c counts the chunks of all
+                            // tiles, and K (a multiple of 1024) leaves none ragged
+                            wf = NT > 1 || c * CS + sl < ns ? (h == 0 ? p.a : p.b)
+                                                            : u32x4_t{0u, 0u, 0u, 0u};
                         }
 #pragma unroll
                         for (int tb = 0; tb < NB; ++tb) {
@@ -726,16 +731,36 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
         }
     };
 
+    // NT > 1: after a tile's last chunk its sums are stored and cleared
+    // while the loads of the next tile are in flight
+    auto next_tile = [&](int& tile) __attribute__((always_inline)) {
+        epilogue(tc.nt + tile);
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) acc[tb] = acc2[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        ++tile;
+        wsh = wsh_next;
+        wsh_next += tstep;
+        wu_end += nu;
+    };
     if constexpr (RC == 1) {
         // one chunk turns the ring of PD loads a whole number of times
-        for (int c = 0; c < nch; ++c) {
+        int tile = 0, tleft = nch;
+        for (int c = 0; c < NT * nch; ++c) {
             const char* xc = chunk_begin(c);
 #pragma unroll
             for (int u = 0; u < UPC; u += PD)
 #pragma unroll
                 for (int v = 0; v < PD; ++v) unit(c, xc, u + v, v);
             chunk_end(c);
+            if constexpr (NT > 1) {
+                if (--tleft == 0 && tile < NT - 1) {
+                    next_tile(tile);
+                    tleft = nch;
+                }
+            }
         }
+        epilogue(tc.nt + tile);
+        return;
     } else {
         // MXFP4: a chunk holds fewer than PD loads; RC chunks turn the ring
         // once (unit c * UPC + j of chunk c = c0 + r sits in slot r * UPC + j).
@@ -781,21 +806,13 @@ __device__ __forceinline__ void stream_rows_tile(const GemmArgs& g, const TileCo
             if constexpr (NT > 1) {
                 tleft -= RC;
                 if (tleft == 0 && tile < NT - 1) {
-                    epilogue(tc.nt + tile);
-#pragma unroll
-                    for (int tb = 0; tb < NB; ++tb) acc[tb] = acc2[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    ++tile;
+                    next_tile(tile);
                     tleft = nch;
-                    wsh = wsh_next;
-                    wsh_next += tstep;
-                    wu_end += nu;
                 }
             }
         }
         epilogue(tc.nt + tile);
-        return;
     }
-    epilogue(tc.nt);
 }
 
 // Grouped tiles here hold one whole group of at most 64 rows; dense products
@@ -856,12 +873,15 @@ void launch_stream_rows(const GemmArgs& g, int nm, hipStream_t s) {
     }
 }
 
-// Column tiles per workgroup of an MXFP4 expert down product (fp16 rows)
-// whose block exponents come in vectors: with short rows (K = 2048 is 16
-// load units per row) one tile's stream is mostly the filling and draining
-// of the loads in flight, so a workgroup streams several tiles back to back,
-// each a whole number of ring turns (K a multiple of 1024) of whole tiles
-// (N a multiple of 128).  Gate/up rows (K = 7168) gain nothing from it.
+// Column tiles per workgroup of a quantised expert down product (fp16 rows)
+// with whole-line weight loads: with short rows (K = 2048 is 16 MXFP4 or 32
+// FP8 load units per row) one tile's stream is mostly the filling and
+// draining of the loads in flight, so a workgroup streams several tiles back
+// to back, each a whole number of chunks and ring turns (K a multiple of
+// 1024) of whole tiles (N a multiple of 128).  Decode down product with
+// paired runs: FP8 0.850-0.853 -> 0.819-0.820 ms; bf16 rows (64 units at
+// K = 2048) 1.55-1.58 -> 1.62 ms, so bf16 keeps one tile.  Gate/up rows
+// (K = 7168) gain nothing from it.
 int stream_tiles_per_group(const GemmArgs& g) {
     if (g.epi != EPI_F16 || g.K % 1024 != 0 || g.N % 128 != 0) return 1;
     const int ntn = g.N / 128;
@@ -892,7 +912,10 @@ hipError_t launch_stream_gemm(const GemmArgs& g, int nm, hipStream_t s) {
         if (g.b_fmt != WF_BF16 && g.A2) return hipErrorInvalidValue;
         if (g.b_fmt == WF_MXFP4 && g.K % 128 != 0) return hipErrorInvalidValue;
         if (g.b_fmt == WF_FP8 && g.K % 128 == 0) {
-            launch_stream_rows<false, WF_FP8, true, 8>(g, nm, s);
+            if (stream_tiles_per_group(g) == 2)
+                launch_stream_rows<false, WF_FP8, true, 8, 2>(g, nm, s);
+            else
+                launch_stream_rows<false, WF_FP8, true, 8>(g, nm, s);
         } else if (g.b_fmt == WF_FP8) {
             launch_stream_rows<false, WF_FP8, false, 8>(g, nm, s);
         } else if (g.b_fmt == WF_MXFP4 && g.K % 512 == 0) {

@@ -35,6 +35,9 @@ def _gpu_permute(ids_np, E):
     (50, 16, 2, 256, 192),      # few rows per expert: streaming path for bf16
     (700, 8, 3, 320, 256),      # many rows per expert: tiled path, ragged tiles
     (257, 4, 2, 128, 64),       # N smaller than a tile
+    # down product with K = I a multiple of 1024: two column tiles per workgroup
+    (120, 16, 2, 512, 1024),    # ~15 rows, some of at most 4 or 8 (packed token loads)
+    (200, 16, 2, 256, 2048),    # ~25 rows: 1 and 2 token blocks
 ])
 def test_experts_match_oracle(dtype, T, E, k, D, I):
     log(f"experts {dtype} T={T} E={E} k={k} D={D} I={I}")
@@ -85,6 +88,11 @@ def test_combine_matches_oracle(out_dtype):
 SMALL = {
     "tiny_fp32": WORKLOADS["tiny_fp32"],
     "decode_like": Workload("decode_like", T=40, H=512, E=48, k=6, I=256, routed_scaling=2.5),
+    # I a multiple of 1024: whole-line weight pairs with no ragged chunk in
+    # the streaming down product (all-small batch; two chains)
+    "decode_like_i1024": Workload("decode_like_i1024", T=64, H=512, E=32, k=4, I=1024,
+                                  routed_scaling=2.5),
+    "two_chains_i1024": Workload("two_chains_i1024", T=400, H=512, E=64, k=4, I=1024),
     "prefill_like": Workload("prefill_like", T=600, H=384, E=12, k=4, I=320),
     "grouped_like": Workload("grouped_like", T=300, H=256, E=32, k=4, I=192,
                              score="sqrtsoftplus", num_groups=8, topk_group=4,
@@ -255,8 +263,7 @@ def test_forward_two_chains_every_tile_shape():
     """A skewed batch large enough for the two-stream split: groups above 32
     rows in 256-row tiles on the caller's stream (one of 33..64 rows with two
     of its 32-row blocks live), groups of at most 32 rows (1 and 2 token
-    blocks of 16 rows) in 16-wave streaming workgroups on the library's
-    stream."""
+    blocks of 16 rows) in streaming workgroups on the library's stream."""
     w = Workload("t", T=640, H=256, E=16, k=4, I=192, routed_scaling=1.5)
     inp = make_inputs(w, DEV)
     lg = random_logits(w.T, w.E, seed=21)

@@ -43,6 +43,10 @@ def _dequant(inp):
     # K a multiple of 128: whole-line weight load pairs
     (120, 16, 2, 1024, 512),   # ~15 rows: 1 token block
     (320, 16, 2, 512, 256),    # ~40 rows: 2 and 4 token blocks
+    # down product with K = I a multiple of 1024: two column tiles per workgroup
+    (120, 16, 2, 512, 1024),   # ~15 rows: 1 token block
+    (200, 16, 2, 256, 1024),   # ~25 rows: 1 and 2 token blocks
+    (320, 16, 2, 256, 2048),   # ~40 rows: 4 token blocks (4 loads in flight)
 ])
 def test_experts_fp8_match_oracle(T, E, k, D, I):
     log(f"experts fp8 T={T} E={E} k={k} D={D} I={I}")
@@ -107,9 +111,16 @@ def test_experts_ex_errors():
     torch.cuda.synchronize()
 
 
-def test_forward_fp8_given_logits_matches_oracle():
-    w = Workload("t", T=96, H=256, E=16, k=4, I=128, routed_scaling=2.5, weights="fp8_e4m3")
-    log("forward fp8 (logits given)")
+@pytest.mark.parametrize("T,H,E,k,I", [
+    (96, 256, 16, 4, 128),
+    # I a multiple of 1024: the streaming down product's workgroups take two
+    # column tiles each (an all-small batch; a batch with both chains)
+    (64, 512, 32, 4, 1024),
+    (400, 512, 64, 4, 1024),
+])
+def test_forward_fp8_given_logits_matches_oracle(T, H, E, k, I):
+    w = Workload("t", T=T, H=H, E=E, k=k, I=I, routed_scaling=2.5, weights="fp8_e4m3")
+    log(f"forward fp8 (logits given) T={T} H={H} E={E} k={k} I={I}")
     inp = make_inputs(w, DEV)
     logits = random_logits(w.T, w.E, seed=5).to(DEV)
     ids = torch.empty((w.T, w.k), dtype=torch.int32, device=DEV)
