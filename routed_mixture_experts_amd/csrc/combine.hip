@@ -71,6 +71,49 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     store4(a.out, a.out_dtype, t * a.D + d, acc);
 }
 
+// fp16 expert rows, D a multiple of 8, 16-byte aligned operands: each
+// thread eight values of one token row, so every row piece is one 16-byte
+// load (a wave reads 1 KB of a row) and a bf16 output one 16-byte store;
+// same sums, same order.  Grid (T, ceil(D / 1024)), 128 threads.
+__global__ __launch_bounds__(128) void combine_f16x8_kernel(CombineArgs a) {
+    __shared__ int rows[kMaxTopK];
+    __shared__ float ws[kMaxTopK];
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (tid < a.k) {
+        rows[tid] = a.pair_to_row[t * a.k + tid];
+        ws[tid] = a.weights[t * a.k + tid];
+    }
+    __syncthreads();
+    const int d = (blockIdx.y * 128 + tid) * 8;
+    if (d >= a.D) return;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < a.k; ++j) {
+        const uint4 h = *(const uint4*)((const uint16_t*)a.y_rows + (int64_t)rows[j] * a.D + d);
+        const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+        const float w = ws[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = fmaf(w, f16_bits_to_f32(hw[i] & 0xffffu), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(w, f16_bits_to_f32(hw[i] >> 16), acc[2 * i + 1]);
+        }
+    }
+    if (a.addend) {
+        const f32x4_t s0 = *(const f32x4_t*)(a.addend + t * a.D + d);
+        const f32x4_t s1 = *(const f32x4_t*)(a.addend + t * a.D + d + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += s0[i], acc[4 + i] += s1[i];
+    }
+    if (a.out_dtype == 0) {
+        *(f32x4_t*)((float*)a.out + t * a.D + d) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+        *(f32x4_t*)((float*)a.out + t * a.D + d + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+    } else {
+        *(uint4*)((bf16_t*)a.out + t * a.D + d) =
+            make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                       pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    }
+}
+
 // One workgroup per token; the row (D <= 1024 * NV) stays in registers.
 template <int NV>
 __global__ __launch_bounds__(256) void combine_norm_kernel(CombineArgs a) {
@@ -129,6 +172,10 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
         else if (nv <= 2) combine_norm_kernel<2><<<grid, block, 0, s>>>(a);
         else if (nv <= 4) combine_norm_kernel<4><<<grid, block, 0, s>>>(a);
         else combine_norm_kernel<8><<<grid, block, 0, s>>>(a);
+    } else if (a.y_f16 && a.D % 8 == 0 &&
+               (((uintptr_t)a.y_rows | (uintptr_t)a.out | (uintptr_t)a.addend) & 15) == 0) {
+        dim3 grid((unsigned)a.T, (unsigned)((a.D + 1023) / 1024)), block(128);
+        combine_f16x8_kernel<<<grid, block, 0, s>>>(a);
     } else {
         dim3 grid((unsigned)a.T, (unsigned)((a.D + 1023) / 1024)), block(256);
         combine_kernel<<<grid, block, 0, s>>>(a);
