@@ -83,6 +83,28 @@ def test_combine_matches_oracle(out_dtype):
     check_float(np64(out), ref, out_dtype == torch.bfloat16, "combine")
 
 
+def test_forward_combine_aligned_and_unaligned_out_agree():
+    """With fp16 expert rows the combine takes 16-byte row loads and stores
+    when its operands are 16-byte aligned, and 8-byte ones otherwise.  Both
+    sum the same values in the same order, so a layer output that starts 8
+    bytes past a 16-byte boundary is bit-identical to an aligned one."""
+    w = Workload("combine_align", T=40, H=512, E=48, k=6, I=256, routed_scaling=2.5)
+    inp = make_inputs(w, DEV)
+    logits = random_logits(w.T, w.E, seed=41).to(DEV)
+    args = (lib_cfg(w), inp["x"], inp["w13"], inp["w2"])
+    kw = dict(router_logits=logits, router_bias=inp["router_bias"],
+              correction_bias=inp["corr_bias"])
+    out_a = moe.moe_forward(*args, **kw)
+    big = torch.empty(w.T * w.H + 8, dtype=torch.bfloat16, device=DEV)
+    out_u = big[4:4 + w.T * w.H].view(w.T, w.H)
+    assert out_a.data_ptr() % 16 == 0 and out_u.data_ptr() % 16 == 8
+    moe.moe_forward(*args, out=out_u, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_u)
+    ref = _oracle_forward(w, inp, logits=np64(logits))
+    check_float(np64(out_u), ref["out"], True, "out, unaligned combine")
+
+
 # ------------------------------------------------------ whole layer, small ---
 
 SMALL = {
